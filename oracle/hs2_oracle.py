@@ -1,0 +1,367 @@
+"""CPU oracle for the HySparse2 Hybrid Block: plain fp64 NumPy, slow on purpose.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the library's
+product path never does, and this module shares no code with it.
+
+What it computes, step by step (the pages describe the method in prose only):
+
+1. Full layer ("Two-Level KV Sharing: ..." on the openai-hub.net page, section
+   "From Hybrid SWA to HySparse2"): causal attention of every query head over
+   the shared K/V, s_h(p, j) = <Q[p, h], K[j, g(h)]> * scale for j <= p, with
+   grouped-query heads g(h) = floor(h * h_kv / h_q) and scale 1/sqrt(d).
+   Outputs O_full and the per-head natural-log LSE.
+2. Importance score: the same page says the full layer also decides which
+   tokens matter. Reading used: S(p, j) = sum over all query heads of the full
+   layer's softmax probability P_h(p, j), one score row per query.
+3. Token-level selection ("Xiaomi Unveils HySparse2", section "Token-Level
+   Selection and Unified Local Access"; bibibi.cc, section "Article"): the 128
+   most recent tokens are always kept; up to 1024 further tokens are chosen
+   from outside that window. Candidates are C_p = {0 <= j <= p - w}; the
+   chosen set is the first min(k, |C_p|) candidates in the order of
+   (-S(p, j), j), i.e. ties go to the lower index.
+4. Block selection, the previous generation's variant (bibibi.cc, section
+   "Article": 64-token groups kept whole): block score = max candidate score
+   in the block, top blocks ordered by (-score, block id), expanded to their
+   candidate tokens.
+5. Sparse layers ("Xiaomi Unveils HySparse2", section "Two-Level KV Sharing",
+   KV Reuse; and section "Token-Level Selection and Unified Local Access"):
+   every sparse layer attends, with one softmax, over window + selected
+   tokens, reading the same K/V and the same index set as the full layer.
+
+Inputs may be float32/float64 arrays or raw bf16 bit patterns (uint16); they
+are widened exactly to fp64.
+"""
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------
+# input widening
+# ----------------------------------------------------------------------------
+def widen(x) -> np.ndarray:
+    """Exact fp64 copy of an fp32/fp64 array or of raw bf16 bits (uint16)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def group_of(h: int, h_q: int, h_kv: int) -> int:
+    """KV head read by query head h: consecutive query heads share one."""
+    return (h * h_kv) // h_q
+
+
+# ----------------------------------------------------------------------------
+# step 1: full causal attention + per-head LSE (dense, small shapes)
+# ----------------------------------------------------------------------------
+def full_layer(q, k, v, scale=None):
+    """Dense causal GQA attention.
+
+    q [B, n_q, h_q, d], k/v [B, n_kv, h_kv, d]; query i is at position
+    n_kv - n_q + i. Returns (O [B, n_q, h_q, d], lse [B, h_q, n_q]) in fp64.
+    """
+    q, k, v = widen(q), widen(k), widen(v)
+    B, nq, hq, d = q.shape
+    nkv, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    pos = np.arange(nq) + (nkv - nq)
+    keep = np.arange(nkv)[None, :] <= pos[:, None]          # causal mask
+    out = np.zeros((B, nq, hq, d))
+    lse = np.zeros((B, hq, nq))
+    for b in range(B):
+        for h in range(hq):
+            g = group_of(h, hq, hkv)
+            s = (q[b, :, h, :] @ k[b, :, g, :].T) * scale
+            s = np.where(keep, s, NEG_INF)
+            m = s.max(axis=1, keepdims=True)
+            l = np.exp(s - m).sum(axis=1, keepdims=True)
+            row_lse = m + np.log(l)
+            p = np.exp(s - row_lse)
+            out[b, :, h, :] = p @ v[b, :, g, :]
+            lse[b, h, :] = row_lse[:, 0]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# step 2: head-summed importance score
+# ----------------------------------------------------------------------------
+def scores(q, k, lse, scale=None):
+    """S[b, i, j] = sum_h exp(s_h(p, j) - lse_h(p)) for j <= p, 0 beyond p.
+
+    `lse` is the full layer's per-head LSE [B, h_q, n_q] (natural log), so the
+    normaliser covers every key j <= p, window keys included.
+    """
+    q, k = widen(q), widen(k)
+    B, nq, hq, d = q.shape
+    nkv, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    pos = np.arange(nq) + (nkv - nq)
+    keep = np.arange(nkv)[None, :] <= pos[:, None]
+    S = np.zeros((B, nq, nkv))
+    for b in range(B):
+        for h in range(hq):
+            g = group_of(h, hq, hkv)
+            s = (q[b, :, h, :] @ k[b, :, g, :].T) * scale
+            p = np.where(keep, np.exp(np.where(keep, s, 0.0) - lse[b, h][:, None]), 0.0)
+            S[b] += p
+    return S
+
+
+# ----------------------------------------------------------------------------
+# step 3/4: selection
+# ----------------------------------------------------------------------------
+def window_of(p: int, window: int) -> np.ndarray:
+    return np.arange(max(0, p - window + 1), p + 1)
+
+
+def select_token(S_row, p: int, top_k: int, window: int) -> np.ndarray:
+    """Ascending index set: top-k candidates by (-S, j) plus the window."""
+    S_row = np.asarray(S_row, dtype=np.float64)
+    n_cand = max(0, p - window + 1)
+    cand = np.arange(n_cand)
+    order = np.lexsort((cand, -S_row[:n_cand]))       # primary -S, then index
+    chosen = np.sort(cand[order[:min(top_k, n_cand)]])
+    return np.concatenate([chosen, window_of(p, window)]).astype(np.int64)
+
+
+def select_block(S_row, p: int, block_size: int, top_blocks: int,
+                 window: int) -> np.ndarray:
+    """Block-level variant: blocks of candidates ranked by their max score."""
+    S_row = np.asarray(S_row, dtype=np.float64)
+    n_cand = max(0, p - window + 1)
+    n_blocks = (n_cand + block_size - 1) // block_size
+    bscore = np.array([S_row[bi * block_size:min(n_cand, (bi + 1) * block_size)].max()
+                       for bi in range(n_blocks)]) if n_blocks else np.zeros(0)
+    bid = np.arange(n_blocks)
+    order = np.lexsort((bid, -bscore))
+    chosen_blocks = np.sort(bid[order[:min(top_blocks, n_blocks)]])
+    toks = [np.arange(bi * block_size, min(n_cand, (bi + 1) * block_size))
+            for bi in chosen_blocks]
+    chosen = np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+    return np.concatenate([chosen, window_of(p, window)]).astype(np.int64)
+
+
+def block_scores(S_row, p: int, block_size: int, window: int) -> np.ndarray:
+    n_cand = max(0, p - window + 1)
+    n_blocks = (n_cand + block_size - 1) // block_size
+    return np.array([np.asarray(S_row[bi * block_size:min(n_cand, (bi + 1) * block_size)],
+                                dtype=np.float64).max() for bi in range(n_blocks)])
+
+
+def kth_candidate_score(S_row, p: int, top_k: int, window: int) -> float:
+    """tau_p: the score of the k-th ranked candidate (the selection threshold)."""
+    n_cand = max(0, p - window + 1)
+    if n_cand == 0:
+        return np.inf
+    vals = np.sort(np.asarray(S_row[:n_cand], dtype=np.float64))[::-1]
+    return float(vals[min(top_k, n_cand) - 1])
+
+
+def pad_index_row(idx_row, width: int) -> np.ndarray:
+    out = np.full(width, -1, dtype=np.int64)
+    out[:len(idx_row)] = idx_row
+    return out
+
+
+# ----------------------------------------------------------------------------
+# step 5: sparse layers over a given index set
+# ----------------------------------------------------------------------------
+def sparse_layer(q_l, k, v, idx, scale=None):
+    """One sparse layer. q_l [B, n_q, h_q, d]; idx [B, n_q, W] (-1 = unused).
+
+    For each query and head: softmax over the listed keys only, then the
+    probability-weighted sum of their values.
+    """
+    q_l, k, v = widen(q_l), widen(k), widen(v)
+    B, nq, hq, d = q_l.shape
+    hkv = k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    idx = np.asarray(idx)
+    out = np.zeros((B, nq, hq, d))
+    for b in range(B):
+        for i in range(nq):
+            sel = idx[b, i][idx[b, i] >= 0]
+            for h in range(hq):
+                g = group_of(h, hq, hkv)
+                s = (k[b, sel, g, :] @ q_l[b, i, h, :]) * scale
+                e = np.exp(s - s.max())
+                out[b, i, h, :] = (e / e.sum()) @ v[b, sel, g, :]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the whole block, dense (small shapes)
+# ----------------------------------------------------------------------------
+def block_forward(q_full, q_sparse, k, v, top_k=1024, window=128,
+                  select="token", block_size=64, top_blocks=16, scale=None):
+    """Full layer -> scores -> selection -> every sparse layer, all in fp64.
+
+    q_sparse [L, B, n_q, h_q, d]. Returns dict(o_full, lse, S, idx, tau,
+    o_sparse) with idx [B, n_q, W] padded with -1, W = top_k + window in token
+    mode and top_blocks * block_size + window in block mode.
+    """
+    o_full, lse = full_layer(q_full, k, v, scale)
+    S = scores(q_full, k, lse, scale)
+    B, nq = S.shape[0], S.shape[1]
+    nkv = np.asarray(k).shape[1]
+    width = top_k + window if select == "token" else top_blocks * block_size + window
+    idx = np.full((B, nq, width), -1, dtype=np.int64)
+    tau = np.zeros((B, nq))
+    for b in range(B):
+        for i in range(nq):
+            p = nkv - nq + i
+            if select == "token":
+                row = select_token(S[b, i], p, top_k, window)
+                tau[b, i] = kth_candidate_score(S[b, i], p, top_k, window)
+            else:
+                row = select_block(S[b, i], p, block_size, top_blocks, window)
+                bs = block_scores(S[b, i], p, block_size, window)
+                tau[b, i] = (np.sort(bs)[::-1][min(top_blocks, len(bs)) - 1]
+                             if len(bs) else np.inf)
+            idx[b, i, :len(row)] = row
+    q_sparse = np.asarray(q_sparse)
+    o_sparse = np.stack([sparse_layer(q_sparse[l], k, v, idx, scale)
+                         for l in range(q_sparse.shape[0])]) if q_sparse.shape[0] else \
+        np.zeros((0,) + o_full.shape)
+    return dict(o_full=o_full, lse=lse, S=S, idx=idx, tau=tau, o_sparse=o_sparse)
+
+
+# ----------------------------------------------------------------------------
+# the same definitions, streamed over K/V chunks for a few sampled query rows
+# (large contexts: the full score matrix never exists)
+# ----------------------------------------------------------------------------
+def block_rows(q_full, q_sparse, k, v, b: int, rows, top_k=1024, window=128,
+               select="token", block_size=64, top_blocks=16, scale=None,
+               chunk=1 << 16):
+    """Oracle for selected query indices `rows` of batch entry `b`.
+
+    Two sweeps over K/V in chunks of `chunk` keys: the first accumulates each
+    row's per-head LSE with the identity lse(A u B) = logaddexp(lse(A), lse(B));
+    the second forms P = exp(s - lse), accumulating O_full and the score row.
+    Returns dict of per-row results (o_full [R, h_q, d], lse [R, h_q],
+    S [R, n_kv] (0 beyond p), idx [R, W], tau [R], o_sparse [L, R, h_q, d]).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    nq, hq, d = q_full.shape[1], q_full.shape[2], q_full.shape[3]
+    nkv, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    pos = rows + (nkv - nq)
+    R = len(rows)
+    Q = widen(q_full[b, rows])                               # [R, hq, d]
+    groups = np.array([group_of(h, hq, hkv) for h in range(hq)])
+    lse = np.full((R, hq), NEG_INF)
+    last = int(pos.max()) + 1 if R else 0
+    for c0 in range(0, last, chunk):
+        c1 = min(last, c0 + chunk)
+        Kc = widen(k[b, c0:c1])                              # [c, hkv, d]
+        keep = np.arange(c0, c1)[None, :] <= pos[:, None]    # [R, c]
+        for h in range(hq):
+            s = (Q[:, h, :] @ Kc[:, groups[h], :].T) * scale  # [R, c]
+            s = np.where(keep, s, NEG_INF)
+            m = s.max(axis=1)
+            ok = np.isfinite(m)
+            part = np.full(R, NEG_INF)
+            part[ok] = m[ok] + np.log(np.exp(s[ok] - m[ok, None]).sum(axis=1))
+            lse[:, h] = np.logaddexp(lse[:, h], part)
+    o_full = np.zeros((R, hq, d))
+    S = np.zeros((R, nkv))
+    for c0 in range(0, last, chunk):
+        c1 = min(last, c0 + chunk)
+        Kc, Vc = widen(k[b, c0:c1]), widen(v[b, c0:c1])
+        keep = np.arange(c0, c1)[None, :] <= pos[:, None]
+        for h in range(hq):
+            s = (Q[:, h, :] @ Kc[:, groups[h], :].T) * scale
+            p = np.where(keep, np.exp(np.where(keep, s, 0.0) - lse[:, h, None]), 0.0)
+            o_full[:, h, :] += p @ Vc[:, groups[h], :]
+            S[:, c0:c1] += p
+    width = top_k + window if select == "token" else top_blocks * block_size + window
+    idx = np.full((R, width), -1, dtype=np.int64)
+    tau = np.zeros(R)
+    for r in range(R):
+        p = int(pos[r])
+        if select == "token":
+            row = select_token(S[r], p, top_k, window)
+            tau[r] = kth_candidate_score(S[r], p, top_k, window)
+        else:
+            row = select_block(S[r], p, block_size, top_blocks, window)
+            bs = block_scores(S[r], p, block_size, window)
+            tau[r] = np.sort(bs)[::-1][min(top_blocks, len(bs)) - 1] if len(bs) else np.inf
+        idx[r, :len(row)] = row
+    L = q_sparse.shape[0]
+    o_sparse = np.zeros((L, R, hq, d))
+    for r in range(R):
+        sel = idx[r][idx[r] >= 0]
+        Ks, Vs = widen(k[b, sel]), widen(v[b, sel])
+        for l in range(L):
+            ql = widen(q_sparse[l, b, rows[r]])
+            for h in range(hq):
+                g = groups[h]
+                s = (Ks[:, g, :] @ ql[h]) * scale
+                e = np.exp(s - s.max())
+                o_sparse[l, r, h] = (e / e.sum()) @ Vs[:, g, :]
+    return dict(o_full=o_full, lse=lse, S=S, idx=idx, tau=tau, o_sparse=o_sparse,
+                pos=pos)
+
+
+def sparse_rows(q_sparse, k, v, b: int, rows, idx_rows, scale=None):
+    """Sparse layers for sampled rows over GIVEN index rows [R, W] (-1 pad)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    L, hq, d = q_sparse.shape[0], q_sparse.shape[3], q_sparse.shape[4]
+    hkv = k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out = np.zeros((L, len(rows), hq, d))
+    for r in range(len(rows)):
+        sel = np.asarray(idx_rows[r])
+        sel = sel[sel >= 0]
+        Ks, Vs = widen(k[b, sel]), widen(v[b, sel])
+        for l in range(L):
+            ql = widen(q_sparse[l, b, rows[r]])
+            for h in range(hq):
+                g = group_of(h, hq, hkv)
+                s = (Ks[:, g, :] @ ql[h]) * scale
+                e = np.exp(s - s.max())
+                out[l, r, h] = (e / e.sum()) @ Vs[:, g, :]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# agreement rule for index sets at near-ties
+# ----------------------------------------------------------------------------
+TIE_REL = 1e-6
+TIE_ABS = 2.0 ** -126
+
+
+def compare_selection(gpu_row, ref_row, S_row, p: int, window: int, tau: float,
+                      rel: float = TIE_REL, block_size: int = 0):
+    """Compare one GPU index row with the oracle's.
+
+    Both rows are -1 padded. They agree when the window parts are equal, the
+    sizes are equal and every index in the symmetric difference is
+    tie-eligible: |S(p, j) - tau| <= max(rel * tau, 2^-126). In block mode
+    (block_size > 0) the rule is applied to the block scores of the blocks
+    that differ. Returns (ok, n_differing, reason).
+    """
+    g = np.asarray(gpu_row)
+    r = np.asarray(ref_row)
+    g = g[g >= 0]
+    r = r[r >= 0]
+    if len(g) != len(r):
+        return False, abs(len(g) - len(r)), "size"
+    if len(g) and (np.any(np.diff(g) <= 0)):
+        return False, 0, "order"
+    w = window_of(p, window)
+    if not np.array_equal(g[len(g) - len(w):], w):
+        return False, 0, "window"
+    diff = np.setxor1d(g, r)
+    if len(diff) == 0:
+        return True, 0, ""
+    band = max(rel * tau, TIE_ABS)
+    if block_size:
+        blocks = np.unique(diff // block_size)
+        bs = block_scores(S_row, p, block_size, window)
+        ok = bool(np.all(np.abs(bs[blocks] - tau) <= band))
+    else:
+        ok = bool(np.all(np.abs(np.asarray(S_row, np.float64)[diff] - tau) <= band))
+    return ok, len(diff), "" if ok else "beyond-tie"

@@ -1,0 +1,300 @@
+"""Pins for the CPU oracle: checks against facts fixed independently of it.
+
+Each test ties the oracle to something other than its own formulas: a library
+attention routine, closed forms worked out by hand, brute-force enumeration,
+invariants that follow from the definition, or special cases that reduce to
+a simpler problem. All run on the CPU.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import hs2_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def sdpa_reference(q, k, v):
+    """torch's fp64 CPU attention with an explicit end-aligned causal mask."""
+    B, nq, hq, d = q.shape
+    nkv = k.shape[1]
+    pos = torch.arange(nq) + (nkv - nq)
+    mask = torch.arange(nkv)[None, :] <= pos[:, None]
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, enable_gqa=True)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+# --------------------------------------------------------------------------
+# full layer: library routine and closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,nq,nkv,hq,hkv,d", [(1, 9, 9, 4, 1, 8), (2, 5, 13, 6, 2, 4),
+                                               (1, 1, 17, 8, 4, 16), (1, 33, 40, 4, 4, 8)])
+def test_full_layer_matches_torch_sdpa(B, nq, nkv, hq, hkv, d):
+    q, k, v = rand((B, nq, hq, d), 1), rand((B, nkv, hkv, d), 2), rand((B, nkv, hkv, d), 3)
+    o, _ = O.full_layer(q, k, v)
+    np.testing.assert_allclose(o, sdpa_reference(q, k, v), rtol=0, atol=1e-12)
+
+
+def test_lse_closed_form_zero_keys():
+    # all logits are 0, so LSE at position p is log(p + 1)
+    B, nq, nkv, hq, hkv, d = 1, 7, 10, 2, 1, 4
+    q = rand((B, nq, hq, d), 4)
+    k = np.zeros((B, nkv, hkv, d))
+    v = rand((B, nkv, hkv, d), 5)
+    _, lse = O.full_layer(q, k, v)
+    pos = np.arange(nq) + nkv - nq
+    np.testing.assert_allclose(lse[0, 0], np.log(pos + 1.0), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 1], np.log(pos + 1.0), rtol=0, atol=1e-14)
+
+
+def test_first_token_output_is_its_value():
+    # position 0 sees only key 0: softmax weight 1
+    q, k, v = rand((1, 6, 4, 8), 6), rand((1, 6, 2, 8), 7), rand((1, 6, 2, 8), 8)
+    o, lse = O.full_layer(q, k, v)
+    for h in range(4):
+        np.testing.assert_allclose(o[0, 0, h], v[0, 0, h // 2], atol=1e-15)
+        assert abs(lse[0, h, 0] - (q[0, 0, h] @ k[0, 0, h // 2]) / math.sqrt(8)) < 1e-14
+
+
+def test_constant_values_give_constant_outputs():
+    B, n, hq, hkv, d = 1, 40, 4, 2, 8
+    q, k = rand((B, n, hq, d), 9), rand((B, n, hkv, d), 10)
+    row = rand((hkv, d), 11)
+    v = np.broadcast_to(row, (B, n, hkv, d)).copy()
+    o, _ = O.full_layer(q, k, v)
+    res = O.block_forward(q, rand((2, B, n, hq, d), 12), k, v, top_k=5, window=3)
+    for h in range(hq):
+        np.testing.assert_allclose(o[0, :, h], np.broadcast_to(row[h // 2], (n, d)), atol=1e-13)
+        np.testing.assert_allclose(res["o_sparse"][:, 0, :, h],
+                                   np.broadcast_to(row[h // 2], (2, n, d)), atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# worked example with rational scores (hand-derived; see the golden file)
+# --------------------------------------------------------------------------
+def test_worked_example_d1():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_d1.json")))
+    a = [Fraction(x) for x in ex["a"]]
+    n = len(a)
+    c = ex["query_exponents"]           # head h has logit c_h * ln(a_j)
+    # inputs: d = 1, scale 1, q = c_h, k_j = ln(a_j) so exp(logit) = a_j ** c_h
+    q = np.array(c, dtype=np.float64).reshape(1, 1, len(c), 1).repeat(n, axis=1)
+    k = np.log(np.array([float(x) for x in a])).reshape(1, n, 1, 1)
+    v = np.array(ex["v"], dtype=np.float64).reshape(1, n, 1, 1)
+    res = O.block_forward(q, q[None], k, v, top_k=ex["top_k"], window=ex["window"],
+                          scale=1.0)
+    for p_str, want in ex["expected"].items():
+        p = int(p_str)
+        # hand-derived scores from the golden file, as exact fractions
+        for j_str, frac in want["S"].items():
+            assert abs(res["S"][0, p, int(j_str)] - float(Fraction(frac))) < 1e-14
+        got = res["idx"][0, p]
+        assert list(got[got >= 0]) == want["idx"]
+        assert abs(res["o_sparse"][0, 0, p, 0, 0] - float(Fraction(want["o_sparse_h0"]))) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# selection: brute force, rank counting, ties
+# --------------------------------------------------------------------------
+def brute_force_topk(S, k):
+    """All k-subsets; keep the best score multiset, then the smallest indices."""
+    n = len(S)
+    best = None
+    for sub in itertools.combinations(range(n), min(k, n)):
+        key = (tuple(sorted((-S[i] for i in sub))), sub)
+        if best is None or key < best:
+            best = key
+    return list(best[1])
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_token_topk_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n_cand = int(rng.integers(0, 12))
+    k = int(rng.integers(1, 5))
+    w = int(rng.integers(1, 4))
+    p = n_cand + w - 1
+    # small integer scores make ties frequent
+    S = rng.integers(0, 4, size=p + 1).astype(np.float64) / 4
+    got = O.select_token(S, p, k, w)
+    want = brute_force_topk(S[:n_cand], k) + list(range(max(0, p - w + 1), p + 1))
+    assert list(got) == want
+    # rank-count characterisation
+    cand = np.arange(n_cand)
+    for j in cand:
+        rank = np.sum(S[:n_cand] > S[j]) + np.sum((S[:n_cand] == S[j]) & (cand < j))
+        assert (j in got) == (rank < k)
+
+
+def test_exact_ties_take_lowest_indices():
+    # K = 0: every logit equal, every score equal -> the first k candidates
+    B, n, hq, hkv, d = 1, 30, 4, 1, 8
+    q, v = rand((B, n, hq, d), 13), rand((B, n, hkv, d), 14)
+    k = np.zeros((B, n, hkv, d))
+    res = O.block_forward(q, np.zeros((0, B, n, hq, d)), k, v, top_k=5, window=4)
+    for p in range(n):
+        row = res["idx"][0, p]
+        row = list(row[row >= 0])
+        n_cand = max(0, p - 3)
+        assert row == list(range(min(5, n_cand))) + list(range(max(0, p - 3), p + 1))
+
+
+def test_single_head_selection_is_topk_of_dot_products():
+    # one head: P is increasing in the logit, so the score order is the order
+    # of the raw dot products and no exp/LSE is involved
+    B, n, d, k, w = 1, 200, 16, 20, 8
+    q, kk, v = rand((B, n, 1, d), 15), rand((B, n, 1, d), 16), rand((B, n, 1, d), 17)
+    res = O.block_forward(q, np.zeros((0, B, n, 1, d)), kk, v, top_k=k, window=w)
+    for p in range(n):
+        n_cand = max(0, p - w + 1)
+        dots = kk[0, :n_cand, 0] @ q[0, p, 0]
+        order = sorted(range(n_cand), key=lambda j: (-dots[j], j))[:k]
+        want = sorted(order) + list(range(max(0, p - w + 1), p + 1))
+        row = res["idx"][0, p]
+        assert list(row[row >= 0]) == want
+
+
+def test_scores_sum_to_head_count():
+    B, n, hq, hkv, d = 2, 50, 8, 2, 8
+    q, k, v = rand((B, n, hq, d), 18), rand((B, n, hkv, d), 19), rand((B, n, hkv, d), 20)
+    _, lse = O.full_layer(q, k, v)
+    S = O.scores(q, k, lse)
+    np.testing.assert_allclose(S.sum(axis=2), hq, rtol=0, atol=1e-12)
+    assert np.all(S >= 0)
+    assert np.all(S[:, np.arange(n)[:, None] < np.arange(n)[None, :]] == 0)
+
+
+def test_index_set_invariants():
+    B, nq, nkv, hq, hkv, d, k, w = 1, 60, 90, 4, 2, 8, 10, 6
+    q, kk, v = rand((B, nq, hq, d), 21), rand((B, nkv, hkv, d), 22), rand((B, nkv, hkv, d), 23)
+    res = O.block_forward(q, np.zeros((0, B, nq, hq, d)), kk, v, top_k=k, window=w)
+    for i in range(nq):
+        p = nkv - nq + i
+        row = res["idx"][0, i]
+        valid = row[row >= 0]
+        assert len(valid) == min(p + 1, k + w)
+        assert np.all(np.diff(valid) > 0)
+        assert valid[-1] == p and np.all(valid <= p)
+        assert set(range(max(0, p - w + 1), p + 1)) <= set(valid.tolist())
+        assert np.all(row[len(valid):] == -1)
+
+
+# --------------------------------------------------------------------------
+# dense reduction: when k + w covers the whole prefix, sparse == dense
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (6, 3)])
+def test_dense_reduction(hq, hkv):
+    B, n, d = 1, 24, 8
+    q, k, v = rand((B, n, hq, d), 24), rand((B, n, hkv, d), 25), rand((B, n, hkv, d), 26)
+    qs = rand((2, B, n, hq, d), 27)
+    res = O.block_forward(q, qs, k, v, top_k=16, window=8)
+    for i in range(n):
+        row = res["idx"][0, i]
+        assert list(row[row >= 0]) == list(range(i + 1))
+    for layer in range(2):
+        np.testing.assert_allclose(res["o_sparse"][layer], sdpa_reference(qs[layer], k, v),
+                                   rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# block selection
+# --------------------------------------------------------------------------
+def test_block_mode_with_unit_blocks_is_token_mode():
+    B, n, hq, hkv, d = 1, 70, 4, 2, 8
+    q, k, v = rand((B, n, hq, d), 28), rand((B, n, hkv, d), 29), rand((B, n, hkv, d), 30)
+    qs = rand((1, B, n, hq, d), 31)
+    t = O.block_forward(q, qs, k, v, top_k=9, window=5)
+    b = O.block_forward(q, qs, k, v, top_k=9, window=5, select="block",
+                        block_size=1, top_blocks=9)
+    np.testing.assert_array_equal(t["idx"], b["idx"])
+    np.testing.assert_allclose(t["o_sparse"], b["o_sparse"], atol=0)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_block_selection_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    bsz = int(rng.integers(1, 5))
+    tb = int(rng.integers(1, 4))
+    w = int(rng.integers(1, 4))
+    n_cand = int(rng.integers(0, 14))
+    p = n_cand + w - 1
+    S = rng.integers(0, 5, size=p + 1).astype(np.float64)
+    got = O.select_block(S, p, bsz, tb, w)
+    n_blocks = (n_cand + bsz - 1) // bsz
+    bmax = [max(S[b * bsz:min(n_cand, (b + 1) * bsz)]) for b in range(n_blocks)]
+    chosen = brute_force_topk(np.array(bmax), tb) if n_blocks else []
+    toks = [j for b in chosen for j in range(b * bsz, min(n_cand, (b + 1) * bsz))]
+    assert list(got) == toks + list(range(max(0, p - w + 1), p + 1))
+
+
+# --------------------------------------------------------------------------
+# streamed sampled-row oracle agrees with the dense one
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("select", ["token", "block"])
+def test_streamed_rows_match_dense(select):
+    B, nq, nkv, hq, hkv, d = 2, 20, 75, 4, 2, 8
+    q, k, v = rand((B, nq, hq, d), 32), rand((B, nkv, hkv, d), 33), rand((B, nkv, hkv, d), 34)
+    qs = rand((2, B, nq, hq, d), 35)
+    kw = dict(top_k=12, window=5, select=select, block_size=4, top_blocks=3)
+    dense = O.block_forward(q, qs, k, v, **kw)
+    rows = [0, 3, 19]
+    for b in range(B):
+        s = O.block_rows(q, qs, k, v, b, rows, chunk=16, **kw)
+        np.testing.assert_allclose(s["lse"], dense["lse"][b][:, rows].T, atol=1e-12)
+        np.testing.assert_allclose(s["o_full"], dense["o_full"][b, rows], atol=1e-12)
+        np.testing.assert_allclose(s["S"], dense["S"][b, rows], atol=1e-13)
+        np.testing.assert_array_equal(s["idx"], dense["idx"][b, rows])
+        np.testing.assert_allclose(s["o_sparse"], dense["o_sparse"][:, b, rows], atol=1e-12)
+
+
+def test_bf16_bits_widen_exactly():
+    vals = np.array([1.0, -2.5, 0.1015625, 2.0 ** 100, 0.0], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(O.widen(bits), vals.astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# near-tie agreement rule
+# --------------------------------------------------------------------------
+def test_compare_selection_rule():
+    p, w, k = 9, 2, 3
+    S = np.array([0.5, 0.3, 0.3 * (1 - 4e-7), 0.1, 0.3 * (1 - 5e-6), 0.05, 0.0, 0.0, 0.0, 0.0])
+    ref = O.select_token(S, p, k, w)
+    tau = O.kth_candidate_score(S, p, k, w)
+    assert list(ref) == [0, 1, 2, 8, 9]
+    ok, n, _ = O.compare_selection(ref, ref, S, p, w, tau)
+    assert ok and n == 0
+    swapped_tie = [0, 1, 4, 8, 9]      # index 4 is 5e-6 below tau: not a tie
+    ok, _, why = O.compare_selection(swapped_tie, ref, S, p, w, tau)
+    assert not ok and why == "beyond-tie"
+    S2 = S.copy()
+    S2[4] = 0.3 * (1 - 9e-7)
+    ref2 = O.select_token(S2, p, k, w)
+    ok, n, _ = O.compare_selection([0, 1, 4, 8, 9], ref2, S2, p, w,
+                                   O.kth_candidate_score(S2, p, k, w))
+    assert ok and n == 2
+    ok, _, why = O.compare_selection([0, 1, 2, 7, 9], ref, S, p, w, tau)
+    assert not ok and why == "window"
+
+
+def test_pages_constants():
+    c = json.load(open(os.path.join(GOLDEN, "pages_constants.json")))
+    from synth import CONFIGS
+    for w in CONFIGS.values():
+        assert w.top_k == c["top_k_global_tokens"]["value"]
+        assert w.window == c["recent_window_tokens"]["value"]
+        assert w.block_size == c["previous_generation_block_tokens"]["value"]
