@@ -1,0 +1,168 @@
+/*
+ * hs2.h - C ABI of the HySparse2 Hybrid Block engine for AMD MI355X (gfx950).
+ *
+ * The Hybrid Block (HySparse2 pages: "Xiaomi Unveils HySparse2 for Faster
+ * Long-Context AI", section "Two-Level KV Sharing"; openai-hub.net, section
+ * "From Hybrid SWA to HySparse2") is one full-attention layer followed by
+ * sparse-attention layers. The full layer produces the KV cache and decides
+ * which tokens matter; the sparse layers reuse both (KV Reuse). Each sparse
+ * layer attends, in one softmax, over the 128 most recent tokens plus 1024
+ * tokens selected from outside that window (same page, section "Token-Level
+ * Selection and Unified Local Access").
+ *
+ * Definitions used by every entry point (d = head_dim, G = h_q / h_kv):
+ *   position of query i of sequence b:  p = n_kv - n_q + i
+ *   KV head read by query head h:       g(h) = h / G  (integer division)
+ *   logit:  s_h(p, j) = <Q[b,i,h,:], K[b,j,g(h),:]> * softmax_scale, j <= p
+ *   full layer: causal softmax over j <= p; O = sum_j P_h(p, j) V[b,j,g(h),:]
+ *   score:  S(p, j) = sum over all h_q heads of P_h(p, j)
+ *   token selection: candidates j <= p - window; the min(top_k, #candidates)
+ *       best by (-S, j) (ties go to the lower index), plus the window
+ *       max(0, p - window + 1) .. p
+ *   block selection (the previous generation's 64-token groups, bibibi.cc
+ *       article, section "Article"): candidate blocks j / block_size scored by
+ *       their max candidate score, best top_blocks by (-score, block), expanded
+ *       to their candidate tokens, plus the window
+ *   sparse layer l: softmax over the index set of query i, same K and V.
+ *
+ * Memory: every tensor pointer is a DEVICE pointer owned by the caller, in a
+ * contiguous row-major layout, 16-byte aligned:
+ *   Q, O           [batch, n_q, h_q, head_dim]        (dtype)
+ *   K, V           [batch, n_kv, h_kv, head_dim]      (dtype), read only
+ *   Q/O of layers  [n_layers, batch, n_q, h_q, head_dim]
+ *   idx            [batch, n_q, hs2_index_width(p)]   int32; each row is the
+ *                  strictly ascending index set followed by -1 padding
+ *   lse            [batch, h_q, n_q] float, natural log (may be NULL)
+ * The library allocates no device memory and keeps no state between calls.
+ * Scratch space is the caller's workspace (size from hs2_workspace_size);
+ * a smaller workspace only means more query chunks.
+ *
+ * Errors: arguments are checked on the host before anything is launched; a
+ * non-OK status means nothing was written. HS2_ERR_DEVICE reports a HIP
+ * launch failure; hs2_last_error() then holds the HIP error text (thread
+ * local). No C++ exception crosses this interface. Non-finite inputs give
+ * undefined results.
+ *
+ * Streams: every call is asynchronous on `stream` (a hipStream_t, NULL = the
+ * default stream); results are valid once the stream has synchronised. Calls
+ * are reentrant when they use distinct workspaces.
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS2_ABI_VERSION 1
+
+typedef enum {
+  HS2_OK = 0,
+  HS2_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  HS2_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes              */
+  HS2_ERR_UNSUPPORTED = 3,  /* valid but not implemented (dtype, head_dim ...) */
+  HS2_ERR_WORKSPACE = 4,    /* workspace smaller than the minimum              */
+  HS2_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                */
+  HS2_ERR_DEVICE = 6        /* a HIP call failed                               */
+} hs2_status;
+
+typedef enum { HS2_FP32 = 0, HS2_BF16 = 1 } hs2_dtype;
+typedef enum { HS2_SELECT_TOKEN = 0, HS2_SELECT_BLOCK = 1 } hs2_select;
+
+/* One problem description shared by every call on the same block. */
+typedef struct {
+  int32_t abi_version;     /* must equal HS2_ABI_VERSION                       */
+  int32_t dtype;           /* hs2_dtype of Q, K, V and every output tensor     */
+  int32_t batch;           /* independent sequences, each with its own K/V     */
+  int32_t n_q;             /* queries per sequence (1 = decode)                */
+  int32_t n_kv;            /* keys per sequence; n_q <= n_kv                   */
+  int32_t h_q, h_kv;       /* query heads and KV heads; h_q % h_kv == 0        */
+  int32_t head_dim;        /* 64 or 128                                        */
+  int32_t top_k;           /* selected tokens outside the window (1024)       */
+  int32_t window;          /* always-kept recent tokens (128), >= 1            */
+  int32_t select;          /* hs2_select                                       */
+  int32_t block_size;      /* block mode only (64)                             */
+  int32_t top_blocks;      /* block mode only (16)                             */
+  float softmax_scale;     /* 1/sqrt(head_dim)                                 */
+} hs2_problem;
+
+/* Optional test hook: export the score rows of a few queries.
+ * rows[r] is a flattened query (b * n_q + i); scores_out is a DEVICE buffer
+ * [n_rows, n_kv] float that receives S(p, j) for the candidate keys
+ * j <= p - window and -1 everywhere else. */
+typedef struct {
+  const int32_t* rows;     /* HOST array of n_rows flattened query indices     */
+  int32_t n_rows;
+  float* scores_out;       /* DEVICE [n_rows, n_kv]                            */
+} hs2_debug;
+
+/* ABI version compiled into the library. */
+int32_t hs2_abi_version(void);
+
+/* Width of one idx row: top_k + window (token mode) or
+ * top_blocks * block_size + window (block mode); -1 if `p` is invalid. */
+int32_t hs2_index_width(const hs2_problem* p);
+
+/* Workspace needed by hs2_full_attn_select / hs2_block_forward.
+ * *min_bytes lets the call run (one query row per chunk); *preferred_bytes
+ * is what the library would use for the fastest schedule. Host only. */
+hs2_status hs2_workspace_size(const hs2_problem* p, size_t* min_bytes,
+                              size_t* preferred_bytes);
+
+/* The full layer of the block: causal GQA attention (o), the per-head
+ * log-sum-exp (lse, may be NULL), the head-summed scores and the selection
+ * (idx). `dbg` may be NULL. */
+hs2_status hs2_full_attn_select(const hs2_problem* p, const void* q,
+                                const void* k, const void* v, void* o,
+                                int32_t* idx, float* lse, const hs2_debug* dbg,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* n_layers sparse layers over a given index set (KV Reuse): layer l reads
+ * q_layers[l] and writes o_layers[l]; every layer reads the same K, V and
+ * idx. idx rows must be ascending, -1 padded, entries <= p. */
+hs2_status hs2_sparse_attn(const hs2_problem* p, int32_t n_layers,
+                           const void* q_layers, const void* k, const void* v,
+                           const int32_t* idx, void* o_layers, void* stream);
+
+/* The whole Hybrid Block: hs2_full_attn_select followed by n_sparse_layers
+ * sparse layers that reuse its K/V and idx. */
+hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers,
+                             const void* q_full, const void* q_sparse,
+                             const void* k, const void* v, void* o_full,
+                             void* o_sparse, int32_t* idx, float* lse,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Optional pass timing, a profiling aid. While enabled, every call records
+ * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
+ * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT
+ * (selection) and HS2_PASS_SPARSE (sparse layers). hs2_profile_enable(1)
+ * starts a fresh record and (0) stops recording. hs2_profile_read waits for
+ * the recorded events, then writes the summed milliseconds and the number of
+ * timed launches of each pass (arrays of HS2_N_PASSES) and clears the record.
+ * Process-wide state; not meant for concurrent profiled calls. */
+typedef enum {
+  HS2_PASS_FULL = 0,
+  HS2_PASS_SCORE = 1,
+  HS2_PASS_SELECT = 2,
+  HS2_PASS_SPARSE = 3,
+  HS2_N_PASSES = 4
+} hs2_pass;
+hs2_status hs2_profile_enable(int32_t on);
+hs2_status hs2_profile_read(double* ms, int64_t* launches);
+
+/* Static text for a status code. */
+const char* hs2_status_string(hs2_status s);
+
+/* Detail for the last non-OK status returned on this thread ("" if none). */
+const char* hs2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H */

@@ -255,27 +255,29 @@ def block_rows(q_full, q_sparse, k, v, b: int, rows, top_k=1024, window=128,
     last = int(pos.max()) + 1 if R else 0
     for c0 in range(0, last, chunk):
         c1 = min(last, c0 + chunk)
-        Kc = widen(k[b, c0:c1])                              # [c, hkv, d]
         keep = np.arange(c0, c1)[None, :] <= pos[:, None]    # [R, c]
-        for h in range(hq):
-            s = (Q[:, h, :] @ Kc[:, groups[h], :].T) * scale  # [R, c]
-            s = np.where(keep, s, NEG_INF)
-            m = s.max(axis=1)
-            ok = np.isfinite(m)
-            part = np.full(R, NEG_INF)
-            part[ok] = m[ok] + np.log(np.exp(s[ok] - m[ok, None]).sum(axis=1))
-            lse[:, h] = np.logaddexp(lse[:, h], part)
+        for g in range(hkv):
+            Kg = widen(k[b, c0:c1, g])                       # [c, d]
+            for h in np.nonzero(groups == g)[0]:
+                s = (Q[:, h, :] @ Kg.T) * scale              # [R, c]
+                s = np.where(keep, s, NEG_INF)
+                m = s.max(axis=1)
+                ok = np.isfinite(m)
+                part = np.full(R, NEG_INF)
+                part[ok] = m[ok] + np.log(np.exp(s[ok] - m[ok, None]).sum(axis=1))
+                lse[:, h] = np.logaddexp(lse[:, h], part)
     o_full = np.zeros((R, hq, d))
     S = np.zeros((R, nkv))
     for c0 in range(0, last, chunk):
         c1 = min(last, c0 + chunk)
-        Kc, Vc = widen(k[b, c0:c1]), widen(v[b, c0:c1])
         keep = np.arange(c0, c1)[None, :] <= pos[:, None]
-        for h in range(hq):
-            s = (Q[:, h, :] @ Kc[:, groups[h], :].T) * scale
-            p = np.where(keep, np.exp(np.where(keep, s, 0.0) - lse[:, h, None]), 0.0)
-            o_full[:, h, :] += p @ Vc[:, groups[h], :]
-            S[:, c0:c1] += p
+        for g in range(hkv):
+            Kg, Vg = widen(k[b, c0:c1, g]), widen(v[b, c0:c1, g])
+            for h in np.nonzero(groups == g)[0]:
+                s = (Q[:, h, :] @ Kg.T) * scale
+                p = np.where(keep, np.exp(np.where(keep, s, 0.0) - lse[:, h, None]), 0.0)
+                o_full[:, h, :] += p @ Vg
+                S[:, c0:c1] += p
     width = top_k + window if select == "token" else top_blocks * block_size + window
     idx = np.full((R, width), -1, dtype=np.int64)
     tau = np.zeros(R)

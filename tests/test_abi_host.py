@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+entry point, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from token_level_sparse_pass_amd import hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs2.h")
+
+if not os.path.exists(hs2.LIB_PATH):
+    pytest.skip("libhs2.so not built", allow_module_level=True)
+
+FAKE = 0x10000          # aligned, non-null: never dereferenced by failing calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = hs2.load()
+    names = declared_functions()
+    assert {"hs2_full_attn_select", "hs2_sparse_attn", "hs2_block_forward",
+            "hs2_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    lib = hs2.load()
+    assert lib.hs2_abi_version() == hs2.ABI_VERSION
+    for s, text in hs2.STATUS.items():
+        assert lib.hs2_status_string(s).decode() == text
+
+
+def base_problem(**kw):
+    args = dict(dtype=hs2.BF16, batch=1, n_q=256, n_kv=1024, h_q=8, h_kv=2, head_dim=128,
+                top_k=64, window=16)
+    args.update(kw)
+    return hs2.problem(**args)
+
+
+def full_call(p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, idx=FAKE, lse=None, ws=FAKE, ws_bytes=None):
+    lib = hs2.load()
+    if ws_bytes is None:
+        ws_bytes = hs2.workspace_size(p)[1]
+    vp = ctypes.c_void_p
+    return lib.hs2_full_attn_select(ctypes.byref(p), vp(q), vp(k), vp(v), vp(o), vp(idx),
+                                    vp(lse), None, vp(ws), ws_bytes, None)
+
+
+def test_index_width():
+    assert hs2.index_width(base_problem()) == 64 + 16
+    assert hs2.index_width(base_problem(select="block", block_size=8, top_blocks=4)) == 32 + 16
+    assert hs2.index_width(base_problem(top_k=1024, window=128)) == 1152
+
+
+def test_workspace_sizes():
+    p = base_problem()
+    mn, pref = hs2.workspace_size(p)
+    stats = 2 * 1 * 8 * 256 * 4
+    row = (1024 - 16 + 255) // 256 * 256 * 4
+    assert mn >= stats + row
+    assert pref >= mn
+    assert pref >= stats + 256 * row         # one chunk holds every query row
+    # decode needs its logits and partials
+    d = base_problem(n_q=1, batch=4)
+    mn_d, pref_d = hs2.workspace_size(d)
+    assert mn_d == pref_d and mn_d >= 4 * 8 * 1024 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 3), (dict(h_q=6, h_kv=4), 2), (dict(n_q=2048), 2),
+    (dict(batch=0), 2), (dict(window=0), 2), (dict(top_k=5000), 3),
+    (dict(select="block", top_blocks=300), 3), (dict(dtype=7), 3),
+    (dict(softmax_scale=0.0), 2), (dict(h_q=128, h_kv=1), 3),
+])
+def test_problem_rejected(kw, status):
+    p = base_problem(**kw)
+    assert full_call(p, ws_bytes=1 << 30) == status
+    assert hs2.load().hs2_last_error().decode() != ""
+
+
+def test_abi_version_mismatch():
+    p = base_problem()
+    p.abi_version = 99
+    assert full_call(p, ws_bytes=1 << 30) == 3
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "idx", "ws"])
+def test_null_pointers(name):
+    p = base_problem()
+    assert full_call(p, **{name: None}) == 1
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "idx", "ws", "lse"])
+def test_misaligned_pointers(name):
+    p = base_problem()
+    assert full_call(p, **{name: FAKE + 4}) == 5
+
+
+def test_workspace_too_small():
+    p = base_problem()
+    mn, _ = hs2.workspace_size(p)
+    assert full_call(p, ws_bytes=mn - 1) == 4
+    assert "workspace" in hs2.load().hs2_last_error().decode()
+
+
+def test_sparse_rejections():
+    lib = hs2.load()
+    p = base_problem()
+    vp = ctypes.c_void_p
+    assert lib.hs2_sparse_attn(ctypes.byref(p), -1, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                               vp(FAKE), None) == 2
+    assert lib.hs2_sparse_attn(ctypes.byref(p), 2, None, vp(FAKE), vp(FAKE), vp(FAKE),
+                               vp(FAKE), None) == 1
+    assert lib.hs2_sparse_attn(ctypes.byref(p), 2, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE + 8),
+                               vp(FAKE), None) == 5
+    # zero layers is a valid no-op that touches nothing
+    assert lib.hs2_sparse_attn(ctypes.byref(p), 0, None, None, None, None, None, None) == 0
+
+
+def test_block_forward_rejections():
+    lib = hs2.load()
+    p = base_problem()
+    vp = ctypes.c_void_p
+    mn, _ = hs2.workspace_size(p)
+    args = [vp(FAKE)] * 8
+    assert lib.hs2_block_forward(ctypes.byref(p), 3, *args[:6], vp(FAKE), None, vp(FAKE),
+                                 mn - 16, None) == 4
+    assert lib.hs2_block_forward(None, 3, *args[:6], vp(FAKE), None, vp(FAKE), mn, None) == 1
+
+
+def test_debug_rows_validated():
+    lib = hs2.load()
+    p = base_problem()
+    rows = (ctypes.c_int32 * 1)(256)             # out of range: batch * n_q = 256
+    dbg = hs2.Debug(rows, 1, FAKE)
+    vp = ctypes.c_void_p
+    st = lib.hs2_full_attn_select(ctypes.byref(p), *([vp(FAKE)] * 5), None, ctypes.byref(dbg),
+                                  vp(FAKE), hs2.workspace_size(p)[1], None)
+    assert st == 2

@@ -1,0 +1,331 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Index sets must match exactly except at near-ties (|S - tau| <= 1e-6 tau);
+outputs must be within 2e-2 (bf16) or 1e-5 (fp32) max-abs of the oracle.
+Where a GPU index row differs at a tie, its outputs are compared with the
+oracle evaluated on the GPU's own index row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hs2_oracle as O
+from synth import CONFIGS, Workload, make_inputs, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-5}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name, dtype, B, nq, nkv, hq, hkv, d, top_k, window, L=2, structure="none", cid=0,
+          **extra):
+    return Workload(cid, name, dtype, batch=B, n_q=nq, n_kv=nkv, h_q=hq, h_kv=hkv, d=d,
+                    top_k=top_k, window=window, n_sparse=L, structure=structure, extra=extra)
+
+
+def host(x):
+    return to_host(x) if isinstance(x, torch.Tensor) else x
+
+
+def as_np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def compare_index_rows(gpu_idx, S_rows, pos, ref_idx, tau, window, block_size=0):
+    """Returns list of row numbers that differ at ties; asserts every other row equal."""
+    tied = []
+    for r in range(len(pos)):
+        ok, nd, why = O.compare_selection(gpu_idx[r], ref_idx[r], S_rows[r], int(pos[r]), window,
+                                          float(tau[r]), block_size=block_size)
+        assert ok, f"row {r} (p={pos[r]}): {why}, {nd} differing indices"
+        if nd:
+            tied.append(r)
+    return tied
+
+
+def check_invariants(idx, w: Workload, block_mode=False):
+    """Every GPU row: size, strictly ascending, entries <= p, window present."""
+    B, nq, W = idx.shape
+    pos = torch.arange(nq, device=idx.device) + (w.n_kv - w.n_q)
+    valid = idx >= 0
+    n = valid.sum(-1)
+    want = torch.clamp(pos + 1, max=w.top_k + w.window)
+    if block_mode:
+        assert bool((n <= want[None]).all())
+    else:
+        assert bool((n == want[None]).all()), "index set sizes"
+    # valid entries form a prefix
+    assert bool((valid[..., 1:] <= valid[..., :-1]).all())
+    big = torch.where(valid, idx, torch.full_like(idx, 1 << 30))
+    asc = (big[..., 1:] > big[..., :-1]) | ~valid[..., 1:]
+    assert bool(asc.all()), "ascending"
+    assert bool((torch.where(valid, idx, -1) <= pos[None, :, None]).all()), "causal"
+    last = idx.gather(-1, (n - 1).clamp(min=0).unsqueeze(-1)).squeeze(-1)
+    assert bool((last == pos[None]).all()), "own position last"
+
+
+# ---------------------------------------------------------------------------
+# sparse layers alone, fed the oracle's index sets
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [
+    small("sp_bf16", "bf16", 2, 300, 300, 8, 2, 128, 64, 16, L=3),
+    small("sp_fp32", "fp32", 1, 200, 260, 4, 1, 64, 40, 8, L=3),
+    small("sp_bf16_d64_L5", "bf16", 1, 150, 400, 16, 2, 64, 100, 20, L=5),
+    small("sp_decode", "bf16", 5, 1, 3000, 32, 4, 128, 1024, 128, L=3),
+    small("sp_fp32_d128", "fp32", 1, 64, 300, 8, 4, 128, 50, 10, L=2),
+], ids=lambda c: c.name)
+def test_sparse_attn_on_oracle_indices(gpu_lib, case):
+    say("case", case)
+    inp = make_inputs(case, device="cuda")
+    q, k, v, qs = (host(inp[n]) for n in ("q_full", "k", "v", "q_sparse"))
+    ref = O.block_forward(q, qs, k, v, top_k=case.top_k, window=case.window)
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+    out = gpu_lib.sparse_attn(inp["q_sparse"], inp["k"], inp["v"], idx,
+                              top_k=case.top_k, window=case.window)
+    torch.cuda.synchronize()
+    err = np.abs(as_np(out) - ref["o_sparse"]).max()
+    say("max abs err", err)
+    assert err <= TOL[case.dtype]
+
+
+# ---------------------------------------------------------------------------
+# full layer + selection, small shapes against the dense oracle
+# ---------------------------------------------------------------------------
+FULL_CASES = [
+    small("f_fp32_4_1_d64", "fp32", 1, 700, 700, 4, 1, 64, 64, 16),
+    small("f_bf16_8_2_d128", "bf16", 1, 520, 520, 8, 2, 128, 48, 16),
+    small("f_bf16_chunk_b2", "bf16", 2, 150, 900, 8, 4, 128, 100, 32),
+    small("f_bf16_ragged", "bf16", 1, 333, 1201, 4, 2, 64, 77, 13),
+    small("f_fp32_chunk", "fp32", 1, 129, 1153, 8, 2, 128, 1024, 128),
+    small("f_bf16_tiny_dense", "bf16", 1, 37, 37, 4, 1, 128, 30, 8),
+    small("f_bf16_no_candidates", "bf16", 1, 20, 50, 4, 2, 64, 8, 64),
+    small("f_decode", "bf16", 3, 1, 2500, 16, 2, 128, 256, 64),
+    small("f_decode_fp32", "fp32", 2, 1, 777, 8, 8, 64, 100, 16),
+]
+
+
+def run_full_case(gpu_lib, case, select="token", block_size=64, top_blocks=16, debug_rows=None):
+    inp = make_inputs(case, device="cuda")
+    kw = dict(top_k=case.top_k, window=case.window, select=select, block_size=block_size,
+              top_blocks=top_blocks)
+    o, idx, lse, scores = gpu_lib.full_attn_select(inp["q_full"], inp["k"], inp["v"],
+                                                   debug_rows=debug_rows, **kw)
+    torch.cuda.synchronize()
+    q, k, v = (host(inp[n]) for n in ("q_full", "k", "v"))
+    ref = O.block_forward(q, np.zeros((0,) + q.shape, dtype=q.dtype), k, v, **kw)
+    return inp, o, idx, lse, scores, ref
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=lambda c: c.name)
+def test_full_attn_select(gpu_lib, case):
+    say("case", case)
+    rows = [0, case.batch * case.n_q - 1]
+    inp, o, idx, lse, scores, ref = run_full_case(gpu_lib, case, debug_rows=rows)
+    tol = TOL[case.dtype]
+    err_o = np.abs(as_np(o) - ref["o_full"]).max()
+    err_lse = np.abs(lse.cpu().numpy() - ref["lse"]).max()
+    say("o_full err", err_o, "lse err", err_lse)
+    assert err_o <= tol
+    assert err_lse <= 1e-4
+    check_invariants(idx, case)
+    gi = idx.cpu().numpy()
+    nq = case.n_q
+    for b in range(case.batch):
+        pos = np.arange(nq) + case.n_kv - nq
+        tied = compare_index_rows(gi[b], ref["S"][b], pos, ref["idx"][b], ref["tau"][b],
+                                  case.window)
+        say("batch", b, "tie rows", len(tied))
+    # score precision on the exported rows
+    for r, f in enumerate(rows):
+        b, i = divmod(f, nq)
+        p = case.n_kv - nq + i
+        n_c = max(0, p - case.window + 1)
+        g = scores[r].cpu().numpy().astype(np.float64)
+        assert np.all(g[n_c:] == -1.0)
+        s_ref = ref["S"][b, i, :n_c]
+        if n_c:
+            rel = np.abs(g[:n_c] - s_ref) / np.maximum(s_ref, 1e-30)
+            say("score rel err max", rel.max())
+            assert rel.max() < 5e-6
+
+
+def test_exact_ties_pick_lowest_indices(gpu_lib):
+    # K = 0 makes every logit and every score equal (in any precision)
+    case = small("ties", "bf16", 1, 300, 1500, 8, 2, 128, 100, 16)
+    inp = make_inputs(case, device="cuda")
+    k = torch.zeros_like(inp["k"])
+    o, idx, lse, _ = gpu_lib.full_attn_select(inp["q_full"], k, inp["v"], top_k=100, window=16)
+    gi = idx.cpu().numpy()[0]
+    for i in range(case.n_q):
+        p = case.n_kv - case.n_q + i
+        row = gi[i][gi[i] >= 0]
+        n_c = p - 16 + 1
+        assert list(row) == list(range(min(100, n_c))) + list(range(p - 15, p + 1))
+    pos = torch.arange(case.n_q, device="cuda") + case.n_kv - case.n_q
+    np.testing.assert_allclose(lse[0].cpu().numpy(),
+                               np.log(pos.cpu().numpy() + 1.0)[None].repeat(8, 0), atol=1e-5)
+
+
+@pytest.mark.parametrize("case", [
+    small("blk_bf16", "bf16", 1, 300, 2000, 8, 2, 128, 0, 16),
+    small("blk_fp32_unit", "fp32", 1, 120, 400, 4, 1, 64, 0, 8),
+], ids=lambda c: c.name)
+def test_block_selection(gpu_lib, case):
+    bs, tb = (16, 6) if case.dtype == "bf16" else (1, 30)
+    inp, o, idx, lse, _, ref = run_full_case(gpu_lib, case, select="block", block_size=bs,
+                                             top_blocks=tb)
+    check_invariants(idx, case.with_(top_k=bs * tb), block_mode=True)
+    gi = idx.cpu().numpy()[0]
+    pos = np.arange(case.n_q) + case.n_kv - case.n_q
+    tied = compare_index_rows(gi, ref["S"][0], pos, ref["idx"][0], ref["tau"][0], case.window,
+                              block_size=bs)
+    say("block tie rows", len(tied))
+
+
+@pytest.mark.parametrize("case", [
+    small("blk_fwd_bf16", "bf16", 1, 400, 1400, 8, 2, 128, 128, 32, L=3),
+    small("blk_fwd_fp32", "fp32", 2, 96, 500, 4, 2, 64, 64, 16, L=2),
+    small("blk_fwd_decode", "bf16", 4, 1, 4000, 32, 4, 128, 1024, 128, L=3),
+], ids=lambda c: c.name)
+def test_block_forward_small(gpu_lib, case):
+    say("case", case)
+    inp = make_inputs(case, device="cuda")
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
+                                top_k=case.top_k, window=case.window)
+    torch.cuda.synchronize()
+    q, k, v, qs = (host(inp[n]) for n in ("q_full", "k", "v", "q_sparse"))
+    ref = O.block_forward(q, qs, k, v, top_k=case.top_k, window=case.window)
+    tol = TOL[case.dtype]
+    gi = out["idx"].cpu().numpy()
+    check_invariants(out["idx"], case)
+    og = as_np(out["o_sparse"])
+    for b in range(case.batch):
+        pos = np.arange(case.n_q) + case.n_kv - case.n_q
+        tied = compare_index_rows(gi[b], ref["S"][b], pos, ref["idx"][b], ref["tau"][b],
+                                  case.window)
+        exact = [r for r in range(case.n_q) if r not in tied]
+        assert np.abs(og[:, b, exact] - ref["o_sparse"][:, b, exact]).max() <= tol
+        if tied:
+            alt = O.sparse_rows(qs, k, v, b, tied, gi[b][tied])
+            assert np.abs(og[:, b, tied] - alt).max() <= tol
+    assert np.abs(as_np(out["o_full"]) - ref["o_full"]).max() <= tol
+
+
+def test_deterministic(gpu_lib):
+    case = small("det", "bf16", 1, 700, 3000, 16, 2, 128, 256, 32, L=3)
+    inp = make_inputs(case, device="cuda")
+    args = (inp["q_full"], inp["q_sparse"], inp["k"], inp["v"])
+    outs = [gpu_lib.block_forward(*args, top_k=256, window=32) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for key in ("o_full", "o_sparse", "idx", "lse"):
+            assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_small_workspace_chunks_match(gpu_lib):
+    # a workspace for one 128-row chunk must give the same answer
+    case = small("chunks", "bf16", 1, 600, 2000, 8, 2, 128, 128, 16, L=1)
+    inp = make_inputs(case, device="cuda")
+    p = gpu_lib.problem(torch.bfloat16, 1, 600, 2000, 8, 2, 128, top_k=128, window=16)
+    mn, pref = gpu_lib.workspace_size(p)
+    stats = 2 * 8 * 600 * 4
+    row = (2000 - 16 + 255) // 256 * 256 * 4
+    small_ws = torch.empty(((stats + 255) // 256 * 256 + 128 * row), dtype=torch.uint8,
+                           device="cuda")
+    a = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], top_k=128,
+                              window=16)
+    b = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], top_k=128,
+                              window=16, workspace=small_ws)
+    torch.cuda.synchronize()
+    assert small_ws.numel() < pref
+    for key in ("o_full", "o_sparse", "idx", "lse"):
+        assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# the five workloads: config 1 in full, the others on sampled rows
+# ---------------------------------------------------------------------------
+def test_config1_full(gpu_lib):
+    w = CONFIGS[1]
+    say("config", w)
+    inp = make_inputs(w, device="cuda")
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
+                                top_k=w.top_k, window=w.window)
+    torch.cuda.synchronize()
+    check_invariants(out["idx"], w)
+    q, k, v, qs = (host(inp[n]) for n in ("q_full", "k", "v", "q_sparse"))
+    ref = O.block_forward(q, qs, k, v, top_k=w.top_k, window=w.window)
+    gi = out["idx"].cpu().numpy()[0]
+    pos = np.arange(w.n_q)
+    tied = compare_index_rows(gi, ref["S"][0], pos, ref["idx"][0], ref["tau"][0], w.window)
+    say("tie rows", len(tied))
+    og = as_np(out["o_sparse"])
+    exact = [r for r in range(w.n_q) if r not in tied]
+    err = np.abs(og[:, 0, exact] - ref["o_sparse"][:, 0, exact]).max()
+    err_full = np.abs(as_np(out["o_full"]) - ref["o_full"]).max()
+    say("o_sparse err", err, "o_full err", err_full)
+    assert err <= TOL["fp32"] and err_full <= TOL["fp32"]
+    if tied:
+        alt = O.sparse_rows(qs, k, v, 0, tied, gi[tied])
+        assert np.abs(og[:, 0, tied] - alt).max() <= TOL["fp32"]
+
+
+def sampled_rows(w: Workload, n):
+    nq = w.n_q
+    base = [0, nq - 1]
+    for p in (127, 128, 1151, 1152, 1153):
+        i = p - w.q_off
+        if 0 <= i < nq:
+            base.append(i)
+    rng = np.random.default_rng(w.cid)
+    extra = rng.choice(nq, size=min(nq, n), replace=False).tolist()
+    return sorted(set(base + extra))[:max(n, len(base))]
+
+
+@pytest.mark.parametrize("cid,n_rows", [(2, 6), (3, 4), (4, 3), (5, 2)])
+def test_config_sampled(gpu_lib, cid, n_rows):
+    w = CONFIGS[cid]
+    say("config", w.name)
+    inp = make_inputs(w, device="cuda")
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
+                                top_k=w.top_k, window=w.window)
+    torch.cuda.synchronize()
+    say("gpu done")
+    check_invariants(out["idx"], w)
+    gi = out["idx"].cpu().numpy()
+    o_full = out["o_full"]
+    o_sparse = out["o_sparse"]
+    tol = TOL[w.dtype]
+    batches = [0, w.batch - 1] if w.batch > 1 else [0]
+    for b in batches:
+        rows = sampled_rows(w, n_rows) if w.n_q > 1 else [0]
+        q = host(inp["q_full"][b:b + 1])
+        qs = host(inp["q_sparse"][:, b:b + 1])
+        kb, vb = host(inp["k"][b:b + 1]), host(inp["v"][b:b + 1])
+        ref = O.block_rows(q, qs, kb, vb, 0, rows, top_k=w.top_k, window=w.window)
+        say("oracle rows done", b, rows)
+        tied = compare_index_rows(gi[b, rows], ref["S"], ref["pos"], ref["idx"], ref["tau"],
+                                  w.window)
+        of = as_np(o_full[b, rows])
+        assert np.abs(of - ref["o_full"]).max() <= tol
+        osg = as_np(o_sparse[:, b, rows])
+        for r in range(len(rows)):
+            want = ref["o_sparse"][:, r] if r not in tied else \
+                O.sparse_rows(qs, kb, vb, 0, [rows[r]], gi[b, rows[r]][None])[:, 0]
+            assert np.abs(osg[:, r] - want).max() <= tol
+        say("batch", b, "tied rows", len(tied))
+    if w.structure == "needles":
+        # quality sanity (not parity): each needle is chosen by its target query
+        meta = inp["meta"]
+        hits = 0
+        for j, t in zip(meta["needle_pos"], meta["needle_target"]):
+            hits += int(j in set(gi[0, t - w.q_off].tolist()))
+        say("needle hits", hits, "of", len(meta["needle_pos"]))

@@ -1,0 +1,474 @@
+// C ABI of the Hybrid Block engine (declared in include/hs2.h): argument
+// checks, workspace planning, query chunking and kernel launches. The block
+// is one full-attention layer whose KV cache and token selection are reused
+// by the sparse layers that follow (HySparse2 pages: "Xiaomi Unveils
+// HySparse2 for Faster Long-Context AI", section "Two-Level KV Sharing").
+//
+// Every check runs on the host before the first launch; nothing is written
+// when a call returns an error. No C++ exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+#include <cstring>
+#include <string>
+#include <mutex>
+#include <vector>
+
+#include "hs2.h"
+#include "hs2_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+hs2_status fail(hs2_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hs2_status fail(hs2_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+hs2_status device_fail(hipError_t e, const char* what) {
+  return fail(HS2_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+constexpr int TOPK_MAX = 4096;            // radix select list capacity
+constexpr int MAX_BLOCKS = 16384;         // block mode: blocks per score row
+constexpr int MAX_TOP_BLOCKS = 256;
+constexpr size_t CHUNK_TARGET = (size_t)1 << 30;   // preferred score chunk, bytes
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_decode(const hs2_problem& p) { return p.n_q == 1; }
+
+int index_width(const hs2_problem& p) {
+  return p.select == HS2_SELECT_TOKEN ? p.top_k + p.window : p.top_blocks * p.block_size + p.window;
+}
+
+// longest score row (candidates of the last query), padded to 256 floats
+size_t score_stride(const hs2_problem& p) {
+  const long long n = (long long)p.n_kv - p.window;
+  return n > 0 ? (size_t)((n + 255) / 256 * 256) : 0;
+}
+
+hs2_status check_problem(const hs2_problem* p) {
+  if (!p) return fail(HS2_ERR_NULL, "problem is NULL");
+  if (p->abi_version != HS2_ABI_VERSION)
+    return fail(HS2_ERR_UNSUPPORTED, "abi_version %d, library has %d", p->abi_version,
+                HS2_ABI_VERSION);
+  if (p->dtype != HS2_FP32 && p->dtype != HS2_BF16)
+    return fail(HS2_ERR_UNSUPPORTED, "dtype %d", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(HS2_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", p->head_dim);
+  if (p->batch < 1 || p->n_q < 1 || p->n_kv < 1)
+    return fail(HS2_ERR_SHAPE, "batch %d, n_q %d, n_kv %d must be >= 1", p->batch, p->n_q, p->n_kv);
+  if (p->n_q > p->n_kv) return fail(HS2_ERR_SHAPE, "n_q %d > n_kv %d", p->n_q, p->n_kv);
+  if (p->h_q < 1 || p->h_kv < 1 || p->h_q % p->h_kv != 0)
+    return fail(HS2_ERR_SHAPE, "h_q %d must be a positive multiple of h_kv %d", p->h_q, p->h_kv);
+  const int G = p->h_q / p->h_kv;
+  if (G > 64) return fail(HS2_ERR_UNSUPPORTED, "h_q / h_kv = %d > 64", G);
+  if (p->n_q == 1 && G > 32)
+    return fail(HS2_ERR_UNSUPPORTED, "decode with h_q / h_kv = %d > 32", G);
+  if (p->window < 1) return fail(HS2_ERR_SHAPE, "window %d must be >= 1", p->window);
+  if (p->select != HS2_SELECT_TOKEN && p->select != HS2_SELECT_BLOCK)
+    return fail(HS2_ERR_UNSUPPORTED, "select %d", p->select);
+  if (p->select == HS2_SELECT_TOKEN) {
+    if (p->top_k < 0 || p->top_k > TOPK_MAX)
+      return fail(HS2_ERR_UNSUPPORTED, "top_k %d (0..%d)", p->top_k, TOPK_MAX);
+  } else {
+    if (p->block_size < 1) return fail(HS2_ERR_SHAPE, "block_size %d", p->block_size);
+    if (p->top_blocks < 1 || p->top_blocks > MAX_TOP_BLOCKS)
+      return fail(HS2_ERR_UNSUPPORTED, "top_blocks %d (1..%d)", p->top_blocks, MAX_TOP_BLOCKS);
+    const long long nb = ((long long)p->n_kv - p->window + p->block_size - 1) / p->block_size;
+    if (nb > MAX_BLOCKS)
+      return fail(HS2_ERR_UNSUPPORTED, "%lld candidate blocks per row > %d", nb, MAX_BLOCKS);
+  }
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
+    return fail(HS2_ERR_SHAPE, "softmax_scale must be positive and finite");
+  // element offsets of every tensor must fit the kernels' 64-bit math, and
+  // per-sequence key/row counts their 32-bit math
+  const long long w = index_width(*p);
+  if (w < 1 || w > (1 << 20)) return fail(HS2_ERR_SHAPE, "index width %lld", w);
+  if ((long long)p->n_q * G * 2 > (1LL << 31) || (long long)p->batch * p->n_q > (1LL << 31) / w)
+    return fail(HS2_ERR_SHAPE, "too many query rows");
+  return HS2_OK;
+}
+
+struct Layout {
+  size_t stats = 0;          // [2][B][h_q][n_q] floats
+  size_t part = 0, logits = 0, scores = 0;   // byte offsets
+  size_t n_part = 0, n_logits = 0;
+  size_t stride = 0;         // floats per score row
+  int chunk_rows = 0;        // prefill query rows per chunk
+  int n_split = 0, kps = 0;  // decode split
+  size_t total = 0;
+};
+
+// Workspace layout for `ws_bytes` available (SIZE_MAX = plan the preferred).
+hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_bytes,
+                size_t* pref_bytes) {
+  Layout l;
+  l.stride = score_stride(p);
+  const size_t stats_b = align_up((size_t)2 * p.batch * p.h_q * p.n_q * sizeof(float));
+  l.stats = 0;
+  size_t off = stats_b;
+  if (is_decode(p)) {
+    l.n_split = hs2::decode_n_split(p.n_kv, &l.kps);
+    l.part = off;
+    l.n_part = (size_t)p.batch * p.h_q * l.n_split * (p.head_dim + 2);
+    off += align_up(l.n_part * sizeof(float));
+    l.logits = off;
+    l.n_logits = (size_t)p.batch * p.h_q * p.n_kv;
+    off += align_up(l.n_logits * sizeof(float));
+    l.scores = off;
+    off += align_up((size_t)p.batch * std::max<size_t>(l.stride, 1) * sizeof(float));
+    l.chunk_rows = p.batch;
+    l.total = off;
+    if (min_bytes) *min_bytes = off;
+    if (pref_bytes) *pref_bytes = off;
+  } else {
+    l.scores = off;
+    const size_t row_b = std::max<size_t>(l.stride, 1) * sizeof(float);
+    const size_t mn = off + align_up(row_b);
+    size_t pref_rows = std::max<size_t>(128, CHUNK_TARGET / row_b / 128 * 128);
+    pref_rows = std::min<size_t>(pref_rows, ((size_t)p.n_q + 127) / 128 * 128);
+    const size_t pref = off + align_up(pref_rows * row_b);
+    if (min_bytes) *min_bytes = mn;
+    if (pref_bytes) *pref_bytes = pref;
+    if (ws_bytes != SIZE_MAX) {
+      if (ws_bytes < mn) return HS2_ERR_WORKSPACE;
+      size_t rows = (ws_bytes - off) / row_b;
+      if (rows >= 128) rows = rows / 128 * 128;
+      rows = std::min<size_t>(rows, (size_t)p.n_q);
+      l.chunk_rows = (int)std::max<size_t>(rows, 1);
+      l.total = off + align_up((size_t)l.chunk_rows * row_b);
+    }
+  }
+  if (L) *L = l;
+  return HS2_OK;
+}
+
+// ---- optional pass timing --------------------------------------------------
+struct TimedPass {
+  int pass;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<TimedPass> g_prof;
+
+// Records an event pair around one pass when profiling is on.
+struct PassTimer {
+  hipStream_t st;
+  int pass;
+  hipEvent_t start = nullptr, stop = nullptr;
+  PassTimer(hipStream_t s, int p) : st(s), pass(p) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+      start = stop = nullptr;
+      return;
+    }
+    (void)hipEventRecord(start, st);
+  }
+  ~PassTimer() {
+    if (!start) return;
+    (void)hipEventRecord(stop, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({pass, start, stop});
+  }
+};
+
+float* fptr(void* ws, size_t off) { return reinterpret_cast<float*>((char*)ws + off); }
+
+hs2::Shape shape_of(const hs2_problem& p) {
+  hs2::Shape s;
+  s.batch = p.batch; s.n_q = p.n_q; s.n_kv = p.n_kv; s.h_q = p.h_q; s.h_kv = p.h_kv;
+  s.head_dim = p.head_dim; s.bf16 = p.dtype == HS2_BF16;
+  s.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  return s;
+}
+
+hs2_status check_ptr(const void* ptr, const char* name, bool required = true) {
+  if (!ptr) return required ? fail(HS2_ERR_NULL, "%s is NULL", name) : HS2_OK;
+  if (!aligned16(ptr)) return fail(HS2_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return HS2_OK;
+}
+
+#define HS2_TRY(expr)                  \
+  do {                                 \
+    const hs2_status s_ = (expr);      \
+    if (s_ != HS2_OK) return s_;       \
+  } while (0)
+
+#define HIP_TRY(expr, what)                        \
+  do {                                             \
+    const hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return device_fail(e_, what); \
+  } while (0)
+
+hs2_status check_full_args(const hs2_problem* p, const void* q, const void* k, const void* v,
+                           const void* o, const int32_t* idx, const float* lse,
+                           const hs2_debug* dbg, const void* ws, size_t ws_bytes,
+                           Layout* layout) {
+  HS2_TRY(check_problem(p));
+  HS2_TRY(check_ptr(q, "q"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  HS2_TRY(check_ptr(o, "o"));
+  HS2_TRY(check_ptr(idx, "idx"));
+  HS2_TRY(check_ptr(lse, "lse", false));
+  size_t mn = 0;
+  if (plan(*p, SIZE_MAX, nullptr, &mn, nullptr) != HS2_OK) return fail(HS2_ERR_SHAPE, "plan");
+  if (!ws) return fail(HS2_ERR_NULL, "workspace is NULL (needs %zu bytes)", mn);
+  if (!aligned16(ws)) return fail(HS2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < mn) return fail(HS2_ERR_WORKSPACE, "workspace %zu bytes < minimum %zu", ws_bytes, mn);
+  if (plan(*p, ws_bytes, layout, nullptr, nullptr) != HS2_OK)
+    return fail(HS2_ERR_WORKSPACE, "workspace too small");
+  if (dbg) {
+    if (dbg->n_rows < 0) return fail(HS2_ERR_SHAPE, "debug n_rows %d", dbg->n_rows);
+    if (dbg->n_rows > 0) {
+      if (!dbg->rows) return fail(HS2_ERR_NULL, "debug rows is NULL");
+      if (!dbg->scores_out) return fail(HS2_ERR_NULL, "debug scores_out is NULL");
+      for (int r = 0; r < dbg->n_rows; ++r)
+        if (dbg->rows[r] < 0 || (long long)dbg->rows[r] >= (long long)p->batch * p->n_q)
+          return fail(HS2_ERR_SHAPE, "debug row %d out of range", dbg->rows[r]);
+    }
+  }
+  return HS2_OK;
+}
+
+hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const void* v, void* o,
+                    int32_t* idx, float* lse, const hs2_debug* dbg, void* ws,
+                    const Layout& L, hipStream_t st) {
+  const hs2::Shape s = shape_of(p);
+  float* stats = fptr(ws, L.stats);
+  float* scores = fptr(ws, L.scores);
+  const int width = index_width(p);
+  const bool block_mode = p.select == HS2_SELECT_BLOCK;
+
+  auto export_rows = [&](int flat_lo, int flat_hi) -> hs2_status {
+    if (!dbg) return HS2_OK;
+    for (int r = 0; r < dbg->n_rows; ++r) {
+      const int f = dbg->rows[r];
+      if (f < flat_lo || f >= flat_hi) continue;
+      const int i = f % p.n_q;
+      const int n_c = std::max(0, p.n_kv - p.n_q + i - p.window + 1);
+      HIP_TRY(hs2::launch_export_scores(scores + (size_t)(f - flat_lo) * L.stride, n_c, p.n_kv,
+                                        dbg->scores_out + (size_t)r * p.n_kv, st),
+              "export scores");
+    }
+    return HS2_OK;
+  };
+
+  if (is_decode(p)) {
+    hs2::DecodePlan d;
+    d.s = s; d.q = q; d.k = k; d.v = v; d.o = o; d.stats = stats; d.lse = lse;
+    d.part = fptr(ws, L.part); d.logits = fptr(ws, L.logits);
+    d.keys_per_split = L.kps; d.n_split = L.n_split;
+    {
+      PassTimer t(st, HS2_PASS_FULL);
+      HIP_TRY(hs2::launch_attn_fwd_decode(d, st), "decode attention");
+    }
+    hs2::DecodeScorePlan ds;
+    ds.batch = p.batch; ds.h_q = p.h_q; ds.n_kv = p.n_kv;
+    ds.n_cand = std::max(0, p.n_kv - p.window);
+    ds.logits = d.logits; ds.stats = stats; ds.scores = scores; ds.score_stride = L.stride;
+    {
+      PassTimer t(st, HS2_PASS_SCORE);
+      HIP_TRY(hs2::launch_decode_score(ds, st), "decode score");
+    }
+    HS2_TRY(export_rows(0, p.batch));
+    hs2::SelectPlan sp;
+    sp.rows = p.batch; sp.flat0 = 0; sp.n_q = 1; sp.n_kv = p.n_kv;
+    sp.top_k = p.top_k; sp.window = p.window; sp.width = width;
+    sp.block_mode = block_mode; sp.block_size = p.block_size; sp.top_blocks = p.top_blocks;
+    sp.scores = scores; sp.score_stride = L.stride; sp.idx = idx;
+    {
+      PassTimer t(st, HS2_PASS_SELECT);
+      HIP_TRY(hs2::launch_select(sp, st), "select");
+    }
+    return HS2_OK;
+  }
+
+  hs2::FwdPlan f;
+  f.s = s; f.q = q; f.k = k; f.v = v; f.o = o; f.stats = stats; f.lse = lse;
+  {
+    PassTimer t(st, HS2_PASS_FULL);
+    HIP_TRY(hs2::launch_attn_fwd_prefill(f, st), "full attention");
+  }
+  for (int b = 0; b < p.batch; ++b) {
+    for (int q0 = 0; q0 < p.n_q; q0 += L.chunk_rows) {
+      const int rows = std::min(L.chunk_rows, p.n_q - q0);
+      hs2::ScorePlan sc;
+      sc.s = s; sc.b = b; sc.q0 = q0; sc.rows = rows; sc.window = p.window;
+      sc.q = q; sc.k = k; sc.stats = stats; sc.scores = scores; sc.score_stride = L.stride;
+      {
+        PassTimer t(st, HS2_PASS_SCORE);
+        HIP_TRY(hs2::launch_score_prefill(sc, st), "score");
+      }
+      const int flat0 = b * p.n_q + q0;
+      HS2_TRY(export_rows(flat0, flat0 + rows));
+      hs2::SelectPlan sp;
+      sp.rows = rows; sp.flat0 = flat0; sp.n_q = p.n_q; sp.n_kv = p.n_kv;
+      sp.top_k = p.top_k; sp.window = p.window; sp.width = width;
+      sp.block_mode = block_mode; sp.block_size = p.block_size; sp.top_blocks = p.top_blocks;
+      sp.scores = scores; sp.score_stride = L.stride; sp.idx = idx;
+      {
+        PassTimer t(st, HS2_PASS_SELECT);
+        HIP_TRY(hs2::launch_select(sp, st), "select");
+      }
+    }
+  }
+  return HS2_OK;
+}
+
+hs2_status check_sparse_args(const hs2_problem* p, int32_t n_layers, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const void* o) {
+  HS2_TRY(check_problem(p));
+  if (n_layers < 0) return fail(HS2_ERR_SHAPE, "n_layers %d", n_layers);
+  if (n_layers == 0) return HS2_OK;
+  HS2_TRY(check_ptr(q, "q_layers"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  HS2_TRY(check_ptr(idx, "idx"));
+  HS2_TRY(check_ptr(o, "o_layers"));
+  return HS2_OK;
+}
+
+hs2_status run_sparse(const hs2_problem& p, int32_t n_layers, const void* q, const void* k,
+                      const void* v, const int32_t* idx, void* o, hipStream_t st) {
+  const int G = p.h_q / p.h_kv;
+  const int per = std::max(1, 64 / G);                       // layers per launch
+  const size_t esz = p.dtype == HS2_BF16 ? 2 : 4;
+  const size_t layer_elems = (size_t)p.batch * p.n_q * p.h_q * p.head_dim;
+  for (int l0 = 0; l0 < n_layers; l0 += per) {
+    hs2::SparsePlan sp;
+    sp.layers = std::min(per, n_layers - l0);
+    sp.q = (const char*)q + l0 * layer_elems * esz;
+    sp.o = (char*)o + l0 * layer_elems * esz;
+    sp.k = k; sp.v = v; sp.idx = idx;
+    sp.batch = p.batch; sp.n_q = p.n_q; sp.n_kv = p.n_kv; sp.h_q = p.h_q; sp.h_kv = p.h_kv;
+    sp.head_dim = p.head_dim; sp.width = index_width(p);
+    sp.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+    sp.bf16 = p.dtype == HS2_BF16;
+    PassTimer t(st, HS2_PASS_SPARSE);
+    HIP_TRY(hs2::launch_sparse_attn(sp, st), "sparse attention");
+  }
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hs2_abi_version(void) { return HS2_ABI_VERSION; }
+
+int32_t hs2_index_width(const hs2_problem* p) {
+  if (check_problem(p) != HS2_OK) return -1;
+  return index_width(*p);
+}
+
+hs2_status hs2_workspace_size(const hs2_problem* p, size_t* min_bytes, size_t* preferred_bytes) {
+  g_err.clear();
+  HS2_TRY(check_problem(p));
+  if (!min_bytes && !preferred_bytes) return fail(HS2_ERR_NULL, "no output pointer");
+  return plan(*p, SIZE_MAX, nullptr, min_bytes, preferred_bytes);
+}
+
+hs2_status hs2_full_attn_select(const hs2_problem* p, const void* q, const void* k, const void* v,
+                                void* o, int32_t* idx, float* lse, const hs2_debug* dbg,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Layout L;
+  HS2_TRY(check_full_args(p, q, k, v, o, idx, lse, dbg, workspace, workspace_bytes, &L));
+  return run_full(*p, q, k, v, o, idx, lse, dbg, workspace, L, (hipStream_t)stream);
+}
+
+hs2_status hs2_sparse_attn(const hs2_problem* p, int32_t n_layers, const void* q_layers,
+                           const void* k, const void* v, const int32_t* idx, void* o_layers,
+                           void* stream) {
+  g_err.clear();
+  HS2_TRY(check_sparse_args(p, n_layers, q_layers, k, v, idx, o_layers));
+  if (n_layers == 0) return HS2_OK;
+  return run_sparse(*p, n_layers, q_layers, k, v, idx, o_layers, (hipStream_t)stream);
+}
+
+hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                             const void* q_sparse, const void* k, const void* v, void* o_full,
+                             void* o_sparse, int32_t* idx, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Layout L;
+  HS2_TRY(check_full_args(p, q_full, k, v, o_full, idx, lse, nullptr, workspace, workspace_bytes,
+                          &L));
+  HS2_TRY(check_sparse_args(p, n_sparse_layers, q_sparse, k, v, idx, o_sparse));
+  const hipStream_t st = (hipStream_t)stream;
+  HS2_TRY(run_full(*p, q_full, k, v, o_full, idx, lse, nullptr, workspace, L, st));
+  if (n_sparse_layers == 0) return HS2_OK;
+  return run_sparse(*p, n_sparse_layers, q_sparse, k, v, idx, o_sparse, st);
+}
+
+hs2_status hs2_profile_enable(int32_t on) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) {
+    for (auto& t : g_prof) {
+      (void)hipEventDestroy(t.start);
+      (void)hipEventDestroy(t.stop);
+    }
+    g_prof.clear();
+  }
+  g_prof_on = on != 0;
+  return HS2_OK;
+}
+
+hs2_status hs2_profile_read(double* ms, int64_t* launches) {
+  g_err.clear();
+  if (!ms || !launches) return fail(HS2_ERR_NULL, "output arrays are NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int i = 0; i < HS2_N_PASSES; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  hs2_status st = HS2_OK;
+  for (auto& t : g_prof) {
+    float e = 0.f;
+    hipError_t err = hipEventSynchronize(t.stop);
+    if (err == hipSuccess) err = hipEventElapsedTime(&e, t.start, t.stop);
+    if (err != hipSuccess && st == HS2_OK) st = device_fail(err, "profile events");
+    ms[t.pass] += e;
+    launches[t.pass] += 1;
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  g_prof.clear();
+  return st;
+}
+
+const char* hs2_status_string(hs2_status s) {
+  switch (s) {
+    case HS2_OK: return "ok";
+    case HS2_ERR_NULL: return "null pointer";
+    case HS2_ERR_SHAPE: return "invalid shape";
+    case HS2_ERR_UNSUPPORTED: return "unsupported";
+    case HS2_ERR_WORKSPACE: return "workspace too small";
+    case HS2_ERR_ALIGN: return "misaligned pointer";
+    case HS2_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* hs2_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

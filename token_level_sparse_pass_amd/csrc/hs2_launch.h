@@ -1,0 +1,94 @@
+// Host-side launch descriptions of the Hybrid Block kernels. Each launcher
+// checks nothing: the C ABI layer validates every argument first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hs2 {
+
+// Shape shared by the full-layer kernels.
+struct Shape {
+  int batch, n_q, n_kv, h_q, h_kv, head_dim;
+  bool bf16;
+  float scale_log2;       // softmax scale * log2(e)
+};
+
+// Pass 1 (full causal attention) for prefill-shaped calls.
+// stats: [2][batch][h_q][n_q] floats: m2 (row max in log2 units), l (row sum
+// of 2^(t - m2)); lse (nullable): natural-log LSE.
+struct FwdPlan {
+  Shape s;
+  const void* q; const void* k; const void* v;
+  void* o;
+  float* stats;
+  float* lse;
+};
+hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st);
+
+// Decode (n_q == 1): split-KV pass 1 that also stores every logit (log2
+// units) so the score needs no second read of K; partials are merged by
+// the combine step. part: [batch][h_q][n_split][head_dim + 2] floats,
+// logits: [batch][h_q][n_kv] floats.
+struct DecodePlan {
+  Shape s;
+  const void* q; const void* k; const void* v;
+  void* o;
+  float* stats;
+  float* lse;
+  float* part;
+  float* logits;
+  int keys_per_split;     // multiple of 64
+  int n_split;
+};
+int decode_n_split(int n_kv, int* keys_per_split);
+hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st);
+
+// Decode score: S[b][j] = sum_h 2^(logit - m2) / l for candidate keys.
+struct DecodeScorePlan {
+  int batch, h_q, n_kv, n_cand;   // n_cand = candidates per row (p - window + 1)
+  const float* logits; const float* stats;
+  float* scores; size_t score_stride;
+};
+hipError_t launch_decode_score(const DecodeScorePlan& p, hipStream_t st);
+
+// Pass 2 (prefill): head-summed probabilities for a chunk of queries of one
+// sequence. Writes S[r][j] for r in [0, rows), j in [0, n_cand_max) where
+// row r is query q0 + r; only j <= p - window are meaningful.
+struct ScorePlan {
+  Shape s;
+  int b, q0, rows, window;
+  const void* q; const void* k;
+  const float* stats;
+  float* scores; size_t score_stride;   // floats between rows
+};
+hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st);
+
+// Selection for `rows` score rows: row r is flattened query flat0 + r
+// (flattened query = b * n_q + i).
+struct SelectPlan {
+  int rows, flat0, n_q, n_kv;
+  int top_k, window, width;
+  bool block_mode; int block_size, top_blocks;
+  const float* scores; size_t score_stride;
+  int32_t* idx;                       // [batch, n_q, width]
+};
+hipError_t launch_select(const SelectPlan& p, hipStream_t st);
+
+// Copy one score row into a debug buffer: candidates keep S, others get -1.
+hipError_t launch_export_scores(const float* src, int n_cand, int n_kv, float* dst,
+                                hipStream_t st);
+
+// Sparse layers over a given index set.
+struct SparsePlan {
+  const void* q; const void* k; const void* v;
+  const int32_t* idx;
+  void* o;
+  int layers, batch, n_q, n_kv, h_q, h_kv, head_dim, width;
+  float scale_log2;
+  bool bf16;
+};
+hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st);
+
+}  // namespace hs2

@@ -1,0 +1,195 @@
+"""Python binding of libhs2.so (the C ABI in include/hs2.h).
+
+Argument marshalling only: tensors are passed as raw device pointers and
+every step of the Hybrid Block runs in the library's HIP kernels. PyTorch
+provides device memory and the current stream. If the library has not been
+built, every call raises; there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhs2.so")
+
+ABI_VERSION = 1
+FP32, BF16 = 0, 1
+SELECT_TOKEN, SELECT_BLOCK = 0, 1
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported",
+          4: "workspace too small", 5: "misaligned pointer", 6: "device error"}
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("window", ctypes.c_int32), ("select", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("top_blocks", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("rows", ctypes.POINTER(ctypes.c_int32)), ("n_rows", ctypes.c_int32),
+                ("scores_out", ctypes.c_void_p)]
+
+
+class HS2Error(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"hs2 status {status} ({STATUS.get(status, '?')}): {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libhs2.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with "
+                           "`python -m token_level_sparse_pass_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER(Problem)
+    lib.hs2_abi_version.restype = i32
+    lib.hs2_index_width.argtypes = [P]
+    lib.hs2_index_width.restype = i32
+    lib.hs2_workspace_size.argtypes = [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.hs2_workspace_size.restype = i32
+    lib.hs2_full_attn_select.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Debug),
+                                         vp, sz, vp]
+    lib.hs2_full_attn_select.restype = i32
+    lib.hs2_sparse_attn.argtypes = [P, i32, vp, vp, vp, vp, vp, vp]
+    lib.hs2_sparse_attn.restype = i32
+    lib.hs2_block_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_block_forward.restype = i32
+    lib.hs2_status_string.argtypes = [i32]
+    lib.hs2_status_string.restype = ctypes.c_char_p
+    lib.hs2_last_error.restype = ctypes.c_char_p
+    if lib.hs2_abi_version() != ABI_VERSION:
+        raise RuntimeError("libhs2.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise HS2Error(status, _lib.hs2_last_error().decode())
+
+
+def problem(dtype, batch, n_q, n_kv, h_q, h_kv, head_dim, top_k=1024, window=128,
+            select="token", block_size=64, top_blocks=16, softmax_scale=None) -> Problem:
+    if isinstance(dtype, torch.dtype):
+        dtype = BF16 if dtype == torch.bfloat16 else FP32 if dtype == torch.float32 else -1
+    sel = SELECT_TOKEN if select == "token" else SELECT_BLOCK if select == "block" else select
+    scale = head_dim ** -0.5 if softmax_scale is None else softmax_scale
+    return Problem(ABI_VERSION, dtype, batch, n_q, n_kv, h_q, h_kv, head_dim, top_k, window,
+                   sel, block_size, top_blocks, scale)
+
+
+def index_width(p: Problem) -> int:
+    w = load().hs2_index_width(ctypes.byref(p))
+    if w < 0:
+        raise HS2Error(2, load().hs2_last_error().decode())
+    return w
+
+
+def workspace_size(p: Problem):
+    lib = load()
+    mn, pref = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.hs2_workspace_size(ctypes.byref(p), ctypes.byref(mn), ctypes.byref(pref)))
+    return mn.value, pref.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _problem_from(q, k, kw):
+    B, nq, hq, d = q.shape
+    _, nkv, hkv, _ = k.shape
+    return problem(q.dtype, B, nq, nkv, hq, hkv, d, **kw)
+
+
+def _check_tensor(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def alloc_workspace(p: Problem, device, nbytes=None):
+    mn, pref = workspace_size(p)
+    n = pref if nbytes is None else max(nbytes, mn)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def full_attn_select(q, k, v, *, workspace=None, debug_rows=None, want_lse=True, **kw):
+    """Full layer + scoring + selection. Returns (o, idx, lse, scores|None)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, q.dtype)
+    p = _problem_from(q, k, kw)
+    B, nq, hq, d = q.shape
+    width = index_width(p)
+    o = torch.empty_like(q)
+    idx = torch.empty((B, nq, width), dtype=torch.int32, device=q.device)
+    lse = torch.empty((B, hq, nq), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = alloc_workspace(p, q.device) if workspace is None else workspace
+    dbg_ref, scores = None, None
+    if debug_rows is not None:
+        rows = (ctypes.c_int32 * len(debug_rows))(*[int(r) for r in debug_rows])
+        scores = torch.empty((len(debug_rows), k.shape[1]), dtype=torch.float32, device=q.device)
+        dbg = Debug(rows, len(debug_rows), scores.data_ptr())
+        dbg_ref = ctypes.byref(dbg)
+    _check(lib.hs2_full_attn_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    _ptr(idx), _ptr(lse), dbg_ref, _ptr(ws), ws.numel(),
+                                    _stream(q.device)))
+    return o, idx, lse, scores
+
+
+def sparse_attn(q_layers, k, v, idx, **kw):
+    """Sparse layers over the given index rows. q_layers [L, B, n_q, h_q, d]."""
+    lib = load()
+    for t, n in ((q_layers, "q_layers"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, q_layers.dtype)
+    _check_tensor(idx, "idx", torch.int32)
+    L = q_layers.shape[0]
+    p = _problem_from(q_layers[0] if L else q_layers.new_empty((1,) + q_layers.shape[1:])[0],
+                      k, kw)
+    if idx.shape[-1] != index_width(p):
+        raise ValueError(f"idx width {idx.shape[-1]} != {index_width(p)}")
+    o = torch.empty_like(q_layers)
+    _check(lib.hs2_sparse_attn(ctypes.byref(p), L, _ptr(q_layers), _ptr(k), _ptr(v),
+                               _ptr(idx), _ptr(o), _stream(k.device)))
+    return o
+
+
+def block_forward(q_full, q_sparse, k, v, *, workspace=None, want_lse=True, out=None, **kw):
+    """The whole Hybrid Block. Returns dict(o_full, o_sparse, idx, lse)."""
+    lib = load()
+    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, q_full.dtype)
+    p = _problem_from(q_full, k, kw)
+    B, nq, hq, d = q_full.shape
+    width = index_width(p)
+    if out is None:
+        out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
+                   idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
+                   lse=torch.empty((B, hq, nq), dtype=torch.float32, device=q_full.device)
+                   if want_lse else None)
+    ws = alloc_workspace(p, q_full.device) if workspace is None else workspace
+    _check(lib.hs2_block_forward(ctypes.byref(p), q_sparse.shape[0], _ptr(q_full),
+                                 _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out["o_full"]),
+                                 _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
+                                 _ptr(ws), ws.numel(), _stream(q_full.device)))
+    return out
