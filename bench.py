@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of one HySparse2 Hybrid Block step on one MI355X.
+
+A step is one hs2_block_forward call: causal GQA full attention, the
+head-summed score pass, token top-k selection (1024 + 128-token window) and
+every sparse layer reusing the full layer's K/V and index sets, over one
+batch of synthetic inputs already resident in HBM. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config 5]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selection+sparse-attn tokens/s at 128K-1M ctx; MFMA util and HBM GB/s vs peak"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+PASSES = ["full_attention", "score", "select", "sparse_attention"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(w):
+    """Per-step algorithmic work of each pass (flops or bytes)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    B, nq, nkv, hq, hkv, d = w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.d
+    pos = [nkv - nq + i for i in range(nq)]
+    pairs = sum(p + 1 for p in pos) * B                         # causal (query, key)
+    cand = sum(max(0, p - w.window + 1) for p in pos) * B       # candidate pairs
+    sel = sum(min(p + 1, w.top_k + w.window) for p in pos) * B  # selected keys
+    L = w.n_sparse
+    return {
+        "full_attention": ("mfma", 4.0 * hq * d * pairs),
+        "score": ("mfma", 2.0 * hq * d * cand),
+        "select": ("hbm", 4.0 * cand + 4.0 * B * nq * (w.top_k + w.window)),
+        "sparse_attention": ("hbm", sel * hkv * d * 2.0 * esz + 2.0 * L * B * nq * hq * d * esz),
+    }
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "full_attention": ["token_level_sparse_pass_amd/csrc/attn_fwd.hip",
+                       "token_level_sparse_pass_amd/csrc/hs2_device.h"],
+    "score": ["token_level_sparse_pass_amd/csrc/score.hip",
+              "token_level_sparse_pass_amd/csrc/hs2_device.h"],
+    "select": ["token_level_sparse_pass_amd/csrc/select.hip"],
+    "sparse_attention": ["token_level_sparse_pass_amd/csrc/sparse_attn.hip",
+                         "token_level_sparse_pass_amd/csrc/hs2_device.h"],
+}
+
+
+def measured_traffic(pass_name, workload):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(pass_name)
+    if not rec or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[pass_name]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, target_s=15.0, max_rows=64):
+    """The fp64 oracle on a bounded sample of query rows of the same workload."""
+    import numpy as np
+    from oracle import hs2_oracle as O
+    from synth import to_host
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    b = 0
+    k, v = to_host(inp["k"][b:b + 1]), to_host(inp["v"][b:b + 1])
+    q = to_host(inp["q_full"][b:b + 1])
+    qs = to_host(inp["q_sparse"][:, b:b + 1])
+    rng = np.random.default_rng(12345)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        O.block_rows(q, qs, k, v, 0, rows, top_k=w.top_k, window=w.window)
+        return time.perf_counter() - t0
+
+    first = [w.n_q - 1]
+    t1 = run(first)
+    n = int(max(1, min(max_rows, w.n_q - 1, target_s / max(t1, 1e-3) - 1)))
+    rows = sorted(rng.choice(w.n_q, size=min(n, w.n_q), replace=False).tolist()) \
+        if w.n_q > 1 else [0]
+    t2 = run(rows) if n > 0 and w.n_q > 1 else 0.0
+    total_rows = len(first) + (len(rows) if w.n_q > 1 else 0)
+    total_t = t1 + t2
+    return {"value": total_rows / total_t, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{total_rows} query rows of sequence 0 of {w.name} (full-layer LSE and "
+                      f"score sweeps over all {w.n_kv} keys, token top-{w.top_k} + "
+                      f"{w.window}-token window, {w.n_sparse} sparse layers), "
+                      f"{total_t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Hybrid Block hot path here is a "
+              "single-GPU build (no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import CONFIGS, make_inputs
+    from token_level_sparse_pass_amd import hs2
+
+    lib = hs2.load()
+    w = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: generating inputs")
+    inp = make_inputs(w, device=dev)
+    kw = dict(top_k=w.top_k, window=w.window)
+    p = hs2.problem(inp["q_full"].dtype, w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.d, **kw)
+    ws = hs2.alloc_workspace(p, dev)
+    out = None
+    args_ = (inp["q_full"], inp["q_sparse"], inp["k"], inp["v"])
+    for s in range(args.warmup):
+        out = hs2.block_forward(*args_, workspace=ws, out=out, **kw)
+        torch.cuda.synchronize()
+        log(f"warmup step {s + 1}/{args.warmup} done")
+    if out is None:
+        out = hs2.block_forward(*args_, workspace=ws, **kw)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.hs2_profile_enable(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(args.steps):
+        hs2.block_forward(*args_, workspace=ws, out=out, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = (ctypes.c_double * 4)()
+    nl = (ctypes.c_int64 * 4)()
+    st = lib.hs2_profile_read(ms, nl)
+    lib.hs2_profile_enable(0)
+    if st != 0:
+        raise RuntimeError(lib.hs2_last_error().decode())
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})")
+    tokens = w.batch * w.n_q
+    value = tokens / (ms_step / 1e3)
+
+    work = algorithmic_work(w)
+    peak_mfma = PEAK_MFMA_TFLOPS[w.dtype]
+    passes = {}
+    for i, name in enumerate(PASSES):
+        bound, amount = work[name]
+        per_step_ms = ms[i] / args.steps
+        launches = nl[i] // args.steps if nl[i] else 0
+        if bound == "mfma":
+            ach = amount / (per_step_ms / 1e3) / 1e12 if per_step_ms > 0 else 0.0
+            passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
+                            "bound": "mfma", "achieved": round(ach, 2), "unit": "TFLOP/s",
+                            "frac": round(ach / peak_mfma, 4)}
+        else:
+            ach = amount / (per_step_ms / 1e3) / 1e9 if per_step_ms > 0 else 0.0
+            passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
+                            "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(PASSES, key=lambda n: passes[n]["ms"])
+    d = passes[dom]
+    per_launch = work[dom][1] / max(1, d["launches_per_step"])
+    traffic = measured_traffic(dom, w.name)
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+                "peak": peak_mfma if d["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": d["unit"], "frac": d["frac"],
+                "algorithmic_per_launch": per_launch,
+                "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a sample of rows")
+        cpu = cpu_baseline(w, inp)
+
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
+           "config": {"workload": w.name, "batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv,
+                      "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d, "top_k": w.top_k,
+                      "window": w.window, "sparse_layers": w.n_sparse, "select": "token",
+                      "structure": w.structure, "parallelism": "single GPU"},
+           "roofline": roofline, "passes": passes, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,6 +69,11 @@ def load(path: str = LIB_PATH):
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
+    lib.hs2_profile_enable.argtypes = [i32]
+    lib.hs2_profile_enable.restype = i32
+    lib.hs2_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.hs2_profile_read.restype = i32
     if lib.hs2_abi_version() != ABI_VERSION:
         raise RuntimeError("libhs2.so ABI version mismatch")
     _lib = lib
