@@ -236,10 +236,8 @@ def test_small_workspace_chunks_match(gpu_lib):
     inp = make_inputs(case, device="cuda")
     p = gpu_lib.problem(torch.bfloat16, 1, 600, 2000, 8, 2, 128, top_k=128, window=16)
     mn, pref = gpu_lib.workspace_size(p)
-    stats = 2 * 8 * 600 * 4
-    row = (2000 - 16 + 255) // 256 * 256 * 4
-    small_ws = torch.empty(((stats + 255) // 256 * 256 + 128 * row), dtype=torch.uint8,
-                           device="cuda")
+    row = (2000 - 16 + 255) // 256 * 256 * 4          # one score row, padded
+    small_ws = torch.empty(mn + 127 * row, dtype=torch.uint8, device="cuda")
     a = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], top_k=128,
                               window=16)
     b = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], top_k=128,

@@ -301,7 +301,7 @@ static hipError_t launch_prefill_t(const FwdPlan& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
+hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st) {
   if (p.s.bf16) {
     if (p.s.head_dim == 128) return launch_prefill_t<__bf16, 128>(p, st);
     if (p.s.head_dim == 64) return launch_prefill_t<__bf16, 64>(p, st);

@@ -1,0 +1,344 @@
+// Pass 1 of the full layer, specialised for bf16 and head dim 128 (the
+// long-context workloads). Same contract as attn_fwd.hip: causal GQA
+// attention over the shared K/V plus per-(query, head) statistics
+// (m2, l) and LSE.
+//
+// Differences from the generic kernel, all aimed at keeping the SIMD's
+// issue slots on MFMAs (on gfx950 a SIMD's VALU and MFMA instructions do
+// not overlap, so every VALU instruction in the loop costs MFMA time):
+//  * V is transposed once per call into a tile-major copy in the workspace,
+//    Vt[b][g][tile][d][64 keys], so the PV product reads its operands with
+//    16-byte LDS loads instead of transposing in registers;
+//  * K and Vt tiles go straight from global memory into LDS
+//    (global_load_lds_dwordx4), double-buffered, with XOR-swizzled 16-byte
+//    chunks so the MFMA operand reads are free of bank conflicts;
+//  * the keys of a 64-key tile are assigned to MFMA rows in a permuted order
+//    such that the P^T operand of each lane covers 8 consecutive keys;
+//  * the running max is only moved (and O rescaled) when it grows by more
+//    than 2^8, so the rescale multiply almost never runs; exponents are
+//    formed with one FMA (logit * c - m) from the raw MFMA result;
+//  * the causal mask is applied only on tiles that reach the diagonal.
+// Rows, as in the generic kernel, are (query, head-of-group) pairs: 128 per
+// work-group, 32 per wave (two 16-row MFMA blocks).
+#include "hs2_device.h"
+#include "hs2_launch.h"
+
+namespace hs2 {
+
+namespace {
+
+constexpr int TK = 64;              // keys per tile
+constexpr int D = 128;
+constexpr int ROWS = 128;           // rows per work-group
+constexpr int KT_BYTES = TK * D * 2;        // 16 KB
+constexpr int STAGE_BYTES = 2 * KT_BYTES;   // K tile + Vt tile
+constexpr float RESCALE_GAP = 8.0f;         // log2 units
+constexpr float LN2 = 0.69314718055994530942f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// chunk swizzles: K tile rows are 256 B (16 chunks), Vt rows 128 B (8 chunks)
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+
+// key held in MFMA row m of key block kb: lane group q of the P^T operand
+// then owns keys 32*(kb/2) + 8q .. +7 of the tile
+__device__ __forceinline__ int tile_key(int kb, int m) {
+  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
+}
+
+struct Fwd2Args {
+  const __bf16* q; const __bf16* k; const __bf16* vt;
+  __bf16* o; float* stats; float* lse;
+  int B, n_q, n_kv, h_q, h_kv, n_rt, vt_tiles;
+  float c;                           // softmax scale * log2(e)
+};
+
+}  // namespace
+
+// V [B][n_kv][h_kv][128] -> Vt [B][h_kv][tile][128][64], zero past n_kv.
+__global__ __launch_bounds__(256) void transpose_v_kernel(const __bf16* v, __bf16* vt, int n_kv,
+                                                          int h_kv, int vt_tiles) {
+  __shared__ uint16_t tile[TK][D + 8];
+  const int t = blockIdx.x % vt_tiles;
+  const int bg = blockIdx.x / vt_tiles;
+  const int g = bg % h_kv;
+  const int b = bg / h_kv;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(v) + ((size_t)b * n_kv * h_kv + g) * D;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int u = threadIdx.x + 256 * it;
+    const int r = u >> 4, c = u & 15;
+    const int j = t * TK + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (j < n_kv) val = *reinterpret_cast<const uint4*>(src + (size_t)j * h_kv * D + c * 8);
+    *reinterpret_cast<uint4*>(&tile[r][c * 8]) = val;
+  }
+  __syncthreads();
+  uint16_t* dst = reinterpret_cast<uint16_t*>(vt) + (((size_t)b * h_kv + g) * vt_tiles + t) * D * TK;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int u = threadIdx.x + 256 * it;       // 1024 output chunks of 8 keys
+    const int d = u >> 3, c = u & 7;
+    uint16_t e[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) e[x] = tile[c * 8 + x][d];
+    uint4 w;
+    w.x = e[0] | ((uint32_t)e[1] << 16);
+    w.y = e[2] | ((uint32_t)e[3] << 16);
+    w.z = e[4] | ((uint32_t)e[5] << 16);
+    w.w = e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)d * TK + c * 8) = w;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
+  using OP = Op<__bf16, D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int G = a.h_q / a.h_kv;
+  const int R = a.n_q * G;
+  const int q_off = a.n_kv - a.n_q;
+
+  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int rt = a.n_rt - 1 - (int)(lid % a.n_rt);      // heavy tiles first
+  const int bg = lid / a.n_rt;
+  const int b = bg % a.B;
+  const int g = bg / a.B;
+  const int r0 = rt * ROWS;
+  const int i_hi = min(a.n_q - 1, (r0 + ROWS - 1) / G);
+  const int p_lo = q_off + r0 / G;                      // smallest position here
+  const int p_hi = q_off + i_hi;
+  const int n_tiles = (p_hi + TK) / TK;
+  const int n_full = (p_lo + 1) / TK;                   // tiles with no masked key
+
+  const size_t kstride = (size_t)a.h_kv * D;
+  const __bf16* kseq = a.k + ((size_t)b * a.n_kv * a.h_kv + g) * D;
+  const __bf16* vtseq = a.vt + ((size_t)b * a.h_kv + g) * a.vt_tiles * (size_t)(D * TK);
+
+  // ---- Q fragments and row positions ----
+  Frag<__bf16, D> qf[2];
+  int row_pos[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = r0 + wave * 32 + rb * 16 + l16;
+    if (r < R) {
+      const int i = r / G, hh = r - (r / G) * G;
+      load_slice<__bf16, D>(qf[rb], a.q + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D, lane);
+      row_pos[rb] = q_off + i;
+    } else {
+      zero_slice<__bf16, D>(qf[rb]);
+      row_pos[rb] = -1;
+    }
+  }
+
+  // ---- tile loads straight into LDS ----
+  auto issue = [&](int tile, int stage) {
+    char* base = smem + stage * STAGE_BYTES;
+    const int j0 = tile * TK;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = (wave * 4 + t) * 64 + lane;
+      const int r = slot >> 4, pc = slot & 15;
+      const int c = pc ^ kswz(r);
+      const int key = min(j0 + r, a.n_kv - 1);
+      const __bf16* src = kseq + (size_t)key * kstride + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * 4 + t) * 1024), 16, 0, 0);
+    }
+    const __bf16* vsrc = vtseq + (size_t)tile * (D * TK);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = (wave * 4 + t) * 64 + lane;
+      const int d = slot >> 3, pc = slot & 7;
+      const int c = pc ^ vswz(d);
+      __builtin_amdgcn_global_load_lds(vsrc + d * TK + c * 8,
+                                       (lds_void*)(base + KT_BYTES + (wave * 4 + t) * 1024), 16, 0, 0);
+    }
+  };
+
+  float m_run[2];
+  float l_s[2], l_c[2];                                 // compensated row sums
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    m_run[rb] = -1e30f;
+    l_s[rb] = 0.f;
+    l_c[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // per-lane LDS offsets that do not change between tiles
+  int koff[4][4];                                       // [kb][unit] byte offset in K tile
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int row = tile_key(kb, l16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) koff[kb][u] = row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
+  }
+  int voff[2][8];                                       // [step][db] byte offset in Vt tile
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int d = db * 16 + l16;
+      voff[st][db] = KT_BYTES + d * 128 + (((4 * st + grp) ^ vswz(d)) << 4);
+    }
+
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < n_tiles) issue(t + 1, stage ^ 1);
+    const char* base = smem + stage * STAGE_BYTES;
+    const int j0 = t * TK;
+
+    // logits^T for 4 key blocks x 2 row blocks
+    f32x4 s[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const bf16x8*>(base + koff[kb][u]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x = OP::mma(kf[u], qf[rb].u[u], x);
+        s[rb][kb] = x;
+      }
+    }
+
+    const bool masked = t >= n_full;
+    bf16x8 pu[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = j0 + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + e;
+            if (key > row_pos[rb]) s[rb][kb][e] = -INFINITY;
+          }
+      }
+      float tmax = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
+#pragma unroll
+      for (int kb = 1; kb < 4; ++kb)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3])));
+      tmax = xor_max(tmax, 16);
+      tmax = xor_max(tmax, 32);
+      const float m_tile = tmax * a.c;
+      const bool grow = m_tile > m_run[rb] + RESCALE_GAP;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_tile : m_run[rb];
+        const float alpha = fast_exp2(m_run[rb] - m_new);
+        m_run[rb] = m_new;
+        l_s[rb] *= alpha;
+        l_c[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha;
+      }
+      const float neg_m = -m_run[rb];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pe = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
+          s[rb][kb][e] = pe;
+          psum += pe;
+        }
+      // compensated add of this tile's row sum
+      const float y = psum - l_c[rb];
+      const float tt = l_s[rb] + y;
+      l_c[rb] = (tt - l_s[rb]) - y;
+      l_s[rb] = tt;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pu[rb][st][e] = (__bf16)s[rb][2 * st][e];
+          pu[rb][st][4 + e] = (__bf16)s[rb][2 * st + 1][e];
+        }
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(base + voff[st][db]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf, pu[rb][st], acc[rb][db]);
+      }
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const size_t plane = (size_t)a.B * a.h_q * a.n_q;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float l = l_s[rb] - l_c[rb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int r = r0 + wave * 32 + rb * 16 + l16;
+    if (r >= R) continue;
+    const int i = r / G, hh = r - (r / G) * G;
+    const int h = g * G + hh;
+    const float inv = 1.f / l;
+    __bf16* orow = a.o + (((size_t)b * a.n_q + i) * a.h_q + h) * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      __attribute__((ext_vector_type(4))) __bf16 w4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(acc[rb][db][e] * inv);
+      *reinterpret_cast<decltype(w4)*>(orow + db * 16) = w4;
+    }
+    if (grp == 0) {
+      const size_t si = ((size_t)b * a.h_q + h) * a.n_q + i;
+      a.stats[si] = m_run[rb];
+      a.stats[plane + si] = l;
+      if (a.lse) a.lse[si] = (m_run[rb] + log2f(l)) * LN2;
+    }
+  }
+}
+
+bool prefill_uses_vt(const Shape& s) { return s.bf16 && s.head_dim == D; }
+
+int vt_keys_for(int n_kv) { return (n_kv + TK - 1) / TK * TK; }
+
+hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st);
+
+hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
+  if (!prefill_uses_vt(p.s) || !p.vt) return launch_attn_fwd_prefill_generic(p, st);
+  const int vt_tiles = p.vt_keys / TK;
+  const unsigned tgrid = (unsigned)((size_t)p.s.batch * p.s.h_kv * vt_tiles);
+  hipLaunchKernelGGL(transpose_v_kernel, dim3(tgrid), dim3(256), 0, st,
+                     reinterpret_cast<const __bf16*>(p.v), reinterpret_cast<__bf16*>(p.vt),
+                     p.s.n_kv, p.s.h_kv, vt_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  Fwd2Args a;
+  a.q = reinterpret_cast<const __bf16*>(p.q);
+  a.k = reinterpret_cast<const __bf16*>(p.k);
+  a.vt = reinterpret_cast<const __bf16*>(p.vt);
+  a.o = reinterpret_cast<__bf16*>(p.o);
+  a.stats = p.stats; a.lse = p.lse;
+  a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
+  a.vt_tiles = vt_tiles; a.c = p.s.scale_log2;
+  const int G = a.h_q / a.h_kv;
+  a.n_rt = (a.n_q * G + ROWS - 1) / ROWS;
+  const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(256), 2 * STAGE_BYTES, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs2

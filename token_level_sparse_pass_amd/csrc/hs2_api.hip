@@ -104,8 +104,18 @@ hs2_status check_problem(const hs2_problem* p) {
   return HS2_OK;
 }
 
+hs2::Shape shape_of(const hs2_problem& p) {
+  hs2::Shape s;
+  s.batch = p.batch; s.n_q = p.n_q; s.n_kv = p.n_kv; s.h_q = p.h_q; s.h_kv = p.h_kv;
+  s.head_dim = p.head_dim; s.bf16 = p.dtype == HS2_BF16;
+  s.scale_log2 = p.softmax_scale * 1.4426950408889634f;
+  return s;
+}
+
 struct Layout {
   size_t stats = 0;          // [2][B][h_q][n_q] floats
+  size_t vt = 0;             // transposed V (bf16, head_dim 128 prefill), 0 = none
+  int vt_keys = 0;
   size_t part = 0, logits = 0, scores = 0;   // byte offsets
   size_t n_part = 0, n_logits = 0;
   size_t stride = 0;         // floats per score row
@@ -137,6 +147,11 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
     if (min_bytes) *min_bytes = off;
     if (pref_bytes) *pref_bytes = off;
   } else {
+    if (hs2::prefill_uses_vt(shape_of(p))) {
+      l.vt_keys = hs2::vt_keys_for(p.n_kv);
+      l.vt = off;
+      off += align_up((size_t)p.batch * p.h_kv * p.head_dim * l.vt_keys * 2);
+    }
     l.scores = off;
     const size_t row_b = std::max<size_t>(l.stride, 1) * sizeof(float);
     const size_t mn = off + align_up(row_b);
@@ -191,13 +206,6 @@ struct PassTimer {
 
 float* fptr(void* ws, size_t off) { return reinterpret_cast<float*>((char*)ws + off); }
 
-hs2::Shape shape_of(const hs2_problem& p) {
-  hs2::Shape s;
-  s.batch = p.batch; s.n_q = p.n_q; s.n_kv = p.n_kv; s.h_q = p.h_q; s.h_kv = p.h_kv;
-  s.head_dim = p.head_dim; s.bf16 = p.dtype == HS2_BF16;
-  s.scale_log2 = p.softmax_scale * 1.4426950408889634f;
-  return s;
-}
 
 hs2_status check_ptr(const void* ptr, const char* name, bool required = true) {
   if (!ptr) return required ? fail(HS2_ERR_NULL, "%s is NULL", name) : HS2_OK;
@@ -303,6 +311,8 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
 
   hs2::FwdPlan f;
   f.s = s; f.q = q; f.k = k; f.v = v; f.o = o; f.stats = stats; f.lse = lse;
+  f.vt = L.vt ? (char*)ws + L.vt : nullptr;
+  f.vt_keys = L.vt_keys;
   {
     PassTimer t(st, HS2_PASS_FULL);
     HIP_TRY(hs2::launch_attn_fwd_prefill(f, st), "full attention");

@@ -18,13 +18,20 @@ struct Shape {
 // Pass 1 (full causal attention) for prefill-shaped calls.
 // stats: [2][batch][h_q][n_q] floats: m2 (row max in log2 units), l (row sum
 // of 2^(t - m2)); lse (nullable): natural-log LSE.
+// vt (bf16, head_dim 128 only): workspace for V transposed to
+// [batch][h_kv][head_dim][vt_keys] (keys >= n_kv zero-filled), which lets
+// the PV product read V with 16-byte LDS loads; NULL selects the generic
+// kernel.
 struct FwdPlan {
   Shape s;
   const void* q; const void* k; const void* v;
   void* o;
   float* stats;
   float* lse;
+  void* vt; int vt_keys;
 };
+bool prefill_uses_vt(const Shape& s);
+int vt_keys_for(int n_kv);
 hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st);
 
 // Decode (n_q == 1): split-KV pass 1 that also stores every logit (log2
