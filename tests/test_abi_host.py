@@ -64,9 +64,10 @@ def test_index_width():
 def test_workspace_sizes():
     p = base_problem()
     mn, pref = hs2.workspace_size(p)
-    stats = 2 * 1 * 8 * 256 * 4
+    stats = 3 * 1 * 8 * 256 * 4                   # m2, l, 1/l per (query, head)
     row = (1024 - 16 + 255) // 256 * 256 * 4
-    assert mn >= stats + row
+    vt = 1 * 2 * 128 * 1024 * 2                     # transposed V (bf16, d = 128)
+    assert mn >= stats + row + vt
     assert pref >= mn
     assert pref >= stats + 256 * row         # one chunk holds every query row
     # decode needs its logits and partials

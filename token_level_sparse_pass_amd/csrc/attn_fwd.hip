@@ -281,6 +281,7 @@ __global__ __launch_bounds__(256) void attn_fwd_prefill_kernel(FwdArgs a) {
       const size_t si = ((size_t)b * a.h_q + h) * a.n_q + i;
       a.stats[si] = m_run[rb];
       a.stats[plane + si] = l;
+      a.stats[2 * plane + si] = 1.f / l;
       if (a.lse) a.lse[si] = (m_run[rb] + log2f(l)) * LN2;
     }
   }
@@ -497,6 +498,7 @@ __global__ void decode_combine_kernel(const float* part, int n_split, T* o, floa
   if (d == 0) {
     stats[bh] = M;
     stats[plane + bh] = L;
+    stats[2 * plane + bh] = 1.f / L;
     if (lse) lse[bh] = (M + log2f(L)) * LN2;
   }
 }
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   const size_t plane = (size_t)a.batch * a.h_q;
   for (int h = threadIdx.x; h < a.h_q; h += blockDim.x) {
     sh[h] = a.stats[(size_t)b * a.h_q + h];
-    sh[a.h_q + h] = 1.f / a.stats[plane + (size_t)b * a.h_q + h];
+    sh[a.h_q + h] = a.stats[2 * plane + (size_t)b * a.h_q + h];
   }
   __syncthreads();
   const int j = blockIdx.x * blockDim.x + threadIdx.x;

@@ -306,6 +306,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
       const size_t si = ((size_t)b * a.h_q + h) * a.n_q + i;
       a.stats[si] = m_run[rb];
       a.stats[plane + si] = l;
+      a.stats[2 * plane + si] = 1.f / l;
       if (a.lse) a.lse[si] = (m_run[rb] + log2f(l)) * LN2;
     }
   }

@@ -43,7 +43,7 @@ constexpr size_t ALIGN = 256;
 constexpr int TOPK_MAX = 4096;            // radix select list capacity
 constexpr int MAX_BLOCKS = 16384;         // block mode: blocks per score row
 constexpr int MAX_TOP_BLOCKS = 256;
-constexpr size_t CHUNK_TARGET = (size_t)1 << 30;   // preferred score chunk, bytes
+constexpr size_t CHUNK_TARGET = (size_t)4 << 30;   // preferred score chunk, bytes
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -113,7 +113,7 @@ hs2::Shape shape_of(const hs2_problem& p) {
 }
 
 struct Layout {
-  size_t stats = 0;          // [2][B][h_q][n_q] floats
+  size_t stats = 0;          // [3][B][h_q][n_q] floats: m2, l, 1/l
   size_t vt = 0;             // transposed V (bf16, head_dim 128 prefill), 0 = none
   int vt_keys = 0;
   size_t part = 0, logits = 0, scores = 0;   // byte offsets
@@ -129,7 +129,7 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
                 size_t* pref_bytes) {
   Layout l;
   l.stride = score_stride(p);
-  const size_t stats_b = align_up((size_t)2 * p.batch * p.h_q * p.n_q * sizeof(float));
+  const size_t stats_b = align_up((size_t)3 * p.batch * p.h_q * p.n_q * sizeof(float));
   l.stats = 0;
   size_t off = stats_b;
   if (is_decode(p)) {

@@ -16,8 +16,8 @@ struct Shape {
 };
 
 // Pass 1 (full causal attention) for prefill-shaped calls.
-// stats: [2][batch][h_q][n_q] floats: m2 (row max in log2 units), l (row sum
-// of 2^(t - m2)); lse (nullable): natural-log LSE.
+// stats: [3][batch][h_q][n_q] floats: m2 (row max in log2 units), l (row sum
+// of 2^(t - m2)) and 1/l; lse (nullable): natural-log LSE.
 // vt (bf16, head_dim 128 only): workspace for V transposed to
 // [batch][h_kv][head_dim][vt_keys] (keys >= n_kv zero-filled), which lets
 // the PV product read V with 16-byte LDS loads; NULL selects the generic

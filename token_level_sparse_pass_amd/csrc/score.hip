@@ -174,7 +174,7 @@ static hipError_t launch_score_t(const ScorePlan& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st) {
+hipError_t launch_score_prefill_generic(const ScorePlan& p, hipStream_t st) {
   if (p.s.bf16) {
     if (p.s.head_dim == 128) return launch_score_t<__bf16, 128>(p, st);
     if (p.s.head_dim == 64) return launch_score_t<__bf16, 64>(p, st);

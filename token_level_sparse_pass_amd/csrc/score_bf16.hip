@@ -1,0 +1,230 @@
+// Pass 2 of the full layer, specialised for bf16 and head dim 128: the
+// head-summed softmax probability S(p, j) = sum_h 2^(t_h - m2_h) / l_h over
+// every query head (same contract as score.hip; HySparse2 pages: openai-hub.net,
+// section "From Hybrid SWA to HySparse2": the full layer decides which tokens
+// matter).
+//
+// A work-group owns a 128-query x 256-key block of S and loops over every
+// head in a fixed order (no atomics, bit-reproducible). Eight waves each
+// hold a 64 x 64 block of S in registers and the K rows of their 64 keys
+// for the G heads of the current KV head. Per head, the Q tile (32 KB) and
+// the pass-1 statistics (m2, 1/l) of the 128 queries are loaded straight
+// into LDS (global_load_lds), double-buffered; the next KV head's K rows
+// (64 KB) are staged in LDS the same way while the current one is in use.
+// Chunks are XOR-swizzled so the MFMA operand reads are conflict-free; no
+// global load in the loop writes a register, so nothing waits on the
+// prefetches until the end of each head. Each probability costs one FMA
+// (logit * c - m2), one exp2 and one FMA into the running sum.
+//
+// Work-groups are ordered in blocks of 32 key tiles x all query tiles of
+// the chunk, so a K tile is reused by every query tile from cache, and
+// consecutive blocks land on the same XCD (shared L2).
+#include "hs2_device.h"
+#include "hs2_launch.h"
+
+namespace hs2 {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int TQ = 128;
+constexpr int TKEY = 256;
+constexpr int QT_BYTES = TQ * D * 2;          // 32 KB
+constexpr int ST_BYTES = 2 * TQ * 4;          // m2 and 1/l of the tile's queries
+constexpr int STAGE = QT_BYTES + ST_BYTES;
+constexpr int KT_BYTES = TKEY * D * 2;        // 64 KB: K rows of one KV head
+constexpr int SMEM_BYTES = 2 * STAGE + KT_BYTES;
+constexpr int KT_BLOCK = 32;                  // key tiles per scheduling block
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int qswz(int row) { return row & 15; }
+__device__ __forceinline__ int kswz(int row) { return row & 15; }
+
+struct Score2Args {
+  const __bf16* q; const __bf16* k;
+  const float* stats;
+  float* scores; size_t stride;
+  int B, n_q, n_kv, h_q, h_kv;
+  int b, q0, rows, window;
+  int n_qt, n_kt;
+  float c;
+};
+
+}  // namespace
+
+__global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
+  using OP = Op<__bf16, D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int wq = wave >> 2, wk = wave & 3;
+  const int G = a.h_q / a.h_kv;
+  const int q_off = a.n_kv - a.n_q;
+
+  // blocked order: [key-tile block][query tile][key tile in block]
+  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int per_block = a.n_qt * KT_BLOCK;
+  const int kblk = lid / per_block;
+  const int rem = lid - kblk * per_block;
+  const int kts = min(KT_BLOCK, a.n_kt - kblk * KT_BLOCK);
+  const int qt = rem / kts;
+  const int kt = kblk * KT_BLOCK + (rem - qt * kts);
+
+  const int r_lo = qt * TQ;
+  const int r_hi = min(a.rows, r_lo + TQ) - 1;
+  const int p_hi = q_off + a.q0 + r_hi;
+  const int kj0 = kt * TKEY;
+  if (kj0 > p_hi - a.window) return;                  // no candidate key here
+
+  const __bf16* qseq = a.q + (size_t)a.b * a.n_q * a.h_q * D;
+  const __bf16* kseq = a.k + (size_t)a.b * a.n_kv * a.h_kv * D;
+  const size_t plane = (size_t)a.B * a.h_q * a.n_q;
+
+  auto issue = [&](int h, int stage) {
+    char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int slot = (wave * 4 + t) * 64 + lane;
+      const int r = slot >> 4, pc = slot & 15;
+      const int c = pc ^ qswz(r);
+      const int qi = a.q0 + min(r_lo + r, a.rows - 1);
+      __builtin_amdgcn_global_load_lds(qseq + ((size_t)qi * a.h_q + h) * D + c * 8,
+                                       (lds_void*)(base + (wave * 4 + t) * 1024), 16, 0, 0);
+    }
+    if (wave < 4) {
+      // waves 0,1: m2 of rows 0..63, 64..127; waves 2,3: 1/l
+      const int pl = (wave >> 1) ? 2 : 0;
+      const int r = (wave & 1) * 64 + lane;
+      const int qi = a.q0 + min(r_lo + r, a.rows - 1);
+      const float* src = a.stats + pl * plane + ((size_t)a.b * a.h_q + h) * a.n_q + qi;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + QT_BYTES + wave * 256), 4, 0, 0);
+    }
+  };
+
+  // K rows of the tile's 256 keys for KV head g, into the K buffer
+  auto issue_k = [&](int g) {
+    char* base = smem + 2 * STAGE;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int slot = (wave * 8 + t) * 64 + lane;
+      const int r = slot >> 4, pc = slot & 15;
+      const int c = pc ^ kswz(r);
+      const int j = min(kj0 + r, a.n_kv - 1);
+      __builtin_amdgcn_global_load_lds(kseq + ((size_t)j * a.h_kv + g) * D + c * 8,
+                                       (lds_void*)(base + (wave * 8 + t) * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 sacc[4][4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int qoff[4][4];                                     // [qb][unit] byte offset in Q tile
+  int srow[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int row = wq * 64 + qb * 16 + l16;
+    srow[qb] = row;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qoff[qb][u] = row * 256 + (((4 * grp + u) ^ qswz(row)) << 4);
+  }
+
+  int koff[4][4];                                     // [kb][unit] byte offset in K buffer
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int row = wk * 64 + kb * 16 + l16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) koff[kb][u] = 2 * STAGE + row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
+  }
+
+  issue(0, 0);
+  issue_k(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  bf16x8 kf[4][4];
+  for (int h = 0; h < a.h_q; ++h) {
+    const int stage = h & 1;
+    const int g = h / G;
+    if (h == g * G) {
+      // this KV head's K rows stay in registers for its G query heads; the
+      // buffer is refilled with the next KV head once every wave has them
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kf[kb][u] = *reinterpret_cast<const bf16x8*>(smem + koff[kb][u]);
+      __syncthreads();
+      if (g + 1 < a.h_kv) issue_k(g + 1);
+    }
+    if (h + 1 < a.h_q) issue(h + 1, stage ^ 1);
+    const char* base = smem + stage * STAGE;
+    const float* st = reinterpret_cast<const float*>(base + QT_BYTES);
+
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      bf16x8 qf[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qf[u] = *reinterpret_cast<const bf16x8*>(base + qoff[qb][u]);
+      const float neg_m2 = -st[srow[qb]];
+      const float il = st[TQ + srow[qb]];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x = OP::mma(kf[kb][u], qf[u], x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sacc[qb][kb][e] = fmaf(fast_exp2(fmaf(x[e], a.c, neg_m2)), il, sacc[qb][kb][e]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // keys past n_kv (tile tail) are never read back: rows only use j <= p - w
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int r = r_lo + srow[qb];
+    if (r >= a.rows) continue;
+    float* out = a.scores + (size_t)r * a.stride + kj0 + wk * 64 + 4 * grp;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<f32x4*>(out + kb * 16) = sacc[qb][kb];
+  }
+}
+
+bool score_uses_bf16_kernel(const Shape& s) { return s.bf16 && s.head_dim == D; }
+
+hipError_t launch_score_prefill_generic(const ScorePlan& p, hipStream_t st);
+
+hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st) {
+  if (!score_uses_bf16_kernel(p.s)) return launch_score_prefill_generic(p, st);
+  Score2Args a;
+  a.q = reinterpret_cast<const __bf16*>(p.q);
+  a.k = reinterpret_cast<const __bf16*>(p.k);
+  a.stats = p.stats; a.scores = p.scores; a.stride = p.score_stride;
+  a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
+  a.b = p.b; a.q0 = p.q0; a.rows = p.rows; a.window = p.window; a.c = p.s.scale_log2;
+  const int q_off = a.n_kv - a.n_q;
+  const int n_cand_max = q_off + p.q0 + p.rows - p.window;
+  if (n_cand_max <= 0) return hipSuccess;
+  a.n_qt = (p.rows + TQ - 1) / TQ;
+  a.n_kt = (n_cand_max + TKEY - 1) / TKEY;
+  static bool smem_ok = false;
+  if (!smem_ok) {
+    const hipError_t e = hipFuncSetAttribute((const void*)score_bf16_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    smem_ok = true;
+  }
+  const dim3 grid((unsigned)((size_t)a.n_qt * a.n_kt));
+  hipLaunchKernelGGL(score_bf16_kernel, grid, dim3(512), SMEM_BYTES, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace hs2
