@@ -199,21 +199,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
     const char* base = smem + stage * STAGE_BYTES;
     const int j0 = t * TK;
 
-    // logits^T for 4 key blocks x 2 row blocks
+    // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
+    // kb + 1 are read from LDS while block kb's MFMAs run
     f32x4 s[2][4];
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(base + koff[0][u]);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 kf[4];
+      const int cur = kb & 1;
+      if (kb + 1 < 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kf[u] = *reinterpret_cast<const bf16x8*>(base + koff[kb][u]);
+        for (int u = 0; u < 4; ++u)
+          kf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + koff[kb + 1][u]);
+      }
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x = OP::mma(kf[u], qf[rb].u[u], x);
+        for (int u = 0; u < 4; ++u) x = OP::mma(kf[cur][u], qf[rb].u[u], x);
         s[rb][kb] = x;
       }
     }
+    // V fragments of the first PV step, read during the softmax arithmetic
+    bf16x8 vf0[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vf0[db] = *reinterpret_cast<const bf16x8*>(base + voff[0][db]);
 
     const bool masked = t >= n_full;
     bf16x8 pu[2][2];
@@ -269,15 +280,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
         }
     }
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T (step 1's V fragments are read during step 0)
+    bf16x8 vf1[8];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int db = 0; db < 8; ++db) {
+      vf1[db] = *reinterpret_cast<const bf16x8*>(base + voff[1][db]);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(base + voff[st][db]);
+      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf0[db], pu[rb][0], acc[rb][db]);
+    }
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf, pu[rb][st], acc[rb][db]);
-      }
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

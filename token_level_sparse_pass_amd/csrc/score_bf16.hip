@@ -166,18 +166,30 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
     const char* base = smem + stage * STAGE;
     const float* st = reinterpret_cast<const float*>(base + QT_BYTES);
 
+    // Q fragments of query block qb + 1 are read while block qb computes
+    bf16x8 qf[2][4];
+    float m2v[2], ilv[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qf[0][u] = *reinterpret_cast<const bf16x8*>(base + qoff[0][u]);
+    m2v[0] = st[srow[0]];
+    ilv[0] = st[TQ + srow[0]];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      bf16x8 qf[4];
+      const int cur = qb & 1;
+      if (qb + 1 < 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) qf[u] = *reinterpret_cast<const bf16x8*>(base + qoff[qb][u]);
-      const float neg_m2 = -st[srow[qb]];
-      const float il = st[TQ + srow[qb]];
+        for (int u = 0; u < 4; ++u)
+          qf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + qoff[qb + 1][u]);
+        m2v[cur ^ 1] = st[srow[qb + 1]];
+        ilv[cur ^ 1] = st[TQ + srow[qb + 1]];
+      }
+      const float neg_m2 = -m2v[cur];
+      const float il = ilv[cur];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x = OP::mma(kf[kb][u], qf[u], x);
+        for (int u = 0; u < 4; ++u) x = OP::mma(kf[kb][u], qf[cur][u], x);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           sacc[qb][kb][e] = fmaf(fast_exp2(fmaf(x[e], a.c, neg_m2)), il, sacc[qb][kb][e]);
