@@ -18,8 +18,10 @@
 //    than 2^8, so the rescale multiply almost never runs; exponents are
 //    formed with one FMA (logit * c - m) from the raw MFMA result;
 //  * the causal mask is applied only on tiles that reach the diagonal.
-// Rows, as in the generic kernel, are (query, head-of-group) pairs: 128 per
-// work-group, 32 per wave (two 16-row MFMA blocks).
+// Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
+// 16-row MFMA blocks per wave, four waves per work-group. Each wave reads a
+// whole K and V^T tile from LDS per 64 keys, so rows per wave set the MFMA
+// work per LDS byte (LDS delivers about 64 B/clk per CU for 16-byte reads).
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -29,7 +31,6 @@ namespace {
 
 constexpr int TK = 64;              // keys per tile
 constexpr int D = 128;
-constexpr int ROWS = 128;           // rows per work-group
 constexpr int KT_BYTES = TK * D * 2;        // 16 KB
 constexpr int STAGE_BYTES = 2 * KT_BYTES;   // K tile + Vt tile
 constexpr float RESCALE_GAP = 8.0f;         // log2 units
@@ -92,8 +93,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const __bf16* v, __bf1
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
+template <int RBW, int MINW>
+__global__ __launch_bounds__(256, MINW) void attn_fwd_bf16_kernel(Fwd2Args a) {
   using OP = Op<__bf16, D>;
+  constexpr int ROWS = 64 * RBW;                        // rows per work-group
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -121,11 +124,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
   const __bf16* vtseq = a.vt + ((size_t)b * a.h_kv + g) * a.vt_tiles * (size_t)(D * TK);
 
   // ---- Q fragments and row positions ----
-  Frag<__bf16, D> qf[2];
-  int row_pos[2];
+  Frag<__bf16, D> qf[RBW];
+  int row_pos[RBW];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = r0 + wave * 32 + rb * 16 + l16;
+  for (int rb = 0; rb < RBW; ++rb) {
+    const int r = r0 + wave * 16 * RBW + rb * 16 + l16;
     if (r < R) {
       const int i = r / G, hh = r - (r / G) * G;
       load_slice<__bf16, D>(qf[rb], a.q + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D, lane);
@@ -160,11 +163,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
     }
   };
 
-  float m_run[2];
-  float l_s[2], l_c[2];                                 // compensated row sums
-  f32x4 acc[2][8];
+  float m_run[RBW];
+  float l_s[RBW], l_c[RBW];                             // compensated row sums
+  f32x4 acc[RBW][8];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     m_run[rb] = -1e30f;
     l_s[rb] = 0.f;
     l_c[rb] = 0.f;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
 
     // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
     // kb + 1 are read from LDS while block kb's MFMAs run
-    f32x4 s[2][4];
+    f32x4 s[RBW][4];
     bf16x8 kf[2][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(base + koff[0][u]);
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
           kf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + koff[kb + 1][u]);
       }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < RBW; ++rb) {
         f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 4; ++u) x = OP::mma(kf[cur][u], qf[rb].u[u], x);
@@ -227,9 +230,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
     for (int db = 0; db < 8; ++db) vf0[db] = *reinterpret_cast<const bf16x8*>(base + voff[0][db]);
 
     const bool masked = t >= n_full;
-    bf16x8 pu[2][2];
+    bf16x8 pu[RBW][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RBW; ++rb) {
       if (masked) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -286,12 +289,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
     for (int db = 0; db < 8; ++db) {
       vf1[db] = *reinterpret_cast<const bf16x8*>(base + voff[1][db]);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf0[db], pu[rb][0], acc[rb][db]);
+      for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf0[db], pu[rb][0], acc[rb][db]);
     }
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
+      for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -299,11 +302,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
 
   const size_t plane = (size_t)a.B * a.h_q * a.n_q;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < RBW; ++rb) {
     float l = l_s[rb] - l_c[rb];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int r = r0 + wave * 32 + rb * 16 + l16;
+    const int r = r0 + wave * 16 * RBW + rb * 16 + l16;
     if (r >= R) continue;
     const int i = r / G, hh = r - (r / G) * G;
     const int h = g * G + hh;
@@ -328,6 +331,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
 
 bool prefill_uses_vt(const Shape& s) { return s.bf16 && s.head_dim == D; }
 
+
 int vt_keys_for(int n_kv) { return (n_kv + TK - 1) / TK * TK; }
 
 hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st);
@@ -350,9 +354,14 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
   a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.vt_tiles = vt_tiles; a.c = p.s.scale_log2;
   const int G = a.h_q / a.h_kv;
-  a.n_rt = (a.n_q * G + ROWS - 1) / ROWS;
+  // two 16-row blocks per wave at two waves per SIMD measured best on the
+  // 1M-context workload (48 rows spill registers; 64 rows at one wave per
+  // SIMD lose more to latency than they save in LDS traffic)
+  constexpr int RBW = 2;
+  constexpr int rows = 64 * RBW;
+  a.n_rt = (a.n_q * G + rows - 1) / rows;
   const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(256), 2 * STAGE_BYTES, st, a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, 2>), grid, dim3(256), 2 * STAGE_BYTES, st, a);
   return hipGetLastError();
 }
 
