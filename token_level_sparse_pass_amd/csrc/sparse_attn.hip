@@ -313,7 +313,11 @@ static hipError_t launch_sparse_t(const SparseArgs& a, int rb, bool split, hipSt
   return split ? launch_sparse_rb<T, D, 8>(a, rb, st) : launch_sparse_rb<T, D, 1>(a, rb, st);
 }
 
+bool sparse_uses_bf16_kernel(const SparsePlan& p);
+hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st);
+
 hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st) {
+  if (sparse_uses_bf16_kernel(p)) return launch_sparse_attn_bf16(p, st);
   SparseArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.idx = p.idx; a.o = p.o;
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
