@@ -12,6 +12,12 @@
 // bits) fix the k-th largest key tau, one pass collects every key > tau and
 // the lowest-index keys == tau, and a bitonic sort in LDS puts the chosen
 // indices in ascending order. One 1024-thread work-group per query row.
+// Long rows first take a fast path that reads the row once: a threshold
+// from 8192 sampled keys (2048 runs of 4, aimed at about 3k keys above
+// the threshold), one pass
+// gathering every key at or above it into LDS, and the exact radix select
+// on that small set; it falls back to the full passes when it gathered
+// fewer than k keys or more than fit.
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -19,7 +25,8 @@ namespace hs2 {
 
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
-constexpr int LIST_CAP = 4096;       // top_k limit and tie-list capacity
+constexpr int LIST_CAP = 4096;       // top_k limit
+constexpr int EQ_CAP = 2048;         // keys equal to the threshold sorted in LDS
 constexpr int MAX_BLOCKS = 16384;    // block mode: candidate blocks per row
 constexpr int MAX_TOP_BLOCKS = 256;
 
@@ -99,14 +106,175 @@ __device__ void bitonic_sort(int* arr, int n_pow2) {
     }
 }
 
+// Keys of a full score row (index = position) ...
+struct RowSrc {
+  const uint32_t* row;
+  int n;
+  __device__ __forceinline__ uint32_t key(int j) const { return row[j]; }
+  __device__ __forceinline__ int index(int j) const { return j; }
+};
+// ... or of the candidates gathered into LDS (index stored beside the key).
+struct CandSrc {
+  const uint32_t* keys;
+  const int* idx;
+  int n;
+  __device__ __forceinline__ uint32_t key(int j) const { return keys[j]; }
+  __device__ __forceinline__ int index(int j) const { return idx[j]; }
+};
+
+// Exact k-th largest key of src (12 + 12 + 8-bit radix passes with LDS
+// histograms). Returns tau, how many keys == tau must be taken, and how many
+// keys == tau exist.
+template <class S>
+__device__ void radix_kth(const S& src, int k, int* hist, int* wsum, int* res, uint32_t* tau,
+                          int* need_eq, int* n_eq_total) {
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass], nbins = 1 << widths[pass];
+    for (int x = threadIdx.x; x < nbins; x += SEL_THREADS) hist[x] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < src.n; j += SEL_THREADS) {
+      const uint32_t kk = src.key(j);
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & (nbins - 1)], 1);
+    }
+    __syncthreads();
+    find_digit(hist, nbins, need, wsum, res);
+    const int digit = res[0];
+    need = res[1];
+    if (pass == 2) *n_eq_total = hist[digit];
+    prefix |= (uint32_t)digit << sh;
+    pmask |= (uint32_t)(nbins - 1) << sh;
+    __syncthreads();
+  }
+  *tau = prefix;
+  *need_eq = need;
+}
+
+// Row specialisation of the histogram passes with 16-byte loads.
+template <>
+__device__ void radix_kth<RowSrc>(const RowSrc& src, int k, int* hist, int* wsum, int* res,
+                                  uint32_t* tau, int* need_eq, int* n_eq_total) {
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  const int n_c = src.n;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int sh = shifts[pass], nbins = 1 << widths[pass];
+    for (int x = threadIdx.x; x < nbins; x += SEL_THREADS) hist[x] = 0;
+    __syncthreads();
+    constexpr int STRIDE = SEL_THREADS * 4;
+    for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
+      uint4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * STRIDE;
+        const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < n_c && (ks[e] & pmask) == prefix)
+            atomicAdd(&hist[(ks[e] >> sh) & (nbins - 1)], 1);
+      }
+    }
+    __syncthreads();
+    find_digit(hist, nbins, need, wsum, res);
+    const int digit = res[0];
+    need = res[1];
+    if (pass == 2) *n_eq_total = hist[digit];
+    prefix |= (uint32_t)digit << sh;
+    pmask |= (uint32_t)(nbins - 1) << sh;
+    __syncthreads();
+  }
+  *tau = prefix;
+  *need_eq = need;
+}
+
+// Every key > tau into list, every key == tau into eqlist (when they fit).
+template <class S>
+__device__ void collect_above(const S& src, uint32_t tau, bool eq_fits, int* list, int* eqlist,
+                              int* counters) {
+  if (threadIdx.x < 2) counters[threadIdx.x] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < src.n; j += SEL_THREADS) {
+    const uint32_t kk = src.key(j);
+    if (kk > tau) list[atomicAdd(&counters[0], 1)] = src.index(j);
+    else if (kk == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = src.index(j);
+  }
+  __syncthreads();
+}
+
+// Row specialisation: batched 16-byte loads (rows are padded to a multiple
+// of 256 floats, so a clamped quad never leaves the row's allocation).
+template <>
+__device__ void collect_above<RowSrc>(const RowSrc& src, uint32_t tau, bool eq_fits, int* list,
+                                      int* eqlist, int* counters) {
+  if (threadIdx.x < 2) counters[threadIdx.x] = 0;
+  __syncthreads();
+  const int n_c = src.n;
+  constexpr int STRIDE = SEL_THREADS * 4;
+  for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
+    uint4 kv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = jb + u * STRIDE;
+      const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (j + e >= n_c) continue;
+        if (ks[e] > tau) list[atomicAdd(&counters[0], 1)] = j + e;
+        else if (ks[e] == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = j + e;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Sort the tie list, append its need_eq lowest indices, sort the whole
+// selection ascending and write it, followed by the window.
+__device__ void finish_selection(int* list, int* eqlist, int n_gt, int need_eq, int n_eq_total,
+                                 bool eq_sorted_needed, int top_k, int32_t* out, int p,
+                                 int window, int width) {
+  if (eq_sorted_needed) {
+    int n2 = 1;
+    while (n2 < n_eq_total) n2 <<= 1;
+    for (int x = n_eq_total + threadIdx.x; x < n2; x += SEL_THREADS) eqlist[x] = 0x7FFFFFFF;
+    __syncthreads();
+    if (n_eq_total > 1) bitonic_sort(eqlist, n2);
+    for (int x = threadIdx.x; x < need_eq; x += SEL_THREADS) list[n_gt + x] = eqlist[x];
+  }
+  __syncthreads();
+  int n2 = 1;
+  while (n2 < top_k) n2 <<= 1;
+  for (int x = top_k + threadIdx.x; x < n2; x += SEL_THREADS) list[x] = 0x7FFFFFFF;
+  __syncthreads();
+  bitonic_sort(list, n2);
+  for (int t = threadIdx.x; t < top_k; t += SEL_THREADS) out[t] = list[t];
+  write_window_and_pad(out, top_k, p, window, width);
+}
+
+constexpr int NSAMP = 8192;      // sampled keys per row (fast path)
+constexpr int CAND_CAP = 4096;   // candidates gathered into LDS (fast path)
+
 __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
   __shared__ int hist[4096];
   __shared__ int list[LIST_CAP];
-  __shared__ int eqlist[LIST_CAP];
+  __shared__ int eqlist[EQ_CAP];
+  __shared__ uint32_t ckey[CAND_CAP];
+  __shared__ int cidx[CAND_CAP];
   __shared__ int wsum[SEL_WAVES];
   __shared__ int res[2];
   __shared__ int counters[2];
 
+  const int lane = threadIdx.x & 63;
   const int r = blockIdx.x;
   const int flat = a.flat0 + r;                       // b * n_q + i
   const int i = flat % a.n_q;
@@ -121,69 +289,114 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
     return;
   }
 
-  // ---- radix select of the top_k-th largest key ----
-  uint32_t prefix = 0, pmask = 0;
-  int need = a.top_k;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  int n_eq_total = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = widths[pass];
-    const int nbins = 1 << nb;
-    for (int x = threadIdx.x; x < nbins; x += SEL_THREADS) hist[x] = 0;
+  // ---- fast path: a conservative threshold from a strided sample, one pass
+  // that gathers every key at or above it into LDS, exact selection there.
+  // Exact whenever at least top_k keys were gathered (then the top_k-th
+  // largest key, and every key equal to it, is among them).
+  if (n_c >= 4 * a.top_k && n_c >= 16384) {
+    for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+    if (threadIdx.x == 0) counters[0] = 0;
     __syncthreads();
-    for (int j = threadIdx.x * 4; j < n_c; j += SEL_THREADS * 4) {
-      uint4 kv;
-      if (j + 3 < n_c) {
-        kv = *reinterpret_cast<const uint4*>(row + j);
-      } else {
-        kv.x = row[j];
-        kv.y = (j + 1 < n_c) ? row[j + 1] : 0xFFFFFFFFu;
-        kv.z = (j + 2 < n_c) ? row[j + 2] : 0xFFFFFFFFu;
-        kv.w = 0xFFFFFFFFu;
-      }
-      const uint32_t ks[4] = {kv.x, kv.y, kv.z, kv.w};
+    // 8192 sampled keys: 2048 runs of 4 spread over the row (short runs keep
+    // clustered structure from skewing the sample); two histogram levels
+    // place the threshold at 24-bit precision
+    const int sj0 = (int)(((long long)(2 * threadIdx.x) * (n_c - 4)) / 2047) / 4 * 4;
+    const int sj1 = (int)(((long long)(2 * threadIdx.x + 1) * (n_c - 4)) / 2047) / 4 * 4;
+    const uint4 s0 = *reinterpret_cast<const uint4*>(row + sj0);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(row + sj1);
+    const uint32_t sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (j + e < n_c && (ks[e] & pmask) == prefix)
-          atomicAdd(&hist[(ks[e] >> sh) & (nbins - 1)], 1);
+    for (int e = 0; e < 8; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
+    __syncthreads();
+    // up to two attempts: a gather that overflows retries with a higher
+    // threshold, one that catches fewer than top_k keys with a lower one
+    int rank = min(NSAMP, max(8, (int)(((long long)3 * a.top_k * NSAMP + n_c - 1) / n_c)));
+    int n_cand = 0;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+    if (attempt > 0) {
+      if (n_cand > CAND_CAP) rank = max(1, rank * 3 / 5);
+      else rank = min(NSAMP, rank * 2);
+      for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+      if (threadIdx.x == 0) counters[0] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
+      __syncthreads();
+    }
+    find_digit(hist, 4096, rank, wsum, res);
+    const uint32_t top12 = (uint32_t)res[0];
+    const int rank2 = res[1];
+    __syncthreads();
+    for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((sk[e] >> 20) == top12) atomicAdd(&hist[(sk[e] >> 8) & 4095], 1);
+    __syncthreads();
+    find_digit(hist, 4096, rank2, wsum, res);
+    const uint32_t v_s = (top12 << 20) | ((uint32_t)res[0] << 8);
+    // eight 16-byte loads in flight per thread
+    constexpr int STRIDE = SEL_THREADS * 4;
+    for (int jb = threadIdx.x * 4; jb < n_c; jb += 8 * STRIDE) {
+      // branch-free loads so all eight stay in flight: a position past the
+      // row is clamped to its last aligned quad and masked below (rows are
+      // padded to a multiple of 256 floats, so a quad never leaves them)
+      uint4 kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j0 = min(jb + u * STRIDE, (n_c - 1) & ~3);
+        kv[u] = *reinterpret_cast<const uint4*>(row + j0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j0 = jb + u * STRIDE;
+        const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool f = (j0 + e < n_c) && ks[e] >= v_s;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+          if (m) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&counters[0], __popcll(m));
+            base = __shfl(base, 0, 64);
+            const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+            if (f && pos < CAND_CAP) {
+              ckey[pos] = ks[e];
+              cidx[pos] = j0 + e;
+            }
+          }
+        }
       }
     }
     __syncthreads();
-    find_digit(hist, nbins, need, wsum, res);
-    const int digit = res[0];
-    need = res[1];
-    if (pass == 2) n_eq_total = hist[digit];
-    prefix |= (uint32_t)digit << sh;
-    pmask |= (uint32_t)(nbins - 1) << sh;
+    n_cand = counters[0];
     __syncthreads();
-  }
-  const uint32_t tau = prefix;
-  const int need_eq = need;                       // keys == tau to take
-  const int n_gt = a.top_k - need_eq;
-
-  // ---- collect keys > tau and (if they fit) every key == tau ----
-  if (threadIdx.x < 2) counters[threadIdx.x] = 0;
-  __syncthreads();
-  const bool eq_fits = n_eq_total <= LIST_CAP;
-  for (int j = threadIdx.x; j < n_c; j += SEL_THREADS) {
-    const uint32_t key = row[j];
-    if (key > tau) {
-      list[atomicAdd(&counters[0], 1)] = j;
-    } else if (key == tau && eq_fits) {
-      eqlist[atomicAdd(&counters[1], 1)] = j;
+    if (n_cand >= a.top_k && n_cand <= CAND_CAP) break;
     }
-  }
-  __syncthreads();
-
-  if (eq_fits) {
-    int n2 = 1;
-    while (n2 < n_eq_total) n2 <<= 1;
-    for (int x = n_eq_total + threadIdx.x; x < n2; x += SEL_THREADS) eqlist[x] = 0x7FFFFFFF;
+    if (n_cand >= a.top_k && n_cand <= CAND_CAP) {
+      const CandSrc cs{ckey, cidx, n_cand};
+      uint32_t tau;
+      int need_eq, n_eq_total = 0;
+      radix_kth(cs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
+      if (n_eq_total <= EQ_CAP) {
+        collect_above(cs, tau, true, list, eqlist, counters);
+        finish_selection(list, eqlist, a.top_k - need_eq, need_eq, n_eq_total, true, a.top_k,
+                         out, p, a.window, a.width);
+        return;
+      }
+    }
     __syncthreads();
-    if (n_eq_total > 1) bitonic_sort(eqlist, n2);
-    for (int x = threadIdx.x; x < need_eq; x += SEL_THREADS) list[n_gt + x] = eqlist[x];
-  } else {
+  }
+
+  // ---- general path: radix passes over the whole row ----
+  const RowSrc rs{row, n_c};
+  uint32_t tau;
+  int need_eq, n_eq_total = 0;
+  radix_kth(rs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
+  const int n_gt = a.top_k - need_eq;
+  const bool eq_fits = n_eq_total <= EQ_CAP;
+  collect_above(rs, tau, eq_fits, list, eqlist, counters);
+  if (!eq_fits) {
     // many exact ties: walk the row in index order and keep the first need_eq
     int taken = 0;
     for (int base = 0; base < n_c && taken < need_eq; base += SEL_THREADS) {
@@ -197,15 +410,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
       __syncthreads();
     }
   }
-  __syncthreads();
-
-  int n2 = 1;
-  while (n2 < a.top_k) n2 <<= 1;
-  for (int x = a.top_k + threadIdx.x; x < n2; x += SEL_THREADS) list[x] = 0x7FFFFFFF;
-  __syncthreads();
-  bitonic_sort(list, n2);
-  for (int t = threadIdx.x; t < a.top_k; t += SEL_THREADS) out[t] = list[t];
-  write_window_and_pad(out, a.top_k, p, a.window, a.width);
+  finish_selection(list, eqlist, n_gt, need_eq, n_eq_total, eq_fits, a.top_k, out, p, a.window,
+                   a.width);
 }
 
 // ---------------------------------------------------------------------------
