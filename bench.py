@@ -22,7 +22,8 @@ sys.path.insert(0, ROOT)
 METRIC = "selection+sparse-attn tokens/s at 128K-1M ctx; MFMA util and HBM GB/s vs peak"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
-PASSES = ["full_attention", "score", "select", "sparse_attention"]
+# in the order of the library's pass-timer slots
+PASSES = ["full_attention", "score", "select", "sparse_attention", "v_layout"]
 
 
 def log(*a):
@@ -43,6 +44,8 @@ def algorithmic_work(w):
         "score": ("mfma", 2.0 * hq * d * cand),
         "select": ("hbm", 4.0 * cand + 4.0 * B * nq * (w.top_k + w.window)),
         "sparse_attention": ("hbm", sel * hkv * d * 2.0 * esz + 2.0 * L * B * nq * hq * d * esz),
+        # V read once, written once in key-tile-major transposed order
+        "v_layout": ("hbm", 2.0 * B * nkv * hkv * d * esz),
     }
 
 
@@ -54,14 +57,14 @@ def source_sha(paths):
     return h.hexdigest()[:16]
 
 
+_CSRC = "token_level_sparse_pass_amd/csrc/"
 KERNEL_SOURCES = {
-    "full_attention": ["token_level_sparse_pass_amd/csrc/attn_fwd.hip",
-                       "token_level_sparse_pass_amd/csrc/hs2_device.h"],
-    "score": ["token_level_sparse_pass_amd/csrc/score.hip",
-              "token_level_sparse_pass_amd/csrc/hs2_device.h"],
-    "select": ["token_level_sparse_pass_amd/csrc/select.hip"],
-    "sparse_attention": ["token_level_sparse_pass_amd/csrc/sparse_attn.hip",
-                         "token_level_sparse_pass_amd/csrc/hs2_device.h"],
+    "full_attention": [_CSRC + "attn_fwd_bf16.hip", _CSRC + "attn_fwd.hip", _CSRC + "hs2_device.h"],
+    "score": [_CSRC + "score_bf16.hip", _CSRC + "score.hip", _CSRC + "hs2_device.h"],
+    "select": [_CSRC + "select.hip"],
+    "sparse_attention": [_CSRC + "sparse_attn_bf16.hip", _CSRC + "sparse_attn.hip",
+                         _CSRC + "hs2_device.h"],
+    "v_layout": [_CSRC + "attn_fwd_bf16.hip"],
 }
 
 
@@ -123,6 +126,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (read MIB, write MIB) "
+                         "three times, to scale HBM byte counters, and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Hybrid Block hot path here is a "
@@ -130,6 +136,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)          # one elementwise kernel: n bytes in, n out
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_kernel": "elementwise neg (float32)", "bytes_read": n,
+                          "bytes_written": n, "launches": 3}), flush=True)
+        return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2
 
@@ -161,8 +177,8 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = (ctypes.c_double * 4)()
-    nl = (ctypes.c_int64 * 4)()
+    ms = (ctypes.c_double * len(PASSES))()
+    nl = (ctypes.c_int64 * len(PASSES))()
     st = lib.hs2_profile_read(ms, nl)
     lib.hs2_profile_enable(0)
     if st != 0:
@@ -177,8 +193,10 @@ def main():
     passes = {}
     for i, name in enumerate(PASSES):
         bound, amount = work[name]
+        if nl[i] == 0:
+            continue                      # pass not taken on this path
         per_step_ms = ms[i] / args.steps
-        launches = nl[i] // args.steps if nl[i] else 0
+        launches = nl[i] // args.steps
         if bound == "mfma":
             ach = amount / (per_step_ms / 1e3) / 1e12 if per_step_ms > 0 else 0.0
             passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
@@ -189,7 +207,7 @@ def main():
             passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
                             "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
                             "frac": round(ach / PEAK_HBM_GBS, 4)}
-    dom = max(PASSES, key=lambda n: passes[n]["ms"])
+    dom = max(passes, key=lambda n: passes[n]["ms"])
     d = passes[dom]
     per_launch = work[dom][1] / max(1, d["launches_per_step"])
     traffic = measured_traffic(dom, w.name)

@@ -140,7 +140,10 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers,
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
  * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT
- * (selection) and HS2_PASS_SPARSE (sparse layers). hs2_profile_enable(1)
+ * (selection), HS2_PASS_SPARSE (sparse layers) and HS2_PASS_LAYOUT (the
+ * copy of V into the workspace in key-tile-major transposed order that the
+ * bf16 / head_dim 128 prefill kernel reads; absent on every other path).
+ * hs2_profile_enable(1)
  * starts a fresh record and (0) stops recording. hs2_profile_read waits for
  * the recorded events, then writes the summed milliseconds and the number of
  * timed launches of each pass (arrays of HS2_N_PASSES) and clears the record.
@@ -150,7 +153,8 @@ typedef enum {
   HS2_PASS_SCORE = 1,
   HS2_PASS_SELECT = 2,
   HS2_PASS_SPARSE = 3,
-  HS2_N_PASSES = 4
+  HS2_PASS_LAYOUT = 4,
+  HS2_N_PASSES = 5
 } hs2_pass;
 hs2_status hs2_profile_enable(int32_t on);
 hs2_status hs2_profile_read(double* ms, int64_t* launches);

@@ -336,15 +336,19 @@ int vt_keys_for(int n_kv) { return (n_kv + TK - 1) / TK * TK; }
 
 hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st);
 
-hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
-  if (!prefill_uses_vt(p.s) || !p.vt) return launch_attn_fwd_prefill_generic(p, st);
+hipError_t launch_v_transpose(const FwdPlan& p, hipStream_t st) {
+  if (!prefill_uses_vt(p.s) || !p.vt) return hipSuccess;
   const int vt_tiles = p.vt_keys / TK;
   const unsigned tgrid = (unsigned)((size_t)p.s.batch * p.s.h_kv * vt_tiles);
   hipLaunchKernelGGL(transpose_v_kernel, dim3(tgrid), dim3(256), 0, st,
                      reinterpret_cast<const __bf16*>(p.v), reinterpret_cast<__bf16*>(p.vt),
                      p.s.n_kv, p.s.h_kv, vt_tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
+  if (!prefill_uses_vt(p.s) || !p.vt) return launch_attn_fwd_prefill_generic(p, st);
+  const int vt_tiles = p.vt_keys / TK;
   Fwd2Args a;
   a.q = reinterpret_cast<const __bf16*>(p.q);
   a.k = reinterpret_cast<const __bf16*>(p.k);

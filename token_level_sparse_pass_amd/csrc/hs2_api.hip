@@ -314,6 +314,10 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
   f.vt = L.vt ? (char*)ws + L.vt : nullptr;
   f.vt_keys = L.vt_keys;
   {
+    PassTimer t(st, HS2_PASS_LAYOUT);
+    HIP_TRY(hs2::launch_v_transpose(f, st), "V transpose");
+  }
+  {
     PassTimer t(st, HS2_PASS_FULL);
     HIP_TRY(hs2::launch_attn_fwd_prefill(f, st), "full attention");
   }

@@ -32,6 +32,9 @@ struct FwdPlan {
 };
 bool prefill_uses_vt(const Shape& s);
 int vt_keys_for(int n_kv);
+// Fills vt from v (a no-op unless the bf16 kernel is used); must run before
+// launch_attn_fwd_prefill on the same stream.
+hipError_t launch_v_transpose(const FwdPlan& p, hipStream_t st);
 hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st);
 
 // Decode (n_q == 1): split-KV pass 1 that also stores every logit (log2
