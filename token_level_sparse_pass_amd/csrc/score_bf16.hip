@@ -166,35 +166,48 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
     const char* base = smem + stage * STAGE;
     const float* st = reinterpret_cast<const float*>(base + QT_BYTES);
 
-    // Q fragments of query block qb + 1 are read while block qb computes
+    // Q fragments of query block qb + 1 are read while block qb computes.
+    // The 16 (qb, kb) blocks form a software pipeline: the four MFMAs of
+    // block b are interleaved one by one with the exp work of block b - 1,
+    // so the matrix core and the VALU stay busy together.
     bf16x8 qf[2][4];
     float m2v[2], ilv[2];
 #pragma unroll
     for (int u = 0; u < 4; ++u) qf[0][u] = *reinterpret_cast<const bf16x8*>(base + qoff[0][u]);
     m2v[0] = st[srow[0]];
     ilv[0] = st[TQ + srow[0]];
+    f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f};
+    float pm2 = 0.f, pil = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int cur = qb & 1;
-      if (qb + 1 < 4) {
+    for (int b = 0; b < 16; ++b) {
+      const int qb = b >> 2, kb = b & 3, cur = qb & 1;
+      if (kb == 0 && qb + 1 < 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           qf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + qoff[qb + 1][u]);
         m2v[cur ^ 1] = st[srow[qb + 1]];
         ilv[cur ^ 1] = st[TQ + srow[qb + 1]];
       }
-      const float neg_m2 = -m2v[cur];
-      const float il = ilv[cur];
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x = OP::mma(kf[kb][u], qf[cur][u], x);
+      for (int u = 0; u < 4; ++u) x = OP::mma(kf[kb][u], qf[cur][u], x);
+      if (b > 0) {
+        const int pqb = (b - 1) >> 2, pkb = (b - 1) & 3;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sacc[qb][kb][e] = fmaf(fast_exp2(fmaf(x[e], a.c, neg_m2)), il, sacc[qb][kb][e]);
+          sacc[pqb][pkb][e] = fmaf(fast_exp2(fmaf(xp[e], a.c, pm2)), pil, sacc[pqb][pkb][e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+        }
       }
+      xp = x;
+      pm2 = -m2v[cur];
+      pil = ilv[cur];
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sacc[3][3][e] = fmaf(fast_exp2(fmaf(xp[e], a.c, pm2)), pil, sacc[3][3][e]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
