@@ -39,9 +39,17 @@ def algorithmic_work(w):
     cand = sum(max(0, p - w.window + 1) for p in pos) * B       # candidate pairs
     sel = sum(min(p + 1, w.top_k + w.window) for p in pos) * B  # selected keys
     L = w.n_sparse
+    if nq == 1:
+        # decode: one query per sequence, so pass 1 streams K and V once
+        # (8 flop/B) and the score pass reads the stored logits
+        full = ("hbm", 2.0 * B * nkv * hkv * d * esz + 2.0 * B * hq * d * esz)
+        score = ("hbm", 4.0 * hq * cand + 4.0 * cand)
+    else:
+        full = ("mfma", 4.0 * hq * d * pairs)
+        score = ("mfma", 2.0 * hq * d * cand)
     return {
-        "full_attention": ("mfma", 4.0 * hq * d * pairs),
-        "score": ("mfma", 2.0 * hq * d * cand),
+        "full_attention": full,
+        "score": score,
         "select": ("hbm", 4.0 * cand + 4.0 * B * nq * (w.top_k + w.window)),
         "sparse_attention": ("hbm", sel * hkv * d * 2.0 * esz + 2.0 * L * B * nq * hq * d * esz),
         # V read once, written once in key-tile-major transposed order

@@ -313,7 +313,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
   f.s = s; f.q = q; f.k = k; f.v = v; f.o = o; f.stats = stats; f.lse = lse;
   f.vt = L.vt ? (char*)ws + L.vt : nullptr;
   f.vt_keys = L.vt_keys;
-  {
+  if (f.vt) {
     PassTimer t(st, HS2_PASS_LAYOUT);
     HIP_TRY(hs2::launch_v_transpose(f, st), "V transpose");
   }

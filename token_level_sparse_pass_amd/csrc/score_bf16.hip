@@ -196,15 +196,21 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           sacc[pqb][pkb][e] = fmaf(fast_exp2(fmaf(xp[e], a.c, pm2)), pil, sacc[pqb][pkb][e]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
-        }
+        // two MFMAs first: the previous block's logits leave its last MFMA
+        // only about two MFMA issue slots after it
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
       }
       xp = x;
       pm2 = -m2v[cur];
       pil = ilv[cur];
+      // hard fence: a block's own exp work may not move up next to its MFMAs
+      // (it would wait out their latency); it runs with the next block
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) sacc[3][3][e] = fmaf(fast_exp2(fmaf(xp[e], a.c, pm2)), pil, sacc[3][3][e]);
