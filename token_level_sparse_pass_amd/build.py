@@ -13,7 +13,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhs2.so")
-SOURCES = ["hs2_api.hip", "attn_fwd.hip", "attn_fwd_bf16.hip", "score.hip", "score_bf16.hip",
+SOURCES = ["hs2_api.hip", "attn_fwd.hip", "attn_fwd_bf16.hip", "attn_decode_bf16.hip",
+           "score.hip", "score_bf16.hip",
            "select.hip",
            "sparse_attn.hip", "sparse_attn_bf16.hip"]
 

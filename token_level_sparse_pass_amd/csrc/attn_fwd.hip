@@ -318,7 +318,7 @@ hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st) {
 // ---------------------------------------------------------------------------
 struct DecArgs {
   const void* q; const void* k; const void* v;
-  float* part; float* logits;
+  float* part; float* logits; size_t lstride;
   int B, n_kv, h_q, h_kv, kps, n_split;
   float scale_log2;
 };
@@ -392,23 +392,19 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + kb * 16 + 4 * grp + e;
           float x = sv[e] * a.scale_log2;
-          xs[e] = x;
+          xs[e] = sv[e];
           if (j >= k_end) x = -INFINITY;
           p[rb][kb * 4 + e] = x;
           tmax = fmaxf(tmax, x);
         }
-        // keep the logits (log2 units) of valid heads for the scoring step
+        // keep the raw logits (q.k) of valid heads for the scoring step
         const int hh = rb * 16 + (lane & 15);
         if (hh < G) {
-          float* lrow = a.logits + ((size_t)b * a.h_q + g * G + hh) * a.n_kv;
+          float* lg = a.logits + ((size_t)b * a.h_kv + g) * a.lstride * G + hh;
           const int jb = j0 + kb * 16 + 4 * grp;
-          if (jb + 3 < k_end) {
-            *reinterpret_cast<float4*>(lrow + jb) = make_float4(xs[0], xs[1], xs[2], xs[3]);
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (jb + e < k_end) lrow[jb + e] = xs[e];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (jb + e < k_end) lg[(size_t)(jb + e) * G] = xs[e];
         }
       }
       tmax = xor_max(tmax, 16);
@@ -517,14 +513,20 @@ template <typename T, int D>
 static hipError_t launch_decode_t(const DecodePlan& p, hipStream_t st) {
   DecArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.part = p.part; a.logits = p.logits;
+  a.lstride = p.logits_stride;
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.scale_log2 = p.s.scale_log2;
   const int G = a.h_q / a.h_kv;
   const dim3 grid((unsigned)((size_t)a.B * a.h_kv * (a.n_split / 4)));
-  if (G <= 16) hipLaunchKernelGGL((attn_fwd_decode_kernel<T, D, 1>), grid, dim3(256), 0, st, a);
-  else if (G <= 32) hipLaunchKernelGGL((attn_fwd_decode_kernel<T, D, 2>), grid, dim3(256), 0, st, a);
-  else return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (decode_uses_bf16_kernel(p.s)) {
+    e = launch_attn_decode_bf16(p, st);
+  } else {
+    if (G <= 16) hipLaunchKernelGGL((attn_fwd_decode_kernel<T, D, 1>), grid, dim3(256), 0, st, a);
+    else if (G <= 32) hipLaunchKernelGGL((attn_fwd_decode_kernel<T, D, 2>), grid, dim3(256), 0, st, a);
+    else return hipErrorInvalidValue;
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const size_t plane = (size_t)a.B * a.h_q;
   hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3((unsigned)plane), dim3(D), 0, st,
@@ -543,7 +545,8 @@ hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// S[b][j] = sum over heads (in order) of 2^(logit - m2) / l, candidates only.
+// S[b][j] = sum over heads (in order) of 2^(c * logit - m2) / l, candidates only.
+// The logits of KV head g's query heads are contiguous per key.
 __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   extern __shared__ float sh[];                  // m2[h_q], inv_l[h_q]
   const int b = blockIdx.y;
@@ -555,10 +558,15 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   __syncthreads();
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= a.n_cand) return;
-  const float* lg = a.logits + (size_t)b * a.h_q * a.n_kv + j;
+  const int G = a.h_q / a.h_kv;
   float s = 0.f;
-  for (int h = 0; h < a.h_q; ++h)
-    s = fmaf(fast_exp2(lg[(size_t)h * a.n_kv] - sh[h]), sh[a.h_q + h], s);
+  for (int g = 0; g < a.h_kv; ++g) {
+    const float* lg = a.logits + (((size_t)b * a.h_kv + g) * a.logits_stride + j) * G;
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = g * G + hh;
+      s = fmaf(fast_exp2(fmaf(lg[hh], a.c, -sh[h])), sh[a.h_q + h], s);
+    }
+  }
   a.scores[(size_t)b * a.score_stride + j] = s;
 }
 

@@ -118,6 +118,7 @@ struct Layout {
   int vt_keys = 0;
   size_t part = 0, logits = 0, scores = 0;   // byte offsets
   size_t n_part = 0, n_logits = 0;
+  size_t logits_stride = 0;  // floats per logits row (decode)
   size_t stride = 0;         // floats per score row
   int chunk_rows = 0;        // prefill query rows per chunk
   int n_split = 0, kps = 0;  // decode split
@@ -138,7 +139,8 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
     l.n_part = (size_t)p.batch * p.h_q * l.n_split * (p.head_dim + 2);
     off += align_up(l.n_part * sizeof(float));
     l.logits = off;
-    l.n_logits = (size_t)p.batch * p.h_q * p.n_kv;
+    l.logits_stride = ((size_t)p.n_kv + 63) / 64 * 64;
+    l.n_logits = (size_t)p.batch * p.h_q * l.logits_stride;
     off += align_up(l.n_logits * sizeof(float));
     l.scores = off;
     off += align_up((size_t)p.batch * std::max<size_t>(l.stride, 1) * sizeof(float));
@@ -282,16 +284,16 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
   if (is_decode(p)) {
     hs2::DecodePlan d;
     d.s = s; d.q = q; d.k = k; d.v = v; d.o = o; d.stats = stats; d.lse = lse;
-    d.part = fptr(ws, L.part); d.logits = fptr(ws, L.logits);
+    d.part = fptr(ws, L.part); d.logits = fptr(ws, L.logits); d.logits_stride = L.logits_stride;
     d.keys_per_split = L.kps; d.n_split = L.n_split;
     {
       PassTimer t(st, HS2_PASS_FULL);
       HIP_TRY(hs2::launch_attn_fwd_decode(d, st), "decode attention");
     }
     hs2::DecodeScorePlan ds;
-    ds.batch = p.batch; ds.h_q = p.h_q; ds.n_kv = p.n_kv;
+    ds.batch = p.batch; ds.h_q = p.h_q; ds.h_kv = p.h_kv; ds.n_kv = p.n_kv; ds.c = s.scale_log2;
     ds.n_cand = std::max(0, p.n_kv - p.window);
-    ds.logits = d.logits; ds.stats = stats; ds.scores = scores; ds.score_stride = L.stride;
+    ds.logits = d.logits; ds.logits_stride = L.logits_stride; ds.stats = stats; ds.scores = scores; ds.score_stride = L.stride;
     {
       PassTimer t(st, HS2_PASS_SCORE);
       HIP_TRY(hs2::launch_decode_score(ds, st), "decode score");

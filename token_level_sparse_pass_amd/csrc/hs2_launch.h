@@ -37,10 +37,13 @@ int vt_keys_for(int n_kv);
 hipError_t launch_v_transpose(const FwdPlan& p, hipStream_t st);
 hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st);
 
-// Decode (n_q == 1): split-KV pass 1 that also stores every logit (log2
-// units) so the score needs no second read of K; partials are merged by
+// Decode (n_q == 1): split-KV pass 1 that also stores every raw logit (q.k)
+// so the score needs no second read of K; partials are merged by
 // the combine step. part: [batch][h_q][n_split][head_dim + 2] floats,
-// logits: [batch][h_q][n_kv] floats.
+// logits: [batch][h_kv][logits_stride][G] floats (G = h_q / h_kv: the raw
+// logits q.k of a KV head's query heads are contiguous per key), with
+// logits_stride a multiple of 64 that is >= n_kv, so whole tiles of a ragged
+// last split stay inside.
 struct DecodePlan {
   Shape s;
   const void* q; const void* k; const void* v;
@@ -48,17 +51,23 @@ struct DecodePlan {
   float* stats;
   float* lse;
   float* part;
-  float* logits;
+  float* logits; size_t logits_stride;
   int keys_per_split;     // multiple of 64
   int n_split;
 };
 int decode_n_split(int n_kv, int* keys_per_split);
 hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st);
+// bf16 / head_dim 128 split kernel (G <= 16); writes the partials and raw
+// logits only, launch_attn_fwd_decode runs the combine
+bool decode_uses_bf16_kernel(const Shape& s);
+hipError_t launch_attn_decode_bf16(const DecodePlan& p, hipStream_t st);
 
-// Decode score: S[b][j] = sum_h 2^(logit - m2) / l for candidate keys.
+// Decode score: S[b][j] = sum_h 2^(c * logit - m2) / l for candidate keys,
+// from the raw logits (q.k) the decode pass stored.
 struct DecodeScorePlan {
-  int batch, h_q, n_kv, n_cand;   // n_cand = candidates per row (p - window + 1)
-  const float* logits; const float* stats;
+  int batch, h_q, h_kv, n_kv, n_cand;   // n_cand = candidates per row (p - window + 1)
+  float c;                        // softmax scale * log2(e)
+  const float* logits; size_t logits_stride; const float* stats;
   float* scores; size_t score_stride;
 };
 hipError_t launch_decode_score(const DecodeScorePlan& p, hipStream_t st);
