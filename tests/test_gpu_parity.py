@@ -109,6 +109,12 @@ FULL_CASES = [
     small("f_bf16_no_candidates", "bf16", 1, 20, 50, 4, 2, 64, 8, 64),
     small("f_decode", "bf16", 3, 1, 2500, 16, 2, 128, 256, 64),
     small("f_decode_fp32", "fp32", 2, 1, 777, 8, 8, 64, 100, 16),
+    # one query head per KV head on the bf16 / head_dim 128 kernels
+    small("f_bf16_g1", "bf16", 1, 200, 700, 4, 4, 128, 64, 16),
+    # 16 query heads per KV head: the widest group the decode kernel takes
+    small("f_decode_g16", "bf16", 2, 1, 3000, 32, 2, 128, 256, 64),
+    # every key inside the window: no candidate to rank
+    small("f_decode_nocand", "bf16", 2, 1, 100, 8, 2, 128, 64, 128),
 ]
 
 
@@ -174,9 +180,28 @@ def test_exact_ties_pick_lowest_indices(gpu_lib):
                                np.log(pos.cpu().numpy() + 1.0)[None].repeat(8, 0), atol=1e-5)
 
 
+@pytest.mark.parametrize("nq,B", [(4, 1), (1, 2)], ids=["prefill", "decode"])
+def test_exact_ties_long_rows(gpu_lib, nq, B):
+    # rows of more than 16384 candidates first try a sampled threshold; with
+    # every score equal it gathers too many keys, retries, falls back to the
+    # exact select and must still take the lowest indices
+    n_kv, top_k, w = 40000, 1024, 128
+    case = small("ties_long", "bf16", B, nq, n_kv, 8, 2, 128, top_k, w)
+    inp = make_inputs(case, device="cuda")
+    k = torch.zeros_like(inp["k"])
+    _, idx, _, _ = gpu_lib.full_attn_select(inp["q_full"], k, inp["v"], top_k=top_k, window=w)
+    gi = idx.cpu().numpy()
+    for b in range(B):
+        for i in range(nq):
+            p = n_kv - nq + i
+            row = gi[b, i][gi[b, i] >= 0]
+            assert list(row) == list(range(top_k)) + list(range(p - w + 1, p + 1)), (b, i)
+
+
 @pytest.mark.parametrize("case", [
     small("blk_bf16", "bf16", 1, 300, 2000, 8, 2, 128, 0, 16),
     small("blk_fp32_unit", "fp32", 1, 120, 400, 4, 1, 64, 0, 8),
+    small("blk_decode", "bf16", 3, 1, 5000, 16, 2, 128, 0, 64),
 ], ids=lambda c: c.name)
 def test_block_selection(gpu_lib, case):
     bs, tb = (16, 6) if case.dtype == "bf16" else (1, 30)
