@@ -127,6 +127,89 @@ def cpu_baseline(w, inp, target_s=15.0, max_rows=64):
                       f"{total_t:.1f} s"}
 
 
+def decode_loop(args):
+    """Steps of hs2_decode_step over a growing, ragged cache (decode workload).
+
+    The 64-sequence, 128K-capacity decode workload starts every sequence at
+    a seeded length in [cap/2, cap - steps - 1); each step appends one token
+    per sequence and runs the whole block for it. Inputs of every step are
+    drawn before the timed region; one step = one decode_step call.
+    """
+    import numpy as np
+    import torch
+    from synth import CONFIGS, decode_step_inputs, make_inputs
+    from token_level_sparse_pass_amd import hs2
+
+    lib = hs2.load()
+    w = CONFIGS[3]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_steps = args.warmup + args.steps
+    cap = w.n_kv
+    rng = np.random.default_rng(2024)
+    lens0 = rng.integers(cap // 2, cap - n_steps - 1, size=w.batch).tolist()
+    log(f"decode loop on {w.name}: generating the cache and {n_steps} steps of inputs")
+    inp = make_inputs(w, device=dev, sparse_layers=0)
+    k_cache, v_cache = inp["k"], inp["v"]
+    xs = [decode_step_inputs(w, s, device=dev) for s in range(n_steps)]
+    kw = dict(top_k=w.top_k, window=w.window)
+    p = hs2.problem(k_cache.dtype, w.batch, 1, cap, w.h_q, w.h_kv, w.d, **kw)
+    ws = hs2.alloc_workspace(p, dev)
+    lens = list(lens0)
+    out = None
+    for s in range(args.warmup):
+        x = xs[s]
+        out = hs2.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
+                              v_cache, lens, workspace=ws, out=out, **kw)
+        lens = [n + 1 for n in lens]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    keys_read = 0
+    lib.hs2_profile_enable(1)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for s in range(args.warmup, n_steps):
+        x = xs[s]
+        out = hs2.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
+                              v_cache, lens, workspace=ws, out=out, **kw)
+        keys_read += sum(n + 1 for n in lens)
+        lens = [n + 1 for n in lens]
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (ctypes.c_double * len(PASSES))()
+    nl = (ctypes.c_int64 * len(PASSES))()
+    st = lib.hs2_profile_read(ms, nl)
+    lib.hs2_profile_enable(0)
+    if st != 0:
+        raise RuntimeError(lib.hs2_last_error().decode())
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    esz = 2
+    kv_bytes = 2.0 * keys_read * w.h_kv * w.d * esz / args.steps      # K + V per step
+    passes = {}
+    for i, name in enumerate(PASSES):
+        if nl[i] == 0:
+            continue
+        per = ms[i] / args.steps
+        passes[name] = {"ms": round(per, 4), "launches_per_step": int(nl[i] // args.steps)}
+    fa = passes["full_attention"]["ms"]
+    ach = kv_bytes / (fa / 1e3) / 1e9
+    rec = {"metric": "decode-loop tokens/s (one Hybrid Block step per new token, ragged batch)",
+           "value": round(w.batch / (ms_step / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
+           "config": {"workload": w.name + "_decode_loop", "batch": w.batch, "capacity": cap,
+                      "start_lengths": [int(min(lens0)), int(max(lens0))], "h_q": w.h_q,
+                      "h_kv": w.h_kv, "head_dim": w.d, "top_k": w.top_k, "window": w.window,
+                      "sparse_layers": w.n_sparse, "parallelism": "single GPU"},
+           "roofline": {"kernel": "full_attention", "bound": "hbm", "achieved": round(ach, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                        "algorithmic_per_launch": kv_bytes, "traffic": None},
+           "passes": passes, "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +217,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="time decode steps over a growing ragged cache (the 64 x 128K decode "
+                         "workload) instead of the default workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB) "
                          "three times, to scale HBM byte counters, and exit")
@@ -153,6 +239,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_kernel": "elementwise neg (float32)", "bytes_read": n,
                           "bytes_written": n, "launches": 3}), flush=True)
+        return
+    if args.decode_loop:
+        decode_loop(args)
         return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2

@@ -137,6 +137,32 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* One decode step of the whole block over a growing KV cache, for a batch
+ * of sequences of different lengths (the block's deployment shape: decode
+ * is where the Cross-Decoder's hybrid blocks run, bound by memory bandwidth;
+ * blog.lynxflow.co, section "Token-Level Sparse Selection and Deployment
+ * Optimization"; the sparse layers reuse the one cache, hitechexpert.top,
+ * section "Two-Level KV Sharing").
+ *   p->n_q must be 1; p->n_kv is the cache capacity.
+ *   k_cache, v_cache  DEVICE [batch, n_kv, h_kv, head_dim]: lens[b] valid rows
+ *   k_new, v_new      DEVICE [batch, 1, h_kv, head_dim]: the new token's rows
+ *   q_full            DEVICE [batch, 1, h_q, head_dim]
+ *   q_sparse          DEVICE [n_sparse_layers, batch, 1, h_q, head_dim]
+ *   lens              HOST [batch] lengths before the step, read during the
+ *                     call only; 0 <= lens[b] < n_kv, else HS2_ERR_SHAPE
+ *                     before any launch. The caller advances it.
+ * The call writes k_new, v_new at row lens[b] of the caches, then runs the
+ * block for the query at position lens[b] over keys 0..lens[b] (its own row
+ * included): outputs as hs2_block_forward, idx entries are cache rows.
+ * Workspace as hs2_workspace_size for the same problem. */
+hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers,
+                           const void* q_full, const void* q_sparse,
+                           const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* lens,
+                           void* o_full, void* o_sparse, int32_t* idx,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
  * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT

@@ -228,6 +228,40 @@ def block_forward(q_full, q_sparse, k, v, top_k=1024, window=128,
     return dict(o_full=o_full, lse=lse, S=S, idx=idx, tau=tau, o_sparse=o_sparse)
 
 
+def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, top_k=1024, window=128,
+                select="token", block_size=64, top_blocks=16, scale=None):
+    """One decode step over a growing cache, per sequence (batch rows may
+    hold different lengths).
+
+    For sequence b the new token's K/V row joins the first lens[b] cached
+    rows, so the cache the full layer and every sparse layer read ("Two-Level
+    KV Sharing", KV Reuse) holds keys 0..lens[b], and the new query sits at
+    position lens[b]; the block is then exactly block_forward on that prefix
+    with one query. q_full [B, 1, h_q, d], q_sparse [L, B, 1, h_q, d], k_new /
+    v_new [B, 1, h_kv, d], k_cache / v_cache [B, cap, h_kv, d] (rows past
+    lens[b] are never read). Returns dict(o_full [B, 1, h_q, d], lse
+    [B, h_q, 1], S (list of B score rows), idx [B, 1, W], tau [B, 1],
+    o_sparse [L, B, 1, h_q, d]).
+    """
+    q_full, q_sparse = np.asarray(q_full), np.asarray(q_sparse)
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+    k_cache, v_cache = np.asarray(k_cache), np.asarray(v_cache)
+    outs = []
+    for b in range(q_full.shape[0]):
+        n = int(lens[b])
+        kb = np.concatenate([k_cache[b, :n], k_new[b]], axis=0)[None]
+        vb = np.concatenate([v_cache[b, :n], v_new[b]], axis=0)[None]
+        outs.append(block_forward(q_full[b:b + 1], q_sparse[:, b:b + 1], kb, vb, top_k=top_k,
+                                  window=window, select=select, block_size=block_size,
+                                  top_blocks=top_blocks, scale=scale))
+    return dict(o_full=np.concatenate([o["o_full"] for o in outs]),
+                lse=np.concatenate([o["lse"] for o in outs]),
+                S=[o["S"][0, 0] for o in outs],
+                idx=np.concatenate([o["idx"] for o in outs]),
+                tau=np.concatenate([o["tau"] for o in outs]),
+                o_sparse=np.concatenate([o["o_sparse"] for o in outs], axis=1))
+
+
 # ----------------------------------------------------------------------------
 # the same definitions, streamed over K/V chunks for a few sampled query rows
 # (large contexts: the full score matrix never exists)

@@ -11,7 +11,7 @@ planted retrieval structure:
 * clusters - 32 runs of 32 consecutive keys get that common direction added.
 
 Streams: 0 = full-layer Q, 1 = K, 2 = V, 3 = structure, 10 + l = sparse Q of
-layer l. The same bits go to the GPU library and (as a host copy) to the
+layer l, 1000 + 16 * step + 0..3 = the new token of decode step `step`. The same bits go to the GPU library and (as a host copy) to the
 oracle. Nothing here computes attention, scores or selections.
 """
 import math
@@ -112,6 +112,22 @@ def make_inputs(w: Workload, device="cpu", sparse_layers=None) -> dict:
         meta.update(cluster_start=starts, cluster_pos=pos,
                     direction=u.cpu().numpy())
     return {"q_full": q_full, "k": k, "v": v, "q_sparse": q_sparse, "meta": meta}
+
+
+def decode_step_inputs(w: Workload, step: int, device="cpu", sparse_layers=None) -> dict:
+    """The new token's tensors for decode step `step` of workload `w`.
+
+    Returns q_full [B, 1, h_q, d], q_sparse [L, B, 1, h_q, d] and the new
+    cache rows k_new, v_new [B, 1, h_kv, d]; streams 1000 + 16 * step + 0..3,
+    so every step draws fresh, reproducible values.
+    """
+    B, hq, hkv, d = w.batch, w.h_q, w.h_kv, w.d
+    L = w.n_sparse if sparse_layers is None else sparse_layers
+    base = 1000 + 16 * step
+    return dict(q_full=_randn((B, 1, hq, d), w, base, device),
+                q_sparse=_randn((L, B, 1, hq, d), w, base + 1, device),
+                k_new=_randn((B, 1, hkv, d), w, base + 2, device),
+                v_new=_randn((B, 1, hkv, d), w, base + 3, device))
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:

@@ -147,3 +147,30 @@ def test_debug_rows_validated():
     st = lib.hs2_full_attn_select(ctypes.byref(p), *([vp(FAKE)] * 5), None, ctypes.byref(dbg),
                                   vp(FAKE), hs2.workspace_size(p)[1], None)
     assert st == 2
+
+
+def decode_call(p, lens, n_layers=2, ptrs=None, ws_bytes=None):
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    P = dict(q=FAKE, qs=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, o=FAKE, os=FAKE, idx=FAKE,
+             ws=FAKE)
+    P.update(ptrs or {})
+    if ws_bytes is None:
+        ws_bytes = hs2.workspace_size(p)[1]
+    arr = None if lens is None else (ctypes.c_int32 * len(lens))(*lens)
+    return lib.hs2_decode_step(ctypes.byref(p), n_layers, vp(P["q"]), vp(P["qs"]), vp(P["kn"]),
+                               vp(P["vn"]), vp(P["kc"]), vp(P["vc"]), arr, vp(P["o"]),
+                               vp(P["os"]), vp(P["idx"]), None, vp(P["ws"]), ws_bytes, None)
+
+
+def test_decode_step_rejections():
+    p = base_problem(n_q=1, batch=3, n_kv=4096)
+    assert decode_call(base_problem(), [1]) == 2                   # n_q != 1
+    assert decode_call(p, None) == 1                               # no lengths
+    assert decode_call(p, [10, 4096, 3]) == 2                      # no room left
+    assert "no room" in hs2.load().hs2_last_error().decode()
+    assert decode_call(p, [10, -1, 3]) == 2
+    assert decode_call(p, [10, 20, 3], ptrs=dict(kn=None)) == 1
+    assert decode_call(p, [10, 20, 3], ptrs=dict(vc=FAKE + 4)) == 5
+    mn, _ = hs2.workspace_size(p)
+    assert decode_call(p, [10, 20, 3], ws_bytes=mn - 1) == 4

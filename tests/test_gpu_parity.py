@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import hs2_oracle as O
-from synth import CONFIGS, Workload, make_inputs, to_host
+from synth import CONFIGS, Workload, decode_step_inputs, make_inputs, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -352,3 +352,65 @@ def test_config_sampled(gpu_lib, cid, n_rows):
         for j, t in zip(meta["needle_pos"], meta["needle_target"]):
             hits += int(j in set(gi[0, t - w.q_off].tolist()))
         say("needle hits", hits, "of", len(meta["needle_pos"]))
+
+
+# ---------------------------------------------------------------------------
+# decode steps over a growing cache, ragged batch
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,hq,hkv,d,select", [
+    ("bf16", 16, 2, 128, "token"),
+    ("fp32", 8, 2, 64, "token"),
+    ("bf16", 16, 2, 128, "block"),
+], ids=["bf16_d128", "fp32_d64", "bf16_block"])
+def test_decode_steps_growing_cache(gpu_lib, dtype, hq, hkv, d, select):
+    # one sequence with fewer candidates than top_k, one past k + w, one long;
+    # cache rows past each length hold unrelated values and must never be read
+    lens = [100, 1150, 2900]
+    cap, top_k, window, L, steps = 3000, 256, 64, 2, 4
+    bs, tb = 16, 12
+    w = small("decode_loop", dtype, len(lens), 1, cap, hq, hkv, d, top_k, window, L=L, cid=7)
+    kw = dict(top_k=top_k, window=window, select=select, block_size=bs, top_blocks=tb)
+    inp = make_inputs(w, device="cuda")
+    k_cache, v_cache = inp["k"].clone(), inp["v"].clone()
+    k_host, v_host = host(k_cache), host(v_cache)
+    p = gpu_lib.problem(inp["k"].dtype, len(lens), 1, cap, hq, hkv, d, **kw)
+    ws = gpu_lib.alloc_workspace(p, "cuda")
+    tol = TOL[dtype]
+    for step in range(steps):
+        say("step", step, "lens", lens)
+        x = decode_step_inputs(w, step, device="cuda")
+        out = gpu_lib.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
+                                  v_cache, lens, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        xh = {n: host(t) for n, t in x.items()}
+        ref = O.decode_step(xh["q_full"], xh["q_sparse"], xh["k_new"], xh["v_new"], k_host,
+                            v_host, lens, **kw)
+        kc, vc = host(k_cache), host(v_cache)
+        for b, n in enumerate(lens):
+            assert np.array_equal(kc[b, n], xh["k_new"][b, 0]), "K row appended"
+            assert np.array_equal(vc[b, n], xh["v_new"][b, 0]), "V row appended"
+            k_host[b, n], v_host[b, n] = xh["k_new"][b, 0], xh["v_new"][b, 0]
+        assert np.array_equal(kc, k_host) and np.array_equal(vc, v_host), "nothing else written"
+        err_o = np.abs(as_np(out["o_full"]) - ref["o_full"]).max()
+        err_lse = np.abs(out["lse"].cpu().numpy() - ref["lse"]).max()
+        say("o_full err", err_o, "lse err", err_lse)
+        assert err_o <= tol and err_lse <= 1e-4
+        gi = out["idx"].cpu().numpy()[:, 0]
+        o_sp = as_np(out["o_sparse"])
+        for b, n in enumerate(lens):
+            ok, nd, why = O.compare_selection(gi[b], ref["idx"][b, 0], ref["S"][b], n, window,
+                                              float(ref["tau"][b, 0]),
+                                              block_size=bs if select == "block" else 0)
+            assert ok, f"step {step} seq {b}: {why}"
+            if nd == 0:
+                want = ref["o_sparse"][:, b, 0]
+            else:
+                # near-tie: the oracle's sparse layers on the GPU's own index row
+                kb = O.widen(k_host[b, :n + 1])[None]
+                vb = O.widen(v_host[b, :n + 1])[None]
+                row = gi[b][None, None]
+                want = np.stack([O.sparse_layer(xh["q_sparse"][l, b:b + 1], kb, vb, row)[0, 0]
+                                 for l in range(L)])
+            err_s = np.abs(o_sp[:, b, 0] - want).max()
+            assert err_s <= tol, f"step {step} seq {b}: sparse err {err_s}"
+        lens = [n + 1 for n in lens]

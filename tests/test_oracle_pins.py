@@ -298,3 +298,57 @@ def test_pages_constants():
         assert w.top_k == c["top_k_global_tokens"]["value"]
         assert w.window == c["recent_window_tokens"]["value"]
         assert w.block_size == c["previous_generation_block_tokens"]["value"]
+
+
+# ----------------------------------------------------------------------------
+# one decode step over a growing cache
+# ----------------------------------------------------------------------------
+def _decode_case(seed, lens, cap=40, hq=4, hkv=2, d=8, L=2):
+    B = len(lens)
+    return dict(q_full=rand((B, 1, hq, d), seed), q_sparse=rand((L, B, 1, hq, d), seed + 1),
+                k_new=rand((B, 1, hkv, d), seed + 2), v_new=rand((B, 1, hkv, d), seed + 3),
+                k_cache=rand((B, cap, hkv, d), seed + 4), v_cache=rand((B, cap, hkv, d), seed + 5),
+                lens=lens)
+
+
+def test_decode_step_is_last_row_of_prefill():
+    # the step's query sees keys 0..lens[b] with its own row last: the same
+    # as the last row of the causal prefill over that prefix
+    c = _decode_case(40, [20, 33, 3])
+    got = O.decode_step(**c, top_k=5, window=4)
+    for b, n in enumerate(c["lens"]):
+        k = np.concatenate([c["k_cache"][b, :n], c["k_new"][b]])[None]
+        v = np.concatenate([c["v_cache"][b, :n], c["v_new"][b]])[None]
+        q = np.concatenate([rand((n, 4, 8), 90 + b), c["q_full"][b]])[None]
+        qs = np.concatenate([rand((2, n, 4, 8), 95 + b), c["q_sparse"][:, b]], axis=1)[:, None]
+        ref = O.block_forward(q, qs, k, v, top_k=5, window=4)
+        np.testing.assert_allclose(got["o_full"][b, 0], ref["o_full"][0, -1], atol=1e-12)
+        np.testing.assert_allclose(got["lse"][b, :, 0], ref["lse"][0, :, -1], atol=1e-12)
+        np.testing.assert_array_equal(got["idx"][b, 0], ref["idx"][0, -1])
+        np.testing.assert_allclose(got["o_sparse"][:, b, 0], ref["o_sparse"][:, 0, -1], atol=1e-12)
+
+
+def test_decode_step_ignores_rows_past_length():
+    c = _decode_case(50, [7, 25])
+    base = O.decode_step(**c, top_k=4, window=3)
+    for b, n in enumerate(c["lens"]):
+        c["k_cache"][b, n:] = 1e6
+        c["v_cache"][b, n:] = -1e6
+    again = O.decode_step(**c, top_k=4, window=3)
+    for key in ("o_full", "lse", "idx", "o_sparse"):
+        np.testing.assert_array_equal(base[key], again[key])
+
+
+def test_decode_step_zero_keys_closed_form():
+    # every logit 0: LSE = log(n + 1) over the n + 1 keys, and ties take the
+    # lowest candidate indices before the window
+    c = _decode_case(60, [30, 10, 0])
+    c["k_cache"][:] = 0
+    c["k_new"][:] = 0
+    got = O.decode_step(**c, top_k=6, window=5)
+    for b, n in enumerate(c["lens"]):
+        np.testing.assert_allclose(got["lse"][b, :, 0], math.log(n + 1), atol=1e-12)
+        n_c = max(0, n - 5 + 1)
+        want = list(range(min(6, n_c))) + list(range(max(0, n - 4), n + 1))
+        row = got["idx"][b, 0]
+        assert list(row[row >= 0]) == want

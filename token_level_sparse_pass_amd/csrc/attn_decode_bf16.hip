@@ -36,6 +36,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct Dec2Args {
   const __bf16* q; const __bf16* k; const __bf16* v;
   float* part; float* logits; size_t lstride;
+  const int32_t* seq_len;
   int B, n_kv, h_q, h_kv, kps, n_split;
   float c;                                   // softmax scale * log2(e)
 };
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
   const int bs = unit / a.h_kv;
   const int split = bs % a.n_split;
   const int b = bs / a.n_split;
+  const int n_keys = a.seq_len ? a.seq_len[b] : a.n_kv;   // keys of this sequence
   const int k_begin = split * a.kps;
-  const int k_end = min(a.n_kv, k_begin + a.kps);
+  const int k_end = min(n_keys, k_begin + a.kps);
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + TK - 1) / TK : 0;
 
   const size_t kvs = (size_t)a.h_kv * D;
@@ -257,7 +259,7 @@ hipError_t launch_attn_decode_bf16(const DecodePlan& p, hipStream_t st) {
   a.q = reinterpret_cast<const __bf16*>(p.q);
   a.k = reinterpret_cast<const __bf16*>(p.k);
   a.v = reinterpret_cast<const __bf16*>(p.v);
-  a.part = p.part; a.logits = p.logits; a.lstride = p.logits_stride;
+  a.part = p.part; a.logits = p.logits; a.lstride = p.logits_stride; a.seq_len = p.seq_len;
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.c = p.s.scale_log2;
   const dim3 grid((unsigned)((size_t)a.B * a.h_kv * a.n_split));

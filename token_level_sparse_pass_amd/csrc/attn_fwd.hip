@@ -319,6 +319,7 @@ hipError_t launch_attn_fwd_prefill_generic(const FwdPlan& p, hipStream_t st) {
 struct DecArgs {
   const void* q; const void* k; const void* v;
   float* part; float* logits; size_t lstride;
+  const int32_t* seq_len;
   int B, n_kv, h_q, h_kv, kps, n_split;
   float scale_log2;
 };
@@ -336,8 +337,9 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
   const int split = (blockIdx.x - bg * wg_per_bg) * 4 + wave;
   const int b = bg / a.h_kv;
   const int g = bg - b * a.h_kv;
+  const int n_keys = a.seq_len ? a.seq_len[b] : a.n_kv;   // keys of this sequence
   const int k_begin = split * a.kps;
-  const int k_end = min(a.n_kv, k_begin + a.kps);
+  const int k_end = min(n_keys, k_begin + a.kps);
 
   const T* qb = reinterpret_cast<const T*>(a.q);
   const T* kseq = reinterpret_cast<const T*>(a.k) + ((size_t)b * a.n_kv * a.h_kv + g) * D;
@@ -513,7 +515,7 @@ template <typename T, int D>
 static hipError_t launch_decode_t(const DecodePlan& p, hipStream_t st) {
   DecArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.part = p.part; a.logits = p.logits;
-  a.lstride = p.logits_stride;
+  a.lstride = p.logits_stride; a.seq_len = p.seq_len;
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.scale_log2 = p.s.scale_log2;
   const int G = a.h_q / a.h_kv;
@@ -557,7 +559,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   }
   __syncthreads();
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= a.n_cand) return;
+  const int n_cand = a.seq_len ? a.seq_len[b] - a.window : a.n_cand;
+  if (j >= n_cand) return;
   const int G = a.h_q / a.h_kv;
   float s = 0.f;
   for (int g = 0; g < a.h_kv; ++g) {

@@ -119,6 +119,7 @@ struct Layout {
   size_t part = 0, logits = 0, scores = 0;   // byte offsets
   size_t n_part = 0, n_logits = 0;
   size_t logits_stride = 0;  // floats per logits row (decode)
+  size_t lens = 0;           // [B] int32 keys per sequence (decode step)
   size_t stride = 0;         // floats per score row
   int chunk_rows = 0;        // prefill query rows per chunk
   int n_split = 0, kps = 0;  // decode split
@@ -144,6 +145,8 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
     off += align_up(l.n_logits * sizeof(float));
     l.scores = off;
     off += align_up((size_t)p.batch * std::max<size_t>(l.stride, 1) * sizeof(float));
+    l.lens = off;
+    off += align_up((size_t)p.batch * sizeof(int32_t));
     l.chunk_rows = p.batch;
     l.total = off;
     if (min_bytes) *min_bytes = off;
@@ -258,9 +261,11 @@ hs2_status check_full_args(const hs2_problem* p, const void* q, const void* k, c
   return HS2_OK;
 }
 
+// seq_len (decode only, device, may be NULL): keys held by each sequence,
+// whose query then sits at seq_len[b] - 1; NULL means n_kv for all.
 hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const void* v, void* o,
                     int32_t* idx, float* lse, const hs2_debug* dbg, void* ws,
-                    const Layout& L, hipStream_t st) {
+                    const Layout& L, hipStream_t st, const int32_t* seq_len = nullptr) {
   const hs2::Shape s = shape_of(p);
   float* stats = fptr(ws, L.stats);
   float* scores = fptr(ws, L.scores);
@@ -285,7 +290,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
     hs2::DecodePlan d;
     d.s = s; d.q = q; d.k = k; d.v = v; d.o = o; d.stats = stats; d.lse = lse;
     d.part = fptr(ws, L.part); d.logits = fptr(ws, L.logits); d.logits_stride = L.logits_stride;
-    d.keys_per_split = L.kps; d.n_split = L.n_split;
+    d.keys_per_split = L.kps; d.n_split = L.n_split; d.seq_len = seq_len;
     {
       PassTimer t(st, HS2_PASS_FULL);
       HIP_TRY(hs2::launch_attn_fwd_decode(d, st), "decode attention");
@@ -293,6 +298,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
     hs2::DecodeScorePlan ds;
     ds.batch = p.batch; ds.h_q = p.h_q; ds.h_kv = p.h_kv; ds.n_kv = p.n_kv; ds.c = s.scale_log2;
     ds.n_cand = std::max(0, p.n_kv - p.window);
+    ds.window = p.window; ds.seq_len = seq_len;
     ds.logits = d.logits; ds.logits_stride = L.logits_stride; ds.stats = stats; ds.scores = scores; ds.score_stride = L.stride;
     {
       PassTimer t(st, HS2_PASS_SCORE);
@@ -300,7 +306,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
     }
     HS2_TRY(export_rows(0, p.batch));
     hs2::SelectPlan sp;
-    sp.rows = p.batch; sp.flat0 = 0; sp.n_q = 1; sp.n_kv = p.n_kv;
+    sp.rows = p.batch; sp.flat0 = 0; sp.n_q = 1; sp.n_kv = p.n_kv; sp.seq_len = seq_len;
     sp.top_k = p.top_k; sp.window = p.window; sp.width = width;
     sp.block_mode = block_mode; sp.block_size = p.block_size; sp.top_blocks = p.top_blocks;
     sp.scores = scores; sp.score_stride = L.stride; sp.idx = idx;
@@ -433,6 +439,39 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers, cons
   HS2_TRY(run_full(*p, q_full, k, v, o_full, idx, lse, nullptr, workspace, L, st));
   if (n_sparse_layers == 0) return HS2_OK;
   return run_sparse(*p, n_sparse_layers, q_sparse, k, v, idx, o_sparse, st);
+}
+
+hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                           const void* q_sparse, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* lens, void* o_full,
+                           void* o_sparse, int32_t* idx, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  HS2_TRY(check_problem(p));
+  if (p->n_q != 1) return fail(HS2_ERR_SHAPE, "a decode step has one query per sequence (n_q %d)",
+                               p->n_q);
+  if (!lens) return fail(HS2_ERR_NULL, "lens is NULL");
+  for (int b = 0; b < p->batch; ++b)
+    if (lens[b] < 0 || lens[b] >= p->n_kv)
+      return fail(HS2_ERR_SHAPE, "lens[%d] = %d: a cache of %d keys has no room for one more", b,
+                  lens[b], p->n_kv);
+  HS2_TRY(check_ptr(k_new, "k_new"));
+  HS2_TRY(check_ptr(v_new, "v_new"));
+  Layout L;
+  HS2_TRY(check_full_args(p, q_full, k_cache, v_cache, o_full, idx, lse, nullptr, workspace,
+                          workspace_bytes, &L));
+  HS2_TRY(check_sparse_args(p, n_sparse_layers, q_sparse, k_cache, v_cache, idx, o_sparse));
+  const hipStream_t st = (hipStream_t)stream;
+  int32_t* seq_len = reinterpret_cast<int32_t*>((char*)workspace + L.lens);
+  const int row_bytes = p->h_kv * p->head_dim * (p->dtype == HS2_BF16 ? 2 : 4);
+  HIP_TRY(hs2::launch_set_lens(lens, 0, p->batch, seq_len, st), "sequence lengths");
+  HIP_TRY(hs2::launch_kv_append(k_new, v_new, k_cache, v_cache, seq_len, p->batch, p->n_kv,
+                                row_bytes, st),
+          "KV append");
+  HS2_TRY(run_full(*p, q_full, k_cache, v_cache, o_full, idx, lse, nullptr, workspace, L, st,
+                   seq_len));
+  if (n_sparse_layers == 0) return HS2_OK;
+  return run_sparse(*p, n_sparse_layers, q_sparse, k_cache, v_cache, idx, o_sparse, st);
 }
 
 hs2_status hs2_profile_enable(int32_t on) {

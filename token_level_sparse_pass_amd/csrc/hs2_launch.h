@@ -54,6 +54,10 @@ struct DecodePlan {
   float* logits; size_t logits_stride;
   int keys_per_split;     // multiple of 64
   int n_split;
+  // optional [batch] device array: sequence b holds seq_len[b] <= n_kv keys
+  // (its query sits at seq_len[b] - 1); NULL means every sequence holds n_kv.
+  // n_kv stays the batch stride of K and V (the cache capacity).
+  const int32_t* seq_len = nullptr;
 };
 int decode_n_split(int n_kv, int* keys_per_split);
 hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st);
@@ -66,9 +70,11 @@ hipError_t launch_attn_decode_bf16(const DecodePlan& p, hipStream_t st);
 // from the raw logits (q.k) the decode pass stored.
 struct DecodeScorePlan {
   int batch, h_q, h_kv, n_kv, n_cand;   // n_cand = candidates per row (p - window + 1)
+  int window;
   float c;                        // softmax scale * log2(e)
   const float* logits; size_t logits_stride; const float* stats;
   float* scores; size_t score_stride;
+  const int32_t* seq_len = nullptr;   // as in DecodePlan; n_cand then follows it
 };
 hipError_t launch_decode_score(const DecodeScorePlan& p, hipStream_t st);
 
@@ -92,8 +98,20 @@ struct SelectPlan {
   bool block_mode; int block_size, top_blocks;
   const float* scores; size_t score_stride;
   int32_t* idx;                       // [batch, n_q, width]
+  const int32_t* seq_len = nullptr;   // decode rows (n_q == 1): keys per sequence
 };
 hipError_t launch_select(const SelectPlan& p, hipStream_t st);
+
+// Decode step over a growing cache: launch_set_lens writes `lens[i] + 1`
+// (host values passed as kernel arguments) to seq_len[first + i];
+// launch_kv_append then copies each sequence's new K and V row (row_bytes =
+// h_kv * head_dim * element size, a multiple of 16) to position
+// seq_len[b] - 1 of the caches [batch][cap][h_kv][head_dim].
+hipError_t launch_set_lens(const int32_t* lens_host, int first, int count, int32_t* seq_len,
+                           hipStream_t st);
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* seq_len, int batch, int cap, int row_bytes,
+                            hipStream_t st);
 
 // Copy one score row into a debug buffer: candidates keep S, others get -1.
 hipError_t launch_export_scores(const float* src, int n_cand, int n_kv, float* dst,

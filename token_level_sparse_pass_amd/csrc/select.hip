@@ -34,6 +34,7 @@ struct SelArgs {
   const float* scores; size_t stride;
   int32_t* idx;
   int flat0, n_q, n_kv, top_k, window, width;
+  const int32_t* seq_len;            // keys per sequence (decode rows), or NULL
   int block_size, top_blocks;
 };
 
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
   const int r = blockIdx.x;
   const int flat = a.flat0 + r;                       // b * n_q + i
   const int i = flat % a.n_q;
-  const int p = a.n_kv - a.n_q + i;
+  const int p = (a.seq_len ? a.seq_len[flat / a.n_q] : a.n_kv) - a.n_q + i;
   const int n_c = max(0, p - a.window + 1);
   int32_t* out = a.idx + (size_t)flat * a.width;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(a.scores + (size_t)r * a.stride);
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_block_kernel(SelArgs a) {
   const int r = blockIdx.x;
   const int flat = a.flat0 + r;                       // b * n_q + i
   const int i = flat % a.n_q;
-  const int p = a.n_kv - a.n_q + i;
+  const int p = (a.seq_len ? a.seq_len[flat / a.n_q] : a.n_kv) - a.n_q + i;
   const int n_c = max(0, p - a.window + 1);
   const int bs = a.block_size;
   const int n_blocks = (n_c + bs - 1) / bs;
@@ -508,7 +509,7 @@ hipError_t launch_select(const SelectPlan& p, hipStream_t st) {
   if (p.rows <= 0) return hipSuccess;
   SelArgs a;
   a.scores = p.scores; a.stride = p.score_stride; a.idx = p.idx;
-  a.flat0 = p.flat0; a.n_q = p.n_q; a.n_kv = p.n_kv;
+  a.flat0 = p.flat0; a.n_q = p.n_q; a.n_kv = p.n_kv; a.seq_len = p.seq_len;
   a.top_k = p.top_k; a.window = p.window; a.width = p.width;
   a.block_size = p.block_size; a.top_blocks = p.top_blocks;
   if (p.block_mode)

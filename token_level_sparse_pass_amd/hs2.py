@@ -66,6 +66,9 @@ def load(path: str = LIB_PATH):
     lib.hs2_sparse_attn.restype = i32
     lib.hs2_block_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_block_forward.restype = i32
+    lib.hs2_decode_step.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp,
+                                    vp, vp, vp, sz, vp]
+    lib.hs2_decode_step.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
@@ -197,4 +200,35 @@ def block_forward(q_full, q_sparse, k, v, *, workspace=None, want_lse=True, out=
                                  _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out["o_full"]),
                                  _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
                                  _ptr(ws), ws.numel(), _stream(q_full.device)))
+    return out
+
+
+def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, *, workspace=None,
+                want_lse=True, out=None, **kw):
+    """One decode step over a growing cache (hs2_decode_step).
+
+    q_full [B, 1, h_q, d], q_sparse [L, B, 1, h_q, d], k_new / v_new
+    [B, 1, h_kv, d], k_cache / v_cache [B, capacity, h_kv, d] (modified in
+    place: the new rows land at row lens[b]); lens: the B lengths before the
+    step (a sequence of ints, kept on the host). Returns dict(o_full,
+    o_sparse, idx, lse); the caller advances lens.
+    """
+    lib = load()
+    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
+                 (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_tensor(t, n, q_full.dtype)
+    p = _problem_from(q_full, k_cache, kw)
+    B, nq, hq, d = q_full.shape
+    lens_h = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+    width = index_width(p)
+    if out is None:
+        out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
+                   idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
+                   lse=torch.empty((B, hq, nq), dtype=torch.float32, device=q_full.device)
+                   if want_lse else None)
+    ws = alloc_workspace(p, q_full.device) if workspace is None else workspace
+    _check(lib.hs2_decode_step(ctypes.byref(p), q_sparse.shape[0], _ptr(q_full), _ptr(q_sparse),
+                               _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), lens_h,
+                               _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]),
+                               _ptr(out["lse"]), _ptr(ws), ws.numel(), _stream(q_full.device)))
     return out
