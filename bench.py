@@ -155,12 +155,27 @@ def decode_loop(args):
     kw = dict(top_k=w.top_k, window=w.window)
     p = hs2.problem(k_cache.dtype, w.batch, 1, cap, w.h_q, w.h_kv, w.d, **kw)
     ws = hs2.alloc_workspace(p, dev)
+    ps = args.page_size
+    if ps:
+        # the same memory as a pool of pages, handed out in shuffled order
+        n_pages = w.batch * cap // ps
+        perm = torch.from_numpy(np.random.default_rng(7).permutation(n_pages).astype(np.int32))
+        table = perm.view(w.batch, cap // ps).to(dev)
+        k_cache = k_cache.view(w.batch * cap, w.h_kv, w.d)
+        v_cache = v_cache.view(w.batch * cap, w.h_kv, w.d)
+
+    def step(x, lens, out):
+        if ps:
+            return hs2.decode_step_paged(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"],
+                                         k_cache, v_cache, table, ps, lens, workspace=ws,
+                                         out=out, **kw)
+        return hs2.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
+                               v_cache, lens, workspace=ws, out=out, **kw)
+
     lens = list(lens0)
     out = None
     for s in range(args.warmup):
-        x = xs[s]
-        out = hs2.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
-                              v_cache, lens, workspace=ws, out=out, **kw)
+        out = step(xs[s], lens, out)
         lens = [n + 1 for n in lens]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -170,9 +185,7 @@ def decode_loop(args):
     torch.cuda.synchronize()
     ev0.record(stream)
     for s in range(args.warmup, n_steps):
-        x = xs[s]
-        out = hs2.decode_step(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"], k_cache,
-                              v_cache, lens, workspace=ws, out=out, **kw)
+        out = step(xs[s], lens, out)
         keys_read += sum(n + 1 for n in lens)
         lens = [n + 1 for n in lens]
     ev1.record(stream)
@@ -199,7 +212,8 @@ def decode_loop(args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
            "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
-           "config": {"workload": w.name + "_decode_loop", "batch": w.batch, "capacity": cap,
+           "config": {"workload": w.name + "_decode_loop" + (f"_paged{ps}" if ps else ""),
+                      "batch": w.batch, "capacity": cap, "page_size": ps or None,
                       "start_lengths": [int(min(lens0)), int(max(lens0))], "h_q": w.h_q,
                       "h_kv": w.h_kv, "head_dim": w.d, "top_k": w.top_k, "window": w.window,
                       "sparse_layers": w.n_sparse, "parallelism": "single GPU"},
@@ -220,6 +234,9 @@ def main():
     ap.add_argument("--decode-loop", action="store_true",
                     help="time decode steps over a growing ragged cache (the 64 x 128K decode "
                          "workload) instead of the default workload")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="with --decode-loop: keep the cache in a pool of pages of this many "
+                         "rows, handed out in shuffled order (hs2_decode_step_paged)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB) "
                          "three times, to scale HBM byte counters, and exit")

@@ -163,6 +163,32 @@ hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers,
                            float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* A paged KV pool: the K and V buffers are pools of n_pages pages of
+ * page_size rows ([n_pages * page_size, h_kv, head_dim] each), and row j of
+ * sequence b lives in page page_table[b * max_pages + j / page_size] at row
+ * j % page_size. page_size is a power of two >= 32; the problem's n_kv must
+ * equal max_pages * page_size (the longest a sequence may grow). Page ids
+ * are read on the device and clamped to [0, n_pages): a bad id reads or
+ * writes a wrong page of the pool, never memory outside it. */
+typedef struct {
+  const int32_t* page_table;   /* DEVICE [batch, max_pages]                  */
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t n_pages;
+} hs2_kv_pages;
+
+/* hs2_decode_step over a paged KV pool (serving layout for batched turns of
+ * different lengths): k_pool, v_pool are the pools described by `pages`;
+ * everything else as hs2_decode_step. idx entries are sequence positions
+ * (not pool rows). HS2_ERR_SHAPE on a bad page geometry. */
+hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                 int32_t n_sparse_layers, const void* q_full,
+                                 const void* q_sparse, const void* k_new,
+                                 const void* v_new, void* k_pool, void* v_pool,
+                                 const int32_t* lens, void* o_full, void* o_sparse,
+                                 int32_t* idx, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
  * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT

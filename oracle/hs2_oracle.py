@@ -262,6 +262,30 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, top_k=10
                 o_sparse=np.concatenate([o["o_sparse"] for o in outs], axis=1))
 
 
+def pool_rows(page_table, page_size: int, b: int, n: int) -> np.ndarray:
+    """Pool rows of positions 0..n-1 of sequence b in a paged KV pool."""
+    j = np.arange(n)
+    return np.asarray(page_table)[b, j // page_size].astype(np.int64) * page_size + j % page_size
+
+
+def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table, page_size,
+                      lens, **kw):
+    """decode_step with the cache in a paged pool: each sequence's first
+    lens[b] rows are read through its page-table row (position j at pool row
+    page_table[b, j // page_size] * page_size + j % page_size), then the step
+    is decode_step on that prefix. The pool's layout changes nothing else."""
+    k_pool, v_pool = np.asarray(k_pool), np.asarray(v_pool)
+    B = np.asarray(q_full).shape[0]
+    n_max = max(1, max(int(x) for x in lens))
+    kc = np.zeros((B, n_max) + k_pool.shape[1:], dtype=k_pool.dtype)
+    vc = np.zeros((B, n_max) + v_pool.shape[1:], dtype=v_pool.dtype)
+    for b in range(B):
+        rows = pool_rows(page_table, page_size, b, int(lens[b]))
+        kc[b, :len(rows)] = k_pool[rows]
+        vc[b, :len(rows)] = v_pool[rows]
+    return decode_step(q_full, q_sparse, k_new, v_new, kc, vc, lens, **kw)
+
+
 # ----------------------------------------------------------------------------
 # the same definitions, streamed over K/V chunks for a few sampled query rows
 # (large contexts: the full score matrix never exists)

@@ -174,3 +174,24 @@ def test_decode_step_rejections():
     assert decode_call(p, [10, 20, 3], ptrs=dict(vc=FAKE + 4)) == 5
     mn, _ = hs2.workspace_size(p)
     assert decode_call(p, [10, 20, 3], ws_bytes=mn - 1) == 4
+
+
+def test_decode_step_paged_rejections():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+
+    def call(p, pages, lens=(10, 20, 3)):
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        return lib.hs2_decode_step_paged(ctypes.byref(p), None if pages is None else
+                                         ctypes.byref(pages), 2, *([vp(FAKE)] * 6), arr,
+                                         *([vp(FAKE)] * 3), None, vp(FAKE),
+                                         hs2.workspace_size(p)[1], None)
+    p = base_problem(n_q=1, batch=3, n_kv=64 * 50)
+    assert call(p, None) == 1
+    assert call(p, hs2.KvPages(None, 64, 50, 200)) == 1            # no table
+    assert call(p, hs2.KvPages(FAKE, 48, 50, 200)) == 2            # not a power of two
+    assert call(p, hs2.KvPages(FAKE, 16, 200, 200)) == 2           # pages below 32 rows
+    assert call(p, hs2.KvPages(FAKE, 64, 40, 200)) == 2            # n_kv != max_pages * page_size
+    assert "max_pages" in lib.hs2_last_error().decode()
+    assert call(p, hs2.KvPages(FAKE, 64, 50, 0)) == 2              # empty pool
+    assert call(p, hs2.KvPages(FAKE, 64, 50, 200), lens=(10, 3200, 3)) == 2

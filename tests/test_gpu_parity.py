@@ -414,3 +414,73 @@ def test_decode_steps_growing_cache(gpu_lib, dtype, hq, hkv, d, select):
             err_s = np.abs(o_sp[:, b, 0] - want).max()
             assert err_s <= tol, f"step {step} seq {b}: sparse err {err_s}"
         lens = [n + 1 for n in lens]
+
+
+def check_decode_outputs(out, ref, xh, lens, k_rows, v_rows, window, tol, block_size=0, tag=""):
+    """Outputs of one GPU decode step against the oracle's; k_rows(b, n) /
+    v_rows(b, n) give sequence b's first n K / V rows (host bits)."""
+    err_o = np.abs(as_np(out["o_full"]) - ref["o_full"]).max()
+    err_lse = np.abs(out["lse"].cpu().numpy() - ref["lse"]).max()
+    say(tag, "o_full err", err_o, "lse err", err_lse)
+    assert err_o <= tol and err_lse <= 1e-4
+    gi = out["idx"].cpu().numpy()[:, 0]
+    o_sp = as_np(out["o_sparse"])
+    L = o_sp.shape[0]
+    for b, n in enumerate(lens):
+        ok, nd, why = O.compare_selection(gi[b], ref["idx"][b, 0], ref["S"][b], n, window,
+                                          float(ref["tau"][b, 0]), block_size=block_size)
+        assert ok, f"{tag} seq {b}: {why}"
+        if nd == 0:
+            want = ref["o_sparse"][:, b, 0]
+        else:
+            kb, vb = O.widen(k_rows(b, n + 1))[None], O.widen(v_rows(b, n + 1))[None]
+            row = gi[b][None, None]
+            want = np.stack([O.sparse_layer(xh["q_sparse"][l, b:b + 1], kb, vb, row)[0, 0]
+                             for l in range(L)])
+        err_s = np.abs(o_sp[:, b, 0] - want).max()
+        assert err_s <= tol, f"{tag} seq {b}: sparse err {err_s}"
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,ps,mp", [
+    ("bf16", 16, 2, 128, 64, 50),
+    ("bf16", 16, 2, 128, 256, 13),     # key splits start mid-page
+    ("fp32", 8, 2, 64, 32, 100),
+], ids=["bf16_p64", "bf16_p256", "fp32_p32"])
+def test_paged_decode_steps(gpu_lib, dtype, hq, hkv, d, ps, mp):
+    # the cache lives in shuffled pages of a shared pool; pool rows outside
+    # each sequence's pages hold unrelated values and must never be read
+    lens = [100, 1150, 2900]
+    B, top_k, window, L, steps = len(lens), 256, 64, 2, 3
+    cap, n_pages = ps * mp, B * mp + 5
+    table = np.random.default_rng(11).permutation(n_pages)[:B * mp].reshape(B, mp)
+    table = table.astype(np.int32)
+    w = small("paged", dtype, B, 1, cap, hq, hkv, d, top_k, window, L=L, cid=8)
+    pool = make_inputs(small("pool", dtype, 1, 1, n_pages * ps, hq, hkv, d, top_k, window, L=0,
+                             cid=9), device="cuda", sparse_layers=0)
+    k_pool, v_pool = pool["k"][0].clone(), pool["v"][0].clone()
+    kh, vh = host(k_pool), host(v_pool)
+    table_d = torch.from_numpy(table).cuda()
+    ws = gpu_lib.alloc_workspace(gpu_lib.problem(k_pool.dtype, B, 1, cap, hq, hkv, d,
+                                                 top_k=top_k, window=window), "cuda")
+    for step in range(steps):
+        say("step", step, "lens", lens)
+        x = decode_step_inputs(w, step, device="cuda")
+        out = gpu_lib.decode_step_paged(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"],
+                                        k_pool, v_pool, table_d, ps, lens, workspace=ws,
+                                        top_k=top_k, window=window)
+        torch.cuda.synchronize()
+        xh = {n: host(t) for n, t in x.items()}
+        ref = O.decode_step_paged(xh["q_full"], xh["q_sparse"], xh["k_new"], xh["v_new"], kh,
+                                  vh, table, ps, lens, top_k=top_k, window=window)
+        kp, vp = host(k_pool), host(v_pool)
+        for b, n in enumerate(lens):
+            r = O.pool_rows(table, ps, b, n + 1)[-1]
+            assert np.array_equal(kp[r], xh["k_new"][b, 0]), "K row in its page"
+            assert np.array_equal(vp[r], xh["v_new"][b, 0]), "V row in its page"
+            kh[r], vh[r] = xh["k_new"][b, 0], xh["v_new"][b, 0]
+        assert np.array_equal(kp, kh) and np.array_equal(vp, vh), "nothing else written"
+        check_decode_outputs(out, ref, xh, lens,
+                             lambda b, n: kh[O.pool_rows(table, ps, b, n)],
+                             lambda b, n: vh[O.pool_rows(table, ps, b, n)],
+                             window, TOL[dtype], tag=f"step {step}")
+        lens = [n + 1 for n in lens]

@@ -352,3 +352,28 @@ def test_decode_step_zero_keys_closed_form():
         want = list(range(min(6, n_c))) + list(range(max(0, n - 4), n + 1))
         row = got["idx"][b, 0]
         assert list(row[row >= 0]) == want
+
+
+def test_paged_decode_step_matches_contiguous():
+    # a pool whose pages hold the same rows in shuffled order gives the same
+    # step as the contiguous cache
+    c = _decode_case(70, [37, 64, 5], cap=64)
+    ps, mp = 16, 4
+    B = 3
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(B * mp + 2)[:B * mp]       # pool of 14 pages, 12 used
+    table = perm.reshape(B, mp).astype(np.int32)
+    k_pool = rand(((B * mp + 2) * ps, 2, 8), 71)
+    v_pool = rand(((B * mp + 2) * ps, 2, 8), 72)
+    for b in range(B):
+        rows = O.pool_rows(table, ps, b, mp * ps)
+        k_pool[rows] = c["k_cache"][b]
+        v_pool[rows] = c["v_cache"][b]
+    want = O.decode_step(**c, top_k=5, window=4)
+    got = O.decode_step_paged(c["q_full"], c["q_sparse"], c["k_new"], c["v_new"], k_pool, v_pool,
+                              table, ps, c["lens"], top_k=5, window=4)
+    for key in ("o_full", "lse", "idx", "o_sparse"):
+        np.testing.assert_array_equal(want[key], got[key])
+    # pool rows: position j of sequence b sits in page table[b, j // ps]
+    assert list(O.pool_rows(table, ps, 1, 20)[15:18]) == [
+        table[1, 0] * ps + 15, table[1, 1] * ps + 0, table[1, 1] * ps + 1]

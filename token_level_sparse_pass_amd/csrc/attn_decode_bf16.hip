@@ -37,6 +37,7 @@ struct Dec2Args {
   const __bf16* q; const __bf16* k; const __bf16* v;
   float* part; float* logits; size_t lstride;
   const int32_t* seq_len;
+  KvRows kv;
   int B, n_kv, h_q, h_kv, kps, n_split;
   float c;                                   // softmax scale * log2(e)
 };
@@ -92,17 +93,32 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
   const int n_tiles = k_end > k_begin ? (k_end - k_begin + TK - 1) / TK : 0;
 
   const size_t kvs = (size_t)a.h_kv * D;
-  const __bf16* kseq = a.k + ((size_t)b * a.n_kv * a.h_kv + g) * D;
-  const __bf16* vseq = a.v + ((size_t)b * a.n_kv * a.h_kv + g) * D;
+  const __bf16* kseq = a.k + (size_t)g * D;             // + row * kvs
+  const __bf16* vseq = a.v + (size_t)g * D;
+
+  // paged pool: lane i holds the id of the split's i-th page (a split spans
+  // at most 64 pages of >= 32 rows); a 32-key tile never crosses a page
+  const int first_page = a.kv.paged() ? (k_begin >> a.kv.page_shift) : 0;
+  int page_id = 0;
+  if (a.kv.paged() && first_page + lane < a.kv.max_pages && n_tiles > 0)
+    page_id = a.kv.table[(size_t)b * a.kv.max_pages + first_page + lane];
 
   // tile t into ring stage `stage`: lane group grp of instruction j carries
   // key 4j + grp (clamped to the last key, whose rows are never used)
   auto issue = [&](int t, int stage) {
     char* base = smem + stage * TILE_BYTES;
+    const int j0 = k_begin + t * TK;
+    size_t row0;                                        // cache row of key j0
+    if (a.kv.paged()) {
+      const int pid = __builtin_amdgcn_readlane(page_id, (j0 >> a.kv.page_shift) - first_page);
+      row0 = a.kv.page_row(pid, j0);
+    } else {
+      row0 = (size_t)b * a.n_kv + j0;
+    }
 #pragma unroll
     for (int j = 0; j < TK / 4; ++j) {
       const int key = j * 4 + grp;
-      const size_t row = (size_t)min(k_begin + t * TK + key, k_end - 1) * kvs;
+      const size_t row = (row0 + (size_t)(min(j0 + key, k_end - 1) - j0)) * kvs;
       __builtin_amdgcn_global_load_lds(kseq + row + ((l16 ^ kswz(key)) << 3),
                                        (lds_void*)(base + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vseq + row + (l16 << 3),
@@ -260,6 +276,7 @@ hipError_t launch_attn_decode_bf16(const DecodePlan& p, hipStream_t st) {
   a.k = reinterpret_cast<const __bf16*>(p.k);
   a.v = reinterpret_cast<const __bf16*>(p.v);
   a.part = p.part; a.logits = p.logits; a.lstride = p.logits_stride; a.seq_len = p.seq_len;
+  a.kv = p.kv;
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.c = p.s.scale_log2;
   const dim3 grid((unsigned)((size_t)a.B * a.h_kv * a.n_split));

@@ -320,6 +320,7 @@ struct DecArgs {
   const void* q; const void* k; const void* v;
   float* part; float* logits; size_t lstride;
   const int32_t* seq_len;
+  KvRows kv;
   int B, n_kv, h_q, h_kv, kps, n_split;
   float scale_log2;
 };
@@ -342,8 +343,9 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
   const int k_end = min(n_keys, k_begin + a.kps);
 
   const T* qb = reinterpret_cast<const T*>(a.q);
-  const T* kseq = reinterpret_cast<const T*>(a.k) + ((size_t)b * a.n_kv * a.h_kv + g) * D;
-  const T* vseq = reinterpret_cast<const T*>(a.v) + ((size_t)b * a.n_kv * a.h_kv + g) * D;
+  // K/V rows of key j: kseq + kv.row(b, j) * kstride (contiguous or paged)
+  const T* kseq = reinterpret_cast<const T*>(a.k) + (size_t)g * D;
+  const T* vseq = reinterpret_cast<const T*>(a.v) + (size_t)g * D;
   const size_t kstride = (size_t)a.h_kv * D;
 
   Frag<T, D> qf[RB];
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int j = j0 + kb * 16 + (lane & 15);
-      if (j < k_end) load_slice<T, D>(kf[kb], kseq + (size_t)j * kstride, lane);
+      if (j < k_end) load_slice<T, D>(kf[kb], kseq + a.kv.row(b, j) * kstride, lane);
       else zero_slice<T, D>(kf[kb]);
     }
     // V rows for the lane's slots: st-th 32-key step, slot sl
@@ -379,7 +381,8 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) {
         const int j = j0 + st * 32 + (sl < 4 ? 4 * grp + sl : 16 + 4 * grp + sl - 4);
-        load_vrow<T, D>(&vraw[st][sl][0], vseq + (size_t)(j < k_end ? j : k_begin) * kstride, lane);
+        load_vrow<T, D>(&vraw[st][sl][0], vseq + a.kv.row(b, j < k_end ? j : k_begin) * kstride,
+                        lane);
       }
 
     float p[RB][16];
@@ -515,7 +518,7 @@ template <typename T, int D>
 static hipError_t launch_decode_t(const DecodePlan& p, hipStream_t st) {
   DecArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.part = p.part; a.logits = p.logits;
-  a.lstride = p.logits_stride; a.seq_len = p.seq_len;
+  a.lstride = p.logits_stride; a.seq_len = p.seq_len; a.kv = p.kv;
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.scale_log2 = p.s.scale_log2;
   const int G = a.h_q / a.h_kv;

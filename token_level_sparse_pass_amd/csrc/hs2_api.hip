@@ -261,11 +261,19 @@ hs2_status check_full_args(const hs2_problem* p, const void* q, const void* k, c
   return HS2_OK;
 }
 
+hs2::KvRows contiguous_rows(const hs2_problem& p) {
+  hs2::KvRows kv;
+  kv.n_kv = p.n_kv;
+  return kv;
+}
+
 // seq_len (decode only, device, may be NULL): keys held by each sequence,
 // whose query then sits at seq_len[b] - 1; NULL means n_kv for all.
+// kv (decode only, may be NULL): where K/V rows live; NULL = contiguous.
 hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const void* v, void* o,
                     int32_t* idx, float* lse, const hs2_debug* dbg, void* ws,
-                    const Layout& L, hipStream_t st, const int32_t* seq_len = nullptr) {
+                    const Layout& L, hipStream_t st, const int32_t* seq_len = nullptr,
+                    const hs2::KvRows* kv = nullptr) {
   const hs2::Shape s = shape_of(p);
   float* stats = fptr(ws, L.stats);
   float* scores = fptr(ws, L.scores);
@@ -291,6 +299,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
     d.s = s; d.q = q; d.k = k; d.v = v; d.o = o; d.stats = stats; d.lse = lse;
     d.part = fptr(ws, L.part); d.logits = fptr(ws, L.logits); d.logits_stride = L.logits_stride;
     d.keys_per_split = L.kps; d.n_split = L.n_split; d.seq_len = seq_len;
+    d.kv = kv ? *kv : contiguous_rows(p);
     {
       PassTimer t(st, HS2_PASS_FULL);
       HIP_TRY(hs2::launch_attn_fwd_decode(d, st), "decode attention");
@@ -369,7 +378,8 @@ hs2_status check_sparse_args(const hs2_problem* p, int32_t n_layers, const void*
 }
 
 hs2_status run_sparse(const hs2_problem& p, int32_t n_layers, const void* q, const void* k,
-                      const void* v, const int32_t* idx, void* o, hipStream_t st) {
+                      const void* v, const int32_t* idx, void* o, hipStream_t st,
+                      const hs2::KvRows* kv = nullptr) {
   const int G = p.h_q / p.h_kv;
   const int per = std::max(1, 64 / G);                       // layers per launch
   const size_t esz = p.dtype == HS2_BF16 ? 2 : 4;
@@ -384,6 +394,7 @@ hs2_status run_sparse(const hs2_problem& p, int32_t n_layers, const void* q, con
     sp.head_dim = p.head_dim; sp.width = index_width(p);
     sp.scale_log2 = p.softmax_scale * 1.4426950408889634f;
     sp.bf16 = p.dtype == HS2_BF16;
+    sp.kv = kv ? *kv : contiguous_rows(p);
     PassTimer t(st, HS2_PASS_SPARSE);
     HIP_TRY(hs2::launch_sparse_attn(sp, st), "sparse attention");
   }
@@ -441,15 +452,36 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers, cons
   return run_sparse(*p, n_sparse_layers, q_sparse, k, v, idx, o_sparse, st);
 }
 
-hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
-                           const void* q_sparse, const void* k_new, const void* v_new,
-                           void* k_cache, void* v_cache, const int32_t* lens, void* o_full,
-                           void* o_sparse, int32_t* idx, float* lse, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  g_err.clear();
+namespace {
+
+// Shared by the contiguous and paged decode steps: validate, set the
+// per-sequence key counts, append the new rows, run the block.
+hs2_status decode_step_impl(const hs2_problem* p, const hs2_kv_pages* pages,
+                            int32_t n_sparse_layers, const void* q_full, const void* q_sparse,
+                            const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* lens, void* o_full, void* o_sparse, int32_t* idx,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   HS2_TRY(check_problem(p));
   if (p->n_q != 1) return fail(HS2_ERR_SHAPE, "a decode step has one query per sequence (n_q %d)",
                                p->n_q);
+  hs2::KvRows kv = contiguous_rows(*p);
+  if (pages) {
+    if (!pages->page_table) return fail(HS2_ERR_NULL, "page_table is NULL");
+    const int ps = pages->page_size;
+    if (ps < 32 || (ps & (ps - 1)))
+      return fail(HS2_ERR_SHAPE, "page_size %d: a power of two >= 32 is needed", ps);
+    if (pages->max_pages < 1 || pages->n_pages < 1)
+      return fail(HS2_ERR_SHAPE, "max_pages %d, n_pages %d", pages->max_pages, pages->n_pages);
+    if ((long long)pages->max_pages * ps != p->n_kv)
+      return fail(HS2_ERR_SHAPE, "n_kv %d must be max_pages * page_size = %lld", p->n_kv,
+                  (long long)pages->max_pages * ps);
+    if ((long long)pages->n_pages * ps > INT32_MAX)
+      return fail(HS2_ERR_UNSUPPORTED, "pool of %d pages of %d rows", pages->n_pages, ps);
+    kv.table = pages->page_table;
+    kv.page_shift = __builtin_ctz((unsigned)ps);
+    kv.max_pages = pages->max_pages;
+    kv.n_pages = pages->n_pages;
+  }
   if (!lens) return fail(HS2_ERR_NULL, "lens is NULL");
   for (int b = 0; b < p->batch; ++b)
     if (lens[b] < 0 || lens[b] >= p->n_kv)
@@ -465,13 +497,39 @@ hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers, const 
   int32_t* seq_len = reinterpret_cast<int32_t*>((char*)workspace + L.lens);
   const int row_bytes = p->h_kv * p->head_dim * (p->dtype == HS2_BF16 ? 2 : 4);
   HIP_TRY(hs2::launch_set_lens(lens, 0, p->batch, seq_len, st), "sequence lengths");
-  HIP_TRY(hs2::launch_kv_append(k_new, v_new, k_cache, v_cache, seq_len, p->batch, p->n_kv,
-                                row_bytes, st),
+  HIP_TRY(hs2::launch_kv_append(k_new, v_new, k_cache, v_cache, seq_len, p->batch, kv, row_bytes,
+                                st),
           "KV append");
   HS2_TRY(run_full(*p, q_full, k_cache, v_cache, o_full, idx, lse, nullptr, workspace, L, st,
-                   seq_len));
+                   seq_len, &kv));
   if (n_sparse_layers == 0) return HS2_OK;
-  return run_sparse(*p, n_sparse_layers, q_sparse, k_cache, v_cache, idx, o_sparse, st);
+  return run_sparse(*p, n_sparse_layers, q_sparse, k_cache, v_cache, idx, o_sparse, st, &kv);
+}
+
+}  // namespace
+
+hs2_status hs2_decode_step(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                           const void* q_sparse, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int32_t* lens, void* o_full,
+                           void* o_sparse, int32_t* idx, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return decode_step_impl(p, nullptr, n_sparse_layers, q_full, q_sparse, k_new, v_new, k_cache,
+                          v_cache, lens, o_full, o_sparse, idx, lse, workspace, workspace_bytes,
+                          stream);
+}
+
+hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                 int32_t n_sparse_layers, const void* q_full,
+                                 const void* q_sparse, const void* k_new, const void* v_new,
+                                 void* k_pool, void* v_pool, const int32_t* lens, void* o_full,
+                                 void* o_sparse, int32_t* idx, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!pages) return fail(HS2_ERR_NULL, "pages is NULL");
+  return decode_step_impl(p, pages, n_sparse_layers, q_full, q_sparse, k_new, v_new, k_pool,
+                          v_pool, lens, o_full, o_sparse, idx, lse, workspace, workspace_bytes,
+                          stream);
 }
 
 hs2_status hs2_profile_enable(int32_t on) {

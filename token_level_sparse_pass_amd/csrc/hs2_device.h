@@ -112,4 +112,5 @@ __device__ __forceinline__ uint32_t xcd_swizzle(uint32_t bid, uint32_t nblocks) 
   return (bid % nx) * per + bid / nx;
 }
 
+
 }  // namespace hs2

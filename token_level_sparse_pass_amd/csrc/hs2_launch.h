@@ -8,6 +8,27 @@
 
 namespace hs2 {
 
+// Where key j of sequence b lives in a K/V buffer of [rows][h_kv][d]: a
+// contiguous cache holds each sequence's n_kv rows back to back; a paged
+// pool maps j through the sequence's page-table row (2^page_shift rows per
+// page). Page ids are clamped to the pool, so a bad id reads a wrong page
+// but never leaves the buffer.
+struct KvRows {
+  const int32_t* table = nullptr;   // [batch][max_pages], or NULL
+  int n_kv = 0;
+  int page_shift = 0, max_pages = 0, n_pages = 0;
+  __device__ __forceinline__ bool paged() const { return table != nullptr; }
+  __device__ __forceinline__ size_t page_row(int page_id, int j) const {
+    const int pid = min(max(page_id, 0), n_pages - 1);
+    return ((size_t)pid << page_shift) + (j & ((1 << page_shift) - 1));
+  }
+  __device__ __forceinline__ size_t row(int b, int j) const {
+    if (!table) return (size_t)b * n_kv + j;
+    return page_row(table[(size_t)b * max_pages + (j >> page_shift)], j);
+  }
+};
+
+
 // Shape shared by the full-layer kernels.
 struct Shape {
   int batch, n_q, n_kv, h_q, h_kv, head_dim;
@@ -58,6 +79,8 @@ struct DecodePlan {
   // (its query sits at seq_len[b] - 1); NULL means every sequence holds n_kv.
   // n_kv stays the batch stride of K and V (the cache capacity).
   const int32_t* seq_len = nullptr;
+  // K/V rows (kv.n_kv = n_kv for a contiguous cache, or a paged pool)
+  KvRows kv;
 };
 int decode_n_split(int n_kv, int* keys_per_split);
 hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st);
@@ -110,7 +133,7 @@ hipError_t launch_select(const SelectPlan& p, hipStream_t st);
 hipError_t launch_set_lens(const int32_t* lens_host, int first, int count, int32_t* seq_len,
                            hipStream_t st);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                            const int32_t* seq_len, int batch, int cap, int row_bytes,
+                            const int32_t* seq_len, int batch, const KvRows& kv, int row_bytes,
                             hipStream_t st);
 
 // Copy one score row into a debug buffer: candidates keep S, others get -1.
@@ -125,6 +148,7 @@ struct SparsePlan {
   int layers, batch, n_q, n_kv, h_q, h_kv, head_dim, width;
   float scale_log2;
   bool bf16;
+  KvRows kv;                          // kv.n_kv = n_kv, or a paged pool
 };
 hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st);
 

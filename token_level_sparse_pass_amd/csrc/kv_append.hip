@@ -35,12 +35,12 @@ __global__ __launch_bounds__(LENS_PER_LAUNCH) void set_lens_kernel(LensArg lens,
 // contiguous (h_kv * head_dim elements), copied as 16-byte chunks
 __global__ __launch_bounds__(256) void kv_append_kernel(const char* k_new, const char* v_new,
                                                         char* k_cache, char* v_cache,
-                                                        const int32_t* seq_len, int cap,
+                                                        const int32_t* seq_len, KvRows kv,
                                                         int row_bytes) {
   const int b = blockIdx.x >> 1;
   const bool is_v = blockIdx.x & 1;
   const char* src = (is_v ? v_new : k_new) + (size_t)b * row_bytes;
-  char* dst = (is_v ? v_cache : k_cache) + ((size_t)b * cap + (seq_len[b] - 1)) * row_bytes;
+  char* dst = (is_v ? v_cache : k_cache) + kv.row(b, seq_len[b] - 1) * row_bytes;
   for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x)
     reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
 }
@@ -60,13 +60,13 @@ hipError_t launch_set_lens(const int32_t* lens_host, int first, int count, int32
 }
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                            const int32_t* seq_len, int batch, int cap, int row_bytes,
+                            const int32_t* seq_len, int batch, const KvRows& kv, int row_bytes,
                             hipStream_t st) {
   if (batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)batch * 2), dim3(256), 0, st,
                      reinterpret_cast<const char*>(k_new), reinterpret_cast<const char*>(v_new),
                      reinterpret_cast<char*>(k_cache), reinterpret_cast<char*>(v_cache), seq_len,
-                     cap, row_bytes);
+                     kv, row_bytes);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct SparseArgs {
   void* o;              // [L, B, n_q, h_q, D]
   int L, B, n_q, n_kv, h_q, h_kv, W;
   float scale_log2;     // softmax scale * log2(e)
+  KvRows kv;            // key j of sequence b is K/V buffer row kv.row(b, j)
 };
 
 template <typename T, int D>
@@ -116,9 +117,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
     for (int db = 0; db < DV; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t kv_row_stride = (size_t)a.h_kv * D;      // elements between keys
-  const T* kseq = kb + ((size_t)b * a.n_kv * a.h_kv + g) * D;
-  const T* vseq = vb + ((size_t)b * a.n_kv * a.h_kv + g) * D;
+  const size_t kv_row_stride = (size_t)a.h_kv * D;      // elements between buffer rows
+  const T* kseq = kb + (size_t)g * D;                   // + buffer row * kv_row_stride
+  const T* vseq = vb + (size_t)g * D;
   const int grp = lane >> 4;
 
   for (int t = t_begin; t < t_end; ++t) {
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
       const bool ok = pos < n_valid;
       const int j = ok ? irow[pos] : 0;
       kvalid[kb2] = ok;
-      load_slice<T, D>(kf[kb2], kseq + (size_t)j * kv_row_stride, lane);
+      load_slice<T, D>(kf[kb2], kseq + a.kv.row(b, j) * kv_row_stride, lane);
     }
     // V rows for this lane's 8 key slots
     size_t voff[8];
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
       const int pos = base + (s < 4 ? 4 * grp + s : 16 + 4 * grp + (s - 4));
       const bool ok = pos < n_valid;
       vvalid[s] = ok;
-      voff[s] = (size_t)(ok ? irow[pos] : 0) * kv_row_stride;
+      voff[s] = a.kv.row(b, ok ? irow[pos] : 0) * kv_row_stride;
     }
     VTile<T, D> vt;
     load_v_rows<T, D>(vt, vseq, voff, lane);
@@ -321,7 +322,7 @@ hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st) {
   SparseArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.idx = p.idx; a.o = p.o;
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
-  a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.scale_log2 = p.scale_log2;
+  a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.scale_log2 = p.scale_log2; a.kv = p.kv;
   const int G = p.h_q / p.h_kv;
   const int rb = (p.layers * G + 15) / 16;
   // few work-groups: split each index list over 8 waves of one work-group

@@ -34,6 +34,7 @@ struct Sp2Args {
   __bf16* o;
   int L, B, n_q, n_kv, h_q, h_kv, W;
   float c;
+  KvRows kv;
 };
 
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
@@ -70,8 +71,12 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
 
   // the index row lives in LDS after the ring, so reading it in the loop
   // never waits on the gathers in flight
+  // (entries become K/V buffer rows here: contiguous or through the page table)
   int* sidx = reinterpret_cast<int*>(smem + NS * TILE_BYTES);
-  for (int t = threadIdx.x; t < a.W; t += 64 * NWV) sidx[t] = irow[t];
+  for (int t = threadIdx.x; t < a.W; t += 64 * NWV) {
+    const int j = irow[t];
+    sidx[t] = j >= 0 ? (int)a.kv.row(b, j) : -1;
+  }
   __syncthreads();
   int n_valid = 0;
   for (int t = lane; t < a.W; t += 64) n_valid += (sidx[t] >= 0) ? 1 : 0;
@@ -81,8 +86,8 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   const int fallback = n_valid > 0 ? sidx[0] : 0;
 
   const size_t kvs = (size_t)a.h_kv * D;
-  const __bf16* kseq = a.k + ((size_t)b * a.n_kv * a.h_kv + g) * D;
-  const __bf16* vseq = a.v + ((size_t)b * a.n_kv * a.h_kv + g) * D;
+  const __bf16* kseq = a.k + (size_t)g * D;             // + buffer row * kvs
+  const __bf16* vseq = a.v + (size_t)g * D;
 
   // index entries of the lane's keys in the next tile to gather
   int nidx[IPW];
@@ -243,7 +248,7 @@ hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
   a.idx = p.idx;
   a.o = reinterpret_cast<__bf16*>(p.o);
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
-  a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.c = p.scale_log2;
+  a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.c = p.scale_log2; a.kv = p.kv;
   const int G = p.h_q / p.h_kv;
   const int rb = (p.layers * G + 15) / 16;
   const dim3 grid((unsigned)((size_t)p.batch * p.n_q * p.h_kv));

@@ -34,6 +34,11 @@ class Debug(ctypes.Structure):
                 ("scores_out", ctypes.c_void_p)]
 
 
+class KvPages(ctypes.Structure):
+    _fields_ = [("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
 class HS2Error(RuntimeError):
     def __init__(self, status, detail):
         super().__init__(f"hs2 status {status} ({STATUS.get(status, '?')}): {detail}")
@@ -69,6 +74,9 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_step.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp,
                                     vp, vp, vp, sz, vp]
     lib.hs2_decode_step.restype = i32
+    lib.hs2_decode_step_paged.argtypes = [P, ctypes.POINTER(KvPages), i32, vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(i32), vp, vp, vp, vp, vp, sz, vp]
+    lib.hs2_decode_step_paged.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
@@ -231,4 +239,38 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, *, works
                                _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), lens_h,
                                _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]),
                                _ptr(out["lse"]), _ptr(ws), ws.numel(), _stream(q_full.device)))
+    return out
+
+
+def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table, page_size,
+                      lens, *, workspace=None, want_lse=True, out=None, **kw):
+    """hs2_decode_step_paged: decode_step over a paged KV pool.
+
+    k_pool / v_pool [n_pages * page_size, h_kv, d] (modified in place),
+    page_table int32 device tensor [B, max_pages]; row j of sequence b is
+    pool row page_table[b, j // page_size] * page_size + j % page_size.
+    """
+    lib = load()
+    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
+                 (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _check_tensor(t, n, q_full.dtype)
+    _check_tensor(page_table, "page_table", torch.int32)
+    B, nq, hq, d = q_full.shape
+    max_pages = page_table.shape[1]
+    n_pages = k_pool.shape[0] // page_size
+    p = problem(q_full.dtype, B, nq, max_pages * page_size, hq, k_pool.shape[1], d, **kw)
+    pages = KvPages(page_table.data_ptr(), page_size, max_pages, n_pages)
+    lens_h = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+    width = index_width(p)
+    if out is None:
+        out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
+                   idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
+                   lse=torch.empty((B, hq, nq), dtype=torch.float32, device=q_full.device)
+                   if want_lse else None)
+    ws = alloc_workspace(p, q_full.device) if workspace is None else workspace
+    _check(lib.hs2_decode_step_paged(ctypes.byref(p), ctypes.byref(pages), q_sparse.shape[0],
+                                     _ptr(q_full), _ptr(q_sparse), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_pool), _ptr(v_pool), lens_h, _ptr(out["o_full"]),
+                                     _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
+                                     _ptr(ws), ws.numel(), _stream(q_full.device)))
     return out
