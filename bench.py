@@ -224,6 +224,51 @@ def decode_loop(args):
     print(json.dumps(rec), flush=True)
 
 
+def kv_bridge_bench(args):
+    """The KV Bridging projection for the 1M-token context: K and V of one
+    Cross-Decoder full layer (8 KV heads x 128) from 1M hidden states of
+    width 4096 (hidden width: a reading; the pages give none)."""
+    import torch
+    from synth import CONFIGS, bridge_inputs
+    from token_level_sparse_pass_amd import hs2
+
+    hs2.load()
+    w = CONFIGS[5]
+    d_model = 4096
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"KV bridge for {w.name}: generating {w.n_kv} hidden states of width {d_model}")
+    x = bridge_inputs(w, d_model, device=dev)
+    out = hs2.kv_bridge(x["hidden"], x["w_kv"], w.h_kv)
+    for _ in range(args.warmup):
+        hs2.kv_bridge(x["hidden"], x["w_kv"], w.h_kv, out=out)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        hs2.kv_bridge(x["hidden"], x["w_kv"], w.h_kv, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.0 * w.batch * w.n_kv * d_model * 2 * w.h_kv * w.d
+    ach = flops / (ms / 1e3) / 1e12
+    rec = {"metric": "KV-bridge projection TFLOP/s (K and V of one full layer from hidden states)",
+           "value": round(ach, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; shapes of the workload, random weights)",
+           "config": {"workload": w.name + "_kv_bridge", "tokens": w.batch * w.n_kv,
+                      "d_model": d_model, "h_kv": w.h_kv, "head_dim": w.d,
+                      "parallelism": "single GPU"},
+           "roofline": {"kernel": "kv_bridge", "bound": "mfma", "achieved": round(ach, 2),
+                        "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_MFMA_TFLOPS["bf16"], 4),
+                        "algorithmic_per_launch": flops, "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +279,8 @@ def main():
     ap.add_argument("--decode-loop", action="store_true",
                     help="time decode steps over a growing ragged cache (the 64 x 128K decode "
                          "workload) instead of the default workload")
+    ap.add_argument("--kv-bridge", action="store_true",
+                    help="time the KV Bridging projection for the 1M-token context instead")
     ap.add_argument("--page-size", type=int, default=0,
                     help="with --decode-loop: keep the cache in a pool of pages of this many "
                          "rows, handed out in shuffled order (hs2_decode_step_paged)")
@@ -259,6 +306,9 @@ def main():
         return
     if args.decode_loop:
         decode_loop(args)
+        return
+    if args.kv_bridge:
+        kv_bridge_bench(args)
         return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2

@@ -189,6 +189,20 @@ hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages
                                  int32_t* idx, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* KV Bridging: the K and V a Cross-Decoder full layer reads are projections
+ * of the hidden states of its Self-Decoder full layer (blog.lynxflow.co,
+ * section "Architectural Innovation: Two-Level KV Sharing"; hitechexpert.top,
+ * section "Two-Level KV Sharing"). Writes, for every token m of the batch,
+ *   k[m, :] = hidden[m, :] . W_k^T,   v[m, :] = hidden[m, :] . W_v^T
+ * straight into the [batch, n_kv, h_kv, head_dim] buffers every call above
+ * reads. hidden DEVICE [batch, n_kv, d_model]; w_kv DEVICE
+ * [2, h_kv * head_dim, d_model] (W_k then W_v, one row per output feature).
+ * bf16 only (HS2_ERR_UNSUPPORTED otherwise), fp32 accumulation, results
+ * rounded to bf16; d_model a positive multiple of 64. Uses only p's dtype,
+ * batch, n_kv, h_kv and head_dim. */
+hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidden,
+                         const void* w_kv, void* k, void* v, void* stream);
+
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
  * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT

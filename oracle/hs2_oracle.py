@@ -262,6 +262,23 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, top_k=10
                 o_sparse=np.concatenate([o["o_sparse"] for o in outs], axis=1))
 
 
+def kv_bridge(hidden, w_kv, h_kv: int):
+    """KV Bridging ("Architectural Innovation: Two-Level KV Sharing" on
+    blog.lynxflow.co; "Two-Level KV Sharing" on hitechexpert.top): a
+    Cross-Decoder full layer's K and V are linear projections of the hidden
+    states of its Self-Decoder full layer, token by token:
+    k[b, t] = hidden[b, t] . W_k^T, v[b, t] = hidden[b, t] . W_v^T.
+    hidden [B, n, d_model], w_kv [2, h_kv * d, d_model] (W_k, W_v; one row per
+    output feature). Returns fp64 (k, v), each [B, n, h_kv, d]."""
+    h, w = widen(hidden), widen(w_kv)
+    B, n, dm = h.shape
+    d = w.shape[1] // h_kv
+    flat = h.reshape(B * n, dm)
+    k = (flat @ w[0].T).reshape(B, n, h_kv, d)
+    v = (flat @ w[1].T).reshape(B, n, h_kv, d)
+    return k, v
+
+
 def pool_rows(page_table, page_size: int, b: int, n: int) -> np.ndarray:
     """Pool rows of positions 0..n-1 of sequence b in a paged KV pool."""
     j = np.arange(n)

@@ -130,6 +130,23 @@ def decode_step_inputs(w: Workload, step: int, device="cpu", sparse_layers=None)
                 v_new=_randn((B, 1, hkv, d), w, base + 3, device))
 
 
+def bridge_inputs(w: Workload, d_model: int, device="cpu") -> dict:
+    """Hidden states [B, n_kv, d_model] (N(0,1)) and bridging weights
+    [2, h_kv * d, d_model] (N(0, 1/d_model), so projections come out near
+    unit scale) for the KV Bridging projection; streams 20 and 21."""
+    B, n, F = w.batch, w.n_kv, w.h_kv * w.d
+    hidden = _randn((B, n, d_model), w, 20, device)
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(w.cid, 21))
+    wk = torch.empty((2, F, d_model), dtype=_torch_dtype(w), device=device)
+    flat = wk.view(-1)
+    for s in range(0, flat.numel(), _CHUNK_ELEMS):
+        e = min(flat.numel(), s + _CHUNK_ELEMS)
+        flat[s:e] = (torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+                     * d_model ** -0.5).to(wk.dtype)
+    return dict(hidden=hidden, w_kv=wk)
+
+
 def to_host(t: torch.Tensor) -> np.ndarray:
     """Host copy of a tensor: float32 values for fp32, raw uint16 bits for bf16."""
     t = t.detach()

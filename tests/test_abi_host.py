@@ -195,3 +195,16 @@ def test_decode_step_paged_rejections():
     assert "max_pages" in lib.hs2_last_error().decode()
     assert call(p, hs2.KvPages(FAKE, 64, 50, 0)) == 2              # empty pool
     assert call(p, hs2.KvPages(FAKE, 64, 50, 200), lens=(10, 3200, 3)) == 2
+
+
+def test_kv_bridge_rejections():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    p = base_problem(n_kv=1000)
+    args = [vp(FAKE)] * 4
+    assert lib.hs2_kv_bridge(ctypes.byref(base_problem(dtype=hs2.FP32)), 256, *args, None) == 3
+    assert lib.hs2_kv_bridge(ctypes.byref(p), 100, *args, None) == 2       # not a multiple of 64
+    assert lib.hs2_kv_bridge(ctypes.byref(p), 0, *args, None) == 2
+    assert lib.hs2_kv_bridge(ctypes.byref(p), 256, None, *args[1:], None) == 1
+    assert lib.hs2_kv_bridge(ctypes.byref(p), 256, vp(FAKE), vp(FAKE), vp(FAKE + 2), vp(FAKE),
+                             None) == 5

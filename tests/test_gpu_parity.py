@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import hs2_oracle as O
-from synth import CONFIGS, Workload, decode_step_inputs, make_inputs, to_host
+from synth import CONFIGS, Workload, bridge_inputs, decode_step_inputs, make_inputs, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -484,3 +484,38 @@ def test_paged_decode_steps(gpu_lib, dtype, hq, hkv, d, ps, mp):
                              lambda b, n: vh[O.pool_rows(table, ps, b, n)],
                              window, TOL[dtype], tag=f"step {step}")
         lens = [n + 1 for n in lens]
+
+
+# ---------------------------------------------------------------------------
+# KV Bridging projection, then the block on the bridged K/V
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,n,dm,hkv,d", [(2, 300, 256, 4, 64), (1, 1000, 4096, 8, 128)],
+                         ids=["small_ragged", "d4096"])
+def test_kv_bridge(gpu_lib, B, n, dm, hkv, d):
+    w = small("bridge", "bf16", B, 64, n, 2 * hkv, hkv, d, 64, 16, L=2, cid=10)
+    x = bridge_inputs(w, dm, device="cuda")
+    k, v = gpu_lib.kv_bridge(x["hidden"], x["w_kv"], hkv)
+    torch.cuda.synchronize()
+    hh, ww = host(x["hidden"]), host(x["w_kv"])
+    rk, rv = O.kv_bridge(hh, ww, hkv)
+    # error bound: an fp32 sum of dm exact products is within
+    # dm * 2^-24 * sum |h| |w| of the exact sum, and rounding it to bf16
+    # adds 2^-9 of its magnitude
+    ak, av = O.kv_bridge(np.abs(O.widen(hh)), np.abs(O.widen(ww)), hkv)
+    for got, ref, mag in ((k, rk, ak), (v, rv, av)):
+        err = np.abs(as_np(got) - ref)
+        bound = 2.0 ** -8 * np.abs(ref) + 2.0 * dm * 2.0 ** -24 * mag
+        say("bridge max rel excess", float((err - bound).max()))
+        assert bool((err <= bound).all())
+    if dm != 4096:
+        return
+    # one buffer, many consumers: the block reads the bridged K/V directly
+    inp = make_inputs(w, device="cuda")
+    kw = dict(top_k=64, window=16)
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], k, v, **kw)
+    torch.cuda.synchronize()
+    ref = O.block_forward(host(inp["q_full"]), host(inp["q_sparse"]), host(k), host(v), **kw)
+    assert np.abs(as_np(out["o_full"]) - ref["o_full"]).max() <= TOL["bf16"]
+    gi = out["idx"].cpu().numpy()
+    pos = np.arange(w.n_q) + n - w.n_q
+    compare_index_rows(gi[0], ref["S"][0], pos, ref["idx"][0], ref["tau"][0], 16)

@@ -377,3 +377,31 @@ def test_paged_decode_step_matches_contiguous():
     # pool rows: position j of sequence b sits in page table[b, j // ps]
     assert list(O.pool_rows(table, ps, 1, 20)[15:18]) == [
         table[1, 0] * ps + 15, table[1, 1] * ps + 0, table[1, 1] * ps + 1]
+
+
+# ----------------------------------------------------------------------------
+# KV Bridging projection
+# ----------------------------------------------------------------------------
+def test_kv_bridge_brute_force():
+    h = rand((2, 3, 5), 80)
+    w = rand((2, 6, 5), 81)
+    k, v = O.kv_bridge(h, w, h_kv=2)
+    for b in range(2):
+        for t in range(3):
+            for f in range(6):
+                want_k = sum(h[b, t, c] * w[0, f, c] for c in range(5))
+                want_v = sum(h[b, t, c] * w[1, f, c] for c in range(5))
+                assert abs(k[b, t, f // 3, f % 3] - want_k) < 1e-12
+                assert abs(v[b, t, f // 3, f % 3] - want_v) < 1e-12
+
+
+def test_kv_bridge_feature_selection():
+    # weight rows that are unit vectors copy hidden features: exact
+    h = rand((1, 4, 8), 82)
+    perm = np.random.default_rng(83).permutation(8)
+    w = np.zeros((2, 8, 8))
+    w[0, np.arange(8), perm] = 1.0
+    w[1, np.arange(8), perm[::-1]] = 2.0
+    k, v = O.kv_bridge(h, w, h_kv=2)
+    np.testing.assert_array_equal(k.reshape(1, 4, 8), h[:, :, perm])
+    np.testing.assert_array_equal(v.reshape(1, 4, 8), 2.0 * h[:, :, perm[::-1]])

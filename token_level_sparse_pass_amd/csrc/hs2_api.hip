@@ -532,6 +532,26 @@ hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages
                           stream);
 }
 
+hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidden,
+                         const void* w_kv, void* k, void* v, void* stream) {
+  g_err.clear();
+  HS2_TRY(check_problem(p));
+  if (p->dtype != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "KV bridging is bf16 only");
+  if (d_model <= 0 || d_model % 64)
+    return fail(HS2_ERR_SHAPE, "d_model %d: a positive multiple of 64 is needed", d_model);
+  const long long tokens = (long long)p->batch * p->n_kv;
+  if (tokens > INT32_MAX) return fail(HS2_ERR_UNSUPPORTED, "%lld tokens", tokens);
+  HS2_TRY(check_ptr(hidden, "hidden"));
+  HS2_TRY(check_ptr(w_kv, "w_kv"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  hs2::BridgePlan b;
+  b.hidden = hidden; b.w_kv = w_kv; b.k = k; b.v = v;
+  b.tokens = (int)tokens; b.features = p->h_kv * p->head_dim; b.d_model = d_model;
+  HIP_TRY(hs2::launch_kv_bridge(b, (hipStream_t)stream), "KV bridge");
+  return HS2_OK;
+}
+
 hs2_status hs2_profile_enable(int32_t on) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_prof_mu);

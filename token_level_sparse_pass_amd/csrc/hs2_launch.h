@@ -152,4 +152,13 @@ struct SparsePlan {
 };
 hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st);
 
+// KV Bridging (bf16): k, v [tokens][features] = hidden [tokens][d_model] .
+// w_kv[0 or 1]^T, w_kv [2 * features][d_model]; d_model a multiple of 64.
+struct BridgePlan {
+  const void* hidden; const void* w_kv;
+  void* k; void* v;
+  int tokens, features, d_model;
+};
+hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st);
+
 }  // namespace hs2

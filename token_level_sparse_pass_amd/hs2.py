@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_step_paged.argtypes = [P, ctypes.POINTER(KvPages), i32, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(i32), vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_decode_step_paged.restype = i32
+    lib.hs2_kv_bridge.argtypes = [P, i32, vp, vp, vp, vp, vp]
+    lib.hs2_kv_bridge.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
@@ -273,4 +275,22 @@ def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table
                                      _ptr(k_pool), _ptr(v_pool), lens_h, _ptr(out["o_full"]),
                                      _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
                                      _ptr(ws), ws.numel(), _stream(q_full.device)))
+    return out
+
+
+def kv_bridge(hidden, w_kv, h_kv, *, out=None):
+    """hs2_kv_bridge: K, V [B, n, h_kv, d] from hidden [B, n, d_model] and
+    w_kv [2, h_kv * d, d_model] (bf16). Returns (k, v)."""
+    lib = load()
+    _check_tensor(hidden, "hidden", torch.bfloat16)
+    _check_tensor(w_kv, "w_kv", torch.bfloat16)
+    B, n, dm = hidden.shape
+    feats = w_kv.shape[1]
+    d = feats // h_kv
+    p = problem(torch.bfloat16, B, 1, n, h_kv, h_kv, d, top_k=1, window=1)
+    if out is None:
+        out = (torch.empty((B, n, h_kv, d), dtype=torch.bfloat16, device=hidden.device),
+               torch.empty((B, n, h_kv, d), dtype=torch.bfloat16, device=hidden.device))
+    _check(lib.hs2_kv_bridge(ctypes.byref(p), dm, _ptr(hidden), _ptr(w_kv), _ptr(out[0]),
+                             _ptr(out[1]), _stream(hidden.device)))
     return out
