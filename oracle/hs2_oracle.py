@@ -29,6 +29,14 @@ What it computes, step by step (the pages describe the method in prose only):
    every sparse layer attends, with one softmax, over window + selected
    tokens, reading the same K/V and the same index set as the full layer.
 
+6. Backward pass, for fine-tuning ("Xiaomi Unveils HySparse2", section
+   "Performance Gains: Cost, Speed, and Long-Context Capabilities": the
+   compared models are fine-tuned alike before evaluation). Reading used: the
+   index sets are held fixed (a discrete choice has no gradient, so the score
+   and selection steps pass none back); the full layer and every sparse layer
+   are differentiated as ordinary softmax attention, and because all of them
+   read the one K/V buffer (KV Reuse) their K and V gradients add up.
+
 Inputs may be float32/float64 arrays or raw bf16 bit patterns (uint16); they
 are widened exactly to fp64.
 """
@@ -401,6 +409,125 @@ def sparse_rows(q_sparse, k, v, b: int, rows, idx_rows, scale=None):
                 e = np.exp(s - s.max())
                 out[l, r, h] = (e / e.sum()) @ Vs[:, g, :]
     return out
+
+
+# ----------------------------------------------------------------------------
+# step 6: backward pass with the index sets held fixed
+# ----------------------------------------------------------------------------
+def attention_grads(q, k, v, keep, dout, scale):
+    """Gradients of one softmax-attention head, the textbook way.
+
+    q [n, d], k/v [m, d], keep [n, m] bool (which keys each query sees; every
+    query sees at least one), dout [n, d] = dLoss/dO. With s = scale q k^T
+    (masked), P = softmax(s) per row and O = P v:
+      dv = P^T dout
+      dP = dout v^T
+      ds = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied to dP)
+      dq = scale ds k,   dk = scale ds^T q.
+    Returns (dq, dk, dv) in fp64.
+    """
+    s = np.where(keep, (q @ k.T) * scale, NEG_INF)
+    m = s.max(axis=1, keepdims=True)
+    e = np.where(keep, np.exp(s - m), 0.0)
+    P = e / e.sum(axis=1, keepdims=True)
+    dv = P.T @ dout
+    dP = dout @ v.T
+    ds = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    return scale * ds @ k, scale * ds.T @ q, dv
+
+
+def block_backward(q_full, q_sparse, k, v, idx, do_full, do_sparse, scale=None):
+    """Backward of the whole block for given output gradients, dense.
+
+    q_full / do_full [B, n_q, h_q, d], q_sparse / do_sparse [L, B, n_q, h_q, d],
+    k/v [B, n_kv, h_kv, d], idx [B, n_q, W] (-1 padded; the sparse layers'
+    index sets, held fixed). Returns dict(dq_full, dq_sparse, dk, dv) in fp64;
+    dk and dv sum the full layer's and every sparse layer's contributions.
+    """
+    qf, kk, vv, dof = widen(q_full), widen(k), widen(v), widen(do_full)
+    qs, dos = widen(q_sparse), widen(do_sparse)
+    B, nq, hq, d = qf.shape
+    nkv, hkv = kk.shape[1], kk.shape[2]
+    L = qs.shape[0]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    idx = np.asarray(idx)
+    pos = np.arange(nq) + (nkv - nq)
+    causal = np.arange(nkv)[None, :] <= pos[:, None]
+    dq_full = np.zeros_like(qf)
+    dq_sparse = np.zeros_like(qs)
+    dk = np.zeros_like(kk)
+    dv = np.zeros_like(vv)
+    for b in range(B):
+        chosen = np.zeros((nq, nkv), dtype=bool)
+        for i in range(nq):
+            sel = idx[b, i][idx[b, i] >= 0]
+            chosen[i, sel] = True
+        for h in range(hq):
+            g = group_of(h, hq, hkv)
+            a, bk, bv = attention_grads(qf[b, :, h], kk[b, :, g], vv[b, :, g], causal,
+                                        dof[b, :, h], scale)
+            dq_full[b, :, h] = a
+            dk[b, :, g] += bk
+            dv[b, :, g] += bv
+            for l in range(L):
+                a, bk, bv = attention_grads(qs[l, b, :, h], kk[b, :, g], vv[b, :, g], chosen,
+                                            dos[l, b, :, h], scale)
+                dq_sparse[l, b, :, h] = a
+                dk[b, :, g] += bk
+                dv[b, :, g] += bv
+    return dict(dq_full=dq_full, dq_sparse=dq_sparse, dk=dk, dv=dv)
+
+
+def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int, j_lo: int,
+                        scale=None):
+    """block_backward for large contexts, restricted to what a tail of keys
+    decides: the K/V gradient rows j >= j_lo and the query gradients of every
+    query at position p >= j_lo (only those queries can reach such a key:
+    causality, and index entries never exceed p). Each of those queries is
+    handled alone over its whole key range, so nothing of size n_q x n_kv is
+    ever formed.
+
+    Returns dict(rows (query indices i), dq_full [R, h_q, d],
+    dq_sparse [L, R, h_q, d], dk, dv [n_kv - j_lo, h_kv, d]).
+    """
+    nq, hq, d = q_full.shape[1], q_full.shape[2], q_full.shape[3]
+    nkv, hkv = k.shape[1], k.shape[2]
+    L = np.asarray(q_sparse).shape[0]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    q_off = nkv - nq
+    rows = np.arange(max(0, j_lo - q_off), nq)
+    R = len(rows)
+    dq_full = np.zeros((R, hq, d))
+    dq_sparse = np.zeros((L, R, hq, d))
+    dk = np.zeros((nkv - j_lo, hkv, d))
+    dv = np.zeros((nkv - j_lo, hkv, d))
+    idx = np.asarray(idx)
+    for r, i in enumerate(rows):
+        p = q_off + int(i)
+        keys = np.arange(p + 1)
+        sel = idx[b, i][idx[b, i] >= 0]
+        for g in range(hkv):
+            Kg, Vg = widen(k[b, :p + 1, g]), widen(v[b, :p + 1, g])
+            heads = [h for h in range(hq) if group_of(h, hq, hkv) == g]
+            passes = [(None, keys)] + [(l, sel) for l in range(L)]
+            for layer, ks in passes:
+                Kl, Vl = Kg[ks], Vg[ks]
+                for h in heads:
+                    if layer is None:
+                        qv, dov = widen(q_full[b, i, h]), widen(do_full[b, i, h])
+                    else:
+                        qv = widen(q_sparse[layer, b, i, h])
+                        dov = widen(do_sparse[layer, b, i, h])
+                    a, bk, bv = attention_grads(qv[None], Kl, Vl, np.ones((1, len(ks)), bool),
+                                                dov[None], scale)
+                    if layer is None:
+                        dq_full[r, h] = a[0]
+                    else:
+                        dq_sparse[layer, r, h] = a[0]
+                    tail = ks >= j_lo
+                    dk[ks[tail] - j_lo, g] += bk[tail]
+                    dv[ks[tail] - j_lo, g] += bv[tail]
+    return dict(rows=rows, dq_full=dq_full, dq_sparse=dq_sparse, dk=dk, dv=dv)
 
 
 # ----------------------------------------------------------------------------

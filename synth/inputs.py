@@ -11,7 +11,9 @@ planted retrieval structure:
 * clusters - 32 runs of 32 consecutive keys get that common direction added.
 
 Streams: 0 = full-layer Q, 1 = K, 2 = V, 3 = structure, 10 + l = sparse Q of
-layer l, 1000 + 16 * step + 0..3 = the new token of decode step `step`. The same bits go to the GPU library and (as a host copy) to the
+layer l, 20/21 = bridging hidden states / weights, 40 = full-layer output
+gradient, 41 + l = sparse-layer output gradient of layer l, 60 = random index
+sets, 1000 + 16 * step + 0..3 = the new token of decode step `step`. The same bits go to the GPU library and (as a host copy) to the
 oracle. Nothing here computes attention, scores or selections.
 """
 import math
@@ -153,3 +155,55 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     return t.contiguous().cpu().numpy()
+
+
+def grad_inputs(w: Workload, device="cpu", sparse_layers=None) -> dict:
+    """Output gradients for the backward pass: do_full [B, n_q, h_q, d]
+    (stream 40) and do_sparse [L, B, n_q, h_q, d] (streams 41 + l), N(0,1)."""
+    B, nq, hq, d = w.batch, w.n_q, w.h_q, w.d
+    L = w.n_sparse if sparse_layers is None else sparse_layers
+    do_full = _randn((B, nq, hq, d), w, 40, device)
+    do_sparse = torch.empty((L, B, nq, hq, d), dtype=do_full.dtype, device=device)
+    for layer in range(L):
+        do_sparse[layer] = _randn((B, nq, hq, d), w, 41 + layer, device)
+    return {"do_full": do_full, "do_sparse": do_sparse}
+
+
+def random_index_rows(w: Workload, device="cpu", rows_per_chunk=4096) -> torch.Tensor:
+    """Valid index sets drawn at random (stream 60), to drive the backward
+    pass independently of any selection: for query i at position
+    p = q_off + i, the window max(0, p - window + 1) .. p plus min(top_k, C)
+    of the C = p - window + 1 candidates 0 .. p - window, one drawn uniformly
+    from each of min(top_k, C) consecutive, disjoint integer ranges that tile
+    0 .. C - 1 (so the picks are distinct and ascending). Rows are
+    ascending and -1 padded to top_k + window; int32 [B, n_q, top_k + window].
+    """
+    B, nq, k, win = w.batch, w.n_q, w.top_k, w.window
+    width = k + win
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(w.cid, 60))
+    out = torch.full((B, nq, width), -1, dtype=torch.int32, device=device)
+    t = torch.arange(k, device=device, dtype=torch.int64)
+    wj = torch.arange(win, device=device, dtype=torch.int64)
+    for b in range(B):
+        for i0 in range(0, nq, rows_per_chunk):
+            i1 = min(nq, i0 + rows_per_chunk)
+            p = torch.arange(i0, i1, device=device, dtype=torch.int64) + (w.n_kv - nq)
+            C = torch.clamp(p - win + 1, min=0)                        # candidates
+            n_pick = torch.clamp(C, max=k)
+            lo = (t[None, :] * C[:, None]) // k                        # range t starts
+            hi = ((t[None, :] + 1) * C[:, None]) // k                  # and ends
+            u = torch.rand((i1 - i0, k), generator=g, device=device, dtype=torch.float64)
+            pick = lo + torch.minimum((u * (hi - lo)).to(torch.int64), hi - lo - 1)
+            # fewer candidates than top_k: take them all
+            pick = torch.where((C < k)[:, None], t[None, :], pick)
+            valid = t[None, :] < n_pick[:, None]
+            wpos = torch.clamp(p - win + 1, min=0)[:, None] + wj[None, :]
+            wvalid = wpos <= p[:, None]
+            # candidates first (ascending), then the window (also ascending and
+            # above every candidate); valid entries are packed to the front
+            vals = torch.cat([torch.where(valid, pick, -1), torch.where(wvalid, wpos, -1)], 1)
+            order = torch.argsort((vals < 0).to(torch.int8), dim=1, stable=True)
+            rows = torch.gather(vals, 1, order)
+            out[b, i0:i1] = rows.to(torch.int32)
+    return out

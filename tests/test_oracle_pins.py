@@ -405,3 +405,122 @@ def test_kv_bridge_feature_selection():
     k, v = O.kv_bridge(h, w, h_kv=2)
     np.testing.assert_array_equal(k.reshape(1, 4, 8), h[:, :, perm])
     np.testing.assert_array_equal(v.reshape(1, 4, 8), 2.0 * h[:, :, perm[::-1]])
+
+
+# ----------------------------------------------------------------------------
+# backward pass (index sets held fixed)
+# ----------------------------------------------------------------------------
+def _bwd_case(seed, B=1, nq=6, nkv=9, hq=4, hkv=2, d=3, L=2, top_k=2, window=2):
+    q, qs = rand((B, nq, hq, d), seed), rand((L, B, nq, hq, d), seed + 1)
+    k, v = rand((B, nkv, hkv, d), seed + 2), rand((B, nkv, hkv, d), seed + 3)
+    dof, dos = rand((B, nq, hq, d), seed + 4), rand((L, B, nq, hq, d), seed + 5)
+    idx = O.block_forward(q, qs, k, v, top_k=top_k, window=window)["idx"]
+    return dict(q_full=q, q_sparse=qs, k=k, v=v, idx=idx, do_full=dof, do_sparse=dos)
+
+
+def _block_loss(c):
+    """sum(dO * O) over the full layer and every sparse layer: its gradient
+    with respect to any input is what the backward pass returns."""
+    o, _ = O.full_layer(c["q_full"], c["k"], c["v"])
+    total = float((c["do_full"] * o).sum())
+    for l in range(c["q_sparse"].shape[0]):
+        ol = O.sparse_layer(c["q_sparse"][l], c["k"], c["v"], c["idx"])
+        total += float((c["do_sparse"][l] * ol).sum())
+    return total
+
+
+def test_backward_matches_finite_differences():
+    # central differences of the (separately pinned) forward pass, for every
+    # input element; the idx sets stay fixed while inputs move
+    c = _bwd_case(100)
+    g = O.block_backward(**c)
+    eps = 1e-6
+    for name, gname in (("q_full", "dq_full"), ("q_sparse", "dq_sparse"), ("k", "dk"),
+                        ("v", "dv")):
+        x = c[name]
+        num = np.zeros_like(x)
+        for pos in np.ndindex(*x.shape):
+            old = x[pos]
+            x[pos] = old + eps
+            up = _block_loss(c)
+            x[pos] = old - eps
+            down = _block_loss(c)
+            x[pos] = old
+            num[pos] = (up - down) / (2 * eps)
+        np.testing.assert_allclose(g[gname], num, rtol=0, atol=2e-7, err_msg=name)
+
+
+def test_backward_matches_torch_autograd():
+    # torch's fp64 attention differentiated by autograd: the full layer with
+    # an end-aligned causal mask, the sparse layers with the idx sets as mask
+    B, nq, nkv, hq, hkv, d, L = 2, 7, 11, 6, 2, 8, 2
+    c = _bwd_case(110, B=B, nq=nq, nkv=nkv, hq=hq, hkv=hkv, d=d, L=L, top_k=3, window=3)
+    got = O.block_backward(**c)
+    t = {n: torch.from_numpy(c[n].copy()).requires_grad_(True)
+         for n in ("q_full", "q_sparse", "k", "v")}
+    pos = torch.arange(nq) + (nkv - nq)
+    causal = torch.arange(nkv)[None, :] <= pos[:, None]
+    kt, vt = t["k"].permute(0, 2, 1, 3), t["v"].permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(t["q_full"].permute(0, 2, 1, 3), kt, vt, attn_mask=causal,
+                                       enable_gqa=True)
+    loss = (o * torch.from_numpy(c["do_full"]).permute(0, 2, 1, 3)).sum()
+    chosen = torch.zeros((B, 1, nq, nkv), dtype=torch.bool)
+    for b in range(B):
+        for i in range(nq):
+            sel = c["idx"][b, i][c["idx"][b, i] >= 0]
+            chosen[b, 0, i, torch.from_numpy(sel)] = True
+    for l in range(L):
+        ol = F.scaled_dot_product_attention(t["q_sparse"][l].permute(0, 2, 1, 3), kt, vt,
+                                            attn_mask=chosen, enable_gqa=True)
+        loss = loss + (ol * torch.from_numpy(c["do_sparse"][l]).permute(0, 2, 1, 3)).sum()
+    loss.backward()
+    for n, gn in (("q_full", "dq_full"), ("q_sparse", "dq_sparse"), ("k", "dk"), ("v", "dv")):
+        np.testing.assert_allclose(got[gn], t[n].grad.numpy(), rtol=0, atol=1e-11, err_msg=n)
+
+
+def test_backward_sum_invariants():
+    # every softmax row sums to 1, so the V gradients of a KV group add up to
+    # the group's output gradients; the softmax Jacobian kills constants, so
+    # the K gradients of a group sum to zero
+    c = _bwd_case(120, B=2, nq=10, nkv=16, hq=6, hkv=3, d=5, L=3, top_k=4, window=3)
+    g = O.block_backward(**c)
+    G = 2
+    for b in range(2):
+        for kv in range(3):
+            heads = slice(kv * G, (kv + 1) * G)
+            want = c["do_full"][b, :, heads].sum(axis=(0, 1)) + \
+                c["do_sparse"][:, b, :, heads].sum(axis=(0, 1, 2))
+            np.testing.assert_allclose(g["dv"][b, :, kv].sum(axis=0), want, atol=1e-12)
+            np.testing.assert_allclose(g["dk"][b, :, kv].sum(axis=0), 0.0, atol=1e-12)
+
+
+def test_backward_constant_values_closed_form():
+    # V rows all equal: every output is that row whatever the weights, so Q
+    # and K get no gradient and dV spreads dO by the probabilities
+    c = _bwd_case(130, nq=8, nkv=8, top_k=3, window=2)
+    c["v"][:] = rand((1, 1, 2, 3), 131)
+    g = O.block_backward(**c)
+    np.testing.assert_allclose(g["dq_full"], 0.0, atol=1e-13)
+    np.testing.assert_allclose(g["dq_sparse"], 0.0, atol=1e-13)
+    np.testing.assert_allclose(g["dk"], 0.0, atol=1e-13)
+    # the first query sees only key 0 in the full layer: P = 1
+    d0 = O.block_backward(**{**c, "do_sparse": np.zeros_like(c["do_sparse"]),
+                             "do_full": np.where(np.arange(8)[None, :, None, None] == 0,
+                                                 c["do_full"], 0.0)})
+    np.testing.assert_allclose(d0["dv"][0, 0, 0], c["do_full"][0, 0, :2].sum(axis=0), atol=1e-13)
+    np.testing.assert_allclose(d0["dv"][0, 1:], 0.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("j_lo", [0, 9, 15])
+def test_backward_tail_matches_dense(j_lo):
+    c = _bwd_case(140, B=2, nq=8, nkv=17, hq=4, hkv=2, d=6, L=2, top_k=3, window=3)
+    dense = O.block_backward(**c)
+    for b in range(2):
+        t = O.block_backward_tail(c["q_full"], c["q_sparse"], c["k"], c["v"], c["idx"],
+                                  c["do_full"], c["do_sparse"], b, j_lo)
+        rows = t["rows"]
+        assert list(rows) == list(range(max(0, j_lo - 9), 8))
+        np.testing.assert_allclose(t["dq_full"], dense["dq_full"][b, rows], atol=1e-12)
+        np.testing.assert_allclose(t["dq_sparse"], dense["dq_sparse"][:, b, rows], atol=1e-12)
+        np.testing.assert_allclose(t["dk"], dense["dk"][b, j_lo:], atol=1e-12)
+        np.testing.assert_allclose(t["dv"], dense["dv"][b, j_lo:], atol=1e-12)
