@@ -203,12 +203,45 @@ hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages
 hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidden,
                          const void* w_kv, void* k, void* v, void* stream);
 
+/* Backward pass of the block, for fine-tuning (hitechexpert.top, section
+ * "Performance Gains: Cost, Speed, and Long-Context Capabilities": the
+ * compared models are fine-tuned alike). The index sets are held fixed (a
+ * discrete selection passes no gradient back, so the score and selection
+ * steps have none); the full layer and every sparse layer are
+ * differentiated as softmax attention, and since they all read the one K/V
+ * buffer (KV Reuse, section "Two-Level KV Sharing") their K/V gradients add:
+ *   dK = dK_full + sum over layers dK_l,   dV likewise.
+ * Inputs (DEVICE): everything hs2_block_forward read (q_full, q_sparse, k,
+ * v) and wrote (o_full, o_sparse, idx, lse: the natural-log LSE, required),
+ * plus the output gradients do_full [batch, n_q, h_q, head_dim] and do_sparse
+ * [n_sparse_layers, batch, n_q, h_q, head_dim]. idx rows must be ascending,
+ * -1 padded, entries <= p (as hs2_block_forward writes them).
+ * Outputs (DEVICE, dtype, overwritten): dq_full, dq_sparse (shapes of
+ * q_full, q_sparse), dk, dv (shape of k). Gradients are accumulated in fp32
+ * and rounded once. The sparse layers' K/V sums use fp32 atomic adds, so
+ * their last bits may differ from run to run; everything else is
+ * deterministic. With n_sparse_layers = 0, q_sparse, o_sparse, idx,
+ * do_sparse and dq_sparse may be NULL.
+ * Workspace: hs2_backward_workspace_size bytes (Delta = rowsum(dO * O) per
+ * row, and the sparse layers' fp32 K/V accumulators), 16-byte aligned. */
+hs2_status hs2_backward_workspace_size(const hs2_problem* p, int32_t n_sparse_layers,
+                                       size_t* bytes);
+hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
+                              const void* q_full, const void* q_sparse,
+                              const void* k, const void* v,
+                              const void* o_full, const void* o_sparse,
+                              const float* lse, const int32_t* idx,
+                              const void* do_full, const void* do_sparse,
+                              void* dq_full, void* dq_sparse, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,
  * pass 1), HS2_PASS_SCORE (head-summed scores, pass 2), HS2_PASS_SELECT
- * (selection), HS2_PASS_SPARSE (sparse layers) and HS2_PASS_LAYOUT (the
+ * (selection), HS2_PASS_SPARSE (sparse layers), HS2_PASS_LAYOUT (the
  * copy of V into the workspace in key-tile-major transposed order that the
- * bf16 / head_dim 128 prefill kernel reads; absent on every other path).
+ * bf16 / head_dim 128 prefill kernel reads; absent on every other path),
+ * HS2_PASS_BWD_FULL and HS2_PASS_BWD_SPARSE (hs2_block_backward).
  * hs2_profile_enable(1)
  * starts a fresh record and (0) stops recording. hs2_profile_read waits for
  * the recorded events, then writes the summed milliseconds and the number of
@@ -220,7 +253,9 @@ typedef enum {
   HS2_PASS_SELECT = 2,
   HS2_PASS_SPARSE = 3,
   HS2_PASS_LAYOUT = 4,
-  HS2_N_PASSES = 5
+  HS2_PASS_BWD_FULL = 5,    /* hs2_block_backward: the full layer            */
+  HS2_PASS_BWD_SPARSE = 6,  /* hs2_block_backward: the sparse layers         */
+  HS2_N_PASSES = 7
 } hs2_pass;
 hs2_status hs2_profile_enable(int32_t on);
 hs2_status hs2_profile_read(double* ms, int64_t* launches);

@@ -482,10 +482,10 @@ def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int,
                         scale=None):
     """block_backward for large contexts, restricted to what a tail of keys
     decides: the K/V gradient rows j >= j_lo and the query gradients of every
-    query at position p >= j_lo (only those queries can reach such a key:
-    causality, and index entries never exceed p). Each of those queries is
-    handled alone over its whole key range, so nothing of size n_q x n_kv is
-    ever formed.
+    query at position p >= j_lo. Only those queries can reach such a key
+    (causality, and index entries never exceed p), so summing their
+    contributions alone gives those K/V rows exactly; nothing of size
+    n_q x n_kv is formed, only (queries in the tail) x n_kv per KV group.
 
     Returns dict(rows (query indices i), dq_full [R, h_q, d],
     dq_sparse [L, R, h_q, d], dk, dv [n_kv - j_lo, h_kv, d]).
@@ -493,40 +493,39 @@ def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int,
     nq, hq, d = q_full.shape[1], q_full.shape[2], q_full.shape[3]
     nkv, hkv = k.shape[1], k.shape[2]
     L = np.asarray(q_sparse).shape[0]
+    G = hq // hkv
     scale = 1.0 / np.sqrt(d) if scale is None else scale
     q_off = nkv - nq
     rows = np.arange(max(0, j_lo - q_off), nq)
     R = len(rows)
+    pos = rows + q_off
+    causal = np.arange(nkv)[None, :] <= pos[:, None]                 # [R, n_kv]
+    idx = np.asarray(idx)
+    chosen = np.zeros((R, nkv), dtype=bool)
+    for r, i in enumerate(rows):
+        sel = idx[b, i][idx[b, i] >= 0]
+        chosen[r, sel] = True
     dq_full = np.zeros((R, hq, d))
     dq_sparse = np.zeros((L, R, hq, d))
     dk = np.zeros((nkv - j_lo, hkv, d))
     dv = np.zeros((nkv - j_lo, hkv, d))
-    idx = np.asarray(idx)
-    for r, i in enumerate(rows):
-        p = q_off + int(i)
-        keys = np.arange(p + 1)
-        sel = idx[b, i][idx[b, i] >= 0]
-        for g in range(hkv):
-            Kg, Vg = widen(k[b, :p + 1, g]), widen(v[b, :p + 1, g])
-            heads = [h for h in range(hq) if group_of(h, hq, hkv) == g]
-            passes = [(None, keys)] + [(l, sel) for l in range(L)]
-            for layer, ks in passes:
-                Kl, Vl = Kg[ks], Vg[ks]
-                for h in heads:
-                    if layer is None:
-                        qv, dov = widen(q_full[b, i, h]), widen(do_full[b, i, h])
-                    else:
-                        qv = widen(q_sparse[layer, b, i, h])
-                        dov = widen(do_sparse[layer, b, i, h])
-                    a, bk, bv = attention_grads(qv[None], Kl, Vl, np.ones((1, len(ks)), bool),
-                                                dov[None], scale)
-                    if layer is None:
-                        dq_full[r, h] = a[0]
-                    else:
-                        dq_sparse[layer, r, h] = a[0]
-                    tail = ks >= j_lo
-                    dk[ks[tail] - j_lo, g] += bk[tail]
-                    dv[ks[tail] - j_lo, g] += bv[tail]
+    for g in range(hkv):
+        heads = [h for h in range(hq) if group_of(h, hq, hkv) == g]
+        Kg, Vg = widen(k[b, :, g]), widen(v[b, :, g])
+        # every (query, head of the group) pair is one attention row
+        passes = [(None, causal)] + [(l, chosen) for l in range(L)]
+        for layer, keep in passes:
+            qsrc = q_full[b, rows] if layer is None else np.asarray(q_sparse)[layer, b, rows]
+            dsrc = do_full[b, rows] if layer is None else np.asarray(do_sparse)[layer, b, rows]
+            Q = widen(qsrc)[:, heads].reshape(R * G, d)
+            dO = widen(dsrc)[:, heads].reshape(R * G, d)
+            a, bk, bv = attention_grads(Q, Kg, Vg, np.repeat(keep, G, axis=0), dO, scale)
+            if layer is None:
+                dq_full[:, heads] = a.reshape(R, G, d)
+            else:
+                dq_sparse[layer][:, heads] = a.reshape(R, G, d)
+            dk[:, g] += bk[j_lo:]
+            dv[:, g] += bv[j_lo:]
     return dict(rows=rows, dq_full=dq_full, dq_sparse=dq_sparse, dk=dk, dv=dv)
 
 

@@ -208,3 +208,34 @@ def test_kv_bridge_rejections():
     assert lib.hs2_kv_bridge(ctypes.byref(p), 256, None, *args[1:], None) == 1
     assert lib.hs2_kv_bridge(ctypes.byref(p), 256, vp(FAKE), vp(FAKE), vp(FAKE + 2), vp(FAKE),
                              None) == 5
+
+
+def test_backward_workspace_and_rejections():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    p = base_problem()
+    # Delta rows, then two fp32 K/V accumulators when there are sparse layers
+    delta = 1 * 8 * 256 * 4
+    acc = 1 * 1024 * 2 * 128 * 4
+    assert hs2.backward_workspace_size(p, 0) == delta
+    assert hs2.backward_workspace_size(p, 3) == delta + 2 * acc
+    ws = hs2.backward_workspace_size(p, 2)
+
+    def call(L=2, ws_bytes=ws, **over):
+        names = ["q_full", "q_sparse", "k", "v", "o_full", "o_sparse", "lse", "idx", "do_full",
+                 "do_sparse", "dq_full", "dq_sparse", "dk", "dv", "ws"]
+        a = {n: FAKE for n in names}
+        a.update(over)
+        ptrs = [vp(a[n]) for n in names]
+        return lib.hs2_block_backward(ctypes.byref(p), L, *ptrs[:-1], ptrs[-1], ws_bytes, None)
+
+    assert call(L=-1) == 2
+    for n in ("q_full", "k", "v", "o_full", "lse", "do_full", "dq_full", "dk", "dv", "ws"):
+        assert call(**{n: None}) == 1, n
+        assert call(**{n: FAKE + 4}) == 5, n
+    for n in ("q_sparse", "o_sparse", "idx", "do_sparse", "dq_sparse"):
+        assert call(**{n: None}) == 1, n
+    assert call(ws_bytes=ws - 1) == 4
+    assert b"workspace" in lib.hs2_last_error()
+    bad = base_problem(h_q=6, h_kv=4)
+    assert lib.hs2_backward_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ctypes.c_size_t())) == 2

@@ -552,6 +552,117 @@ hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidd
   return HS2_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: Delta [B][h_q][n_q] floats, then (with sparse layers)
+// the fp32 K and V gradient accumulators, [B][n_kv][h_kv][head_dim] each.
+struct BwdLayout {
+  size_t delta = 0, acc_k = 0, acc_v = 0, acc_elems = 0, total = 0;
+};
+
+BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
+  BwdLayout L;
+  size_t off = 0;
+  L.delta = off;
+  off += align_up((size_t)p.batch * p.h_q * p.n_q * sizeof(float));
+  if (n_sparse > 0) {
+    L.acc_elems = (size_t)p.batch * p.n_kv * p.h_kv * p.head_dim;
+    L.acc_k = off;
+    off += align_up(L.acc_elems * sizeof(float));
+    L.acc_v = off;
+    off += align_up(L.acc_elems * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_backward_workspace_size(const hs2_problem* p, int32_t n_sparse_layers,
+                                       size_t* bytes) {
+  g_err.clear();
+  HS2_TRY(check_problem(p));
+  if (n_sparse_layers < 0) return fail(HS2_ERR_SHAPE, "n_sparse_layers %d", n_sparse_layers);
+  if (!bytes) return fail(HS2_ERR_NULL, "bytes is NULL");
+  *bytes = bwd_layout(*p, n_sparse_layers).total;
+  return HS2_OK;
+}
+
+hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                              const void* q_sparse, const void* k, const void* v,
+                              const void* o_full, const void* o_sparse, const float* lse,
+                              const int32_t* idx, const void* do_full, const void* do_sparse,
+                              void* dq_full, void* dq_sparse, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  HS2_TRY(check_problem(p));
+  if (n_sparse_layers < 0) return fail(HS2_ERR_SHAPE, "n_sparse_layers %d", n_sparse_layers);
+  HS2_TRY(check_ptr(q_full, "q_full"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  HS2_TRY(check_ptr(o_full, "o_full"));
+  HS2_TRY(check_ptr(lse, "lse"));
+  HS2_TRY(check_ptr(do_full, "do_full"));
+  HS2_TRY(check_ptr(dq_full, "dq_full"));
+  HS2_TRY(check_ptr(dk, "dk"));
+  HS2_TRY(check_ptr(dv, "dv"));
+  const bool sparse = n_sparse_layers > 0;
+  HS2_TRY(check_ptr(q_sparse, "q_sparse", sparse));
+  HS2_TRY(check_ptr(o_sparse, "o_sparse", sparse));
+  HS2_TRY(check_ptr(idx, "idx", sparse));
+  HS2_TRY(check_ptr(do_sparse, "do_sparse", sparse));
+  HS2_TRY(check_ptr(dq_sparse, "dq_sparse", sparse));
+  const BwdLayout L = bwd_layout(*p, n_sparse_layers);
+  if (!workspace) return fail(HS2_ERR_NULL, "workspace is NULL (needs %zu bytes)", L.total);
+  if (!aligned16(workspace)) return fail(HS2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(HS2_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, L.total);
+
+  const hipStream_t st = (hipStream_t)stream;
+  const float scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  float* acc_k = sparse ? fptr(workspace, L.acc_k) : nullptr;
+  float* acc_v = sparse ? fptr(workspace, L.acc_v) : nullptr;
+  if (sparse) {
+    PassTimer t(st, HS2_PASS_BWD_SPARSE);
+    HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");
+    HIP_TRY(hs2::launch_zero_f32(acc_v, L.acc_elems, st), "zero accumulators");
+    const int G = p->h_q / p->h_kv;
+    const int per = std::max(1, 64 / G);                     // layers per launch
+    const size_t esz = p->dtype == HS2_BF16 ? 2 : 4;
+    const size_t layer_bytes = (size_t)p->batch * p->n_q * p->h_q * p->head_dim * esz;
+    for (int l0 = 0; l0 < n_sparse_layers; l0 += per) {
+      hs2::SparseBwdPlan sp;
+      sp.layers = std::min(per, n_sparse_layers - l0);
+      sp.q = (const char*)q_sparse + l0 * layer_bytes;
+      sp.o = (const char*)o_sparse + l0 * layer_bytes;
+      sp.dout = (const char*)do_sparse + l0 * layer_bytes;
+      sp.dq = (char*)dq_sparse + l0 * layer_bytes;
+      sp.k = k; sp.v = v; sp.idx = idx; sp.acc_k = acc_k; sp.acc_v = acc_v;
+      sp.batch = p->batch; sp.n_q = p->n_q; sp.n_kv = p->n_kv; sp.h_q = p->h_q;
+      sp.h_kv = p->h_kv; sp.head_dim = p->head_dim; sp.width = index_width(*p);
+      sp.scale = p->softmax_scale; sp.scale_log2 = scale_log2;
+      sp.bf16 = p->dtype == HS2_BF16;
+      HIP_TRY(hs2::launch_sparse_bwd(sp, st), "sparse backward");
+    }
+  }
+  {
+    PassTimer t(st, HS2_PASS_BWD_FULL);
+    hs2::BwdPlan bp;
+    bp.s = shape_of(*p);
+    bp.scale = p->softmax_scale;
+    bp.q = q_full; bp.k = k; bp.v = v; bp.o = o_full; bp.dout = do_full;
+    bp.lse = lse; bp.delta = fptr(workspace, L.delta);
+    bp.acc_k = acc_k; bp.acc_v = acc_v;
+    bp.dq = dq_full; bp.dk = dk; bp.dv = dv;
+    HIP_TRY(hs2::launch_attn_bwd(bp, st), "full-layer backward");
+  }
+  return HS2_OK;
+}
+
 hs2_status hs2_profile_enable(int32_t on) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_prof_mu);

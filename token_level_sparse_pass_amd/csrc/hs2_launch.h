@@ -161,4 +161,38 @@ struct BridgePlan {
 };
 hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st);
 
+// Backward pass of the full layer (prefill shapes): Delta = rowsum(dO * O)
+// into `delta` ([batch][h_q][n_q] floats), then dK/dV and dQ. lse is the
+// forward's natural-log LSE. acc_k / acc_v (nullable) hold the sparse
+// layers' fp32 K/V gradient sums in the K/V layout; they are added into dK,
+// dV, so launch_sparse_bwd must run first on the same stream.
+struct BwdPlan {
+  Shape s;
+  float scale;                         // softmax scale
+  const void* q; const void* k; const void* v; const void* o; const void* dout;
+  const float* lse;
+  float* delta;
+  const float* acc_k; const float* acc_v;
+  void* dq; void* dk; void* dv;
+};
+hipError_t launch_attn_bwd(const BwdPlan& p, hipStream_t st);
+
+// Backward of `layers` sparse layers (layers * h_q / h_kv <= 64) over a
+// fixed index set: writes dq and ADDS the K/V gradients into acc_k / acc_v
+// (fp32, [batch][n_kv][h_kv][head_dim], zeroed by the caller) with atomics.
+struct SparseBwdPlan {
+  const void* q; const void* o; const void* dout;
+  const void* k; const void* v;
+  const int32_t* idx;
+  void* dq;
+  float* acc_k; float* acc_v;
+  int layers, batch, n_q, n_kv, h_q, h_kv, head_dim, width;
+  float scale, scale_log2;
+  bool bf16;
+};
+hipError_t launch_sparse_bwd(const SparseBwdPlan& p, hipStream_t st);
+
+// p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned)
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);
+
 }  // namespace hs2

@@ -1,0 +1,324 @@
+// Backward pass of the sparse layers over their fixed index sets (KV Reuse:
+// HySparse2 pages, "Xiaomi Unveils HySparse2 for Faster Long-Context AI",
+// section "Two-Level KV Sharing": every sparse layer reads the full layer's
+// K/V, so their K and V gradients all land in the same buffer; section
+// "Performance Gains: Cost, Speed, and Long-Context Capabilities" for the
+// fine-tuning that needs them).
+//
+// One work-group serves one (sequence b, query i, KV head g), like the
+// forward kernel: its rows are all (layer, head of group g) pairs (at most
+// 64), and the index list is walked in 32-key tiles. Row waves (one per 16
+// rows) first re-derive each row's log-sum-exp over the list, then per tile
+//   S^T = K_sel Q^T, dP^T = V_sel dO^T, P^T = 2^(t - lse2),
+//   dS^T = P^T (dP^T - Delta),  dQ^T += K_sel^T dS^T      (kept in registers)
+// and put P^T and dS^T into LDS. Then all four waves contract over the rows:
+//   dK_sel = scale dS^T Q,  dV_sel = P^T dO      (32 keys x D each)
+// and add the results to fp32 accumulators [B][n_kv][h_kv][D] with atomics:
+// a key appears in the index sets of many queries, and the accumulators are
+// folded into dK and dV by the full layer's dK/dV kernel.
+//
+// LDS tiles hold P^T and dS^T as [key][row], rows of each 32-row step
+// stored in the slot order of the accumulator layout (hs2_bwd.h), so the
+// A operand of the row contraction is one contiguous 8-element read.
+#include "hs2_bwd.h"
+#include "hs2_device.h"
+#include "hs2_launch.h"
+
+namespace hs2 {
+
+namespace {
+
+constexpr int MAX_ROWS = 64;
+
+struct SparseBwdArgs {
+  const void* q;        // [L, B, n_q, h_q, D] (this launch's layers)
+  const void* o;
+  const void* dout;
+  const void* k;        // [B, n_kv, h_kv, D]
+  const void* v;
+  const int32_t* idx;   // [B, n_q, W]
+  void* dq;             // [L, B, n_q, h_q, D]
+  float* acc_k;         // [B, n_kv, h_kv, D]
+  float* acc_v;
+  int L, B, n_q, n_kv, h_q, h_kv, W;
+  float scale, scale_log2;
+};
+
+// position of row rr (0..31 within its step) in the slot order
+__device__ __forceinline__ int slot_pos(int rr) {
+  const int hi = rr >> 4, x = rr & 15;
+  return (x >> 2) * 8 + hi * 4 + (x & 3);
+}
+
+}  // namespace
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
+  using OP = Op<T, D>;
+  constexpr int DB = D / 16;                 // 16-wide head-dim blocks
+  constexpr int DBW = DB / 2;                // per wave in the row contraction
+  constexpr int NSM = MAX_ROWS / 32;         // 32-row steps at most
+  constexpr int TLD = MAX_ROWS + 16 / sizeof(T);   // padded: spreads the banks
+  __shared__ __attribute__((aligned(16))) T s_p[32][TLD];
+  __shared__ __attribute__((aligned(16))) T s_ds[32][TLD];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int G = a.h_q / a.h_kv;
+  const int R = a.L * G;
+  const int nrb = (R + 15) / 16;
+  const int n_steps = (R + 31) / 32;
+
+  const uint32_t wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int g = wg % a.h_kv;
+  const int bi = wg / a.h_kv;
+  const int b = bi / a.n_q;
+  const int i = bi - b * a.n_q;
+
+  const T* kseq = reinterpret_cast<const T*>(a.k) + (size_t)b * a.n_kv * a.h_kv * D + g * D;
+  const T* vseq = reinterpret_cast<const T*>(a.v) + (size_t)b * a.n_kv * a.h_kv * D + g * D;
+  const size_t kstride = (size_t)a.h_kv * D;
+  const int32_t* irow = a.idx + (size_t)bi * a.W;
+
+  int n_valid = 0;
+  for (int t = lane; t < a.W; t += 64) n_valid += (irow[t] >= 0) ? 1 : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
+  const int n_tiles = (n_valid + 31) / 32;
+
+  // element offset of row r (layer r / G, head g * G + r % G) in the
+  // [L, B, n_q, h_q, D] tensors
+  auto row_off = [&](int r) {
+    const int layer = r / G, hh = r - (r / G) * G;
+    return ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
+  };
+
+  for (int x = threadIdx.x; x < 32 * TLD; x += 256) {
+    (&s_p[0][0])[x] = to_elem<T>(0.f);
+    (&s_ds[0][0])[x] = to_elem<T>(0.f);
+  }
+
+  // ---- row waves: Q, dO fragments, Delta and the log-sum-exp ---------------
+  const bool row_wave = wave < nrb;
+  const int my_row = wave * 16 + l16;
+  const bool row_ok = row_wave && my_row < R;
+  Frag<T, D> qf, df;
+  float delta = 0.f, lse2 = INFINITY;
+  if (row_ok) {
+    const size_t off = row_off(my_row);
+    load_slice<T, D>(qf, reinterpret_cast<const T*>(a.q) + off, lane);
+    load_slice<T, D>(df, reinterpret_cast<const T*>(a.dout) + off, lane);
+    Frag<T, D> of;
+    load_slice<T, D>(of, reinterpret_cast<const T*>(a.o) + off, lane);
+    const T* dp = reinterpret_cast<const T*>(&df.u[0]);
+    const T* op = reinterpret_cast<const T*>(&of.u[0]);
+#pragma unroll
+    for (int e = 0; e < OP::SLICE; ++e) delta += to_f32(dp[e]) * to_f32(op[e]);
+  } else {
+    zero_slice<T, D>(qf);
+    zero_slice<T, D>(df);
+  }
+  delta += __shfl_xor(delta, 16, 64);
+  delta += __shfl_xor(delta, 32, 64);
+
+  auto key_row = [&](int pos) -> size_t {
+    return (size_t)irow[pos < n_valid ? pos : 0] * kstride;
+  };
+
+  if (row_wave) {
+    float m = -INFINITY, l = 0.f;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int base = t * 32;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<T, D> kf;
+        load_slice<T, D>(kf, kseq + key_row(base + kb * 16 + l16), lane);
+        const f32x4 s = dot_tile<T, D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+        float x[4], tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = base + kb * 16 + 4 * grp + e < n_valid ? s[e] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[e]);
+        }
+        const float m_new = fmaxf(m, tmax);
+        if (m_new > -INFINITY) {
+          float add = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) add += fast_exp2(x[e] - m_new);
+          l = l * fast_exp2(m - m_new) + add;
+          m = m_new;
+        }
+      }
+    }
+    // combine the four lane groups that share a row
+#pragma unroll
+    for (int mask = 16; mask <= 32; mask <<= 1) {
+      const float mo = __shfl_xor(m, mask, 64);
+      const float lo = __shfl_xor(l, mask, 64);
+      const float mn = fmaxf(m, mo);
+      if (mn > -INFINITY) {
+        l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
+        m = mn;
+      }
+    }
+    if (row_ok && l > 0.f) lse2 = m + __log2f(l);
+  }
+
+  // ---- constant B operands of the row contraction ---------------------------
+  // waves 0, 1: dK (B = Q rows); waves 2, 3: dV (B = dO rows); each takes
+  // DBW of the DB head-dim blocks. Slot s of step st is row
+  // 32 * st + slot_index(s, grp); the lane's column is d = 16 * dbk + l16.
+  const bool for_dk = wave < 2;
+  const int dbk0 = (wave & 1) * DBW;
+  T cu[DBW][NSM][8];
+  {
+    const T* src = reinterpret_cast<const T*>(for_dk ? a.q : a.dout);
+#pragma unroll
+    for (int bk = 0; bk < DBW; ++bk)
+#pragma unroll
+      for (int st = 0; st < NSM; ++st)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int r = 32 * st + slot_index(s, grp);
+          cu[bk][st][s] = (st < n_steps && r < R) ? src[row_off(r) + 16 * (dbk0 + bk) + l16]
+                                                  : to_elem<T>(0.f);
+        }
+  }
+
+  f32x4 dq[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) dq[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();                                  // zeroed tiles visible
+
+  float* accb = for_dk ? a.acc_k : a.acc_v;
+  const float mul = for_dk ? a.scale : 1.f;
+  const size_t acc_base = (size_t)b * a.n_kv * a.h_kv * D + (size_t)g * D;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int base = t * 32;
+    if (row_wave) {
+      f32x4 p[2], ds[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const size_t kr = key_row(base + kb * 16 + l16);
+        Frag<T, D> kf, vf;
+        load_slice<T, D>(kf, kseq + kr, lane);
+        load_slice<T, D>(vf, vseq + kr, lane);
+        const f32x4 s = dot_tile<T, D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 dp = dot_tile<T, D>(vf, df, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = fast_exp2(s[e] * a.scale_log2 - lse2);
+          if (base + kb * 16 + 4 * grp + e >= n_valid) x = 0.f;
+          p[kb][e] = x;
+          ds[kb][e] = x * (dp[e] - delta);
+        }
+      }
+      // dQ^T += K_sel^T dS^T: K rows of this lane's 8 key slots
+      TRows<T, D> tr;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const T* src = kseq + key_row(base + slot_index(s, grp)) + DB * l16;
+        constexpr int BYTES = DB * sizeof(T);
+        if constexpr (BYTES == 16) {
+          *reinterpret_cast<uint4*>(&tr.raw[s][0]) = *reinterpret_cast<const uint4*>(src);
+        } else if constexpr (BYTES == 8) {
+          *reinterpret_cast<uint2*>(&tr.raw[s][0]) = *reinterpret_cast<const uint2*>(src);
+        } else {
+#pragma unroll
+          for (int w = 0; w < BYTES / 16; ++w)
+            reinterpret_cast<uint4*>(&tr.raw[s][0])[w] = reinterpret_cast<const uint4*>(src)[w];
+        }
+      }
+      mma_t<T, D>(dq, tr, ds[0], ds[1]);
+      // P^T and dS^T into LDS: key 16 kb + 4 grp + e, row my_row
+      const int col = (my_row >> 5) * 32 + slot_pos(my_row & 31);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s_p[kb * 16 + 4 * grp + e][col] = to_elem<T>(p[kb][e]);
+          s_ds[kb * 16 + 4 * grp + e][col] = to_elem<T>(ds[kb][e]);
+        }
+    }
+    __syncthreads();
+
+    // row contraction: C[key 4 grp + e of kb][d = 16 dbk + l16]
+    const T(*tile)[TLD] = for_dk ? s_ds : s_p;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 c[DBW];
+#pragma unroll
+      for (int bk = 0; bk < DBW; ++bk) c[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NSM; ++st) {
+        if (st >= n_steps) break;
+        const T* arow = &tile[kb * 16 + l16][st * 32 + grp * 8];
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 au = *reinterpret_cast<const bf16x8*>(arow);
+#pragma unroll
+          for (int bk = 0; bk < DBW; ++bk) {
+            bf16x8 bu;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) bu[s] = cu[bk][st][s];
+            c[bk] = OP::mma(au, bu, c[bk]);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const float av = arow[s];
+#pragma unroll
+            for (int bk = 0; bk < DBW; ++bk) c[bk] = OP::mma(av, cu[bk][st][s], c[bk]);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pos = base + kb * 16 + 4 * grp + e;
+        if (pos >= n_valid) continue;
+        float* dst = accb + acc_base + (size_t)irow[pos] * kstride + l16;
+#pragma unroll
+        for (int bk = 0; bk < DBW; ++bk)
+          unsafeAtomicAdd(dst + 16 * (dbk0 + bk), c[bk][e] * mul);
+      }
+    }
+    __syncthreads();                                // tiles are rewritten next
+  }
+
+  if (row_ok) {
+    T* dst = reinterpret_cast<T*>(a.dq) + row_off(my_row);
+    store_t_row<T, D>(dst, dq, a.scale, nullptr, grp);
+  }
+}
+
+namespace {
+
+template <typename T, int D>
+hipError_t launch_sparse_bwd_t(const SparseBwdArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((size_t)a.B * a.n_q * a.h_kv));
+  hipLaunchKernelGGL((sparse_bwd_kernel<T, D>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_bwd(const SparseBwdPlan& p, hipStream_t st) {
+  SparseBwdArgs a;
+  a.q = p.q; a.o = p.o; a.dout = p.dout; a.k = p.k; a.v = p.v; a.idx = p.idx;
+  a.dq = p.dq; a.acc_k = p.acc_k; a.acc_v = p.acc_v;
+  a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv; a.h_q = p.h_q;
+  a.h_kv = p.h_kv; a.W = p.width; a.scale = p.scale; a.scale_log2 = p.scale_log2;
+  if (p.layers * (p.h_q / p.h_kv) > MAX_ROWS) return hipErrorInvalidValue;
+  if (p.bf16) {
+    if (p.head_dim == 128) return launch_sparse_bwd_t<__bf16, 128>(a, st);
+    if (p.head_dim == 64) return launch_sparse_bwd_t<__bf16, 64>(a, st);
+  } else {
+    if (p.head_dim == 128) return launch_sparse_bwd_t<float, 128>(a, st);
+    if (p.head_dim == 64) return launch_sparse_bwd_t<float, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hs2

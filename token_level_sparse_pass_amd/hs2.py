@@ -79,6 +79,10 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_step_paged.restype = i32
     lib.hs2_kv_bridge.argtypes = [P, i32, vp, vp, vp, vp, vp]
     lib.hs2_kv_bridge.restype = i32
+    lib.hs2_backward_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
+    lib.hs2_backward_workspace_size.restype = i32
+    lib.hs2_block_backward.argtypes = [P, i32] + [vp] * 14 + [vp, sz, vp]
+    lib.hs2_block_backward.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
@@ -293,4 +297,46 @@ def kv_bridge(hidden, w_kv, h_kv, *, out=None):
                torch.empty((B, n, h_kv, d), dtype=torch.bfloat16, device=hidden.device))
     _check(lib.hs2_kv_bridge(ctypes.byref(p), dm, _ptr(hidden), _ptr(w_kv), _ptr(out[0]),
                              _ptr(out[1]), _stream(hidden.device)))
+    return out
+
+
+def backward_workspace_size(p: Problem, n_sparse_layers: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load().hs2_backward_workspace_size(ctypes.byref(p), int(n_sparse_layers),
+                                              ctypes.byref(n)))
+    return n.value
+
+
+def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, do_sparse, *,
+                   workspace=None, out=None, **kw):
+    """Backward of the whole block with the index sets held fixed. Takes the
+    forward's inputs and outputs (lse: natural log, required) and the output
+    gradients; returns dict(dq_full, dq_sparse, dk, dv)."""
+    lib = load()
+    dt = q_full.dtype
+    for t, n in ((q_full, "q_full"), (k, "k"), (v, "v"), (o_full, "o_full"),
+                 (do_full, "do_full")):
+        _check_tensor(t, n, dt)
+    _check_tensor(lse, "lse", torch.float32)
+    L = 0 if q_sparse is None else q_sparse.shape[0]
+    if L:
+        for t, n in ((q_sparse, "q_sparse"), (o_sparse, "o_sparse"), (do_sparse, "do_sparse")):
+            _check_tensor(t, n, dt)
+        _check_tensor(idx, "idx", torch.int32)
+    p = _problem_from(q_full, k, kw)
+    if L and idx.shape[-1] != index_width(p):
+        raise ValueError(f"idx width {idx.shape[-1]} != {index_width(p)}")
+    if out is None:
+        out = dict(dq_full=torch.empty_like(q_full),
+                   dq_sparse=torch.empty_like(q_sparse) if L else None,
+                   dk=torch.empty_like(k), dv=torch.empty_like(v))
+    if workspace is None:
+        workspace = torch.empty(max(16, backward_workspace_size(p, L)), dtype=torch.uint8,
+                                device=q_full.device)
+    _check(lib.hs2_block_backward(
+        ctypes.byref(p), L, _ptr(q_full), _ptr(q_sparse if L else None), _ptr(k), _ptr(v),
+        _ptr(o_full), _ptr(o_sparse if L else None), _ptr(lse), _ptr(idx if L else None),
+        _ptr(do_full), _ptr(do_sparse if L else None), _ptr(out["dq_full"]),
+        _ptr(out["dq_sparse"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
+        workspace.numel(), _stream(q_full.device)))
     return out
