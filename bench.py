@@ -23,7 +23,8 @@ METRIC = "selection+sparse-attn tokens/s at 128K-1M ctx; MFMA util and HBM GB/s 
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 # in the order of the library's pass-timer slots
-PASSES = ["full_attention", "score", "select", "sparse_attention", "v_layout"]
+PASSES = ["full_attention", "score", "select", "sparse_attention", "v_layout",
+          "bwd_prep", "bwd_sparse", "bwd_dkdv", "bwd_dq"]
 
 
 def log(*a):
@@ -269,6 +270,147 @@ def kv_bridge_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def backward_work(w):
+    """Per-step algorithmic work of each backward kernel (flops or bytes).
+
+    Full layer, per causal (query, key) pair and query head: the products
+    S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q and dQ += dS K, 2 d
+    flops each. The dK/dV kernel performs the first four; the dQ kernel's
+    own share is dQ (it recomputes S and dP, which is not counted).
+    Sparse layers: the K and V rows each query selects, gathered once per KV
+    head; Q, O, dO read and dQ written for every layer; the fp32 K/V
+    gradient rows read and written once per selected key.
+    """
+    esz = 2 if w.dtype == "bf16" else 4
+    B, nq, nkv, hq, hkv, d, L = w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.d, w.n_sparse
+    pos = [nkv - nq + i for i in range(nq)]
+    pairs = sum(p + 1 for p in pos) * B
+    sel = sum(min(p + 1, w.top_k + w.window) for p in pos) * B
+    return {
+        "bwd_prep": ("hbm", 2.0 * B * nq * hq * d * esz + 4.0 * B * hq * nq +
+                     (2.0 * B * nkv * hkv * d * 4 if L else 0.0)),
+        "bwd_sparse": ("hbm", sel * hkv * d * 2.0 * esz + 4.0 * L * B * nq * hq * d * esz +
+                       sel * hkv * d * 2.0 * 4 * 2),
+        "bwd_dkdv": ("mfma", 8.0 * hq * d * pairs),
+        "bwd_dq": ("mfma", 2.0 * hq * d * pairs),
+    }
+
+
+def backward_cpu_baseline(w, inp, grads, idx, n_rows=64):
+    """The oracle's backward (block_backward_tail) for the last n_rows
+    queries of sequence 0: each query's complete gradient work."""
+    from oracle import hs2_oracle as O
+    from synth import to_host
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
+    except Exception:
+        pass
+    n_rows = min(n_rows, w.n_q)
+    j_lo = w.n_kv - n_rows
+    t0 = time.perf_counter()
+    O.block_backward_tail(to_host(inp["q_full"][:1]), to_host(inp["q_sparse"][:, :1]),
+                          to_host(inp["k"][:1]), to_host(inp["v"][:1]), to_host(idx[:1]),
+                          to_host(grads["do_full"][:1]), to_host(grads["do_sparse"][:, :1]),
+                          0, j_lo)
+    t = time.perf_counter() - t0
+    return {"value": n_rows / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the last {n_rows} queries of sequence 0 of {w.name}: their dQ (full "
+                      f"and {w.n_sparse} sparse layers) and every K/V-gradient contribution "
+                      f"they make, over all {w.n_kv} keys, {t:.1f} s"}
+
+
+def backward_bench(args):
+    """Backward pass of the block (fine-tuning) on the 32K-token prefill
+    workload by default: the forward runs once, then K timed backward steps
+    over its outputs and index sets."""
+    import torch
+    from synth import CONFIGS, grad_inputs, make_inputs
+    from token_level_sparse_pass_amd import hs2
+
+    lib = hs2.load()
+    w = CONFIGS[args.bwd_config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"backward on {w.name}: generating inputs")
+    inp = make_inputs(w, device=dev)
+    grads = grad_inputs(w, device=dev)
+    kw = dict(top_k=w.top_k, window=w.window)
+    fwd = hs2.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], **kw)
+    torch.cuda.synchronize()
+    log("forward done")
+    p = hs2.problem(inp["q_full"].dtype, w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.d, **kw)
+    ws = torch.empty(hs2.backward_workspace_size(p, w.n_sparse), dtype=torch.uint8, device=dev)
+    args_ = (inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], fwd["o_full"], fwd["o_sparse"],
+             fwd["lse"], fwd["idx"], grads["do_full"], grads["do_sparse"])
+    out = None
+    for s in range(args.warmup):
+        out = hs2.block_backward(*args_, workspace=ws, out=out, **kw)
+        torch.cuda.synchronize()
+        log(f"warmup step {s + 1}/{args.warmup} done")
+    if out is None:
+        out = hs2.block_backward(*args_, workspace=ws, **kw)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.hs2_profile_enable(1)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        hs2.block_backward(*args_, workspace=ws, out=out, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (ctypes.c_double * len(PASSES))()
+    nl = (ctypes.c_int64 * len(PASSES))()
+    st = lib.hs2_profile_read(ms, nl)
+    lib.hs2_profile_enable(0)
+    if st != 0:
+        raise RuntimeError(lib.hs2_last_error().decode())
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+    work = backward_work(w)
+    peak_mfma = PEAK_MFMA_TFLOPS[w.dtype]
+    passes = {}
+    for i, name in enumerate(PASSES):
+        if nl[i] == 0 or name not in work:
+            continue
+        bound, amount = work[name]
+        per = ms[i] / args.steps
+        if bound == "mfma":
+            ach = amount / (per / 1e3) / 1e12
+            passes[name] = {"ms": round(per, 4), "launches_per_step": int(nl[i] // args.steps),
+                            "bound": "mfma", "achieved": round(ach, 2), "unit": "TFLOP/s",
+                            "frac": round(ach / peak_mfma, 4)}
+        else:
+            ach = amount / (per / 1e3) / 1e9
+            passes[name] = {"ms": round(per, 4), "launches_per_step": int(nl[i] // args.steps),
+                            "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(passes, key=lambda n: passes[n]["ms"])
+    d = passes[dom]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+                "peak": peak_mfma if d["bound"] == "mfma" else PEAK_HBM_GBS, "unit": d["unit"],
+                "frac": d["frac"],
+                "algorithmic_per_launch": work[dom][1] / max(1, d["launches_per_step"]),
+                "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle's backward on a sample of queries")
+        cpu = backward_cpu_baseline(w, inp, grads, fwd["idx"])
+    tokens = w.batch * w.n_q
+    rec = {"metric": "backward tokens/s (Hybrid Block with its index sets held fixed)",
+           "value": round(tokens / (ms_step / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
+           "config": {"workload": w.name + "_backward", "batch": w.batch, "n_q": w.n_q,
+                      "n_kv": w.n_kv, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
+                      "top_k": w.top_k, "window": w.window, "sparse_layers": w.n_sparse,
+                      "parallelism": "single GPU"},
+           "roofline": roofline, "passes": passes, "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +423,10 @@ def main():
                          "workload) instead of the default workload")
     ap.add_argument("--kv-bridge", action="store_true",
                     help="time the KV Bridging projection for the 1M-token context instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (fixed index sets) instead")
+    ap.add_argument("--bwd-config", type=int, default=2,
+                    help="with --backward: the workload (default 2, the 32K-token prefill)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="with --decode-loop: keep the cache in a pool of pages of this many "
                          "rows, handed out in shuffled order (hs2_decode_step_paged)")
@@ -309,6 +455,9 @@ def main():
         return
     if args.kv_bridge:
         kv_bridge_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2
@@ -356,9 +505,9 @@ def main():
     peak_mfma = PEAK_MFMA_TFLOPS[w.dtype]
     passes = {}
     for i, name in enumerate(PASSES):
-        bound, amount = work[name]
         if nl[i] == 0:
             continue                      # pass not taken on this path
+        bound, amount = work[name]
         per_step_ms = ms[i] / args.steps
         launches = nl[i] // args.steps
         if bound == "mfma":

@@ -241,7 +241,7 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
  * (selection), HS2_PASS_SPARSE (sparse layers), HS2_PASS_LAYOUT (the
  * copy of V into the workspace in key-tile-major transposed order that the
  * bf16 / head_dim 128 prefill kernel reads; absent on every other path),
- * HS2_PASS_BWD_FULL and HS2_PASS_BWD_SPARSE (hs2_block_backward).
+ * and the four HS2_PASS_BWD_* steps of hs2_block_backward.
  * hs2_profile_enable(1)
  * starts a fresh record and (0) stops recording. hs2_profile_read waits for
  * the recorded events, then writes the summed milliseconds and the number of
@@ -253,9 +253,11 @@ typedef enum {
   HS2_PASS_SELECT = 2,
   HS2_PASS_SPARSE = 3,
   HS2_PASS_LAYOUT = 4,
-  HS2_PASS_BWD_FULL = 5,    /* hs2_block_backward: the full layer            */
-  HS2_PASS_BWD_SPARSE = 6,  /* hs2_block_backward: the sparse layers         */
-  HS2_N_PASSES = 7
+  HS2_PASS_BWD_PREP = 5,    /* backward: Delta rows, accumulators cleared    */
+  HS2_PASS_BWD_SPARSE = 6,  /* backward: the sparse layers                   */
+  HS2_PASS_BWD_DKDV = 7,    /* backward: the full layer's dK, dV             */
+  HS2_PASS_BWD_DQ = 8,      /* backward: the full layer's dQ                 */
+  HS2_N_PASSES = 9
 } hs2_pass;
 hs2_status hs2_profile_enable(int32_t on);
 hs2_status hs2_profile_read(double* ms, int64_t* launches);

@@ -437,26 +437,51 @@ BwdArgs args_of(const BwdPlan& p) {
 }
 
 template <typename T, int D>
-hipError_t launch_bwd_t(const BwdPlan& p, hipStream_t st) {
-  BwdArgs a = args_of(p);
+hipError_t launch_delta_t(const BwdPlan& p, hipStream_t st) {
+  const BwdArgs a = args_of(p);
   const size_t rows = (size_t)a.B * a.n_q * a.h_q;
   hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
                      st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dK/dV
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dkdv_t(const BwdPlan& p, hipStream_t st) {
+  BwdArgs a = args_of(p);
   a.n_tiles = (a.n_kv + 127) / 128;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>),
                      dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(256), 0, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dQ
-  const int G = a.h_q / a.h_kv;
-  a.n_tiles = (a.n_q * G + 127) / 128;
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_dq_t(const BwdPlan& p, hipStream_t st) {
+  BwdArgs a = args_of(p);
+  a.n_tiles = (a.n_q * (a.h_q / a.h_kv) + 127) / 128;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>),
                      dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+
+// dispatch on (dtype, head_dim)
+template <template <typename, int> class F>
+hipError_t dispatch(const BwdPlan& p, hipStream_t st) {
+  if (p.s.bf16) {
+    if (p.s.head_dim == 128) return F<__bf16, 128>::run(p, st);
+    if (p.s.head_dim == 64) return F<__bf16, 64>::run(p, st);
+  } else {
+    if (p.s.head_dim == 128) return F<float, 128>::run(p, st);
+    if (p.s.head_dim == 64) return F<float, 64>::run(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+struct DeltaF { static hipError_t run(const BwdPlan& p, hipStream_t st) { return launch_delta_t<T, D>(p, st); } };
+template <typename T, int D>
+struct DkdvF { static hipError_t run(const BwdPlan& p, hipStream_t st) { return launch_dkdv_t<T, D>(p, st); } };
+template <typename T, int D>
+struct DqF { static hipError_t run(const BwdPlan& p, hipStream_t st) { return launch_dq_t<T, D>(p, st); } };
 
 }  // namespace
 
@@ -469,15 +494,8 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const BwdPlan& p, hipStream_t st) {
-  if (p.s.bf16) {
-    if (p.s.head_dim == 128) return launch_bwd_t<__bf16, 128>(p, st);
-    if (p.s.head_dim == 64) return launch_bwd_t<__bf16, 64>(p, st);
-  } else {
-    if (p.s.head_dim == 128) return launch_bwd_t<float, 128>(p, st);
-    if (p.s.head_dim == 64) return launch_bwd_t<float, 64>(p, st);
-  }
-  return hipErrorInvalidValue;
-}
+hipError_t launch_bwd_delta(const BwdPlan& p, hipStream_t st) { return dispatch<DeltaF>(p, st); }
+hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st) { return dispatch<DkdvF>(p, st); }
+hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st) { return dispatch<DqF>(p, st); }
 
 }  // namespace hs2

@@ -626,10 +626,23 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
   const float scale_log2 = p->softmax_scale * 1.4426950408889634f;
   float* acc_k = sparse ? fptr(workspace, L.acc_k) : nullptr;
   float* acc_v = sparse ? fptr(workspace, L.acc_v) : nullptr;
+  hs2::BwdPlan bp;
+  bp.s = shape_of(*p);
+  bp.scale = p->softmax_scale;
+  bp.q = q_full; bp.k = k; bp.v = v; bp.o = o_full; bp.dout = do_full;
+  bp.lse = lse; bp.delta = fptr(workspace, L.delta);
+  bp.acc_k = acc_k; bp.acc_v = acc_v;
+  bp.dq = dq_full; bp.dk = dk; bp.dv = dv;
+  {
+    PassTimer t(st, HS2_PASS_BWD_PREP);
+    HIP_TRY(hs2::launch_bwd_delta(bp, st), "backward Delta");
+    if (sparse) {
+      HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");
+      HIP_TRY(hs2::launch_zero_f32(acc_v, L.acc_elems, st), "zero accumulators");
+    }
+  }
   if (sparse) {
     PassTimer t(st, HS2_PASS_BWD_SPARSE);
-    HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");
-    HIP_TRY(hs2::launch_zero_f32(acc_v, L.acc_elems, st), "zero accumulators");
     const int G = p->h_q / p->h_kv;
     const int per = std::max(1, 64 / G);                     // layers per launch
     const size_t esz = p->dtype == HS2_BF16 ? 2 : 4;
@@ -650,15 +663,12 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
     }
   }
   {
-    PassTimer t(st, HS2_PASS_BWD_FULL);
-    hs2::BwdPlan bp;
-    bp.s = shape_of(*p);
-    bp.scale = p->softmax_scale;
-    bp.q = q_full; bp.k = k; bp.v = v; bp.o = o_full; bp.dout = do_full;
-    bp.lse = lse; bp.delta = fptr(workspace, L.delta);
-    bp.acc_k = acc_k; bp.acc_v = acc_v;
-    bp.dq = dq_full; bp.dk = dk; bp.dv = dv;
-    HIP_TRY(hs2::launch_attn_bwd(bp, st), "full-layer backward");
+    PassTimer t(st, HS2_PASS_BWD_DKDV);
+    HIP_TRY(hs2::launch_bwd_dkdv(bp, st), "full-layer dK/dV");
+  }
+  {
+    PassTimer t(st, HS2_PASS_BWD_DQ);
+    HIP_TRY(hs2::launch_bwd_dq(bp, st), "full-layer dQ");
   }
   return HS2_OK;
 }

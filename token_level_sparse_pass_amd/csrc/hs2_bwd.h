@@ -78,7 +78,8 @@ __device__ __forceinline__ void mma_t(f32x4 (&acc)[D / 16], const TRows<T, D>& x
   }
 }
 
-// Store a transposed accumulator set (d = DV*(4*grp + e) + db) as row `dst`.
+// Store a transposed accumulator set (d = DV*(4*grp + e) + db) as row `dst`,
+// times `mul`, plus the fp32 row `add` (nullable).
 template <typename T, int D>
 __device__ __forceinline__ void store_t_row(T* dst, const f32x4 (&acc)[D / 16], float mul,
                                             const float* add, int grp) {

@@ -161,8 +161,8 @@ struct BridgePlan {
 };
 hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st);
 
-// Backward pass of the full layer (prefill shapes): Delta = rowsum(dO * O)
-// into `delta` ([batch][h_q][n_q] floats), then dK/dV and dQ. lse is the
+// Backward pass of the full layer: Delta = rowsum(dO * O) into `delta`
+// ([batch][h_q][n_q] floats), then dK/dV and dQ, in that order on a stream. lse is the
 // forward's natural-log LSE. acc_k / acc_v (nullable) hold the sparse
 // layers' fp32 K/V gradient sums in the K/V layout; they are added into dK,
 // dV, so launch_sparse_bwd must run first on the same stream.
@@ -175,7 +175,9 @@ struct BwdPlan {
   const float* acc_k; const float* acc_v;
   void* dq; void* dk; void* dv;
 };
-hipError_t launch_attn_bwd(const BwdPlan& p, hipStream_t st);
+hipError_t launch_bwd_delta(const BwdPlan& p, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st);   // after the delta
+hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st);     // after the delta
 
 // Backward of `layers` sparse layers (layers * h_q / h_kv <= 64) over a
 // fixed index set: writes dq and ADDS the K/V gradients into acc_k / acc_v

@@ -7,15 +7,21 @@
 //
 // One work-group serves one (sequence b, query i, KV head g), like the
 // forward kernel: its rows are all (layer, head of group g) pairs (at most
-// 64), and the index list is walked in 32-key tiles. Row waves (one per 16
-// rows) first re-derive each row's log-sum-exp over the list, then per tile
+// 64), and the index list is walked in 32-key tiles. All eight waves first
+// re-derive each row's log-sum-exp over the list. Then row waves 0..3 (one
+// per 16 rows) compute, per tile,
 //   S^T = K_sel Q^T, dP^T = V_sel dO^T, P^T = 2^(t - lse2),
 //   dS^T = P^T (dP^T - Delta),  dQ^T += K_sel^T dS^T      (kept in registers)
-// and put P^T and dS^T into LDS. Then all four waves contract over the rows:
+// and put P^T and dS^T into LDS, while contraction waves 4..7 take the
+// previous tile and contract over the rows:
 //   dK_sel = scale dS^T Q,  dV_sel = P^T dO      (32 keys x D each)
-// and add the results to fp32 accumulators [B][n_kv][h_kv][D] with atomics:
+// adding the results to fp32 accumulators [B][n_kv][h_kv][D] with atomics:
 // a key appears in the index sets of many queries, and the accumulators are
-// folded into dK and dV by the full layer's dK/dV kernel.
+// folded into dK and dV by the full layer's dK/dV kernel. Keeping the
+// atomics on waves that issue no loads matters: a wave's vector memory
+// operations complete in order, so a load issued after a burst of atomics
+// would wait for all of them. Each atomic instruction covers four keys x 16
+// consecutive floats (64-byte segments), the cheapest pattern measured.
 //
 // LDS tiles hold P^T and dS^T as [key][row], rows of each 32-row step
 // stored in the slot order of the accumulator layout (hs2_bwd.h), so the
@@ -53,14 +59,16 @@ __device__ __forceinline__ int slot_pos(int rr) {
 }  // namespace
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
+__global__ __launch_bounds__(512) void sparse_bwd_kernel(SparseBwdArgs a) {
   using OP = Op<T, D>;
   constexpr int DB = D / 16;                 // 16-wide head-dim blocks
-  constexpr int DBW = DB / 2;                // per wave in the row contraction
+  constexpr int DBW = DB / 2;                // per contraction wave
   constexpr int NSM = MAX_ROWS / 32;         // 32-row steps at most
   constexpr int TLD = MAX_ROWS + 16 / sizeof(T);   // padded: spreads the banks
-  __shared__ __attribute__((aligned(16))) T s_p[32][TLD];
-  __shared__ __attribute__((aligned(16))) T s_ds[32][TLD];
+  __shared__ __attribute__((aligned(16))) T s_p[2][32][TLD];
+  __shared__ __attribute__((aligned(16))) T s_ds[2][32][TLD];
+  __shared__ int s_key[2][32];               // buffer row of each tile key, -1 past the list
+  __shared__ float s_m[4][8][16], s_l[4][8][16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -94,18 +102,74 @@ __global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
     const int layer = r / G, hh = r - (r / G) * G;
     return ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
   };
+  auto key_row = [&](int pos) -> size_t {
+    return (size_t)irow[pos < n_valid ? pos : 0] * kstride;
+  };
 
-  for (int x = threadIdx.x; x < 32 * TLD; x += 256) {
-    (&s_p[0][0])[x] = to_elem<T>(0.f);
-    (&s_ds[0][0])[x] = to_elem<T>(0.f);
+  for (int x = threadIdx.x; x < 2 * 32 * TLD; x += 512) {
+    (&s_p[0][0][0])[x] = to_elem<T>(0.f);
+    (&s_ds[0][0][0])[x] = to_elem<T>(0.f);
   }
 
-  // ---- row waves: Q, dO fragments, Delta and the log-sum-exp ---------------
+  // ---- log-sum-exp of every row over the list, split over all 8 waves:
+  // row block wave % nrb, tiles part, part + n_parts, ...
+  {
+    const int n_parts = 8 / nrb;
+    const int rb = wave % nrb, part = wave / nrb;
+    float m = -INFINITY, l = 0.f;
+    if (part < n_parts) {
+      Frag<T, D> qs;
+      const int r = rb * 16 + l16;
+      if (r < R) load_slice<T, D>(qs, reinterpret_cast<const T*>(a.q) + row_off(r), lane);
+      else zero_slice<T, D>(qs);
+      for (int t = part; t < n_tiles; t += n_parts) {
+        const int base = t * 32;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<T, D> kf;
+          load_slice<T, D>(kf, kseq + key_row(base + kb * 16 + l16), lane);
+          const f32x4 s = dot_tile<T, D>(kf, qs, f32x4{0.f, 0.f, 0.f, 0.f});
+          float x[4], tmax = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = base + kb * 16 + 4 * grp + e < n_valid ? s[e] * a.scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[e]);
+          }
+          const float m_new = fmaxf(m, tmax);
+          if (m_new > -INFINITY) {
+            float add = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) add += fast_exp2(x[e] - m_new);
+            l = l * fast_exp2(m - m_new) + add;
+            m = m_new;
+          }
+        }
+      }
+      // the four lane groups that share a row
+#pragma unroll
+      for (int mask = 16; mask <= 32; mask <<= 1) {
+        const float mo = __shfl_xor(m, mask, 64);
+        const float lo = __shfl_xor(l, mask, 64);
+        const float mn = fmaxf(m, mo);
+        if (mn > -INFINITY) {
+          l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
+          m = mn;
+        }
+      }
+      if (grp == 0) {
+        s_m[rb][part][l16] = m;
+        s_l[rb][part][l16] = l;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- row waves: Q, dO fragments, Delta, the combined log-sum-exp --------
   const bool row_wave = wave < nrb;
   const int my_row = wave * 16 + l16;
   const bool row_ok = row_wave && my_row < R;
   Frag<T, D> qf, df;
-  float delta = 0.f, lse2 = INFINITY;
+  float delta = 0.f, lse2 = INFINITY;             // INFINITY: P = 0 on padding rows
   if (row_ok) {
     const size_t off = row_off(my_row);
     load_slice<T, D>(qf, reinterpret_cast<const T*>(a.q) + off, lane);
@@ -116,6 +180,12 @@ __global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
     const T* op = reinterpret_cast<const T*>(&of.u[0]);
 #pragma unroll
     for (int e = 0; e < OP::SLICE; ++e) delta += to_f32(dp[e]) * to_f32(op[e]);
+    float m = -INFINITY;
+    for (int pt = 0; pt < 8 / nrb; ++pt) m = fmaxf(m, s_m[wave][pt][l16]);
+    float l = 0.f;
+    for (int pt = 0; pt < 8 / nrb; ++pt)
+      if (s_m[wave][pt][l16] > -INFINITY) l += s_l[wave][pt][l16] * fast_exp2(s_m[wave][pt][l16] - m);
+    if (l > 0.f) lse2 = m + __log2f(l);
   } else {
     zero_slice<T, D>(qf);
     zero_slice<T, D>(df);
@@ -123,57 +193,16 @@ __global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
   delta += __shfl_xor(delta, 16, 64);
   delta += __shfl_xor(delta, 32, 64);
 
-  auto key_row = [&](int pos) -> size_t {
-    return (size_t)irow[pos < n_valid ? pos : 0] * kstride;
-  };
-
-  if (row_wave) {
-    float m = -INFINITY, l = 0.f;
-    for (int t = 0; t < n_tiles; ++t) {
-      const int base = t * 32;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<T, D> kf;
-        load_slice<T, D>(kf, kseq + key_row(base + kb * 16 + l16), lane);
-        const f32x4 s = dot_tile<T, D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
-        float x[4], tmax = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = base + kb * 16 + 4 * grp + e < n_valid ? s[e] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[e]);
-        }
-        const float m_new = fmaxf(m, tmax);
-        if (m_new > -INFINITY) {
-          float add = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) add += fast_exp2(x[e] - m_new);
-          l = l * fast_exp2(m - m_new) + add;
-          m = m_new;
-        }
-      }
-    }
-    // combine the four lane groups that share a row
-#pragma unroll
-    for (int mask = 16; mask <= 32; mask <<= 1) {
-      const float mo = __shfl_xor(m, mask, 64);
-      const float lo = __shfl_xor(l, mask, 64);
-      const float mn = fmaxf(m, mo);
-      if (mn > -INFINITY) {
-        l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
-        m = mn;
-      }
-    }
-    if (row_ok && l > 0.f) lse2 = m + __log2f(l);
-  }
-
-  // ---- constant B operands of the row contraction ---------------------------
-  // waves 0, 1: dK (B = Q rows); waves 2, 3: dV (B = dO rows); each takes
+  // ---- contraction waves (4..7): constant B operands ------------------------
+  // waves 4, 5: dK (B = Q rows); waves 6, 7: dV (B = dO rows); each takes
   // DBW of the DB head-dim blocks. Slot s of step st is row
   // 32 * st + slot_index(s, grp); the lane's column is d = 16 * dbk + l16.
-  const bool for_dk = wave < 2;
-  const int dbk0 = (wave & 1) * DBW;
+  const bool contract_wave = wave >= 4;
+  const int cw = wave - 4;
+  const bool for_dk = cw < 2;
+  const int dbk0 = (cw & 1) * DBW;
   T cu[DBW][NSM][8];
-  {
+  if (contract_wave) {
     const T* src = reinterpret_cast<const T*>(for_dk ? a.q : a.dout);
 #pragma unroll
     for (int bk = 0; bk < DBW; ++bk)
@@ -190,15 +219,18 @@ __global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
   f32x4 dq[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) dq[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();                                  // zeroed tiles visible
 
-  float* accb = for_dk ? a.acc_k : a.acc_v;
+  float* accb = (for_dk ? a.acc_k : a.acc_v) + (size_t)b * a.n_kv * a.h_kv * D + (size_t)g * D;
   const float mul = for_dk ? a.scale : 1.f;
-  const size_t acc_base = (size_t)b * a.n_kv * a.h_kv * D + (size_t)g * D;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int base = t * 32;
-    if (row_wave) {
+  // Software pipeline over the tiles: in step t the row waves work on tile t
+  // (buffer t & 1) while the contraction waves contract tile t - 1 (the
+  // other buffer) and issue its atomics. The row waves issue no atomics, so
+  // their loads never wait behind them.
+  for (int t = 0; t <= n_tiles; ++t) {
+    if (row_wave && t < n_tiles) {
+      const int base = t * 32;
+      const int buf = t & 1;
       f32x4 p[2], ds[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -239,52 +271,57 @@ __global__ __launch_bounds__(256) void sparse_bwd_kernel(SparseBwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s_p[kb * 16 + 4 * grp + e][col] = to_elem<T>(p[kb][e]);
-          s_ds[kb * 16 + 4 * grp + e][col] = to_elem<T>(ds[kb][e]);
+          s_p[buf][kb * 16 + 4 * grp + e][col] = to_elem<T>(p[kb][e]);
+          s_ds[buf][kb * 16 + 4 * grp + e][col] = to_elem<T>(ds[kb][e]);
         }
+      if (wave == 0 && lane < 32) {
+        const int pos = base + lane;
+        s_key[buf][lane] = pos < n_valid ? irow[pos] : -1;
+      }
+    }
+    if (contract_wave && t > 0) {
+      // row contraction of tile t - 1: C[key 4 grp + e of kb][d = 16 dbk + l16]
+      const int buf = (t - 1) & 1;
+      const T(*tile)[TLD] = for_dk ? s_ds[buf] : s_p[buf];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 c[DBW];
+#pragma unroll
+        for (int bk = 0; bk < DBW; ++bk) c[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < NSM; ++st) {
+          if (st >= n_steps) break;
+          const T* arow = &tile[kb * 16 + l16][st * 32 + grp * 8];
+          if constexpr (sizeof(T) == 2) {
+            const bf16x8 au = *reinterpret_cast<const bf16x8*>(arow);
+#pragma unroll
+            for (int bk = 0; bk < DBW; ++bk) {
+              bf16x8 bu;
+#pragma unroll
+              for (int s = 0; s < 8; ++s) bu[s] = cu[bk][st][s];
+              c[bk] = OP::mma(au, bu, c[bk]);
+            }
+          } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+              const float av = arow[s];
+#pragma unroll
+              for (int bk = 0; bk < DBW; ++bk) c[bk] = OP::mma(av, cu[bk][st][s], c[bk]);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = s_key[buf][kb * 16 + 4 * grp + e];
+          if (key < 0) continue;
+          float* dst = accb + (size_t)key * kstride + l16;
+#pragma unroll
+          for (int bk = 0; bk < DBW; ++bk)
+            unsafeAtomicAdd(dst + 16 * (dbk0 + bk), c[bk][e] * mul);
+        }
+      }
     }
     __syncthreads();
-
-    // row contraction: C[key 4 grp + e of kb][d = 16 dbk + l16]
-    const T(*tile)[TLD] = for_dk ? s_ds : s_p;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x4 c[DBW];
-#pragma unroll
-      for (int bk = 0; bk < DBW; ++bk) c[bk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < NSM; ++st) {
-        if (st >= n_steps) break;
-        const T* arow = &tile[kb * 16 + l16][st * 32 + grp * 8];
-        if constexpr (sizeof(T) == 2) {
-          const bf16x8 au = *reinterpret_cast<const bf16x8*>(arow);
-#pragma unroll
-          for (int bk = 0; bk < DBW; ++bk) {
-            bf16x8 bu;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) bu[s] = cu[bk][st][s];
-            c[bk] = OP::mma(au, bu, c[bk]);
-          }
-        } else {
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            const float av = arow[s];
-#pragma unroll
-            for (int bk = 0; bk < DBW; ++bk) c[bk] = OP::mma(av, cu[bk][st][s], c[bk]);
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int pos = base + kb * 16 + 4 * grp + e;
-        if (pos >= n_valid) continue;
-        float* dst = accb + acc_base + (size_t)irow[pos] * kstride + l16;
-#pragma unroll
-        for (int bk = 0; bk < DBW; ++bk)
-          unsafeAtomicAdd(dst + 16 * (dbk0 + bk), c[bk][e] * mul);
-      }
-    }
-    __syncthreads();                                // tiles are rewritten next
   }
 
   if (row_ok) {
@@ -298,7 +335,7 @@ namespace {
 template <typename T, int D>
 hipError_t launch_sparse_bwd_t(const SparseBwdArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)a.B * a.n_q * a.h_kv));
-  hipLaunchKernelGGL((sparse_bwd_kernel<T, D>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sparse_bwd_kernel<T, D>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
