@@ -68,6 +68,20 @@ __device__ __forceinline__ void load_slice(Frag<T, D>& f, const T* row, int lane
   for (int i = 0; i < BYTES / 16; ++i) dst[i] = src[i];
 }
 
+// The same operand with another k order, for rows gathered from global
+// memory: lane group q takes the 16-byte chunks q, 4 + q, 8 + q, ... of the
+// row, so the four lane groups of one load instruction read 64 contiguous
+// bytes of each row (the per-lane slice above makes them read four pieces
+// 64 bytes apart). A and B must be loaded with the same rule.
+template <typename T, int D>
+__device__ __forceinline__ void load_slice_il(Frag<T, D>& f, const T* row, int lane) {
+  constexpr int BYTES = Op<T, D>::SLICE * sizeof(T);
+  const uint4* src = reinterpret_cast<const uint4*>(row) + (lane >> 4);
+  uint4* dst = reinterpret_cast<uint4*>(&f.u[0]);
+#pragma unroll
+  for (int m = 0; m < BYTES / 16; ++m) dst[m] = src[4 * m];
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void zero_slice(Frag<T, D>& f) {
   constexpr int BYTES = Op<T, D>::SLICE * sizeof(T);

@@ -82,17 +82,6 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
   const T* vb = reinterpret_cast<const T*>(a.v);
   const int32_t* irow = a.idx + (size_t)bi * a.W;
 
-  // number of valid indices: rows are a valid prefix followed by -1
-  int n_valid = 0;
-  for (int t = lane; t < a.W; t += 64) n_valid += (irow[t] >= 0) ? 1 : 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
-
-  // this wave's share of the index list, in whole 32-key tiles
-  const int n_tiles = (n_valid + 31) / 32;
-  const int t_begin = (n_tiles * wave) / NW;
-  const int t_end = (n_tiles * (wave + 1)) / NW;
-
   // Q fragments (B operand): row r = layer * G + hh
   Frag<T, D> qf[RB];
 #pragma unroll
@@ -101,11 +90,35 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
     if (r < rows_total) {
       const int layer = r / G, hh = r - (r / G) * G;
       const T* qrow = qb + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
-      load_slice<T, D>(qf[rb], qrow, lane);
+      load_slice_il<T, D>(qf[rb], qrow, lane);
     } else {
       zero_slice<T, D>(qf[rb]);
     }
   }
+
+  // Split kernel: the index row is staged in LDS once, so a tile's gathers
+  // do not wait on a global index load first.
+  constexpr int IDX_LDS = NW > 1 ? 4096 : 1;
+  __shared__ int s_idx[IDX_LDS];
+  if constexpr (NW > 1) {
+    for (int x = threadIdx.x; x < min(a.W, IDX_LDS); x += 64 * NW) s_idx[x] = irow[x];
+    __syncthreads();
+  }
+  auto idx_at = [&](int pos) -> int {
+    if constexpr (NW > 1) return pos < IDX_LDS ? s_idx[pos] : irow[pos];
+    return irow[pos];
+  };
+
+  // number of valid indices: rows are a valid prefix followed by -1
+  int n_valid = 0;
+  for (int t = lane; t < a.W; t += 64) n_valid += (idx_at(t) >= 0) ? 1 : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
+
+  // this wave's share of the index list, in whole 32-key tiles
+  const int n_tiles = (n_valid + 31) / 32;
+  const int t_begin = (n_tiles * wave) / NW;
+  const int t_end = (n_tiles * (wave + 1)) / NW;
 
   float m_run[RB], l_run[RB];
   f32x4 acc[RB][DV];
@@ -122,32 +135,33 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
   const T* vseq = vb + (size_t)g * D;
   const int grp = lane >> 4;
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int base = t * 32;
-    // K rows: key slot 16*kb + lane%16
+  // one 32-key tile's K rows (key slot 16*kb + lane%16) and V rows (this
+  // lane's 8 key slots)
+  struct TileRegs {
     Frag<T, D> kf[2];
-    bool kvalid[2];
+    VTile<T, D> vt;
+  };
+  auto fetch = [&](int t, TileRegs& r) {
+    const int base = t * 32;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int pos = base + kb2 * 16 + (lane & 15);
-      const bool ok = pos < n_valid;
-      const int j = ok ? irow[pos] : 0;
-      kvalid[kb2] = ok;
-      load_slice<T, D>(kf[kb2], kseq + a.kv.row(b, j) * kv_row_stride, lane);
+      const int j = pos < n_valid ? idx_at(pos) : 0;
+      load_slice_il<T, D>(r.kf[kb2], kseq + a.kv.row(b, j) * kv_row_stride, lane);
     }
-    // V rows for this lane's 8 key slots
     size_t voff[8];
-    bool vvalid[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int pos = base + (s < 4 ? 4 * grp + s : 16 + 4 * grp + (s - 4));
-      const bool ok = pos < n_valid;
-      vvalid[s] = ok;
-      voff[s] = a.kv.row(b, ok ? irow[pos] : 0) * kv_row_stride;
+      voff[s] = a.kv.row(b, pos < n_valid ? idx_at(pos) : 0) * kv_row_stride;
     }
-    VTile<T, D> vt;
-    load_v_rows<T, D>(vt, vseq, voff, lane);
-    (void)vvalid;
+    load_v_rows<T, D>(r.vt, vseq, voff, lane);
+  };
+
+  auto compute = [&](int t, const TileRegs& r) {
+    const int base = t * 32;
+    const Frag<T, D>(&kf)[2] = r.kf;
+    const VTile<T, D>& vt = r.vt;
 
     // logits and online softmax per row block
     typename OP::unit pu[RB][(sizeof(T) == 2) ? 1 : 8];
@@ -218,6 +232,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
           for (int rb = 0; rb < RB; ++rb)
             acc[rb][db] = OP::mma(to_f32(vt.raw[s][db]), pu[rb][s], acc[rb][db]);
     }
+  };
+
+  for (int t = t_begin; t < t_end; ++t) {
+    TileRegs tr;
+    fetch(t, tr);
+    compute(t, tr);
   }
 
   // row totals over the 4 lanes that share a row
