@@ -10,8 +10,9 @@
 //    Vt[b][g][tile][d][64 keys], so the PV product reads its operands with
 //    16-byte LDS loads instead of transposing in registers;
 //  * K and Vt tiles go straight from global memory into LDS
-//    (global_load_lds_dwordx4), double-buffered, with XOR-swizzled 16-byte
-//    chunks so the MFMA operand reads are free of bank conflicts;
+//    (global_load_lds_dwordx4) through a three-stage ring (two tiles in
+//    flight, waits counted per tile), with XOR-swizzled 16-byte chunks so
+//    the MFMA operand reads are free of bank conflicts;
 //  * the keys of a 64-key tile are assigned to MFMA rows in a permuted order
 //    such that the P^T operand of each lane covers 8 consecutive keys;
 //  * the running max is only moved (and O rescaled) when it grows by more
@@ -19,13 +20,21 @@
 //    formed with one FMA (logit * c - m) from the raw MFMA result;
 //  * the causal mask is applied only on tiles that reach the diagonal.
 // Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
-// 16-row MFMA blocks per wave, four waves per work-group. Each wave reads a
+// 16-row MFMA blocks per wave, eight waves (two per SIMD) per work-group,
+// all sharing each tile in LDS. Each wave reads a
 // whole K and V^T tile from LDS per 64 keys, so rows per wave set the MFMA
 // work per LDS byte (LDS delivers about 64 B/clk per CU for 16-byte reads).
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
 namespace hs2 {
+
+#ifndef FWD_WAVES
+#define FWD_WAVES 8
+#endif
+#ifndef FWD_STAGES
+#define FWD_STAGES 3
+#endif
 
 namespace {
 
@@ -47,6 +56,8 @@ __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int tile_key(int kb, int m) {
   return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
 }
+
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct Fwd2Args {
   const __bf16* q; const __bf16* k; const __bf16* vt;
@@ -93,10 +104,13 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const __bf16* v, __bf1
   }
 }
 
-template <int RBW, int MINW>
-__global__ __launch_bounds__(256, MINW) void attn_fwd_bf16_kernel(Fwd2Args a) {
+// RBW 16-row blocks per wave, NWV waves per work-group (all of them share
+// each K/V tile in LDS), NST-stage LDS ring (tiles in flight: NST - 1).
+template <int RBW, int NWV, int NST>
+__global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
   using OP = Op<__bf16, D>;
-  constexpr int ROWS = 64 * RBW;                        // rows per work-group
+  constexpr int ROWS = 16 * RBW * NWV;                  // rows per work-group
+  constexpr int CPT = 1024 / (64 * NWV);                // 16-byte chunks per thread per tensor
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -144,22 +158,22 @@ __global__ __launch_bounds__(256, MINW) void attn_fwd_bf16_kernel(Fwd2Args a) {
     char* base = smem + stage * STAGE_BYTES;
     const int j0 = tile * TK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int slot = (wave * 4 + t) * 64 + lane;
+    for (int t = 0; t < CPT; ++t) {
+      const int slot = (wave * CPT + t) * 64 + lane;
       const int r = slot >> 4, pc = slot & 15;
       const int c = pc ^ kswz(r);
       const int key = min(j0 + r, a.n_kv - 1);
       const __bf16* src = kseq + (size_t)key * kstride + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * 4 + t) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
     }
     const __bf16* vsrc = vtseq + (size_t)tile * (D * TK);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int slot = (wave * 4 + t) * 64 + lane;
+    for (int t = 0; t < CPT; ++t) {
+      const int slot = (wave * CPT + t) * 64 + lane;
       const int d = slot >> 3, pc = slot & 7;
       const int c = pc ^ vswz(d);
-      __builtin_amdgcn_global_load_lds(vsrc + d * TK + c * 8,
-                                       (lds_void*)(base + KT_BYTES + (wave * 4 + t) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vsrc + d * TK + c * 8, (lds_void*)(base + KT_BYTES + (wave * CPT + t) * 1024), 16, 0, 0);
     }
   };
 
@@ -192,13 +206,25 @@ __global__ __launch_bounds__(256, MINW) void attn_fwd_bf16_kernel(Fwd2Args a) {
       voff[st][db] = KT_BYTES + d * 128 + (((4 * st + grp) ^ vswz(d)) << 4);
     }
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < n_tiles) issue(s0, s0);
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, stage ^ 1);
+    // tile t has landed once at most the loads of the tiles issued after it
+    // (2 * CPT per tile) are still in flight; the loop issues no other
+    // vector-memory operation, and this wave's operations complete in order
+    {
+      const int pending = min(NST - 2, n_tiles - 1 - t);    // tiles issued after t
+      if (NST > 3 && pending >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * CPT));
+      else if (NST > 2 && pending == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPT));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+    // the stage refilled here held tile t - 1, which every wave finished
+    // reading before the barrier above
+    if (t + NST - 1 < n_tiles) issue(t + NST - 1, (t + NST - 1) % NST);
+    const int stage = t % NST;
     const char* base = smem + stage * STAGE_BYTES;
     const int j0 = t * TK;
 
@@ -295,9 +321,6 @@ __global__ __launch_bounds__(256, MINW) void attn_fwd_bf16_kernel(Fwd2Args a) {
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
-
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
   const size_t plane = (size_t)a.B * a.h_q * a.n_q;
@@ -360,12 +383,23 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
   const int G = a.h_q / a.h_kv;
   // two 16-row blocks per wave at two waves per SIMD measured best on the
   // 1M-context workload (48 rows spill registers; 64 rows at one wave per
-  // SIMD lose more to latency than they save in LDS traffic)
-  constexpr int RBW = 2;
-  constexpr int rows = 64 * RBW;
+  // SIMD lose more to latency than they save in LDS traffic); eight waves
+  // sharing a three-stage ring beat four waves on two stages by about 3 %
+  constexpr int RBW = 2, NWV = FWD_WAVES, NST = FWD_STAGES;
+  constexpr int rows = 16 * RBW * NWV;
+  constexpr int smem_bytes = NST * STAGE_BYTES;
+  static bool smem_ok = false;
+  if (!smem_ok && smem_bytes > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16_kernel<RBW, NWV, NST>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             smem_bytes);
+    if (e != hipSuccess) return e;
+  }
+  smem_ok = true;
   a.n_rt = (a.n_q * G + rows - 1) / rows;
   const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, 2>), grid, dim3(256), 2 * STAGE_BYTES, st, a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV, NST>), grid, dim3(64 * NWV), smem_bytes, st,
+                     a);
   return hipGetLastError();
 }
 
