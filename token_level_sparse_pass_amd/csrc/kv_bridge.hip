@@ -118,18 +118,34 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
     __syncthreads();
     if (ks + 1 < n_k) issue((ks + 1) * BK, (ks + 1) & 1);
     const char* base = smem + (ks & 1) * STAGE_BYTES;
+    // H fragments stay in registers for a k-substep; W fragments stream one
+    // feature block ahead of the MFMAs that use them, and the next
+    // substep's H fragments are read during the last two feature blocks
+    bf16x8 hf[8], hn[8], wf[2];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) hf[b] = *reinterpret_cast<const bf16x8*>(base + hoff[0] + b * 16 * ROW_BYTES);
+    wf[0] = *reinterpret_cast<const bf16x8*>(base + woff[0]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8 hf[8], wf[8];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        hf[b] = *reinterpret_cast<const bf16x8*>(base + hoff[u] + b * 16 * ROW_BYTES);
-        wf[b] = *reinterpret_cast<const bf16x8*>(base + woff[u] + b * 16 * ROW_BYTES);
+      for (int fb = 0; fb < 8; ++fb) {
+        if (fb + 1 < 8)
+          wf[(fb + 1) & 1] =
+              *reinterpret_cast<const bf16x8*>(base + woff[u] + (fb + 1) * 16 * ROW_BYTES);
+        else if (u == 0)
+          wf[0] = *reinterpret_cast<const bf16x8*>(base + woff[1]);
+        if (u == 0 && fb >= 6) {
+#pragma unroll
+          for (int b = (fb - 6) * 4; b < (fb - 5) * 4; ++b)
+            hn[b] = *reinterpret_cast<const bf16x8*>(base + hoff[1] + b * 16 * ROW_BYTES);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 8; ++tb) acc[fb][tb] = OP::mma(wf[fb & 1], hf[tb], acc[fb][tb]);
       }
+      if (u == 0) {
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb)
-#pragma unroll
-        for (int tb = 0; tb < 8; ++tb) acc[fb][tb] = OP::mma(wf[fb], hf[tb], acc[fb][tb]);
+        for (int b = 0; b < 8; ++b) hf[b] = hn[b];
+      }
     }
   }
 
