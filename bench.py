@@ -423,6 +423,9 @@ def main():
                          "workload) instead of the default workload")
     ap.add_argument("--kv-bridge", action="store_true",
                     help="time the KV Bridging projection for the 1M-token context instead")
+    ap.add_argument("--select", choices=["token", "block"], default="token",
+                    help="selection of the timed block: token top-k (the method) or the "
+                         "64-token block ablation")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fixed index sets) instead")
     ap.add_argument("--bwd-config", type=int, default=2,
@@ -469,6 +472,8 @@ def main():
     log(f"workload {w.name}: generating inputs")
     inp = make_inputs(w, device=dev)
     kw = dict(top_k=w.top_k, window=w.window)
+    if args.select == "block":
+        kw.update(select="block", block_size=w.block_size, top_blocks=w.top_blocks)
     p = hs2.problem(inp["q_full"].dtype, w.batch, w.n_q, w.n_kv, w.h_q, w.h_kv, w.d, **kw)
     ws = hs2.alloc_workspace(p, dev)
     out = None
@@ -541,10 +546,36 @@ def main():
            "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
            "config": {"workload": w.name, "batch": w.batch, "n_q": w.n_q, "n_kv": w.n_kv,
                       "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d, "top_k": w.top_k,
-                      "window": w.window, "sparse_layers": w.n_sparse, "select": "token",
+                      "window": w.window, "sparse_layers": w.n_sparse, "select": args.select,
                       "structure": w.structure, "parallelism": "single GPU"},
-           "roofline": roofline, "passes": passes, "cpu_baseline": cpu}
+           "roofline": roofline, "passes": passes, "cpu_baseline": cpu,
+           "quality": selection_quality(w, inp["meta"], out["idx"])}
     print(json.dumps(rec), flush=True)
+
+
+def selection_quality(w, meta, idx):
+    """How much of the planted structure the selection found (a sanity
+    figure, not parity): needle workloads, the fraction of needles their
+    target query selects; cluster workloads, the mean over query rows of the
+    fraction of the clustered tokens the row selects. None otherwise."""
+    import torch
+    if meta.get("structure") == "needles":
+        hits = 0
+        for j, t in zip(meta["needle_pos"].tolist(), meta["needle_target"].tolist()):
+            row = idx[0, int(t) - w.q_off]
+            hits += int(bool((row == int(j)).any()))
+        return {"needle_hits": hits, "needles": len(meta["needle_pos"]),
+                "fraction": round(hits / max(1, len(meta["needle_pos"])), 4)}
+    if meta.get("structure") == "clusters":
+        mark = torch.zeros(w.n_kv + 1, dtype=torch.int32, device=idx.device)
+        pos = torch.as_tensor(meta["cluster_pos"], dtype=torch.long, device=idx.device)
+        mark[pos] = 1
+        got = mark[torch.where(idx >= 0, idx, w.n_kv).long()].sum(-1).float()   # [B, n_q]
+        recall = got / float(len(meta["cluster_pos"]))
+        return {"cluster_tokens": int(len(meta["cluster_pos"])),
+                "mean_recall": round(float(recall.mean()), 4),
+                "min_recall": round(float(recall.min()), 4)}
+    return None
 
 
 if __name__ == "__main__":
