@@ -91,6 +91,20 @@ def measured_traffic(pass_name, workload):
     return rec.get("bytes_per_launch")
 
 
+def host_cpu():
+    """CPU model and the number of cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, inp, target_s=15.0, max_rows=64):
     """The fp64 oracle on a bounded sample of query rows of the same workload."""
     import numpy as np
@@ -121,7 +135,7 @@ def cpu_baseline(w, inp, target_s=15.0, max_rows=64):
     total_rows = len(first) + (len(rows) if w.n_q > 1 else 0)
     total_t = t1 + t2
     return {"value": total_rows / total_t, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": f"{total_rows} query rows of sequence 0 of {w.name} (full-layer LSE and "
                       f"score sweeps over all {w.n_kv} keys, token top-{w.top_k} + "
                       f"{w.window}-token window, {w.n_sparse} sparse layers), "
@@ -316,6 +330,7 @@ def backward_cpu_baseline(w, inp, grads, idx, n_rows=64):
                           0, j_lo)
     t = time.perf_counter() - t0
     return {"value": n_rows / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            **host_cpu(),
             "sample": f"the last {n_rows} queries of sequence 0 of {w.name}: their dQ (full "
                       f"and {w.n_sparse} sparse layers) and every K/V-gradient contribution "
                       f"they make, over all {w.n_kv} keys, {t:.1f} s"}
