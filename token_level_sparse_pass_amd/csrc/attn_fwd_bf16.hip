@@ -388,14 +388,12 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
   constexpr int RBW = 2, NWV = FWD_WAVES, NST = FWD_STAGES;
   constexpr int rows = 16 * RBW * NWV;
   constexpr int smem_bytes = NST * STAGE_BYTES;
-  static bool smem_ok = false;
-  if (!smem_ok && smem_bytes > 65536) {
-    const hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_bf16_kernel<RBW, NWV, NST>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             smem_bytes);
+  struct FwdLdsTag {};
+  if (smem_bytes > 65536) {
+    const hipError_t e = ensure_dynamic_lds<FwdLdsTag>(
+        (const void*)attn_fwd_bf16_kernel<RBW, NWV, NST>, smem_bytes);
     if (e != hipSuccess) return e;
   }
-  smem_ok = true;
   a.n_rt = (a.n_q * G + rows - 1) / rows;
   const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV, NST>), grid, dim3(64 * NWV), smem_bytes, st,

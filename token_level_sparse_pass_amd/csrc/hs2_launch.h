@@ -6,7 +6,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace hs2 {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device (the
+// attribute is per device; the flag is set only after the call succeeded).
+// Kernels with one cache slot each, so `Tag` distinguishes the callers.
+template <typename Tag>
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Where key j of sequence b lives in a K/V buffer of [rows][h_kv][d]: a
 // contiguous cache holds each sequence's n_kv rows back to back; a paged

@@ -176,12 +176,10 @@ hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st) {
   a.M = p.tokens; a.F = p.features; a.Dm = p.d_model;
   a.n_mt = (a.M + BM - 1) / BM;
   a.n_nt = (2 * a.F + BN - 1) / BN;
-  static bool smem_ok = false;
-  if (!smem_ok) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kv_bridge_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+  struct BridgeLdsTag {};
+  {
+    const hipError_t e = ensure_dynamic_lds<BridgeLdsTag>((const void*)kv_bridge_kernel, SMEM_BYTES);
     if (e != hipSuccess) return e;
-    smem_ok = true;
   }
   const dim3 grid((unsigned)((size_t)a.n_mt * a.n_nt));
   hipLaunchKernelGGL(kv_bridge_kernel, grid, dim3(256), SMEM_BYTES, st, a);

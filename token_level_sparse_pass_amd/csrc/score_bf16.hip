@@ -246,12 +246,10 @@ hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st) {
   if (n_cand_max <= 0) return hipSuccess;
   a.n_qt = (p.rows + TQ - 1) / TQ;
   a.n_kt = (n_cand_max + TKEY - 1) / TKEY;
-  static bool smem_ok = false;
-  if (!smem_ok) {
-    const hipError_t e = hipFuncSetAttribute((const void*)score_bf16_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, SMEM_BYTES);
+  struct ScoreLdsTag {};
+  {
+    const hipError_t e = ensure_dynamic_lds<ScoreLdsTag>((const void*)score_bf16_kernel, SMEM_BYTES);
     if (e != hipSuccess) return e;
-    smem_ok = true;
   }
   const dim3 grid((unsigned)((size_t)a.n_qt * a.n_kt));
   hipLaunchKernelGGL(score_bf16_kernel, grid, dim3(512), SMEM_BYTES, st, a);
