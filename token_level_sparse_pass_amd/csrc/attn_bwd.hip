@@ -7,11 +7,13 @@
 //   dV += P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta = rowsum(dO * O)
 //   dQ = scale dS K,  dK = scale dS^T Q
 // Two kernels keep every sum in one place (no atomics, deterministic):
-//   dK/dV: a work-group owns 128 keys of one (sequence, KV head) and walks
-//          every row (query, head of the group) that can see them, 32 rows
-//          at a time staged in LDS; each wave keeps 32 keys' dK^T and dV^T.
-//   dQ:    a work-group owns 128 rows, like the forward pass, and walks the
-//          key tiles up to the causal limit, 64 keys at a time in LDS.
+//   dK/dV: a work-group owns 16 keys per wave of one (sequence, KV head)
+//          and walks every row (query, head of the group) that can see
+//          them, 32 rows at a time staged in LDS; each wave keeps its keys'
+//          dK^T and dV^T.
+//   dQ:    a work-group owns 16 rows per wave, like the forward pass, and
+//          walks the key tiles up to the causal limit, 64 keys at a time in
+//          LDS.
 // A third, small kernel forms Delta from O and dO.
 //
 // MFMA mapping (16x16 tiles, hs2_device.h). dK/dV kernel:
@@ -31,6 +33,23 @@
 #include "hs2_bwd.h"
 #include "hs2_device.h"
 #include "hs2_launch.h"
+
+// Work-group shapes (measured on the 32K prefill): dK/dV with one 16-key
+// block per wave and eight waves (two per SIMD: 50 ms, against 56 ms for two
+// blocks per wave at one wave per SIMD); dQ with one 16-row block per wave
+// and eight waves.
+#ifndef BWD_KB
+#define BWD_KB 1
+#endif
+#ifndef BWD_NW
+#define BWD_NW 8
+#endif
+#ifndef BWD_DQ_RBW
+#define BWD_DQ_RBW 1
+#endif
+#ifndef BWD_DQ_NW
+#define BWD_DQ_NW 8
+#endif
 
 namespace hs2 {
 
@@ -86,7 +105,7 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float4* p, size_t n4) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves x 32 keys, rows in blocks of 32
+// dK, dV: KB 16-key blocks per wave, NW waves, rows in blocks of 32
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DkdvSmem {
@@ -97,14 +116,14 @@ struct DkdvSmem {
   float delta[2][32];
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdArgs a) {
+template <typename T, int D, int KB, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DV = D / 16;
-  constexpr int KB = 2;                               // 16-key blocks per wave
-  constexpr int KT = 4 * KB * 16;                     // keys per work-group
+  constexpr int NT = 64 * NW;                         // threads
+  constexpr int KT = NW * KB * 16;                    // keys per work-group
   constexpr int VEC = 16 / sizeof(T);
   constexpr int C16 = D / VEC;                        // 16-byte chunks per row
-  constexpr int LOADS = 32 * C16 / 256;               // per thread per tensor
+  constexpr int LOADS = (32 * C16 + NT - 1) / NT;     // per thread per tensor
   using SM = DkdvSmem<T, D>;
   __shared__ SM sm;
 
@@ -162,10 +181,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int r0 = r_begin + rbk * 32;
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int u = threadIdx.x + 256 * it;
+      const int u = threadIdx.x + NT * it;
       const int row = u / C16, c = u - (u / C16) * C16;
       const int r = r0 + row;
-      if (r < R) {
+      if (row < 32 && r < R) {
         const int i = r / G, h = g * G + (r - (r / G) * G);
         const size_t off = (((size_t)b * a.n_q + i) * a.h_q + h) * D + c * VEC;
         qreg[it] = *reinterpret_cast<const uint4*>(qb + off);
@@ -191,8 +210,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdArgs a) {
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int u = threadIdx.x + 256 * it;
+      const int u = threadIdx.x + NT * it;
       const int row = u / C16, c = u - (u / C16) * C16;
+      if (row >= 32) break;
       *reinterpret_cast<uint4*>(&sm.q[buf][row][c * VEC]) = qreg[it];
       *reinterpret_cast<uint4*>(&sm.dout[buf][row][c * VEC]) = dreg[it];
     }
@@ -268,7 +288,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: 4 waves x 2 row blocks, key tiles of 64 in LDS
+// dQ: RBW 16-row blocks per wave, NW waves, key tiles of 64 in LDS
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DqSmem {
@@ -277,14 +297,14 @@ struct DqSmem {
   T v[2][64][LD];
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
+template <typename T, int D, int RBW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int DV = D / 16;
-  constexpr int RBW = 2;
-  constexpr int ROWS = 4 * RBW * 16;
+  constexpr int NT = 64 * NW;
+  constexpr int ROWS = NW * RBW * 16;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int C16 = D / VEC;
-  constexpr int LOADS = 64 * C16 / 256;
+  constexpr int LOADS = (64 * C16 + NT - 1) / NT;
   using SM = DqSmem<T, D>;
   __shared__ SM sm;
 
@@ -345,10 +365,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
   auto gload = [&](int tile) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int u = threadIdx.x + 256 * it;
+      const int u = threadIdx.x + NT * it;
       const int row = u / C16, c = u - (u / C16) * C16;
       const int j = tile * 64 + row;
-      if (j < a.n_kv) {
+      if (row < 64 && j < a.n_kv) {
         kreg[it] = *reinterpret_cast<const uint4*>(kseq + (size_t)j * kstride + c * VEC);
         vreg[it] = *reinterpret_cast<const uint4*>(vseq + (size_t)j * kstride + c * VEC);
       } else {
@@ -360,8 +380,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdArgs a) {
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < LOADS; ++it) {
-      const int u = threadIdx.x + 256 * it;
+      const int u = threadIdx.x + NT * it;
       const int row = u / C16, c = u - (u / C16) * C16;
+      if (row >= 64) break;
       *reinterpret_cast<uint4*>(&sm.k[buf][row][c * VEC]) = kreg[it];
       *reinterpret_cast<uint4*>(&sm.v[buf][row][c * VEC]) = vreg[it];
     }
@@ -448,18 +469,20 @@ hipError_t launch_delta_t(const BwdPlan& p, hipStream_t st) {
 template <typename T, int D>
 hipError_t launch_dkdv_t(const BwdPlan& p, hipStream_t st) {
   BwdArgs a = args_of(p);
-  a.n_tiles = (a.n_kv + 127) / 128;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>),
-                     dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(256), 0, st, a);
+  constexpr int KB = BWD_KB, NW = BWD_NW;
+  a.n_tiles = (a.n_kv + NW * KB * 16 - 1) / (NW * KB * 16);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, KB, NW>),
+                     dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_dq_t(const BwdPlan& p, hipStream_t st) {
   BwdArgs a = args_of(p);
-  a.n_tiles = (a.n_q * (a.h_q / a.h_kv) + 127) / 128;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>),
-                     dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(256), 0, st, a);
+  constexpr int RBW = BWD_DQ_RBW, NW = BWD_DQ_NW;
+  a.n_tiles = (a.n_q * (a.h_q / a.h_kv) + NW * RBW * 16 - 1) / (NW * RBW * 16);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, RBW, NW>),
+                     dim3((unsigned)((size_t)a.n_tiles * a.B * a.h_kv)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
