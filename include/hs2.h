@@ -203,6 +203,38 @@ hs2_status hs2_decode_step_paged(const hs2_problem* p, const hs2_kv_pages* pages
 hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidden,
                          const void* w_kv, void* k, void* v, void* stream);
 
+/* Variable-length batches (batched agent turns: every sequence appends its
+ * own number of new tokens to a context of its own length; hitechexpert.top,
+ * section "Two-Level KV Sharing": the one shared cache serves all of a
+ * sequence's layers). The batch is packed token-major:
+ *   cu_q, cu_kv   HOST [batch + 1] int32 offsets, starting at 0 and not
+ *                 decreasing; sequence b owns queries cu_q[b] .. cu_q[b+1]
+ *                 and keys cu_kv[b] .. cu_kv[b+1], with
+ *                 n_q(b) = cu_q[b+1] - cu_q[b] <= n_kv(b) = cu_kv[b+1] - cu_kv[b]
+ *                 (query i of sequence b sits at position n_kv(b) - n_q(b) + i);
+ *                 sequences with no query are skipped
+ *   q_full, o_full  DEVICE [total_q, h_q, head_dim]
+ *   q_sparse, o_sparse DEVICE [n_sparse_layers, total_q, h_q, head_dim]
+ *   k, v            DEVICE [total_kv, h_kv, head_dim]
+ *   idx             DEVICE [total_q, hs2_index_width(p)], key positions
+ *                   within the sequence
+ *   lse (nullable)  DEVICE float, sequence b's [h_q][n_q(b)] block at offset
+ *                   h_q * cu_q[b]
+ * p->batch is the number of sequences; p->n_q and p->n_kv are not used. Each
+ * sequence is computed as hs2_block_forward with batch 1 and its own
+ * lengths (one query: the decode path), one after another on `stream`,
+ * sharing the workspace (hs2_workspace_size_varlen: the largest any
+ * sequence needs). Every sequence's shape is checked before any launch. */
+hs2_status hs2_workspace_size_varlen(const hs2_problem* p, const int32_t* cu_q,
+                                     const int32_t* cu_kv, size_t* min_bytes,
+                                     size_t* preferred_bytes);
+hs2_status hs2_block_forward_varlen(const hs2_problem* p, int32_t n_sparse_layers,
+                                    const int32_t* cu_q, const int32_t* cu_kv,
+                                    const void* q_full, const void* q_sparse,
+                                    const void* k, const void* v, void* o_full,
+                                    void* o_sparse, int32_t* idx, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward pass of the block, for fine-tuning (hitechexpert.top, section
  * "Performance Gains: Cost, Speed, and Long-Context Capabilities": the
  * compared models are fine-tuned alike). The index sets are held fixed (a

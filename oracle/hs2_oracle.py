@@ -270,6 +270,36 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, top_k=10
                 o_sparse=np.concatenate([o["o_sparse"] for o in outs], axis=1))
 
 
+def block_forward_varlen(q_full, q_sparse, k, v, cu_q, cu_kv, **kw):
+    """The block over a packed batch of sequences of different lengths:
+    sequence b owns queries cu_q[b]..cu_q[b+1] and keys cu_kv[b]..cu_kv[b+1]
+    of the packed tensors (q_full [total_q, h_q, d], q_sparse
+    [L, total_q, h_q, d], k/v [total_kv, h_kv, d]) and is exactly
+    block_forward of batch 1 on its slices. Returns dict(o_full, o_sparse,
+    idx [total_q, W], lse list of [h_q, n_q(b)] arrays, S list, tau list)."""
+    q_full, q_sparse = np.asarray(q_full), np.asarray(q_sparse)
+    k, v = np.asarray(k), np.asarray(v)
+    outs = []
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_kv[b]), int(cu_kv[b + 1])
+        if q1 == q0:
+            outs.append(None)
+            continue
+        outs.append(block_forward(q_full[None, q0:q1], q_sparse[:, None, q0:q1],
+                                  k[None, k0:k1], v[None, k0:k1], **kw))
+    live = [o for o in outs if o is not None]
+    L, hq, d = q_sparse.shape[0], q_full.shape[1], q_full.shape[2]
+    width = live[0]["idx"].shape[-1] if live else 0
+    return dict(
+        o_full=np.concatenate([o["o_full"][0] for o in live]) if live else np.zeros((0, hq, d)),
+        o_sparse=np.concatenate([o["o_sparse"][:, 0] for o in live], axis=1) if live
+        else np.zeros((L, 0, hq, d)),
+        idx=np.concatenate([o["idx"][0] for o in live]) if live else np.zeros((0, width)),
+        lse=[None if o is None else o["lse"][0] for o in outs],
+        S=[None if o is None else o["S"][0] for o in outs],
+        tau=[None if o is None else o["tau"][0] for o in outs])
+
+
 def kv_bridge(hidden, w_kv, h_kv: int):
     """KV Bridging ("Architectural Innovation: Two-Level KV Sharing" on
     blog.lynxflow.co; "Two-Level KV Sharing" on hitechexpert.top): a

@@ -239,3 +239,42 @@ def test_backward_workspace_and_rejections():
     assert b"workspace" in lib.hs2_last_error()
     bad = base_problem(h_q=6, h_kv=4)
     assert lib.hs2_backward_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ctypes.c_size_t())) == 2
+
+
+def test_varlen_checks_and_workspace():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    p = base_problem(batch=3)
+    cq = (ctypes.c_int32 * 4)(0, 100, 101, 301)
+    ck = (ctypes.c_int32 * 4)(0, 500, 1500, 1700)
+    mn, pref = hs2.workspace_size_varlen(p, cq, ck)
+    # the largest of the three sequences' own needs
+    want = [hs2.workspace_size(base_problem(batch=1, n_q=a, n_kv=b))
+            for a, b in ((100, 500), (1, 1000), (200, 200))]
+    assert mn == max(w[0] for w in want) and pref == max(w[1] for w in want)
+
+    def call(cq, ck, ws_bytes=pref, **over):
+        a = dict(q_full=FAKE, q_sparse=FAKE, k=FAKE, v=FAKE, o_full=FAKE, o_sparse=FAKE,
+                 idx=FAKE, lse=None, ws=FAKE)
+        a.update(over)
+        arr = lambda x: (ctypes.c_int32 * len(x))(*x)
+        return lib.hs2_block_forward_varlen(
+            ctypes.byref(p), 2, arr(cq), arr(ck), vp(a["q_full"]), vp(a["q_sparse"]), vp(a["k"]),
+            vp(a["v"]), vp(a["o_full"]), vp(a["o_sparse"]), vp(a["idx"]), vp(a["lse"]),
+            vp(a["ws"]), ws_bytes, None)
+
+    ok_q, ok_k = [0, 100, 101, 301], [0, 500, 1500, 1700]
+    assert call([1, 100, 101, 301], ok_k) == 2                  # must start at 0
+    assert call([0, 100, 99, 301], ok_k) == 2                   # decreasing
+    assert call([0, 600, 601, 801], ok_k) == 2                  # more queries than keys
+    assert call(ok_q, ok_k, ws_bytes=mn - 1) == 4
+    assert call(ok_q, ok_k, q_full=None) == 1
+    assert call(ok_q, ok_k, k=FAKE + 8) == 5
+    assert lib.hs2_block_forward_varlen(ctypes.byref(p), 2, None, None, *[vp(FAKE)] * 9,
+                                        pref, None) == 1
+    # a one-query sequence takes the decode path, which caps h_q / h_kv at 32
+    wide = base_problem(batch=1, h_q=64, h_kv=1)
+    one = (ctypes.c_int32 * 2)(0, 1)
+    keys = (ctypes.c_int32 * 2)(0, 300)
+    assert lib.hs2_workspace_size_varlen(ctypes.byref(wide), one, keys,
+                                         ctypes.byref(ctypes.c_size_t()), None) == 3

@@ -554,3 +554,61 @@ def test_kv_bridge(gpu_lib, B, n, dm, hkv, d):
     gi = out["idx"].cpu().numpy()
     pos = np.arange(w.n_q) + n - w.n_q
     compare_index_rows(gi[0], ref["S"][0], pos, ref["idx"][0], ref["tau"][0], 16)
+
+
+# ---------------------------------------------------------------------------
+# variable-length batches (packed sequences of different lengths)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,hq,hkv,d,seqs", [
+    ("bf16", 8, 2, 128, [(300, 900), (1, 700), (0, 50), (128, 128), (37, 1300)]),
+    ("fp32", 4, 1, 64, [(64, 64), (200, 333), (1, 90)]),
+], ids=["bf16_d128", "fp32_d64"])
+def test_block_forward_varlen(gpu_lib, dtype, hq, hkv, d, seqs):
+    top_k, window, L = 64, 16, 2
+    cu_q = np.concatenate([[0], np.cumsum([a for a, _ in seqs])]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum([b for _, b in seqs])]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_kv[-1])
+    w = small("varlen", dtype, 1, tq, tk, hq, hkv, d, top_k, window, L=L, cid=11)
+    inp = make_inputs(w, device="cuda")            # draws [1, tq, ...] and [1, tk, ...]
+    q, qs = inp["q_full"][0].contiguous(), inp["q_sparse"][:, 0].contiguous()
+    k, v = inp["k"][0].contiguous(), inp["v"][0].contiguous()
+    say("case", dtype, seqs)
+    out = gpu_lib.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, top_k=top_k, window=window)
+    torch.cuda.synchronize()
+    ref = O.block_forward_varlen(host(q), host(qs), host(k), host(v), cu_q, cu_kv,
+                                 top_k=top_k, window=window)
+    tol = TOL[dtype]
+    gi = out["idx"].cpu().numpy()
+    lse = out["lse"].cpu().numpy()
+    for b, (nq, nkv) in enumerate(seqs):
+        if nq == 0:
+            continue
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        pos = np.arange(nq) + nkv - nq
+        tied = compare_index_rows(gi[q0:q1], ref["S"][b], pos, ref["idx"][q0:q1], ref["tau"][b],
+                                  window)
+        err = np.abs(as_np(out["o_full"][q0:q1]) - ref["o_full"][q0:q1]).max()
+        lerr = np.abs(lse[hq * q0:hq * q1].reshape(hq, nq) - ref["lse"][b]).max()
+        say("sequence", b, "o_full err", err, "lse err", lerr, "tied rows", len(tied))
+        assert err <= tol and lerr <= 1e-4
+        if not tied:
+            serr = np.abs(as_np(out["o_sparse"][:, q0:q1]) - ref["o_sparse"][:, q0:q1]).max()
+            assert serr <= tol
+
+
+def test_varlen_equal_lengths_match_batched_call(gpu_lib):
+    B, nq, nkv = 3, 200, 700
+    w = small("varlen_eq", "bf16", B, nq, nkv, 8, 2, 128, 64, 16, L=2, cid=12)
+    inp = make_inputs(w, device="cuda")
+    kw = dict(top_k=64, window=16)
+    batched = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], **kw)
+    cu_q = np.arange(B + 1) * nq
+    cu_kv = np.arange(B + 1) * nkv
+    packed = gpu_lib.block_forward_varlen(
+        inp["q_full"].reshape(B * nq, 8, 128), inp["q_sparse"].reshape(2, B * nq, 8, 128),
+        inp["k"].reshape(B * nkv, 2, 128), inp["v"].reshape(B * nkv, 2, 128), cu_q, cu_kv, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(packed["idx"], batched["idx"].reshape(B * nq, -1))
+    assert torch.equal(packed["o_full"], batched["o_full"].reshape(B * nq, 8, 128))
+    assert torch.equal(packed["o_sparse"], batched["o_sparse"].reshape(2, B * nq, 8, 128))
+    assert torch.equal(packed["lse"], batched["lse"].reshape(-1))

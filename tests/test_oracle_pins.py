@@ -524,3 +524,41 @@ def test_backward_tail_matches_dense(j_lo):
         np.testing.assert_allclose(t["dq_sparse"], dense["dq_sparse"][:, b, rows], atol=1e-12)
         np.testing.assert_allclose(t["dk"], dense["dk"][b, j_lo:], atol=1e-12)
         np.testing.assert_allclose(t["dv"], dense["dv"][b, j_lo:], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# variable-length batches
+# ----------------------------------------------------------------------------
+def test_varlen_equal_lengths_is_the_batched_block():
+    B, nq, nkv, hq, hkv, d, L = 3, 6, 14, 4, 2, 8, 2
+    q, qs = rand((B, nq, hq, d), 150), rand((L, B, nq, hq, d), 151)
+    k, v = rand((B, nkv, hkv, d), 152), rand((B, nkv, hkv, d), 153)
+    want = O.block_forward(q, qs, k, v, top_k=3, window=4)
+    cu_q, cu_kv = np.arange(B + 1) * nq, np.arange(B + 1) * nkv
+    got = O.block_forward_varlen(q.reshape(B * nq, hq, d), qs.reshape(L, B * nq, hq, d),
+                                 k.reshape(B * nkv, hkv, d), v.reshape(B * nkv, hkv, d),
+                                 cu_q, cu_kv, top_k=3, window=4)
+    np.testing.assert_array_equal(got["o_full"], want["o_full"].reshape(B * nq, hq, d))
+    np.testing.assert_array_equal(got["o_sparse"], want["o_sparse"].reshape(L, B * nq, hq, d))
+    np.testing.assert_array_equal(got["idx"], want["idx"].reshape(B * nq, -1))
+    for b in range(B):
+        np.testing.assert_array_equal(got["lse"][b], want["lse"][b])
+
+
+def test_varlen_sequences_are_independent():
+    # changing one sequence's data leaves every other sequence's results alone
+    cu_q, cu_kv = [0, 5, 5, 6, 10], [0, 9, 12, 20, 24]
+    hq, hkv, d, L = 4, 1, 8, 2
+    q, qs = rand((10, hq, d), 160), rand((L, 10, hq, d), 161)
+    k, v = rand((24, hkv, d), 162), rand((24, hkv, d), 163)
+    a = O.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, top_k=2, window=3)
+    k2 = k.copy()
+    k2[12:20] = rand((8, hkv, d), 164)             # sequence 2's keys
+    b = O.block_forward_varlen(q, qs, k2, v, cu_q, cu_kv, top_k=2, window=3)
+    other = np.r_[0:5, 6:10]
+    np.testing.assert_array_equal(a["o_full"][other], b["o_full"][other])
+    np.testing.assert_array_equal(a["idx"][other], b["idx"][other])
+    assert not np.array_equal(a["o_full"][5], b["o_full"][5])
+    assert a["lse"][1] is None                     # the empty sequence
+    # the one-query sequence sits at the last position of its 8 keys
+    assert a["idx"][5][a["idx"][5] >= 0][-1] == 7

@@ -377,13 +377,14 @@ hs2_status check_sparse_args(const hs2_problem* p, int32_t n_layers, const void*
   return HS2_OK;
 }
 
+// layer_elems: elements between layers of q and o (0: batch * n_q * h_q * d)
 hs2_status run_sparse(const hs2_problem& p, int32_t n_layers, const void* q, const void* k,
                       const void* v, const int32_t* idx, void* o, hipStream_t st,
-                      const hs2::KvRows* kv = nullptr) {
+                      const hs2::KvRows* kv = nullptr, size_t layer_elems = 0) {
   const int G = p.h_q / p.h_kv;
   const int per = std::max(1, 64 / G);                       // layers per launch
   const size_t esz = p.dtype == HS2_BF16 ? 2 : 4;
-  const size_t layer_elems = (size_t)p.batch * p.n_q * p.h_q * p.head_dim;
+  if (layer_elems == 0) layer_elems = (size_t)p.batch * p.n_q * p.h_q * p.head_dim;
   for (int l0 = 0; l0 < n_layers; l0 += per) {
     hs2::SparsePlan sp;
     sp.layers = std::min(per, n_layers - l0);
@@ -395,6 +396,7 @@ hs2_status run_sparse(const hs2_problem& p, int32_t n_layers, const void* q, con
     sp.scale_log2 = p.softmax_scale * 1.4426950408889634f;
     sp.bf16 = p.dtype == HS2_BF16;
     sp.kv = kv ? *kv : contiguous_rows(p);
+    sp.layer_stride = layer_elems;
     PassTimer t(st, HS2_PASS_SPARSE);
     HIP_TRY(hs2::launch_sparse_attn(sp, st), "sparse attention");
   }
@@ -669,6 +671,111 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
   {
     PassTimer t(st, HS2_PASS_BWD_DQ);
     HIP_TRY(hs2::launch_bwd_dq(bp, st), "full-layer dQ");
+  }
+  return HS2_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Variable-length batches: sequence b owns queries cu_q[b] .. cu_q[b+1] and
+// keys cu_kv[b] .. cu_kv[b+1] of the packed tensors. Checks the offsets and
+// every non-empty sequence's problem (batch 1, its own n_q and n_kv), and
+// returns the largest workspace any of them needs.
+hs2_status check_varlen(const hs2_problem* p, const int32_t* cu_q, const int32_t* cu_kv,
+                        size_t* min_bytes, size_t* pref_bytes, long long* total_q,
+                        long long* total_kv) {
+  if (!p) return fail(HS2_ERR_NULL, "problem is NULL");
+  if (!cu_q || !cu_kv) return fail(HS2_ERR_NULL, "cu_seqlens arrays are NULL");
+  if (p->batch < 1) return fail(HS2_ERR_SHAPE, "batch %d", p->batch);
+  if (cu_q[0] != 0 || cu_kv[0] != 0) return fail(HS2_ERR_SHAPE, "cu_seqlens must start at 0");
+  size_t mn = 0, pref = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const long long nq = (long long)cu_q[b + 1] - cu_q[b];
+    const long long nkv = (long long)cu_kv[b + 1] - cu_kv[b];
+    if (nq < 0 || nkv < 0)
+      return fail(HS2_ERR_SHAPE, "cu_seqlens decrease at sequence %d", b);
+    if (nq > nkv)
+      return fail(HS2_ERR_SHAPE, "sequence %d: %lld queries > %lld keys", b, nq, nkv);
+    if (nq == 0) continue;
+    hs2_problem pb = *p;
+    pb.batch = 1; pb.n_q = (int32_t)nq; pb.n_kv = (int32_t)nkv;
+    HS2_TRY(check_problem(&pb));
+    size_t m = 0, pr = 0;
+    if (plan(pb, SIZE_MAX, nullptr, &m, &pr) != HS2_OK)
+      return fail(HS2_ERR_SHAPE, "sequence %d: plan", b);
+    mn = std::max(mn, m);
+    pref = std::max(pref, pr);
+  }
+  if (min_bytes) *min_bytes = mn;
+  if (pref_bytes) *pref_bytes = pref;
+  if (total_q) *total_q = cu_q[p->batch];
+  if (total_kv) *total_kv = cu_kv[p->batch];
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_workspace_size_varlen(const hs2_problem* p, const int32_t* cu_q,
+                                     const int32_t* cu_kv, size_t* min_bytes,
+                                     size_t* preferred_bytes) {
+  g_err.clear();
+  if (!min_bytes && !preferred_bytes) return fail(HS2_ERR_NULL, "no output pointer");
+  return check_varlen(p, cu_q, cu_kv, min_bytes, preferred_bytes, nullptr, nullptr);
+}
+
+hs2_status hs2_block_forward_varlen(const hs2_problem* p, int32_t n_sparse_layers,
+                                    const int32_t* cu_q, const int32_t* cu_kv, const void* q_full,
+                                    const void* q_sparse, const void* k, const void* v,
+                                    void* o_full, void* o_sparse, int32_t* idx, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  size_t mn = 0;
+  long long total_q = 0, total_kv = 0;
+  HS2_TRY(check_varlen(p, cu_q, cu_kv, &mn, nullptr, &total_q, &total_kv));
+  if (n_sparse_layers < 0) return fail(HS2_ERR_SHAPE, "n_sparse_layers %d", n_sparse_layers);
+  HS2_TRY(check_ptr(q_full, "q_full"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  HS2_TRY(check_ptr(o_full, "o_full"));
+  HS2_TRY(check_ptr(idx, "idx"));
+  HS2_TRY(check_ptr(lse, "lse", false));
+  HS2_TRY(check_ptr(q_sparse, "q_sparse", n_sparse_layers > 0));
+  HS2_TRY(check_ptr(o_sparse, "o_sparse", n_sparse_layers > 0));
+  if (total_q > 0) {
+    if (!workspace) return fail(HS2_ERR_NULL, "workspace is NULL (needs %zu bytes)", mn);
+    if (!aligned16(workspace)) return fail(HS2_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < mn)
+      return fail(HS2_ERR_WORKSPACE, "workspace %zu bytes < minimum %zu", workspace_bytes, mn);
+  }
+  const hipStream_t st = (hipStream_t)stream;
+  const size_t esz = p->dtype == HS2_BF16 ? 2 : 4;
+  const size_t qrow = (size_t)p->h_q * p->head_dim;           // elements per query token
+  const size_t krow = (size_t)p->h_kv * p->head_dim;          // elements per key token
+  const int width = index_width(*p);
+  const size_t layer_elems = (size_t)total_q * qrow;
+  for (int b = 0; b < p->batch; ++b) {
+    const int q0 = cu_q[b], nq = cu_q[b + 1] - cu_q[b];
+    const int k0 = cu_kv[b], nkv = cu_kv[b + 1] - cu_kv[b];
+    if (nq == 0) continue;
+    hs2_problem pb = *p;
+    pb.batch = 1; pb.n_q = nq; pb.n_kv = nkv;
+    Layout L;
+    if (plan(pb, workspace_bytes, &L, nullptr, nullptr) != HS2_OK)
+      return fail(HS2_ERR_WORKSPACE, "sequence %d: workspace too small", b);
+    const char* qb = (const char*)q_full + q0 * qrow * esz;
+    const char* kb = (const char*)k + k0 * krow * esz;
+    const char* vb = (const char*)v + k0 * krow * esz;
+    char* ob = (char*)o_full + q0 * qrow * esz;
+    int32_t* ib = idx + (size_t)q0 * width;
+    float* lb = lse ? lse + (size_t)q0 * p->h_q : nullptr;
+    HS2_TRY(run_full(pb, qb, kb, vb, ob, ib, lb, nullptr, workspace, L, st));
+    if (n_sparse_layers > 0)
+      HS2_TRY(run_sparse(pb, n_sparse_layers, (const char*)q_sparse + q0 * qrow * esz, kb, vb, ib,
+                         (char*)o_sparse + q0 * qrow * esz, st, nullptr, layer_elems));
   }
   return HS2_OK;
 }

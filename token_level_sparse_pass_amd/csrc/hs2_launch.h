@@ -167,6 +167,7 @@ struct SparsePlan {
   float scale_log2;
   bool bf16;
   KvRows kv;                          // kv.n_kv = n_kv, or a paged pool
+  size_t layer_stride = 0;            // elements between layers of q, o (0: batch*n_q*h_q*d)
 };
 hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st);
 

@@ -33,6 +33,7 @@ struct SparseArgs {
   int L, B, n_q, n_kv, h_q, h_kv, W;
   float scale_log2;     // softmax scale * log2(e)
   KvRows kv;            // key j of sequence b is K/V buffer row kv.row(b, j)
+  size_t layer_stride;  // elements between layers of q and o
 };
 
 template <typename T, int D>
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
     const int r = rb * 16 + (lane & 15);
     if (r < rows_total) {
       const int layer = r / G, hh = r - (r / G) * G;
-      const T* qrow = qb + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
+      const T* qrow = qb + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D);
       load_slice_il<T, D>(qf[rb], qrow, lane);
     } else {
       zero_slice<T, D>(qf[rb]);
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
       const int r = rb * 16 + (lane & 15);
       if (r >= rows_total) continue;
       const int layer = r / G, hh = r - (r / G) * G;
-      T* orow = ob + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
+      T* orow = ob + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D);
       const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
       T outv[4 * DV];
 #pragma unroll
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_kernel(SparseArgs a) {
             o += sm_o[w][row][d];
           }
           const int layer = r / G, hh = r - (r / G) * G;
-          T* orow = ob + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D;
+          T* orow = ob + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D);
           orow[d] = to_elem<T>(Lr > 0.f ? o / Lr : 0.f);
         }
       }
@@ -343,6 +344,8 @@ hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st) {
   a.q = p.q; a.k = p.k; a.v = p.v; a.idx = p.idx; a.o = p.o;
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
   a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.scale_log2 = p.scale_log2; a.kv = p.kv;
+  a.layer_stride = p.layer_stride ? p.layer_stride
+                                  : (size_t)p.batch * p.n_q * p.h_q * p.head_dim;
   const int G = p.h_q / p.h_kv;
   const int rb = (p.layers * G + 15) / 16;
   // few work-groups: split each index list over 8 waves of one work-group

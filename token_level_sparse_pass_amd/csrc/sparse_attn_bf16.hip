@@ -35,6 +35,7 @@ struct Sp2Args {
   int L, B, n_q, n_kv, h_q, h_kv, W;
   float c;
   KvRows kv;
+  size_t layer_stride;  // elements between layers of q and o
 };
 
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   Frag<__bf16, D> qf;
   if (r < rows_total) {
     const int layer = r / G, hh = r - (r / G) * G;
-    load_slice<__bf16, D>(qf, a.q + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D,
+    load_slice<__bf16, D>(qf, a.q + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D),
                           lane);
   } else {
     zero_slice<__bf16, D>(qf);
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int layer = r / G, hh = r - (r / G) * G;
-  __bf16* orow = a.o + ((((size_t)layer * a.B + b) * a.n_q + i) * a.h_q + g * G + hh) * D + grp * 32;
+  __bf16* orow = a.o + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D) + grp * 32;
   bf16x8 outv[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
@@ -249,6 +250,7 @@ hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
   a.o = reinterpret_cast<__bf16*>(p.o);
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
   a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.c = p.scale_log2; a.kv = p.kv;
+  a.layer_stride = p.layer_stride ? p.layer_stride : (size_t)p.batch * p.n_q * p.h_q * D;
   const int G = p.h_q / p.h_kv;
   const int rb = (p.layers * G + 15) / 16;
   const dim3 grid((unsigned)((size_t)p.batch * p.n_q * p.h_kv));

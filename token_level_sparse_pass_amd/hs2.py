@@ -79,6 +79,11 @@ def load(path: str = LIB_PATH):
     lib.hs2_decode_step_paged.restype = i32
     lib.hs2_kv_bridge.argtypes = [P, i32, vp, vp, vp, vp, vp]
     lib.hs2_kv_bridge.restype = i32
+    pi = ctypes.POINTER(i32)
+    lib.hs2_workspace_size_varlen.argtypes = [P, pi, pi, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.hs2_workspace_size_varlen.restype = i32
+    lib.hs2_block_forward_varlen.argtypes = [P, i32, pi, pi] + [vp] * 9 + [sz, vp]
+    lib.hs2_block_forward_varlen.restype = i32
     lib.hs2_backward_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
     lib.hs2_backward_workspace_size.restype = i32
     lib.hs2_block_backward.argtypes = [P, i32] + [vp] * 14 + [vp, sz, vp]
@@ -339,4 +344,51 @@ def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, 
         _ptr(do_full), _ptr(do_sparse if L else None), _ptr(out["dq_full"]),
         _ptr(out["dq_sparse"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
         workspace.numel(), _stream(q_full.device)))
+    return out
+
+
+def _cu(x):
+    vals = [int(t) for t in (x.tolist() if hasattr(x, "tolist") else x)]
+    return (ctypes.c_int32 * len(vals))(*vals), vals
+
+
+def workspace_size_varlen(p: Problem, cu_q, cu_kv):
+    cq, _ = _cu(cu_q)
+    ck, _ = _cu(cu_kv)
+    mn, pref = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().hs2_workspace_size_varlen(ctypes.byref(p), cq, ck, ctypes.byref(mn),
+                                            ctypes.byref(pref)))
+    return mn.value, pref.value
+
+
+def block_forward_varlen(q_full, q_sparse, k, v, cu_q, cu_kv, *, workspace=None, want_lse=True,
+                         **kw):
+    """The block over a packed batch of sequences of different lengths.
+    q_full [total_q, h_q, d], q_sparse [L, total_q, h_q, d], k/v
+    [total_kv, h_kv, d]; cu_q / cu_kv: host sequences of batch + 1 offsets.
+    Returns dict(o_full, o_sparse, idx [total_q, W], lse (h_q * total_q
+    floats, sequence b's [h_q][n_q(b)] block at h_q * cu_q[b]))."""
+    lib = load()
+    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k, "k"), (v, "v")):
+        _check_tensor(t, n, q_full.dtype)
+    cq, vq = _cu(cu_q)
+    ck, vk = _cu(cu_kv)
+    batch = len(vq) - 1
+    total_q, hq, d = q_full.shape
+    hkv = k.shape[1]
+    if vq[-1] != total_q or vk[-1] != k.shape[0]:
+        raise ValueError("cu_seqlens do not match the packed tensors")
+    p = problem(q_full.dtype, batch, 1, 1, hq, hkv, d, **kw)
+    width = index_width(p)
+    mn, pref = workspace_size_varlen(p, cq, ck)
+    if workspace is None:
+        workspace = torch.empty(max(16, pref), dtype=torch.uint8, device=q_full.device)
+    out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
+               idx=torch.empty((total_q, width), dtype=torch.int32, device=q_full.device),
+               lse=torch.empty((hq * total_q,), dtype=torch.float32, device=q_full.device)
+               if want_lse else None)
+    _check(lib.hs2_block_forward_varlen(
+        ctypes.byref(p), q_sparse.shape[0], cq, ck, _ptr(q_full), _ptr(q_sparse), _ptr(k),
+        _ptr(v), _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
+        _ptr(workspace), workspace.numel(), _stream(q_full.device)))
     return out
