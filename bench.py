@@ -426,6 +426,96 @@ def backward_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def varlen_bench(args):
+    """A packed batch of agent turns of different lengths
+    (hs2_block_forward_varlen): 8 sequences with contexts of 32K-262K keys,
+    each appending a new chunk of 256-4096 tokens (lengths drawn from a
+    seeded generator), the 8K-on-262K workload's heads and 5 sparse layers."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from synth import CONFIGS, make_inputs
+    from token_level_sparse_pass_amd import hs2
+
+    lib = hs2.load()
+    base = CONFIGS[4]
+    rng = np.random.default_rng([base.cid, 77])
+    n_seq = 8
+    nkv = rng.integers(32768, 262144 + 1, size=n_seq)
+    nq = np.minimum(rng.integers(256, 4096 + 1, size=n_seq), nkv)
+    cu_q = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(nkv)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_kv[-1])
+    w = dataclasses.replace(base, name=base.name + "_varlen", n_q=tq, n_kv=tk, structure="none")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"varlen: {n_seq} sequences, {tq} queries over {tk} keys")
+    inp = make_inputs(w, device=dev)
+    q, qs = inp["q_full"][0].contiguous(), inp["q_sparse"][:, 0].contiguous()
+    k, v = inp["k"][0].contiguous(), inp["v"][0].contiguous()
+    kw = dict(top_k=w.top_k, window=w.window)
+    p = hs2.problem(q.dtype, n_seq, 1, 1, w.h_q, w.h_kv, w.d, **kw)
+    _, pref = hs2.workspace_size_varlen(p, cu_q, cu_kv)
+    ws = torch.empty(pref, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        hs2.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib.hs2_profile_enable(1)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        hs2.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, workspace=ws, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (ctypes.c_double * len(PASSES))()
+    nl = (ctypes.c_int64 * len(PASSES))()
+    st = lib.hs2_profile_read(ms, nl)
+    lib.hs2_profile_enable(0)
+    if st != 0:
+        raise RuntimeError(lib.hs2_last_error().decode())
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # algorithmic work: the sum over sequences, each a batch-1 block
+    work = {}
+    for a_, b_ in zip(nq.tolist(), nkv.tolist()):
+        ws_ = dataclasses.replace(base, batch=1, n_q=int(a_), n_kv=int(b_))
+        for name, (bound, amount) in algorithmic_work(ws_).items():
+            work[name] = (bound, work.get(name, (bound, 0.0))[1] + amount)
+    peak_mfma = PEAK_MFMA_TFLOPS[w.dtype]
+    passes = {}
+    for i, name in enumerate(PASSES):
+        if nl[i] == 0 or name not in work:
+            continue
+        bound, amount = work[name]
+        per = ms[i] / args.steps
+        if bound == "mfma":
+            ach = amount / (per / 1e3) / 1e12
+            passes[name] = {"ms": round(per, 4), "launches_per_step": int(nl[i] // args.steps),
+                            "bound": "mfma", "achieved": round(ach, 2), "unit": "TFLOP/s",
+                            "frac": round(ach / peak_mfma, 4)}
+        else:
+            ach = amount / (per / 1e3) / 1e9
+            passes[name] = {"ms": round(per, 4), "launches_per_step": int(nl[i] // args.steps),
+                            "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(passes, key=lambda n: passes[n]["ms"])
+    d = passes[dom]
+    rec = {"metric": "varlen batch tokens/s (packed agent turns of different lengths)",
+           "value": round(tq / (ms_step / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic (seeded lengths and values; no datasets)",
+           "config": {"workload": "agent_turns_bf16_varlen", "sequences": n_seq,
+                      "n_q": nq.tolist(), "n_kv": nkv.tolist(), "h_q": w.h_q, "h_kv": w.h_kv,
+                      "head_dim": w.d, "top_k": w.top_k, "window": w.window,
+                      "sparse_layers": w.n_sparse, "parallelism": "single GPU"},
+           "roofline": {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
+                        "peak": peak_mfma if d["bound"] == "mfma" else PEAK_HBM_GBS,
+                        "unit": d["unit"], "frac": d["frac"], "traffic": None},
+           "passes": passes, "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,6 +531,8 @@ def main():
     ap.add_argument("--select", choices=["token", "block"], default="token",
                     help="selection of the timed block: token top-k (the method) or the "
                          "64-token block ablation")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time a packed batch of agent turns of different lengths instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fixed index sets) instead")
     ap.add_argument("--bwd-config", type=int, default=2,
@@ -476,6 +568,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.varlen:
+        varlen_bench(args)
         return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2

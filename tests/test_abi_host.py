@@ -248,10 +248,23 @@ def test_varlen_checks_and_workspace():
     cq = (ctypes.c_int32 * 4)(0, 100, 101, 301)
     ck = (ctypes.c_int32 * 4)(0, 500, 1500, 1700)
     mn, pref = hs2.workspace_size_varlen(p, cq, ck)
-    # the largest of the three sequences' own needs
-    want = [hs2.workspace_size(base_problem(batch=1, n_q=a, n_kv=b))
+    # bf16 / head_dim 128: the prefill-shaped sequences (100 x 500, 200 x 200)
+    # share one full-attention launch, so their statistics (3 x h_q floats per
+    # query), transposed V copies (h_kv x 64-key tiles x 128 x 2 B) and a score
+    # chunk (rows of the longest score row) coexist; the one-query sequence
+    # (decode path) reuses the same bytes afterwards
+    up = lambda x: (x + 255) // 256 * 256
+    fixed = up(3 * 8 * 301 * 4) + up(2 * (8 + 4) * 64 * 128 * 2)
+    row = (500 - 16 + 255) // 256 * 256 * 4
+    dec = hs2.workspace_size(base_problem(batch=1, n_q=1, n_kv=1000))
+    assert mn == max(fixed + up(row), dec[0])
+    assert pref == max(fixed + up(256 * row), dec[1])      # rows: 200 rounded up to 128s
+    # other dtypes run sequence by sequence: the largest single need
+    p32 = base_problem(batch=3, dtype=hs2.FP32)
+    mn32, pref32 = hs2.workspace_size_varlen(p32, cq, ck)
+    want = [hs2.workspace_size(base_problem(batch=1, n_q=a, n_kv=b, dtype=hs2.FP32))
             for a, b in ((100, 500), (1, 1000), (200, 200))]
-    assert mn == max(w[0] for w in want) and pref == max(w[1] for w in want)
+    assert mn32 == max(w[0] for w in want) and pref32 == max(w[1] for w in want)
 
     def call(cq, ck, ws_bytes=pref, **over):
         a = dict(q_full=FAKE, q_sparse=FAKE, k=FAKE, v=FAKE, o_full=FAKE, o_sparse=FAKE,

@@ -64,6 +64,7 @@ struct Fwd2Args {
   __bf16* o; float* stats; float* lse;
   int B, n_q, n_kv, h_q, h_kv, n_rt, vt_tiles;
   float c;                           // softmax scale * log2(e)
+  VarlenSeqs vl;                     // vl.n > 0: packed sequences, one launch
 };
 
 }  // namespace
@@ -118,24 +119,62 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.h_q / a.h_kv;
-  const int R = a.n_q * G;
-  const int q_off = a.n_kv - a.n_q;
-
   const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int rt = a.n_rt - 1 - (int)(lid % a.n_rt);      // heavy tiles first
-  const int bg = lid / a.n_rt;
-  const int b = bg % a.B;
-  const int g = bg / a.B;
+
+  // this work-group's sequence: its lengths, token offsets into the packed
+  // tensors, transposed-V block, and its statistics block (3 planes of
+  // h_q x n_q, as a batch-1 call lays them out)
+  int g, rt, nq, nkv;
+  size_t qtok0, ktok0, vt_tile0, st0, plane;
+  int vt_tiles;
+  if (a.vl.n > 0) {
+    // row tiles fastest, KV head slowest: neighbouring ids (one XCD, one
+    // L2) share a sequence's K/V head
+    const int n_t = a.vl.tile0[a.vl.n];
+    g = (int)(lid / n_t);
+    const int t = (int)(lid - (uint32_t)g * n_t);
+    int s = 0;
+    while (s + 1 < a.vl.n && t >= a.vl.tile0[s + 1]) ++s;
+    nq = a.vl.nq[s];
+    nkv = a.vl.nkv[s];
+    rt = a.vl.tile0[s + 1] - 1 - t;                     // heavy tiles first
+    qtok0 = a.vl.q0[s];
+    ktok0 = a.vl.kv0[s];
+    vt_tiles = (nkv + TK - 1) / TK;
+    vt_tile0 = (size_t)a.vl.vt0[s] + (size_t)g * vt_tiles;
+    st0 = (size_t)3 * a.h_q * a.vl.q0[s];
+    plane = (size_t)a.h_q * nq;
+  } else {
+    rt = a.n_rt - 1 - (int)(lid % a.n_rt);              // heavy tiles first
+    const int bg = lid / a.n_rt;
+    const int b = bg % a.B;
+    g = bg / a.B;
+    nq = a.n_q;
+    nkv = a.n_kv;
+    qtok0 = (size_t)b * a.n_q;
+    ktok0 = (size_t)b * a.n_kv;
+    vt_tiles = a.vt_tiles;
+    vt_tile0 = ((size_t)b * a.h_kv + g) * a.vt_tiles;
+    st0 = (size_t)b * a.h_q * a.n_q;
+    plane = (size_t)a.B * a.h_q * a.n_q;
+  }
+  (void)vt_tiles;
+  const int R = nq * G;
+  const int q_off = nkv - nq;
   const int r0 = rt * ROWS;
-  const int i_hi = min(a.n_q - 1, (r0 + ROWS - 1) / G);
+  const int i_hi = min(nq - 1, (r0 + ROWS - 1) / G);
   const int p_lo = q_off + r0 / G;                      // smallest position here
   const int p_hi = q_off + i_hi;
   const int n_tiles = (p_hi + TK) / TK;
   const int n_full = (p_lo + 1) / TK;                   // tiles with no masked key
 
   const size_t kstride = (size_t)a.h_kv * D;
-  const __bf16* kseq = a.k + ((size_t)b * a.n_kv * a.h_kv + g) * D;
-  const __bf16* vtseq = a.vt + ((size_t)b * a.h_kv + g) * a.vt_tiles * (size_t)(D * TK);
+  const __bf16* kseq = a.k + (ktok0 * a.h_kv + g) * D;
+  const __bf16* vtseq = a.vt + vt_tile0 * (size_t)(D * TK);
+  const __bf16* qseq = a.q + qtok0 * a.h_q * D;
+  __bf16* oseq = a.o + qtok0 * a.h_q * D;
+  float* stats = a.stats + st0;
+  float* lse = a.lse ? a.lse + (a.vl.n > 0 ? (size_t)a.h_q * qtok0 : st0) : nullptr;
 
   // ---- Q fragments and row positions ----
   Frag<__bf16, D> qf[RBW];
@@ -145,7 +184,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     const int r = r0 + wave * 16 * RBW + rb * 16 + l16;
     if (r < R) {
       const int i = r / G, hh = r - (r / G) * G;
-      load_slice<__bf16, D>(qf[rb], a.q + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D, lane);
+      load_slice<__bf16, D>(qf[rb], qseq + ((size_t)i * a.h_q + g * G + hh) * D, lane);
       row_pos[rb] = q_off + i;
     } else {
       zero_slice<__bf16, D>(qf[rb]);
@@ -162,7 +201,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       const int slot = (wave * CPT + t) * 64 + lane;
       const int r = slot >> 4, pc = slot & 15;
       const int c = pc ^ kswz(r);
-      const int key = min(j0 + r, a.n_kv - 1);
+      const int key = min(j0 + r, nkv - 1);
       const __bf16* src = kseq + (size_t)key * kstride + c * 8;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
     }
@@ -323,7 +362,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
   }
 
-  const size_t plane = (size_t)a.B * a.h_q * a.n_q;
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     float l = l_s[rb] - l_c[rb];
@@ -334,7 +372,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     const int i = r / G, hh = r - (r / G) * G;
     const int h = g * G + hh;
     const float inv = 1.f / l;
-    __bf16* orow = a.o + (((size_t)b * a.n_q + i) * a.h_q + h) * D + 4 * grp;
+    __bf16* orow = oseq + ((size_t)i * a.h_q + h) * D + 4 * grp;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       __attribute__((ext_vector_type(4))) __bf16 w4;
@@ -343,16 +381,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       *reinterpret_cast<decltype(w4)*>(orow + db * 16) = w4;
     }
     if (grp == 0) {
-      const size_t si = ((size_t)b * a.h_q + h) * a.n_q + i;
-      a.stats[si] = m_run[rb];
-      a.stats[plane + si] = l;
-      a.stats[2 * plane + si] = 1.f / l;
-      if (a.lse) a.lse[si] = (m_run[rb] + log2f(l)) * LN2;
+      const size_t si = (size_t)h * nq + i;
+      stats[si] = m_run[rb];
+      stats[plane + si] = l;
+      stats[2 * plane + si] = 1.f / l;
+      if (lse) lse[si] = (m_run[rb] + log2f(l)) * LN2;
     }
   }
 }
 
 bool prefill_uses_vt(const Shape& s) { return s.bf16 && s.head_dim == D; }
+
+int prefill_rows_per_tile() { return 16 * 2 * FWD_WAVES; }
 
 
 int vt_keys_for(int n_kv) { return (n_kv + TK - 1) / TK * TK; }
@@ -395,7 +435,12 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   a.n_rt = (a.n_q * G + rows - 1) / rows;
-  const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
+  dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
+  if (p.vl) {
+    a.vl = *p.vl;
+    grid = dim3((unsigned)((size_t)a.vl.tile0[a.vl.n] * a.h_kv));
+    if (a.vl.tile0[a.vl.n] == 0) return hipSuccess;
+  }
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV, NST>), grid, dim3(64 * NWV), smem_bytes, st,
                      a);
   return hipGetLastError();

@@ -679,10 +679,64 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
 
 namespace {
 
+// Workspace of a variable-length batch on the bf16 / head_dim 128 path:
+// every prefill-shaped sequence (two or more queries) shares one full-
+// attention launch, so their statistics (one 3 x h_q x n_q block per
+// sequence, at 3 * h_q * cu_q[b]) and transposed V copies coexist; the
+// score chunk (rows x the longest score row) follows. One-query sequences
+// run afterwards on the decode path and reuse the workspace from the start.
+struct VarlenLayout {
+  size_t stats = 0, vt = 0, scores = 0;    // byte offsets
+  size_t stride = 0;                       // floats per score row
+  int chunk_rows = 0;
+  int max_nq = 0;
+  size_t min_bytes = 0, pref_bytes = 0;    // prefill part only
+};
+
+bool varlen_single_launch(const hs2_problem& p) {
+  hs2::Shape s = shape_of(p);
+  return hs2::prefill_uses_vt(s);
+}
+
+VarlenLayout varlen_layout(const hs2_problem& p, const int32_t* cu_q, const int32_t* cu_kv,
+                           size_t ws_bytes) {
+  VarlenLayout l;
+  const size_t total_q = (size_t)cu_q[p.batch];
+  size_t vt_tiles = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    const int nq = cu_q[b + 1] - cu_q[b], nkv = cu_kv[b + 1] - cu_kv[b];
+    if (nq < 2) continue;
+    hs2_problem pb = p;
+    pb.batch = 1; pb.n_q = nq; pb.n_kv = nkv;
+    l.stride = std::max(l.stride, score_stride(pb));
+    l.max_nq = std::max(l.max_nq, nq);
+    vt_tiles += (size_t)p.h_kv * (hs2::vt_keys_for(nkv) / 64);
+  }
+  if (l.max_nq == 0) return l;
+  size_t off = 0;
+  l.stats = off;
+  off += align_up((size_t)3 * p.h_q * total_q * sizeof(float));
+  l.vt = off;
+  off += align_up(vt_tiles * 64 * p.head_dim * 2);
+  l.scores = off;
+  const size_t row_b = std::max<size_t>(l.stride, 1) * sizeof(float);
+  l.min_bytes = off + align_up(row_b);
+  size_t pref_rows = std::max<size_t>(128, CHUNK_TARGET / row_b / 128 * 128);
+  pref_rows = std::min<size_t>(pref_rows, ((size_t)l.max_nq + 127) / 128 * 128);
+  l.pref_bytes = off + align_up(pref_rows * row_b);
+  if (ws_bytes != SIZE_MAX && ws_bytes >= l.min_bytes) {
+    size_t rows = (ws_bytes - off) / row_b;
+    if (rows >= 128) rows = rows / 128 * 128;
+    rows = std::min<size_t>(rows, (size_t)l.max_nq);
+    l.chunk_rows = (int)std::max<size_t>(rows, 1);
+  }
+  return l;
+}
+
 // Variable-length batches: sequence b owns queries cu_q[b] .. cu_q[b+1] and
 // keys cu_kv[b] .. cu_kv[b+1] of the packed tensors. Checks the offsets and
 // every non-empty sequence's problem (batch 1, its own n_q and n_kv), and
-// returns the largest workspace any of them needs.
+// returns the workspace the batch needs.
 hs2_status check_varlen(const hs2_problem* p, const int32_t* cu_q, const int32_t* cu_kv,
                         size_t* min_bytes, size_t* pref_bytes, long long* total_q,
                         long long* total_kv) {
@@ -708,10 +762,138 @@ hs2_status check_varlen(const hs2_problem* p, const int32_t* cu_q, const int32_t
     mn = std::max(mn, m);
     pref = std::max(pref, pr);
   }
+  if (varlen_single_launch(*p)) {
+    // prefill-shaped sequences share the single-launch layout; one-query
+    // sequences keep their own (decode) layout, reusing the same bytes
+    size_t dmn = 0, dpref = 0;
+    for (int b = 0; b < p->batch; ++b) {
+      const int nq = cu_q[b + 1] - cu_q[b];
+      if (nq != 1) continue;
+      hs2_problem pb = *p;
+      pb.batch = 1; pb.n_q = 1; pb.n_kv = cu_kv[b + 1] - cu_kv[b];
+      size_t m = 0, pr = 0;
+      plan(pb, SIZE_MAX, nullptr, &m, &pr);
+      dmn = std::max(dmn, m);
+      dpref = std::max(dpref, pr);
+    }
+    const VarlenLayout vl = varlen_layout(*p, cu_q, cu_kv, SIZE_MAX);
+    mn = std::max(vl.min_bytes, dmn);
+    pref = std::max(vl.pref_bytes, dpref);
+  }
   if (min_bytes) *min_bytes = mn;
   if (pref_bytes) *pref_bytes = pref;
   if (total_q) *total_q = cu_q[p->batch];
   if (total_kv) *total_kv = cu_kv[p->batch];
+  return HS2_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// The prefill-shaped sequences of a bf16 / head_dim 128 variable-length
+// batch: V transposes per sequence, one full-attention launch per group of
+// up to VARLEN_MAX_SEQS sequences (all their row tiles fill the chip
+// together), then per sequence the chunked score + selection and the
+// sparse layers.
+hs2_status run_varlen_prefill(const hs2_problem& p, int32_t n_sparse_layers,
+                              const int32_t* cu_q, const int32_t* cu_kv, const void* q_full,
+                              const void* q_sparse, const void* k, const void* v, void* o_full,
+                              void* o_sparse, int32_t* idx, float* lse, void* ws, size_t ws_bytes,
+                              size_t layer_elems, hipStream_t st) {
+  const VarlenLayout vl = varlen_layout(p, cu_q, cu_kv, ws_bytes);
+  if (vl.max_nq == 0) return HS2_OK;
+  if (ws_bytes < vl.min_bytes) return fail(HS2_ERR_WORKSPACE, "workspace too small");
+  const size_t esz = 2;
+  const size_t qrow = (size_t)p.h_q * p.head_dim, krow = (size_t)p.h_kv * p.head_dim;
+  const int width = index_width(p);
+  const int G = p.h_q / p.h_kv;
+  const int rows_per_tile = hs2::prefill_rows_per_tile();
+  float* stats = fptr(ws, vl.stats);
+  float* scores = fptr(ws, vl.scores);
+  char* vt = (char*)ws + vl.vt;
+  const bool block_mode = p.select == HS2_SELECT_BLOCK;
+  auto sub = [&](int b) {
+    hs2_problem pb = p;
+    pb.batch = 1; pb.n_q = cu_q[b + 1] - cu_q[b]; pb.n_kv = cu_kv[b + 1] - cu_kv[b];
+    return pb;
+  };
+  // V transposes, and the groups of the single launches
+  std::vector<int> seqs;
+  std::vector<int> vt0(p.batch, 0);
+  int vt_tiles = 0;
+  for (int b = 0; b < p.batch; ++b) {
+    if (cu_q[b + 1] - cu_q[b] < 2) continue;
+    const hs2_problem pb = sub(b);
+    seqs.push_back(b);
+    vt0[b] = vt_tiles;
+    hs2::FwdPlan tf;
+    tf.s = shape_of(pb);
+    tf.v = (const char*)v + (size_t)cu_kv[b] * krow * esz;
+    tf.vt = vt + (size_t)vt_tiles * 64 * p.head_dim * esz;
+    tf.vt_keys = hs2::vt_keys_for(pb.n_kv);
+    vt_tiles += p.h_kv * (tf.vt_keys / 64);
+    PassTimer t(st, HS2_PASS_LAYOUT);
+    HIP_TRY(hs2::launch_v_transpose(tf, st), "V transpose");
+  }
+  // sequences in batch order: the work-groups of one sequence then run
+  // together and share its K/V in L2 (dispatching the longest contexts
+  // first measured 15 % slower on a batch of agent turns)
+  const std::vector<int>& order = seqs;
+  for (size_t g0 = 0; g0 < order.size(); g0 += hs2::VARLEN_MAX_SEQS) {
+    hs2::VarlenSeqs d;
+    d.n = (int)std::min<size_t>(hs2::VARLEN_MAX_SEQS, order.size() - g0);
+    d.tile0[0] = 0;
+    for (int s = 0; s < d.n; ++s) {
+      const int b = order[g0 + s];
+      d.q0[s] = cu_q[b];
+      d.kv0[s] = cu_kv[b];
+      d.nq[s] = cu_q[b + 1] - cu_q[b];
+      d.nkv[s] = cu_kv[b + 1] - cu_kv[b];
+      d.vt0[s] = vt0[b];
+      d.tile0[s + 1] = d.tile0[s] + (d.nq[s] * G + rows_per_tile - 1) / rows_per_tile;
+    }
+    hs2::FwdPlan f;
+    f.s = shape_of(p);
+    f.q = q_full; f.k = k; f.v = v; f.o = o_full; f.stats = stats; f.lse = lse;
+    f.vt = vt; f.vt_keys = 64;
+    f.vl = &d;
+    PassTimer t(st, HS2_PASS_FULL);
+    HIP_TRY(hs2::launch_attn_fwd_prefill(f, st), "full attention (packed sequences)");
+  }
+  // per sequence: score chunks + selection, then the sparse layers
+  for (int b : seqs) {
+    const hs2_problem pb = sub(b);
+    const hs2::Shape s1 = shape_of(pb);
+    const char* qb = (const char*)q_full + (size_t)cu_q[b] * qrow * esz;
+    const char* kb = (const char*)k + (size_t)cu_kv[b] * krow * esz;
+    const char* vb = (const char*)v + (size_t)cu_kv[b] * krow * esz;
+    int32_t* ib = idx + (size_t)cu_q[b] * width;
+    float* sb = stats + (size_t)3 * p.h_q * cu_q[b];
+    for (int q0 = 0; q0 < pb.n_q; q0 += vl.chunk_rows) {
+      const int rows = std::min(vl.chunk_rows, pb.n_q - q0);
+      hs2::ScorePlan sc;
+      sc.s = s1; sc.b = 0; sc.q0 = q0; sc.rows = rows; sc.window = p.window;
+      sc.q = qb; sc.k = kb; sc.stats = sb; sc.scores = scores; sc.score_stride = vl.stride;
+      {
+        PassTimer t(st, HS2_PASS_SCORE);
+        HIP_TRY(hs2::launch_score_prefill(sc, st), "score");
+      }
+      hs2::SelectPlan sp;
+      sp.rows = rows; sp.flat0 = q0; sp.n_q = pb.n_q; sp.n_kv = pb.n_kv;
+      sp.top_k = p.top_k; sp.window = p.window; sp.width = width;
+      sp.block_mode = block_mode; sp.block_size = p.block_size; sp.top_blocks = p.top_blocks;
+      sp.scores = scores; sp.score_stride = vl.stride; sp.idx = ib;
+      {
+        PassTimer t(st, HS2_PASS_SELECT);
+        HIP_TRY(hs2::launch_select(sp, st), "select");
+      }
+    }
+    if (n_sparse_layers > 0)
+      HS2_TRY(run_sparse(pb, n_sparse_layers, (const char*)q_sparse + (size_t)cu_q[b] * qrow * esz,
+                         kb, vb, ib, (char*)o_sparse + (size_t)cu_q[b] * qrow * esz, st, nullptr,
+                         layer_elems));
+  }
   return HS2_OK;
 }
 
@@ -757,8 +939,13 @@ hs2_status hs2_block_forward_varlen(const hs2_problem* p, int32_t n_sparse_layer
   const size_t krow = (size_t)p->h_kv * p->head_dim;          // elements per key token
   const int width = index_width(*p);
   const size_t layer_elems = (size_t)total_q * qrow;
+  const bool single = varlen_single_launch(*p);
+  if (single)
+    HS2_TRY(run_varlen_prefill(*p, n_sparse_layers, cu_q, cu_kv, q_full, q_sparse, k, v, o_full,
+                               o_sparse, idx, lse, workspace, workspace_bytes, layer_elems, st));
   for (int b = 0; b < p->batch; ++b) {
     const int q0 = cu_q[b], nq = cu_q[b + 1] - cu_q[b];
+    if (single && nq >= 2) continue;              // done in the single launch
     const int k0 = cu_kv[b], nkv = cu_kv[b + 1] - cu_kv[b];
     if (nq == 0) continue;
     hs2_problem pb = *p;

@@ -54,6 +54,22 @@ struct Shape {
   float scale_log2;       // softmax scale * log2(e)
 };
 
+// A launch over packed sequences of different lengths (bf16 / head_dim 128
+// prefill): sequence s has nq[s] queries from token q0[s] and nkv[s] keys
+// from token kv0[s] of the packed tensors, its transposed V starts vt0[s]
+// 64-key tiles (all KV heads counted) into the workspace copy, and its
+// row tiles are work-group rows tile0[s] .. tile0[s+1] (times h_kv).
+constexpr int VARLEN_MAX_SEQS = 32;
+struct VarlenSeqs {
+  int n = 0;
+  int tile0[VARLEN_MAX_SEQS + 1];
+  int q0[VARLEN_MAX_SEQS], kv0[VARLEN_MAX_SEQS];
+  int nq[VARLEN_MAX_SEQS], nkv[VARLEN_MAX_SEQS];
+  int vt0[VARLEN_MAX_SEQS];
+};
+// rows (query, head-of-group pairs) per work-group of the bf16 prefill kernel
+int prefill_rows_per_tile();
+
 // Pass 1 (full causal attention) for prefill-shaped calls.
 // stats: [3][batch][h_q][n_q] floats: m2 (row max in log2 units), l (row sum
 // of 2^(t - m2)) and 1/l; lse (nullable): natural-log LSE.
@@ -68,6 +84,11 @@ struct FwdPlan {
   float* stats;
   float* lse;
   void* vt; int vt_keys;
+  // non-NULL (bf16 / head_dim 128 only): packed sequences; s.batch, s.n_q,
+  // s.n_kv are then unused, stats / lse hold one block per sequence (stats:
+  // 3 planes of h_q x nq at 3 * h_q * q0; lse: h_q x nq at h_q * q0), and
+  // vt must already hold every sequence's transposed V
+  const VarlenSeqs* vl = nullptr;
 };
 bool prefill_uses_vt(const Shape& s);
 int vt_keys_for(int n_kv);
