@@ -24,7 +24,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
 # in the order of the library's pass-timer slots
 PASSES = ["full_attention", "score", "select", "sparse_attention", "v_layout",
-          "bwd_prep", "bwd_sparse", "bwd_dkdv", "bwd_dq"]
+          "bwd_prep", "bwd_sparse", "bwd_dkdv", "bwd_dq", "kv_stage"]
 
 
 def log(*a):
@@ -426,11 +426,14 @@ def backward_bench(args):
     print(json.dumps(rec), flush=True)
 
 
-def varlen_bench(args):
+def varlen_bench(args, paged=False):
     """A packed batch of agent turns of different lengths
     (hs2_block_forward_varlen): 8 sequences with contexts of 32K-262K keys,
     each appending a new chunk of 256-4096 tokens (lengths drawn from a
-    seeded generator), the 8K-on-262K workload's heads and 5 sparse layers."""
+    seeded generator), the 8K-on-262K workload's heads and 5 sparse layers.
+    paged: the same turns through hs2_block_forward_paged, the cached
+    context in shuffled 256-row pages of a pool; every step appends the
+    chunks at the same positions, so each step sees the same cache."""
     import dataclasses
     import numpy as np
     import torch
@@ -454,18 +457,57 @@ def varlen_bench(args):
     q, qs = inp["q_full"][0].contiguous(), inp["q_sparse"][:, 0].contiguous()
     k, v = inp["k"][0].contiguous(), inp["v"][0].contiguous()
     kw = dict(top_k=w.top_k, window=w.window)
-    p = hs2.problem(q.dtype, n_seq, 1, 1, w.h_q, w.h_kv, w.d, **kw)
-    _, pref = hs2.workspace_size_varlen(p, cu_q, cu_kv)
-    ws = torch.empty(pref, dtype=torch.uint8, device=dev)
+    if paged:
+        # sequence b's positions 0 .. nkv[b] - 1 live in pages of 256 rows,
+        # handed out in a seeded shuffled order; its last nq[b] keys are the
+        # chunk the call appends, the rest are already cached
+        ps = 256
+        mp = int(-(-nkv.max() // ps))
+        n_pages = int(sum(-(-n // ps) for n in nkv.tolist())) + 1
+        perm = rng.permutation(n_pages)
+        table = np.zeros((n_seq, mp), dtype=np.int32)
+        pool_idx = np.zeros(tk, dtype=np.int64)
+        used = 0
+        for b, n in enumerate(nkv.tolist()):
+            np_b = -(-n // ps)
+            table[b, :np_b] = perm[used:used + np_b]
+            used += np_b
+            j = np.arange(n)
+            pool_idx[cu_kv[b]:cu_kv[b] + n] = table[b, j // ps].astype(np.int64) * ps + j % ps
+        k_pool = torch.zeros((n_pages * ps, w.h_kv, w.d), dtype=k.dtype, device=dev)
+        v_pool = torch.zeros_like(k_pool)
+        pidx = torch.from_numpy(pool_idx).to(dev)
+        k_pool[pidx] = k
+        v_pool[pidx] = v
+        new_rows = torch.from_numpy(np.concatenate(
+            [np.arange(cu_kv[b + 1] - nq[b], cu_kv[b + 1]) for b in range(n_seq)])).to(dev)
+        k_new, v_new = k[new_rows].contiguous(), v[new_rows].contiguous()
+        del k, v, inp
+        lens = (nkv - nq).tolist()
+        table_d = torch.from_numpy(table).to(dev)
+        p, pages = hs2._paged_problem(q, k_pool, table_d, ps, n_seq, kw)
+        _, pref = hs2.workspace_size_paged(p, pages, cu_q, lens)
+        ws = torch.empty(pref, dtype=torch.uint8, device=dev)
+
+        def run():
+            hs2.block_forward_paged(q, qs, k_new, v_new, k_pool, v_pool, table_d, ps, cu_q, lens,
+                                    workspace=ws, **kw)
+    else:
+        p = hs2.problem(q.dtype, n_seq, 1, 1, w.h_q, w.h_kv, w.d, **kw)
+        _, pref = hs2.workspace_size_varlen(p, cu_q, cu_kv)
+        ws = torch.empty(pref, dtype=torch.uint8, device=dev)
+
+        def run():
+            hs2.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, workspace=ws, **kw)
     for _ in range(args.warmup):
-        hs2.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, workspace=ws, **kw)
+        run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     lib.hs2_profile_enable(1)
     ev0.record(stream)
     for _ in range(args.steps):
-        hs2.block_forward_varlen(q, qs, k, v, cu_q, cu_kv, workspace=ws, **kw)
+        run()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = (ctypes.c_double * len(PASSES))()
@@ -481,6 +523,11 @@ def varlen_bench(args):
         ws_ = dataclasses.replace(base, batch=1, n_q=int(a_), n_kv=int(b_))
         for name, (bound, amount) in algorithmic_work(ws_).items():
             work[name] = (bound, work.get(name, (bound, 0.0))[1] + amount)
+        # staging (paged): K and V rows read once (pool or new rows) and
+        # written once to the staging copy, and the new rows to the pool
+        row_b = w.h_kv * w.d * (2 if w.dtype == "bf16" else 4)
+        stage = 2.0 * row_b * (2 * b_ + a_) if a_ >= 2 else 2.0 * row_b * 2 * a_
+        work["kv_stage"] = ("hbm", work.get("kv_stage", ("hbm", 0.0))[1] + stage)
     peak_mfma = PEAK_MFMA_TFLOPS[w.dtype]
     passes = {}
     for i, name in enumerate(PASSES):
@@ -500,12 +547,16 @@ def varlen_bench(args):
                             "frac": round(ach / PEAK_HBM_GBS, 4)}
     dom = max(passes, key=lambda n: passes[n]["ms"])
     d = passes[dom]
-    rec = {"metric": "varlen batch tokens/s (packed agent turns of different lengths)",
+    metric = "varlen batch tokens/s (packed agent turns of different lengths)"
+    if paged:
+        metric = "paged chunked-prefill tokens/s (agent turns appended to a paged KV pool)"
+    rec = {"metric": metric,
            "value": round(tq / (ms_step / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
            "data": "synthetic (seeded lengths and values; no datasets)",
-           "config": {"workload": "agent_turns_bf16_varlen", "sequences": n_seq,
+           "config": {"workload": "agent_turns_bf16_" + ("paged256" if paged else "varlen"),
+                      "sequences": n_seq,
                       "n_q": nq.tolist(), "n_kv": nkv.tolist(), "h_q": w.h_q, "h_kv": w.h_kv,
                       "head_dim": w.d, "top_k": w.top_k, "window": w.window,
                       "sparse_layers": w.n_sparse, "parallelism": "single GPU"},
@@ -533,6 +584,9 @@ def main():
                          "64-token block ablation")
     ap.add_argument("--varlen", action="store_true",
                     help="time a packed batch of agent turns of different lengths instead")
+    ap.add_argument("--paged", action="store_true",
+                    help="the --varlen batch through the paged-pool entry point (chunked "
+                         "prefill over 256-row pages) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fixed index sets) instead")
     ap.add_argument("--bwd-config", type=int, default=2,
@@ -569,8 +623,8 @@ def main():
     if args.backward:
         backward_bench(args)
         return
-    if args.varlen:
-        varlen_bench(args)
+    if args.varlen or args.paged:
+        varlen_bench(args, paged=args.paged)
         return
     from synth import CONFIGS, make_inputs
     from token_level_sparse_pass_amd import hs2

@@ -235,6 +235,49 @@ hs2_status hs2_block_forward_varlen(const hs2_problem* p, int32_t n_sparse_layer
                                     void* o_sparse, int32_t* idx, float* lse,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked prefill over a paged KV pool (batched agent turns: each sequence
+ * appends a chunk of new tokens, a user message or a tool result, after its
+ * own cached context, and every layer of the block reads the one cache;
+ * hitechexpert.top, section "Two-Level KV Sharing"). Pool and page table as
+ * hs2_kv_pages; p->n_kv = pages->max_pages * pages->page_size is the
+ * capacity of one sequence, p->batch the number of sequences, p->n_q unused.
+ *   cu_q          HOST [batch + 1] int32 offsets from 0, not decreasing:
+ *                 sequence b's n_q(b) new tokens are packed rows
+ *                 cu_q[b] .. cu_q[b+1]
+ *   lens          HOST [batch]: tokens sequence b holds before the call;
+ *                 lens[b] + n_q(b) <= p->n_kv, else HS2_ERR_SHAPE before
+ *                 any launch. The caller advances it.
+ *   k_new, v_new  DEVICE [total_q, h_kv, head_dim]: the new tokens' rows
+ *   q_full, o_full DEVICE [total_q, h_q, head_dim]
+ *   q_sparse, o_sparse DEVICE [n_sparse_layers, total_q, h_q, head_dim]
+ *   k_pool, v_pool DEVICE pools (written: the new rows land at positions
+ *                 lens[b] .. lens[b] + n_q(b) - 1 of sequence b's pages)
+ *   idx           DEVICE [total_q, hs2_index_width(p)]: positions within
+ *                 the sequence
+ *   lse (nullable) DEVICE float, as hs2_block_forward_varlen
+ * The results are those of hs2_block_forward_varlen over the sequences'
+ * logical K/V (n_kv(b) = lens[b] + n_q(b), query i at lens[b] + i). A
+ * sequence with two or more new tokens is first copied, K and V rows 0 ..
+ * n_kv(b) - 1, to contiguous staging buffers at the front of the workspace,
+ * which its full layer, score pass and sparse layers then read: prefill is
+ * bound by matrix math, and the copy is small beside it. A one-token
+ * sequence reads the pool in place (the decode path); a batch of decode
+ * steps alone is better served by hs2_decode_step_paged, one launch per pass
+ * for all of them. Pages that a sequence's new tokens are written to must not
+ * be read by another sequence of the same call (shared prefix pages may be).
+ * Workspace: hs2_workspace_size_paged (16-byte aligned). */
+hs2_status hs2_workspace_size_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                   const int32_t* cu_q, const int32_t* lens,
+                                   size_t* min_bytes, size_t* preferred_bytes);
+hs2_status hs2_block_forward_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                   int32_t n_sparse_layers, const int32_t* cu_q,
+                                   const int32_t* lens, const void* q_full,
+                                   const void* q_sparse, const void* k_new,
+                                   const void* v_new, void* k_pool, void* v_pool,
+                                   void* o_full, void* o_sparse, int32_t* idx,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Backward pass of the block, for fine-tuning (hitechexpert.top, section
  * "Performance Gains: Cost, Speed, and Long-Context Capabilities": the
  * compared models are fine-tuned alike). The index sets are held fixed (a
@@ -273,7 +316,8 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
  * (selection), HS2_PASS_SPARSE (sparse layers), HS2_PASS_LAYOUT (the
  * copy of V into the workspace in key-tile-major transposed order that the
  * bf16 / head_dim 128 prefill kernel reads; absent on every other path),
- * and the four HS2_PASS_BWD_* steps of hs2_block_backward.
+ * the four HS2_PASS_BWD_* steps of hs2_block_backward, and HS2_PASS_KV_STAGE
+ * (hs2_block_forward_paged's append and staging copy).
  * hs2_profile_enable(1)
  * starts a fresh record and (0) stops recording. hs2_profile_read waits for
  * the recorded events, then writes the summed milliseconds and the number of
@@ -289,7 +333,8 @@ typedef enum {
   HS2_PASS_BWD_SPARSE = 6,  /* backward: the sparse layers                   */
   HS2_PASS_BWD_DKDV = 7,    /* backward: the full layer's dK, dV             */
   HS2_PASS_BWD_DQ = 8,      /* backward: the full layer's dQ                 */
-  HS2_N_PASSES = 9
+  HS2_PASS_KV_STAGE = 9,    /* paged prefill: new rows in, staging copies    */
+  HS2_N_PASSES = 10
 } hs2_pass;
 hs2_status hs2_profile_enable(int32_t on);
 hs2_status hs2_profile_read(double* ms, int64_t* launches);

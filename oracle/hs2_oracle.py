@@ -341,6 +341,32 @@ def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table
     return decode_step(q_full, q_sparse, k_new, v_new, kc, vc, lens, **kw)
 
 
+def block_forward_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table, page_size,
+                        cu_q, lens, **kw):
+    """Chunked prefill over a paged pool ("Two-Level KV Sharing": one cache
+    serves every layer of the block). Sequence b holds lens[b] tokens, read
+    through its page-table row as in decode_step_paged, and appends its new
+    tokens, packed rows cu_q[b]..cu_q[b+1] of k_new / v_new; its queries sit
+    at positions lens[b] .. lens[b] + n_q(b) - 1. The block is then
+    block_forward_varlen over those logical K/V rows. Returns that dict, plus
+    the pool rows the new tokens land in ("new_rows", one array per
+    sequence)."""
+    k_pool, v_pool = np.asarray(k_pool), np.asarray(v_pool)
+    k_new, v_new = np.asarray(k_new), np.asarray(v_new)
+    ks, vs, cu_kv, new_rows = [], [], [0], []
+    for b in range(len(cu_q) - 1):
+        n, q0, q1 = int(lens[b]), int(cu_q[b]), int(cu_q[b + 1])
+        rows = pool_rows(page_table, page_size, b, n + (q1 - q0))
+        ks += [k_pool[rows[:n]], k_new[q0:q1]]
+        vs += [v_pool[rows[:n]], v_new[q0:q1]]
+        cu_kv.append(cu_kv[-1] + n + (q1 - q0))
+        new_rows.append(rows[n:])
+    out = block_forward_varlen(q_full, q_sparse, np.concatenate(ks), np.concatenate(vs), cu_q,
+                               np.asarray(cu_kv), **kw)
+    out["new_rows"] = new_rows
+    return out
+
+
 # ----------------------------------------------------------------------------
 # the same definitions, streamed over K/V chunks for a few sampled query rows
 # (large contexts: the full score matrix never exists)

@@ -291,3 +291,47 @@ def test_varlen_checks_and_workspace():
     keys = (ctypes.c_int32 * 2)(0, 300)
     assert lib.hs2_workspace_size_varlen(ctypes.byref(wide), one, keys,
                                          ctypes.byref(ctypes.c_size_t()), None) == 3
+
+
+def test_paged_prefill_workspace_and_rejections():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    ps, mp = 64, 50
+    p = base_problem(batch=3, n_kv=ps * mp)
+    pages = hs2.KvPages(FAKE, ps, mp, 200)
+    cu_q, lens = [0, 100, 101, 301], [400, 999, 0]
+    mn, pref = hs2.workspace_size_paged(p, pages, cu_q, lens)
+    # two staging buffers hold the rows of the sequences with two or more new
+    # tokens (500 + 200 rows of 2 * 128 bf16), then the variable-length
+    # batch of the logical lengths (n_kv(b) = lens[b] + n_q(b))
+    up = lambda x: (x + 255) // 256 * 256
+    stage = up((500 + 200) * 2 * 128 * 2)
+    vmn, vpref = hs2.workspace_size_varlen(p, cu_q, [0, 500, 1500, 1700])
+    assert (mn, pref) == (2 * stage + vmn, 2 * stage + vpref)
+    # one-token sequences are not staged
+    mn1, _ = hs2.workspace_size_paged(p, pages, [0, 1, 2, 3], lens)
+    assert mn1 == hs2.workspace_size_varlen(p, [0, 1, 2, 3], [0, 401, 1401, 1402])[0]
+
+    def call(cq=cu_q, ln=lens, pg=pages, ws_bytes=pref, **over):
+        a = dict(q_full=FAKE, q_sparse=FAKE, k_new=FAKE, v_new=FAKE, k_pool=FAKE, v_pool=FAKE,
+                 o_full=FAKE, o_sparse=FAKE, idx=FAKE, lse=None, ws=FAKE)
+        a.update(over)
+        arr = lambda x: None if x is None else (ctypes.c_int32 * len(x))(*x)
+        return lib.hs2_block_forward_paged(
+            ctypes.byref(p), None if pg is None else ctypes.byref(pg), 2, arr(cq), arr(ln),
+            *[vp(a[n]) for n in ("q_full", "q_sparse", "k_new", "v_new", "k_pool", "v_pool",
+                                 "o_full", "o_sparse", "idx", "lse", "ws")], ws_bytes, None)
+
+    assert call(pg=None) == 1
+    assert call(pg=hs2.KvPages(FAKE, 48, mp, 200)) == 2           # page size
+    assert call(pg=hs2.KvPages(FAKE, ps, mp - 1, 200)) == 2       # capacity != n_kv
+    assert call(cq=None) == 1 and call(ln=None) == 1
+    assert call(cq=[1, 100, 101, 301]) == 2                       # must start at 0
+    assert call(cq=[0, 100, 99, 301]) == 2                        # decreasing
+    assert call(ln=[3150, 999, 0]) == 2                           # 3150 + 100 > 3200
+    assert "capacity" in lib.hs2_last_error().decode()
+    assert call(ln=[-1, 999, 0]) == 2
+    assert call(ws_bytes=mn - 1) == 4
+    assert call(k_new=None) == 1 and call(v_pool=None) == 1
+    assert call(idx=FAKE + 4) == 5
+    assert call(ws=FAKE + 8) == 5

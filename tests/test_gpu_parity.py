@@ -612,3 +612,107 @@ def test_varlen_equal_lengths_match_batched_call(gpu_lib):
     assert torch.equal(packed["o_full"], batched["o_full"].reshape(B * nq, 8, 128))
     assert torch.equal(packed["o_sparse"], batched["o_sparse"].reshape(2, B * nq, 8, 128))
     assert torch.equal(packed["lse"], batched["lse"].reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over a paged pool (batched turns appending to their caches)
+# ---------------------------------------------------------------------------
+def _paged_turn_inputs(dtype, hq, hkv, d, chunks, L, turn, cid):
+    tq = int(sum(chunks))
+    w = small(f"paged_turn{turn}", dtype, 1, tq, tq, hq, hkv, d, 64, 16, L=L, cid=cid + turn)
+    x = make_inputs(w, device="cuda")
+    return dict(q_full=x["q_full"][0].contiguous(), q_sparse=x["q_sparse"][:, 0].contiguous(),
+                k_new=x["k"][0].contiguous(), v_new=x["v"][0].contiguous())
+
+
+def _paged_pool(dtype, hq, hkv, d, n_rows, cid):
+    pool = make_inputs(small("pool", dtype, 1, 1, n_rows, hq, hkv, d, 64, 16, L=0, cid=cid),
+                       device="cuda", sparse_layers=0)
+    return pool["k"][0].clone(), pool["v"][0].clone()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,ps,lens,turns", [
+    ("bf16", 8, 2, 128, 64, [700, 1150, 0, 64, 333, 2000],
+     [[300, 1, 200, 0, 37, 128], [1, 64, 130, 5, 0, 1]]),
+    ("fp32", 4, 1, 64, 32, [64, 200, 90], [[64, 133, 1], [1, 2, 40]]),
+], ids=["bf16_d128", "fp32_d64"])
+def test_paged_prefill_turns(gpu_lib, dtype, hq, hkv, d, ps, lens, turns):
+    # two turns of a batch: each sequence appends a chunk (or one token, or
+    # nothing) to its paged cache; pool rows outside the sequences' pages hold
+    # unrelated values that must never be read
+    top_k, window, L = 64, 16, 2
+    B = len(lens)
+    final = [n + sum(t[b] for t in turns) for b, n in enumerate(lens)]
+    mp = max(final) // ps + 1
+    n_pages = B * mp + 3
+    table = np.random.default_rng(21).permutation(n_pages)[:B * mp].reshape(B, mp)
+    table = table.astype(np.int32)
+    table_d = torch.from_numpy(table).cuda()
+    k_pool, v_pool = _paged_pool(dtype, hq, hkv, d, n_pages * ps, cid=14)
+    kh, vh = host(k_pool), host(v_pool)
+    tol = TOL[dtype]
+    for turn, chunks in enumerate(turns):
+        cu_q = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+        x = _paged_turn_inputs(dtype, hq, hkv, d, chunks, L, turn, cid=15)
+        say("turn", turn, dtype, "lens", lens, "chunks", chunks)
+        out = gpu_lib.block_forward_paged(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"],
+                                          k_pool, v_pool, table_d, ps, cu_q, lens, top_k=top_k,
+                                          window=window)
+        torch.cuda.synchronize()
+        xh = {n: host(t) for n, t in x.items()}
+        ref = O.block_forward_paged(xh["q_full"], xh["q_sparse"], xh["k_new"], xh["v_new"], kh,
+                                    vh, table, ps, cu_q, lens, top_k=top_k, window=window)
+        # the new rows are in their pages, and nothing else of the pool moved
+        for b in range(B):
+            rows = ref["new_rows"][b]
+            kh[rows] = xh["k_new"][cu_q[b]:cu_q[b + 1]]
+            vh[rows] = xh["v_new"][cu_q[b]:cu_q[b + 1]]
+        assert np.array_equal(host(k_pool), kh) and np.array_equal(host(v_pool), vh), "pool"
+        gi = out["idx"].cpu().numpy()
+        lse = out["lse"].cpu().numpy()
+        for b, nq in enumerate(chunks):
+            if nq == 0:
+                continue
+            q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+            pos = np.arange(nq) + lens[b]
+            tied = compare_index_rows(gi[q0:q1], ref["S"][b], pos, ref["idx"][q0:q1],
+                                      ref["tau"][b], window)
+            err = np.abs(as_np(out["o_full"][q0:q1]) - ref["o_full"][q0:q1]).max()
+            lerr = np.abs(lse[hq * q0:hq * q1].reshape(hq, nq) - ref["lse"][b]).max()
+            say("sequence", b, "o_full err", err, "lse err", lerr, "tied rows", len(tied))
+            assert err <= tol and lerr <= 1e-4
+            if not tied:
+                serr = np.abs(as_np(out["o_sparse"][:, q0:q1]) - ref["o_sparse"][:, q0:q1]).max()
+                assert serr <= tol
+        lens = [n + c for n, c in zip(lens, chunks)]
+
+
+def test_paged_prefill_matches_contiguous_varlen_call(gpu_lib):
+    # the same kernels on the same values: bit-identical to the
+    # variable-length call over the gathered logical K/V
+    hq, hkv, d, ps, L = 8, 2, 128, 64, 2
+    lens, chunks = [500, 0, 900, 77], [150, 300, 1, 64]
+    B = len(lens)
+    mp = 20
+    table = np.random.default_rng(22).permutation(B * mp + 1)[:B * mp].reshape(B, mp)
+    table = table.astype(np.int32)
+    k_pool, v_pool = _paged_pool("bf16", hq, hkv, d, (B * mp + 1) * ps, cid=17)
+    k0, v0 = k_pool.clone(), v_pool.clone()
+    cu_q = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    x = _paged_turn_inputs("bf16", hq, hkv, d, chunks, L, 0, cid=18)
+    kw = dict(top_k=64, window=16)
+    say("paged vs varlen", lens, chunks)
+    paged = gpu_lib.block_forward_paged(x["q_full"], x["q_sparse"], x["k_new"], x["v_new"],
+                                        k_pool, v_pool, torch.from_numpy(table).cuda(), ps, cu_q,
+                                        lens, **kw)
+    ks, vs = [], []
+    for b in range(B):
+        rows = torch.from_numpy(O.pool_rows(table, ps, b, lens[b])).cuda()
+        ks += [k0[rows], x["k_new"][cu_q[b]:cu_q[b + 1]]]
+        vs += [v0[rows], x["v_new"][cu_q[b]:cu_q[b + 1]]]
+    cu_kv = np.concatenate([[0], np.cumsum([n + c for n, c in zip(lens, chunks)])])
+    packed = gpu_lib.block_forward_varlen(x["q_full"], x["q_sparse"], torch.cat(ks).contiguous(),
+                                          torch.cat(vs).contiguous(), cu_q, cu_kv, **kw)
+    torch.cuda.synchronize()
+    for key in ("o_full", "o_sparse", "idx", "lse"):
+        assert torch.equal(paged[key], packed[key]), key

@@ -562,3 +562,59 @@ def test_varlen_sequences_are_independent():
     assert a["lse"][1] is None                     # the empty sequence
     # the one-query sequence sits at the last position of its 8 keys
     assert a["idx"][5][a["idx"][5] >= 0][-1] == 7
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill over a paged pool
+# ----------------------------------------------------------------------------
+def _paged_prefill_case(seed, lens, chunks, ps=8, mp=6, hq=4, hkv=2, d=8, L=2):
+    B = len(lens)
+    n_pages = B * mp + 3
+    table = np.random.default_rng(seed).permutation(n_pages)[:B * mp].reshape(B, mp)
+    cu_q = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int64)
+    tq = int(cu_q[-1])
+    return dict(q_full=rand((tq, hq, d), seed + 1), q_sparse=rand((L, tq, hq, d), seed + 2),
+                k_new=rand((tq, hkv, d), seed + 3), v_new=rand((tq, hkv, d), seed + 4),
+                k_pool=rand((n_pages * ps, hkv, d), seed + 5),
+                v_pool=rand((n_pages * ps, hkv, d), seed + 6),
+                page_table=table.astype(np.int32), page_size=ps, cu_q=cu_q, lens=lens)
+
+
+def test_paged_prefill_chunk_is_tail_of_full_prefill():
+    # a chunk appended after n cached tokens gives its queries the results
+    # they get as the last rows of a causal prefill over all n + chunk tokens
+    # (earlier queries change nothing for later ones)
+    c = _paged_prefill_case(200, [13, 0, 30], [7, 5, 1])
+    got = O.block_forward_paged(**c, top_k=4, window=3)
+    for b, n in enumerate(c["lens"]):
+        q0, q1 = int(c["cu_q"][b]), int(c["cu_q"][b + 1])
+        rows = O.pool_rows(c["page_table"], c["page_size"], b, n)
+        k = np.concatenate([c["k_pool"][rows], c["k_new"][q0:q1]])[None]
+        v = np.concatenate([c["v_pool"][rows], c["v_new"][q0:q1]])[None]
+        q = np.concatenate([rand((n, 4, 8), 210 + b), c["q_full"][q0:q1]])[None]
+        qs = np.concatenate([rand((2, n, 4, 8), 220 + b), c["q_sparse"][:, q0:q1]], axis=1)[:, None]
+        ref = O.block_forward(q, qs, k, v, top_k=4, window=3)
+        m = q1 - q0
+        np.testing.assert_allclose(got["o_full"][q0:q1], ref["o_full"][0, n:], atol=1e-12)
+        np.testing.assert_allclose(got["lse"][b], ref["lse"][0, :, n:], atol=1e-12)
+        np.testing.assert_array_equal(got["idx"][q0:q1], ref["idx"][0, n:])
+        np.testing.assert_allclose(got["o_sparse"][:, q0:q1], ref["o_sparse"][:, 0, n:],
+                                   atol=1e-12)
+        assert len(got["new_rows"][b]) == m
+
+
+def test_paged_prefill_one_token_is_the_paged_decode_step():
+    # one new token per sequence: the paged decode step
+    c = _paged_prefill_case(230, [9, 40, 0], [1, 1, 1])
+    got = O.block_forward_paged(**c, top_k=3, window=5)
+    want = O.decode_step_paged(c["q_full"][:, None], c["q_sparse"][:, :, None],
+                               c["k_new"][:, None], c["v_new"][:, None], c["k_pool"],
+                               c["v_pool"], c["page_table"], c["page_size"], c["lens"],
+                               top_k=3, window=5)
+    np.testing.assert_array_equal(got["o_full"], want["o_full"][:, 0])
+    np.testing.assert_array_equal(got["idx"], want["idx"][:, 0])
+    np.testing.assert_array_equal(got["o_sparse"], want["o_sparse"][:, :, 0])
+    # the new token of sequence b lands at position lens[b] of its pages
+    for b, n in enumerate(c["lens"]):
+        ps = c["page_size"]
+        assert got["new_rows"][b][0] == c["page_table"][b, n // ps] * ps + n % ps

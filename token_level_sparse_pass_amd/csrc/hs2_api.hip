@@ -456,6 +456,28 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers, cons
 
 namespace {
 
+// A paged pool's geometry; p.n_kv must be its per-sequence capacity.
+hs2_status check_pages(const hs2_problem& p, const hs2_kv_pages* pages, hs2::KvRows* kv) {
+  if (!pages) return fail(HS2_ERR_NULL, "pages is NULL");
+  if (!pages->page_table) return fail(HS2_ERR_NULL, "page_table is NULL");
+  const int ps = pages->page_size;
+  if (ps < 32 || (ps & (ps - 1)))
+    return fail(HS2_ERR_SHAPE, "page_size %d: a power of two >= 32 is needed", ps);
+  if (pages->max_pages < 1 || pages->n_pages < 1)
+    return fail(HS2_ERR_SHAPE, "max_pages %d, n_pages %d", pages->max_pages, pages->n_pages);
+  if ((long long)pages->max_pages * ps != p.n_kv)
+    return fail(HS2_ERR_SHAPE, "n_kv %d must be max_pages * page_size = %lld", p.n_kv,
+                (long long)pages->max_pages * ps);
+  if ((long long)pages->n_pages * ps > INT32_MAX)
+    return fail(HS2_ERR_UNSUPPORTED, "pool of %d pages of %d rows", pages->n_pages, ps);
+  *kv = contiguous_rows(p);
+  kv->table = pages->page_table;
+  kv->page_shift = __builtin_ctz((unsigned)ps);
+  kv->max_pages = pages->max_pages;
+  kv->n_pages = pages->n_pages;
+  return HS2_OK;
+}
+
 // Shared by the contiguous and paged decode steps: validate, set the
 // per-sequence key counts, append the new rows, run the block.
 hs2_status decode_step_impl(const hs2_problem* p, const hs2_kv_pages* pages,
@@ -467,23 +489,7 @@ hs2_status decode_step_impl(const hs2_problem* p, const hs2_kv_pages* pages,
   if (p->n_q != 1) return fail(HS2_ERR_SHAPE, "a decode step has one query per sequence (n_q %d)",
                                p->n_q);
   hs2::KvRows kv = contiguous_rows(*p);
-  if (pages) {
-    if (!pages->page_table) return fail(HS2_ERR_NULL, "page_table is NULL");
-    const int ps = pages->page_size;
-    if (ps < 32 || (ps & (ps - 1)))
-      return fail(HS2_ERR_SHAPE, "page_size %d: a power of two >= 32 is needed", ps);
-    if (pages->max_pages < 1 || pages->n_pages < 1)
-      return fail(HS2_ERR_SHAPE, "max_pages %d, n_pages %d", pages->max_pages, pages->n_pages);
-    if ((long long)pages->max_pages * ps != p->n_kv)
-      return fail(HS2_ERR_SHAPE, "n_kv %d must be max_pages * page_size = %lld", p->n_kv,
-                  (long long)pages->max_pages * ps);
-    if ((long long)pages->n_pages * ps > INT32_MAX)
-      return fail(HS2_ERR_UNSUPPORTED, "pool of %d pages of %d rows", pages->n_pages, ps);
-    kv.table = pages->page_table;
-    kv.page_shift = __builtin_ctz((unsigned)ps);
-    kv.max_pages = pages->max_pages;
-    kv.n_pages = pages->n_pages;
-  }
+  if (pages) HS2_TRY(check_pages(*p, pages, &kv));
   if (!lens) return fail(HS2_ERR_NULL, "lens is NULL");
   for (int b = 0; b < p->batch; ++b)
     if (lens[b] < 0 || lens[b] >= p->n_kv)
@@ -897,6 +903,80 @@ hs2_status run_varlen_prefill(const hs2_problem& p, int32_t n_sparse_layers,
   return HS2_OK;
 }
 
+// Sequence b of a packed batch on its own (batch 1, nq queries over nkv
+// keys): the sequences no single full-attention launch covers. k, v point
+// at the sequence's first key row, or at the pool when kv maps its rows
+// through a page table; ws_bytes bytes of workspace from ws.
+hs2_status run_sequence(const hs2_problem& p, int32_t n_sparse_layers, int b, int q0, int nq,
+                        int nkv, const void* q_full, const void* q_sparse, const void* k,
+                        const void* v, void* o_full, void* o_sparse, int32_t* idx, float* lse,
+                        void* ws, size_t ws_bytes, size_t layer_elems, hipStream_t st,
+                        const hs2::KvRows* kv) {
+  const size_t esz = p.dtype == HS2_BF16 ? 2 : 4;
+  const size_t qrow = (size_t)p.h_q * p.head_dim;
+  hs2_problem pb = p;
+  pb.batch = 1; pb.n_q = nq; pb.n_kv = nkv;
+  Layout L;
+  if (plan(pb, ws_bytes, &L, nullptr, nullptr) != HS2_OK)
+    return fail(HS2_ERR_WORKSPACE, "sequence %d: workspace too small", b);
+  const char* qb = (const char*)q_full + q0 * qrow * esz;
+  char* ob = (char*)o_full + q0 * qrow * esz;
+  int32_t* ib = idx + (size_t)q0 * index_width(p);
+  float* lb = lse ? lse + (size_t)q0 * p.h_q : nullptr;
+  HS2_TRY(run_full(pb, qb, k, v, ob, ib, lb, nullptr, ws, L, st, nullptr, kv));
+  if (n_sparse_layers == 0) return HS2_OK;
+  return run_sparse(pb, n_sparse_layers, (const char*)q_sparse + q0 * qrow * esz, k, v, ib,
+                    (char*)o_sparse + q0 * qrow * esz, st, kv, layer_elems);
+}
+
+// Chunked prefill over a paged pool: sequence b appends n_q(b) = cu_q[b+1]
+// - cu_q[b] tokens after its lens[b] cached ones. cu_kv holds the packed
+// offsets of the logical lengths lens[b] + n_q(b); cu_st those of the
+// staging copies, which only sequences with two or more new tokens get.
+// Workspace: K staging, V staging (stage_bytes each), then what the
+// variable-length batch of the same lengths needs.
+struct PagedPlan {
+  std::vector<int32_t> cu_kv, cu_st;
+  size_t stage_bytes = 0;
+  size_t min_bytes = 0, pref_bytes = 0;
+  long long total_q = 0;
+};
+
+hs2_status plan_paged(const hs2_problem* p, const hs2_kv_pages* pages, const int32_t* cu_q,
+                      const int32_t* lens, PagedPlan* pp, hs2::KvRows* kv) {
+  if (!p) return fail(HS2_ERR_NULL, "problem is NULL");
+  {
+    hs2_problem p1 = *p;
+    p1.n_q = 1;
+    HS2_TRY(check_problem(&p1));
+  }
+  HS2_TRY(check_pages(*p, pages, kv));
+  if (!cu_q || !lens) return fail(HS2_ERR_NULL, "cu_q or lens is NULL");
+  if (cu_q[0] != 0) return fail(HS2_ERR_SHAPE, "cu_q must start at 0");
+  pp->cu_kv.assign(p->batch + 1, 0);
+  pp->cu_st.assign(p->batch + 1, 0);
+  long long kv_sum = 0, st_sum = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const long long nq = (long long)cu_q[b + 1] - cu_q[b];
+    if (nq < 0) return fail(HS2_ERR_SHAPE, "cu_q decreases at sequence %d", b);
+    if (lens[b] < 0 || lens[b] + nq > p->n_kv)
+      return fail(HS2_ERR_SHAPE, "sequence %d: %d cached + %lld new tokens exceed the capacity %d",
+                  b, lens[b], nq, p->n_kv);
+    kv_sum += lens[b] + nq;
+    if (nq >= 2) st_sum += lens[b] + nq;
+    if (kv_sum > INT32_MAX) return fail(HS2_ERR_UNSUPPORTED, "%lld tokens in the batch", kv_sum);
+    pp->cu_kv[b + 1] = (int32_t)kv_sum;
+    pp->cu_st[b + 1] = (int32_t)st_sum;
+  }
+  size_t mn = 0, pref = 0;
+  HS2_TRY(check_varlen(p, cu_q, pp->cu_kv.data(), &mn, &pref, &pp->total_q, nullptr));
+  const size_t row_bytes = (size_t)p->h_kv * p->head_dim * (p->dtype == HS2_BF16 ? 2 : 4);
+  pp->stage_bytes = align_up((size_t)st_sum * row_bytes);
+  pp->min_bytes = 2 * pp->stage_bytes + mn;
+  pp->pref_bytes = 2 * pp->stage_bytes + pref;
+  return HS2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -935,34 +1015,121 @@ hs2_status hs2_block_forward_varlen(const hs2_problem* p, int32_t n_sparse_layer
   }
   const hipStream_t st = (hipStream_t)stream;
   const size_t esz = p->dtype == HS2_BF16 ? 2 : 4;
-  const size_t qrow = (size_t)p->h_q * p->head_dim;           // elements per query token
   const size_t krow = (size_t)p->h_kv * p->head_dim;          // elements per key token
-  const int width = index_width(*p);
-  const size_t layer_elems = (size_t)total_q * qrow;
+  const size_t layer_elems = (size_t)total_q * p->h_q * p->head_dim;
   const bool single = varlen_single_launch(*p);
   if (single)
     HS2_TRY(run_varlen_prefill(*p, n_sparse_layers, cu_q, cu_kv, q_full, q_sparse, k, v, o_full,
                                o_sparse, idx, lse, workspace, workspace_bytes, layer_elems, st));
   for (int b = 0; b < p->batch; ++b) {
     const int q0 = cu_q[b], nq = cu_q[b + 1] - cu_q[b];
-    if (single && nq >= 2) continue;              // done in the single launch
-    const int k0 = cu_kv[b], nkv = cu_kv[b + 1] - cu_kv[b];
-    if (nq == 0) continue;
-    hs2_problem pb = *p;
-    pb.batch = 1; pb.n_q = nq; pb.n_kv = nkv;
-    Layout L;
-    if (plan(pb, workspace_bytes, &L, nullptr, nullptr) != HS2_OK)
-      return fail(HS2_ERR_WORKSPACE, "sequence %d: workspace too small", b);
-    const char* qb = (const char*)q_full + q0 * qrow * esz;
-    const char* kb = (const char*)k + k0 * krow * esz;
-    const char* vb = (const char*)v + k0 * krow * esz;
-    char* ob = (char*)o_full + q0 * qrow * esz;
-    int32_t* ib = idx + (size_t)q0 * width;
-    float* lb = lse ? lse + (size_t)q0 * p->h_q : nullptr;
-    HS2_TRY(run_full(pb, qb, kb, vb, ob, ib, lb, nullptr, workspace, L, st));
-    if (n_sparse_layers > 0)
-      HS2_TRY(run_sparse(pb, n_sparse_layers, (const char*)q_sparse + q0 * qrow * esz, kb, vb, ib,
-                         (char*)o_sparse + q0 * qrow * esz, st, nullptr, layer_elems));
+    if (nq == 0 || (single && nq >= 2)) continue;           // done in the single launch
+    const int k0 = cu_kv[b];
+    HS2_TRY(run_sequence(*p, n_sparse_layers, b, q0, nq, cu_kv[b + 1] - k0, q_full, q_sparse,
+                         (const char*)k + k0 * krow * esz, (const char*)v + k0 * krow * esz,
+                         o_full, o_sparse, idx, lse, workspace, workspace_bytes, layer_elems, st,
+                         nullptr));
+  }
+  return HS2_OK;
+}
+
+hs2_status hs2_workspace_size_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                   const int32_t* cu_q, const int32_t* lens, size_t* min_bytes,
+                                   size_t* preferred_bytes) {
+  g_err.clear();
+  if (!min_bytes && !preferred_bytes) return fail(HS2_ERR_NULL, "no output pointer");
+  PagedPlan pp;
+  hs2::KvRows kv;
+  HS2_TRY(plan_paged(p, pages, cu_q, lens, &pp, &kv));
+  if (min_bytes) *min_bytes = pp.min_bytes;
+  if (preferred_bytes) *preferred_bytes = pp.pref_bytes;
+  return HS2_OK;
+}
+
+hs2_status hs2_block_forward_paged(const hs2_problem* p, const hs2_kv_pages* pages,
+                                   int32_t n_sparse_layers, const int32_t* cu_q,
+                                   const int32_t* lens, const void* q_full, const void* q_sparse,
+                                   const void* k_new, const void* v_new, void* k_pool,
+                                   void* v_pool, void* o_full, void* o_sparse, int32_t* idx,
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_err.clear();
+  PagedPlan pp;
+  hs2::KvRows kv;
+  HS2_TRY(plan_paged(p, pages, cu_q, lens, &pp, &kv));
+  if (n_sparse_layers < 0) return fail(HS2_ERR_SHAPE, "n_sparse_layers %d", n_sparse_layers);
+  HS2_TRY(check_ptr(q_full, "q_full"));
+  HS2_TRY(check_ptr(k_new, "k_new"));
+  HS2_TRY(check_ptr(v_new, "v_new"));
+  HS2_TRY(check_ptr(k_pool, "k_pool"));
+  HS2_TRY(check_ptr(v_pool, "v_pool"));
+  HS2_TRY(check_ptr(o_full, "o_full"));
+  HS2_TRY(check_ptr(idx, "idx"));
+  HS2_TRY(check_ptr(lse, "lse", false));
+  HS2_TRY(check_ptr(q_sparse, "q_sparse", n_sparse_layers > 0));
+  HS2_TRY(check_ptr(o_sparse, "o_sparse", n_sparse_layers > 0));
+  if (pp.total_q == 0) return HS2_OK;
+  if (!workspace) return fail(HS2_ERR_NULL, "workspace is NULL (needs %zu bytes)", pp.min_bytes);
+  if (!aligned16(workspace)) return fail(HS2_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < pp.min_bytes)
+    return fail(HS2_ERR_WORKSPACE, "workspace %zu bytes < minimum %zu", workspace_bytes,
+                pp.min_bytes);
+  const hipStream_t st = (hipStream_t)stream;
+  const size_t row_bytes = (size_t)p->h_kv * p->head_dim * (p->dtype == HS2_BF16 ? 2 : 4);
+  char* k_st = (char*)workspace;
+  char* v_st = k_st + pp.stage_bytes;
+  void* rest = v_st + pp.stage_bytes;
+  const size_t rest_bytes = workspace_bytes - 2 * pp.stage_bytes;
+  const int32_t* cu_st = pp.cu_st.data();
+
+  // the new rows into their pages, and the prefill-shaped sequences' rows
+  // into the staging buffers, up to STAGE_MAX_SEQS sequences per launch
+  {
+    PassTimer t(st, HS2_PASS_KV_STAGE);
+    hs2::StageSeqs g;
+    g.blk0[0] = 0;
+    for (int b = 0; b <= p->batch; ++b) {
+      if (b < p->batch) {
+        const int nq = cu_q[b + 1] - cu_q[b];
+        if (nq == 0) continue;
+        const int r0 = nq >= 2 ? 0 : lens[b], end = lens[b] + nq;
+        g.b[g.n] = b; g.r0[g.n] = r0; g.end[g.n] = end; g.lens[g.n] = lens[b];
+        g.q0[g.n] = cu_q[b];
+        g.st0[g.n] = nq >= 2 ? cu_st[b] : -1;
+        g.blk0[g.n + 1] = g.blk0[g.n] + (end - r0 + hs2::STAGE_ROWS - 1) / hs2::STAGE_ROWS;
+        ++g.n;
+      }
+      if (g.n == hs2::STAGE_MAX_SEQS || (b == p->batch && g.n > 0)) {
+        HIP_TRY(hs2::launch_kv_stage(g, k_new, v_new, k_pool, v_pool, k_st, v_st, kv,
+                                     (int)row_bytes, st),
+                "KV append and staging");
+        g.n = 0;
+      }
+    }
+  }
+  const size_t layer_elems = (size_t)pp.total_q * p->h_q * p->head_dim;
+  // prefill-shaped sequences read their staged rows
+  if (varlen_single_launch(*p)) {
+    HS2_TRY(run_varlen_prefill(*p, n_sparse_layers, cu_q, cu_st, q_full, q_sparse, k_st, v_st,
+                               o_full, o_sparse, idx, lse, rest, rest_bytes, layer_elems, st));
+  } else {
+    for (int b = 0; b < p->batch; ++b) {
+      const int nq = cu_q[b + 1] - cu_q[b];
+      if (nq < 2) continue;
+      HS2_TRY(run_sequence(*p, n_sparse_layers, b, cu_q[b], nq, lens[b] + nq, q_full, q_sparse,
+                           k_st + (size_t)cu_st[b] * row_bytes, v_st + (size_t)cu_st[b] * row_bytes,
+                           o_full, o_sparse, idx, lse, rest, rest_bytes, layer_elems, st,
+                           nullptr));
+    }
+  }
+  // one-token sequences read the pool in place through their page-table row
+  for (int b = 0; b < p->batch; ++b) {
+    if (cu_q[b + 1] - cu_q[b] != 1) continue;
+    hs2::KvRows kvb = kv;
+    kvb.table = kv.table + (size_t)b * kv.max_pages;
+    HS2_TRY(run_sequence(*p, n_sparse_layers, b, cu_q[b], 1, lens[b] + 1, q_full, q_sparse,
+                         k_pool, v_pool, o_full, o_sparse, idx, lse, rest, rest_bytes, layer_elems,
+                         st, &kvb));
   }
   return HS2_OK;
 }

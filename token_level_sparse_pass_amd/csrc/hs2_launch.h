@@ -175,6 +175,26 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             const int32_t* seq_len, int batch, const KvRows& kv, int row_bytes,
                             hipStream_t st);
 
+// Chunked prefill over a paged pool. Sequence s of one launch (page-table
+// row b[s]) visits positions r0[s] .. end[s] - 1 of its page list:
+// positions at or past lens[s] are its new tokens (packed rows
+// q0[s] + j - lens[s] of k_new / v_new), which land in the pool; when
+// st0[s] >= 0 every visited row is also copied to row st0[s] + j of the
+// contiguous staging buffers (new rows from k_new / v_new, older ones from
+// the pool). Work-groups blk0[s] .. blk0[s+1] serve sequence s.
+constexpr int STAGE_MAX_SEQS = 32;
+constexpr int STAGE_ROWS = 8;               // positions per work-group
+struct StageSeqs {
+  int n = 0;
+  int blk0[STAGE_MAX_SEQS + 1];
+  int b[STAGE_MAX_SEQS], r0[STAGE_MAX_SEQS], end[STAGE_MAX_SEQS];
+  int lens[STAGE_MAX_SEQS], q0[STAGE_MAX_SEQS];
+  long long st0[STAGE_MAX_SEQS];
+};
+hipError_t launch_kv_stage(const StageSeqs& s, const void* k_new, const void* v_new, void* k_pool,
+                           void* v_pool, void* k_stage, void* v_stage, const KvRows& kv,
+                           int row_bytes, hipStream_t st);
+
 // Copy one score row into a debug buffer: candidates keep S, others get -1.
 hipError_t launch_export_scores(const float* src, int n_cand, int n_kv, float* dst,
                                 hipStream_t st);

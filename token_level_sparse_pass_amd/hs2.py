@@ -84,6 +84,12 @@ def load(path: str = LIB_PATH):
     lib.hs2_workspace_size_varlen.restype = i32
     lib.hs2_block_forward_varlen.argtypes = [P, i32, pi, pi] + [vp] * 9 + [sz, vp]
     lib.hs2_block_forward_varlen.restype = i32
+    KP = ctypes.POINTER(KvPages)
+    lib.hs2_workspace_size_paged.argtypes = [P, KP, pi, pi, ctypes.POINTER(sz),
+                                             ctypes.POINTER(sz)]
+    lib.hs2_workspace_size_paged.restype = i32
+    lib.hs2_block_forward_paged.argtypes = [P, KP, i32, pi, pi] + [vp] * 11 + [sz, vp]
+    lib.hs2_block_forward_paged.restype = i32
     lib.hs2_backward_workspace_size.argtypes = [P, i32, ctypes.POINTER(sz)]
     lib.hs2_backward_workspace_size.restype = i32
     lib.hs2_block_backward.argtypes = [P, i32] + [vp] * 14 + [vp, sz, vp]
@@ -391,4 +397,61 @@ def block_forward_varlen(q_full, q_sparse, k, v, cu_q, cu_kv, *, workspace=None,
         ctypes.byref(p), q_sparse.shape[0], cq, ck, _ptr(q_full), _ptr(q_sparse), _ptr(k),
         _ptr(v), _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
         _ptr(workspace), workspace.numel(), _stream(q_full.device)))
+    return out
+
+
+def _paged_problem(q_full, k_pool, page_table, page_size, batch, kw):
+    max_pages = page_table.shape[1]
+    p = problem(q_full.dtype, batch, 1, max_pages * page_size, q_full.shape[1], k_pool.shape[1],
+                q_full.shape[2], **kw)
+    pages = KvPages(page_table.data_ptr(), page_size, max_pages, k_pool.shape[0] // page_size)
+    return p, pages
+
+
+def workspace_size_paged(p: Problem, pages: KvPages, cu_q, lens):
+    cq, _ = _cu(cu_q)
+    ln, _ = _cu(lens)
+    mn, pref = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().hs2_workspace_size_paged(ctypes.byref(p), ctypes.byref(pages), cq, ln,
+                                           ctypes.byref(mn), ctypes.byref(pref)))
+    return mn.value, pref.value
+
+
+def block_forward_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table, page_size,
+                        cu_q, lens, *, workspace=None, want_lse=True, **kw):
+    """hs2_block_forward_paged: chunked prefill over a paged KV pool.
+
+    q_full [total_q, h_q, d], q_sparse [L, total_q, h_q, d], k_new / v_new
+    [total_q, h_kv, d] (sequence b's new tokens are rows cu_q[b] ..
+    cu_q[b+1]), k_pool / v_pool [n_pages * page_size, h_kv, d] (modified in
+    place), page_table int32 device tensor [B, max_pages]; lens: the B
+    lengths before the call (host ints; the caller advances them). Returns
+    dict(o_full, o_sparse, idx [total_q, W], lse) as block_forward_varlen."""
+    lib = load()
+    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
+                 (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _check_tensor(t, n, q_full.dtype)
+    _check_tensor(page_table, "page_table", torch.int32)
+    cq, vq = _cu(cu_q)
+    ln, vl = _cu(lens)
+    batch = len(vq) - 1
+    total_q, hq, d = q_full.shape
+    if vq[-1] != total_q or k_new.shape[0] != total_q or len(vl) != batch:
+        raise ValueError("cu_q / lens do not match the packed tensors")
+    if page_table.shape[0] != batch:
+        raise ValueError("page_table needs one row per sequence")
+    p, pages = _paged_problem(q_full, k_pool, page_table, page_size, batch, kw)
+    width = index_width(p)
+    if workspace is None:
+        _, pref = workspace_size_paged(p, pages, vq, vl)
+        workspace = torch.empty(max(16, pref), dtype=torch.uint8, device=q_full.device)
+    out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
+               idx=torch.empty((total_q, width), dtype=torch.int32, device=q_full.device),
+               lse=torch.empty((hq * total_q,), dtype=torch.float32, device=q_full.device)
+               if want_lse else None)
+    _check(lib.hs2_block_forward_paged(
+        ctypes.byref(p), ctypes.byref(pages), q_sparse.shape[0], cq, ln, _ptr(q_full),
+        _ptr(q_sparse), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out["o_full"]),
+        _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]), _ptr(workspace),
+        workspace.numel(), _stream(q_full.device)))
     return out
