@@ -23,11 +23,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 math stays off: plain scalar/float2 code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
+# per-source additions: the bf16 pass-1 kernel takes its row maxima with
+# plain max instructions, which fmaxf emits only when NaNs need no handling
+# (its logits are finite or -inf)
+EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

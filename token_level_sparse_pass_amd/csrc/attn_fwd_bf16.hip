@@ -4,15 +4,23 @@
 // (m2, l) and LSE.
 //
 // Differences from the generic kernel, all aimed at keeping the SIMD's
-// issue slots on MFMAs (on gfx950 a SIMD's VALU and MFMA instructions do
-// not overlap, so every VALU instruction in the loop costs MFMA time):
+// issue slots on MFMAs (with two waves per SIMD issuing both, every VALU
+// instruction in the loop costs MFMA time: about 2-3 cycles each, measured
+// with MFMA and FMA streams interleaved in each wave):
 //  * V is transposed once per call into a tile-major copy in the workspace,
 //    Vt[b][g][tile][d][64 keys], so the PV product reads its operands with
 //    16-byte LDS loads instead of transposing in registers;
 //  * K and Vt tiles go straight from global memory into LDS
-//    (global_load_lds_dwordx4) through a three-stage ring (two tiles in
-//    flight, waits counted per tile), with XOR-swizzled 16-byte chunks so
-//    the MFMA operand reads are free of bank conflicts;
+//    (global_load_lds_dwordx4) through a two-stage ring (the next tile
+//    loads while this one is used), with XOR-swizzled 16-byte chunks so
+//    the MFMA operand reads are free of bank conflicts; the tile loop is
+//    unrolled by two so each stage's LDS offsets are immediates of the
+//    read instructions, and tiles that need no causal mask run a copy of
+//    the loop body without one;
+//  * row maxima use three-input max instructions and the gfx950 permlane
+//    swaps (no LDS round trip for the cross-row step); this file is built
+//    with -fno-honor-nans so that fmaxf does not first quiet every operand
+//    (the kernel never sees a NaN: masked logits are -inf);
 //  * the keys of a 64-key tile are assigned to MFMA rows in a permuted order
 //    such that the P^T operand of each lane covers 8 consecutive keys;
 //  * the running max is only moved (and O rescaled) when it grows by more
@@ -21,19 +29,18 @@
 //  * the causal mask is applied only on tiles that reach the diagonal.
 // Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
 // 16-row MFMA blocks per wave, eight waves (two per SIMD) per work-group,
-// all sharing each tile in LDS. Each wave reads a
-// whole K and V^T tile from LDS per 64 keys, so rows per wave set the MFMA
-// work per LDS byte (LDS delivers about 64 B/clk per CU for 16-byte reads).
+// all sharing each tile in LDS. Each wave reads a whole K and V^T tile from
+// LDS per 64 keys (512 B per MFMA); the counters put the LDS pipe at under
+// half of its cycles, so the loop is bound by instruction issue, not LDS.
 #include "hs2_device.h"
 #include "hs2_launch.h"
+
+#include <type_traits>
 
 namespace hs2 {
 
 #ifndef FWD_WAVES
 #define FWD_WAVES 8
-#endif
-#ifndef FWD_STAGES
-#define FWD_STAGES 3
 #endif
 
 namespace {
@@ -55,6 +62,17 @@ __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
 // then owns keys 32*(kb/2) + 8q .. +7 of the tile
 __device__ __forceinline__ int tile_key(int kb, int m) {
   return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
+}
+
+__device__ __forceinline__ float max2f(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48: each permlane swap hands a
+// lane its partner row's value (16 lanes, then 32 lanes apart)
+__device__ __forceinline__ float row_group_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max2f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2f(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -106,8 +124,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const __bf16* v, __bf1
 }
 
 // RBW 16-row blocks per wave, NWV waves per work-group (all of them share
-// each K/V tile in LDS), NST-stage LDS ring (tiles in flight: NST - 1).
-template <int RBW, int NWV, int NST>
+// each K/V tile in LDS).
+template <int RBW, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
   using OP = Op<__bf16, D>;
   constexpr int ROWS = 16 * RBW * NWV;                  // rows per work-group
@@ -245,26 +263,20 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       voff[st][db] = KT_BYTES + d * 128 + (((4 * st + grp) ^ vswz(d)) << 4);
     }
 
-#pragma unroll
-  for (int s0 = 0; s0 < NST - 1; ++s0)
-    if (s0 < n_tiles) issue(s0, s0);
-
-  for (int t = 0; t < n_tiles; ++t) {
-    // tile t has landed once at most the loads of the tiles issued after it
-    // (2 * CPT per tile) are still in flight; the loop issues no other
-    // vector-memory operation, and this wave's operations complete in order
-    {
-      const int pending = min(NST - 2, n_tiles - 1 - t);    // tiles issued after t
-      if (NST > 3 && pending >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * CPT));
-      else if (NST > 2 && pending == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPT));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+  // two-stage ring: tile t + 1 is loaded into the other stage while tile t
+  // is used; the loop is unrolled by two so each stage's LDS offsets are
+  // compile-time constants folded into the LDS read instructions
+  if (n_tiles > 0) issue(0, 0);
+  auto step = [&](int t, auto stage_c, auto masked_c) {
+    constexpr int STAGE_C = decltype(stage_c)::value;       // -1: runtime
+    constexpr bool masked = decltype(masked_c)::value;
+    const int STAGE = STAGE_C >= 0 ? STAGE_C : (t & 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    // the stage refilled here held tile t - 1, which every wave finished
-    // reading before the barrier above
-    if (t + NST - 1 < n_tiles) issue(t + NST - 1, (t + NST - 1) % NST);
-    const int stage = t % NST;
-    const char* base = smem + stage * STAGE_BYTES;
+    // the other stage held tile t - 1, which every wave finished reading
+    // before the barrier above
+    if (t + 1 < n_tiles) issue(t + 1, STAGE ^ 1);
+    const char* base = smem + STAGE * STAGE_BYTES;
     const int j0 = t * TK;
 
     // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
@@ -294,25 +306,24 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
 #pragma unroll
     for (int db = 0; db < 8; ++db) vf0[db] = *reinterpret_cast<const bf16x8*>(base + voff[0][db]);
 
-    const bool masked = t >= n_full;
     bf16x8 pu[RBW][2];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      if (masked) {
+      if constexpr (masked) {
+        // key j0 + 8 grp + off is past this row when off > lim
+        const int lim = row_pos[rb] - j0 - 8 * grp;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = j0 + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + e;
-            if (key > row_pos[rb]) s[rb][kb][e] = -INFINITY;
-          }
+          for (int e = 0; e < 4; ++e)
+            if (32 * (kb >> 1) + 4 * (kb & 1) + e > lim) s[rb][kb][e] = -INFINITY;
       }
-      float tmax = fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3]));
-#pragma unroll
-      for (int kb = 1; kb < 4; ++kb)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(s[rb][kb][0], s[rb][kb][1]), fmaxf(s[rb][kb][2], s[rb][kb][3])));
-      tmax = xor_max(tmax, 16);
-      tmax = xor_max(tmax, 32);
+      const float m0 = max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]);
+      const float m1 = max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]);
+      const float m2 = max3f(s[rb][1][2], s[rb][1][3], s[rb][2][0]);
+      const float m3 = max3f(s[rb][2][1], s[rb][2][2], s[rb][2][3]);
+      const float m4 = max3f(s[rb][3][0], s[rb][3][1], s[rb][3][2]);
+      const float tmax = row_group_max(max2f(max3f(m0, m1, m2), max3f(m3, m4, s[rb][3][3])));
       const float m_tile = tmax * a.c;
       const bool grow = m_tile > m_run[rb] + RESCALE_GAP;
       if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -360,7 +371,19 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
+  };
+  // tiles below n_full have no key past any row here: no causal mask
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using Open = std::false_type;
+  using Diag = std::true_type;
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    step(t, S0{}, Open{});
+    step(t + 1, S1{}, Open{});
   }
+  if (t < n_full) step(t++, S0{}, Open{});
+  for (; t < n_tiles; ++t) step(t, std::integral_constant<int, -1>{}, Diag{});
 
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
@@ -422,16 +445,17 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
   a.vt_tiles = vt_tiles; a.c = p.s.scale_log2;
   const int G = a.h_q / a.h_kv;
   // two 16-row blocks per wave at two waves per SIMD measured best on the
-  // 1M-context workload (48 rows spill registers; 64 rows at one wave per
-  // SIMD lose more to latency than they save in LDS traffic); eight waves
-  // sharing a three-stage ring beat four waves on two stages by about 3 %
-  constexpr int RBW = 2, NWV = FWD_WAVES, NST = FWD_STAGES;
+  // 1M-context workload: 48 rows fit the registers only with the softmax
+  // split into 32-key halves, which ran slower; 64 rows at one wave per
+  // SIMD lose more to latency than they save in LDS traffic; eight waves
+  // sharing each tile beat four waves by about 3 %
+  constexpr int RBW = 2, NWV = FWD_WAVES;
   constexpr int rows = 16 * RBW * NWV;
-  constexpr int smem_bytes = NST * STAGE_BYTES;
+  constexpr int smem_bytes = 2 * STAGE_BYTES;
   struct FwdLdsTag {};
   if (smem_bytes > 65536) {
     const hipError_t e = ensure_dynamic_lds<FwdLdsTag>(
-        (const void*)attn_fwd_bf16_kernel<RBW, NWV, NST>, smem_bytes);
+        (const void*)attn_fwd_bf16_kernel<RBW, NWV>, smem_bytes);
     if (e != hipSuccess) return e;
   }
   a.n_rt = (a.n_q * G + rows - 1) / rows;
@@ -441,7 +465,7 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
     grid = dim3((unsigned)((size_t)a.vl.tile0[a.vl.n] * a.h_kv));
     if (a.vl.tile0[a.vl.n] == 0) return hipSuccess;
   }
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV, NST>), grid, dim3(64 * NWV), smem_bytes, st,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV>), grid, dim3(64 * NWV), smem_bytes, st,
                      a);
   return hipGetLastError();
 }
