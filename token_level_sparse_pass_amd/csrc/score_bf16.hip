@@ -31,9 +31,11 @@ constexpr int TQ = 128;
 constexpr int TKEY = 256;
 constexpr int QT_BYTES = TQ * D * 2;          // 32 KB
 constexpr int ST_BYTES = 2 * TQ * 4;          // m2 and 1/l of the tile's queries
-constexpr int STAGE = QT_BYTES + ST_BYTES;
 constexpr int KT_BYTES = TKEY * D * 2;        // 64 KB: K rows of one KV head
-constexpr int SMEM_BYTES = 2 * STAGE + KT_BYTES;
+// LDS: the two Q stages, the two statistics stages, the K buffer
+constexpr int ST_BASE = 2 * QT_BYTES;
+constexpr int K_BASE = ST_BASE + 2 * ST_BYTES;
+constexpr int SMEM_BYTES = K_BASE + KT_BYTES;
 constexpr int KT_BLOCK = 32;                  // key tiles per scheduling block
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
   const size_t plane = (size_t)a.B * a.h_q * a.n_q;
 
   auto issue = [&](int h, int stage) {
-    char* base = smem + stage * STAGE;
+    char* base = smem + stage * QT_BYTES;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int slot = (wave * 4 + t) * 64 + lane;
@@ -101,13 +103,14 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
       const int r = (wave & 1) * 64 + lane;
       const int qi = a.q0 + min(r_lo + r, a.rows - 1);
       const float* src = a.stats + pl * plane + ((size_t)a.b * a.h_q + h) * a.n_q + qi;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + QT_BYTES + wave * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + ST_BASE + stage * ST_BYTES + wave * 256),
+                                       4, 0, 0);
     }
   };
 
   // K rows of the tile's 256 keys for KV head g, into the K buffer
   auto issue_k = [&](int g) {
-    char* base = smem + 2 * STAGE;
+    char* base = smem + K_BASE;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int slot = (wave * 8 + t) * 64 + lane;
@@ -125,23 +128,13 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int qoff[4][4];                                     // [qb][unit] byte offset in Q tile
-  int srow[4];
+  // Q rows wq * 64 + 16 qb + l16 all have swizzle l16 (the row's low four
+  // bits), so query block qb sits a constant 16 rows (4 KB) past block 0 and
+  // one offset per unit serves all four blocks; likewise the statistics
+  const int srow0 = wq * 64 + l16;
+  int qoff[4];                                        // [unit] byte offset in Q tile, block 0
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const int row = wq * 64 + qb * 16 + l16;
-    srow[qb] = row;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) qoff[qb][u] = row * 256 + (((4 * grp + u) ^ qswz(row)) << 4);
-  }
-
-  int koff[4][4];                                     // [kb][unit] byte offset in K buffer
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int row = wk * 64 + kb * 16 + l16;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) koff[kb][u] = 2 * STAGE + row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
-  }
+  for (int u = 0; u < 4; ++u) qoff[u] = srow0 * 256 + (((4 * grp + u) ^ qswz(srow0)) << 4);
 
   issue(0, 0);
   issue_k(0);
@@ -156,15 +149,19 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
       // this KV head's K rows stay in registers for its G query heads; the
       // buffer is refilled with the next KV head once every wave has them
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb) {
+        const int row = wk * 64 + kb * 16 + l16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kf[kb][u] = *reinterpret_cast<const bf16x8*>(smem + koff[kb][u]);
+        for (int u = 0; u < 4; ++u)
+          kf[kb][u] = *reinterpret_cast<const bf16x8*>(
+              smem + K_BASE + row * 256 + (((4 * grp + u) ^ kswz(row)) << 4));
+      }
       __syncthreads();
       if (g + 1 < a.h_kv) issue_k(g + 1);
     }
     if (h + 1 < a.h_q) issue(h + 1, stage ^ 1);
-    const char* base = smem + stage * STAGE;
-    const float* st = reinterpret_cast<const float*>(base + QT_BYTES);
+    const char* base = smem + stage * QT_BYTES;
+    const float* st = reinterpret_cast<const float*>(smem + ST_BASE + stage * ST_BYTES);
 
     // Q fragments of query block qb + 1 are read while block qb computes.
     // The 16 (qb, kb) blocks form a software pipeline: the four MFMAs of
@@ -173,9 +170,9 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
     bf16x8 qf[2][4];
     float m2v[2], ilv[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qf[0][u] = *reinterpret_cast<const bf16x8*>(base + qoff[0][u]);
-    m2v[0] = st[srow[0]];
-    ilv[0] = st[TQ + srow[0]];
+    for (int u = 0; u < 4; ++u) qf[0][u] = *reinterpret_cast<const bf16x8*>(base + qoff[u]);
+    m2v[0] = st[srow0];
+    ilv[0] = st[TQ + srow0];
     f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f};
     float pm2 = 0.f, pil = 0.f;
 #pragma unroll
@@ -184,9 +181,9 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
       if (kb == 0 && qb + 1 < 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          qf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + qoff[qb + 1][u]);
-        m2v[cur ^ 1] = st[srow[qb + 1]];
-        ilv[cur ^ 1] = st[TQ + srow[qb + 1]];
+          qf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + qoff[u] + (qb + 1) * 4096);
+        m2v[cur ^ 1] = st[srow0 + (qb + 1) * 16];
+        ilv[cur ^ 1] = st[TQ + srow0 + (qb + 1) * 16];
       }
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -221,7 +218,7 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
   // keys past n_kv (tile tail) are never read back: rows only use j <= p - w
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    const int r = r_lo + srow[qb];
+    const int r = r_lo + srow0 + qb * 16;
     if (r >= a.rows) continue;
     float* out = a.scores + (size_t)r * a.stride + kj0 + wk * 64 + 4 * grp;
 #pragma unroll
