@@ -23,10 +23,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 math stays off: plain scalar/float2 code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
-# per-source additions: the bf16 pass-1 kernel takes its row maxima with
+# per-source additions: the bf16 pass-1 kernels take their row maxima with
 # plain max instructions, which fmaxf emits only when NaNs need no handling
-# (its logits are finite or -inf)
-EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
+# (their logits are finite or -inf)
+EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_decode_bf16.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -206,16 +206,16 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
       }
     }
 
-    float tmax = -INFINITY;
+    if (kbase + TK > k_end) {
+      // the split's last tile: keys past its end take no weight
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (kbase + kb * 16 + 4 * grp + e >= k_end) s[kb][e] = -INFINITY;
-        tmax = fmaxf(tmax, s[kb][e]);
-      }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+        for (int e = 0; e < 4; ++e)
+          if (kbase + kb * 16 + 4 * grp + e >= k_end) s[kb][e] = -INFINITY;
+    }
+    const float tmax = row_group_max(max2f(max3f(s[0][0], s[0][1], s[0][2]),
+                                           max3f(s[0][3], max3f(s[1][0], s[1][1], s[1][2]), s[1][3])));
     const float m_tile = tmax * a.c;
     const bool grow = m_tile > m_run + RESCALE_GAP;
     if (__builtin_amdgcn_ballot_w64(grow)) {

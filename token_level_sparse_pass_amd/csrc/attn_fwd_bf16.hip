@@ -64,17 +64,6 @@ __device__ __forceinline__ int tile_key(int kb, int m) {
   return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
 }
 
-__device__ __forceinline__ float max2f(float a, float b) { return fmaxf(a, b); }
-__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-// max over the lanes l, l ^ 16, l ^ 32, l ^ 48: each permlane swap hands a
-// lane its partner row's value (16 lanes, then 32 lanes apart)
-__device__ __forceinline__ float row_group_max(float v) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = max2f(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return max2f(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct Fwd2Args {

@@ -104,6 +104,20 @@ __device__ __forceinline__ float xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, WAVE));
 }
 
+// Maxima for kernels built with -fno-honor-nans (no operand quieting, so
+// each is one max instruction; three-input maxima become v_max3_f32).
+__device__ __forceinline__ float max2f(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// max over the lanes l, l ^ 16, l ^ 32, l ^ 48: each gfx950 permlane swap
+// hands a lane its partner row's value (16 lanes, then 32 lanes apart), with
+// no LDS round trip
+__device__ __forceinline__ float row_group_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max2f(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2f(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // Round-to-nearest-even store of an fp32 value in the tensor element type.
 template <typename T>
 __device__ __forceinline__ T to_elem(float x);
