@@ -10,13 +10,15 @@
 // One GEMM C[M, 2F] = H[M, Dm] . W[2F, Dm]^T (F = h_kv * head_dim), computed
 // transposed, C^T = W . H^T, so each lane ends up holding four consecutive
 // output features of one token (8-byte stores along a K or V row). A
-// work-group owns a 256-token x 256-feature block and runs one wave per
-// SIMD, so a wave has the whole register file for its 128 x 128 block:
-// 256 fp32 accumulators (AGPRs) and the operand fragments of two k-steps.
-// Every 16-byte fragment a wave reads out of LDS feeds 8 MFMAs (256 B of
-// LDS reads per MFMA), and the 64-wide k-slices of H and W are staged by
-// global_load_lds, double-buffered, with a row swizzle that makes the
-// fragment reads conflict-free.
+// work-group owns a 256-token x 256-feature block with eight waves, two per
+// SIMD: a single wave per SIMD issues MFMAs at only about half the matrix
+// core's rate, so the SIMD needs a second MFMA stream. Each wave computes a
+// 128-token x 64-feature block (128 fp32 accumulators); every 16-byte H
+// fragment it reads out of LDS feeds 4 MFMAs and every W fragment 8 (384 B
+// of LDS reads per MFMA, under the LDS bandwidth at full MFMA rate). The
+// 64-wide k-slices of H and W are staged by buffer loads straight into LDS,
+// double-buffered, with a row swizzle that makes the fragment reads
+// conflict-free.
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -50,7 +52,7 @@ struct BridgeArgs {
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
+__global__ __launch_bounds__(512, 2) void kv_bridge_kernel(BridgeArgs a) {
   using OP = Op<__bf16, 128>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
   const int wave = threadIdx.x >> 6;
   const int grp = lane >> 4;
   const int l16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;          // 2 x 2 waves of 128 x 128
+  const int wm = wave & 1, wn = wave >> 1;          // 2 x 4 waves of 128 x 64
 
   // feature tiles fastest: the tokens' slices are reused from L2 across them
   const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
   const int N = 2 * a.F;
 
   // stage the k-slice [kk, kk + 64) of the block's 256 token rows and 256
-  // weight rows: 2 x 2048 chunks of 16 B, 8 of each per lane. Buffer loads
+  // weight rows: 2 x 2048 chunks of 16 B, 4 of each per lane. Buffer loads
   // address them from one scalar resource per operand (the block's first
   // row) plus a 32-bit row/chunk offset per lane that the H and W slices
   // share; rows past the end of either matrix read as zeros.
@@ -77,39 +79,39 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
       (void*)(a.h + (size_t)m0 * a.Dm), 0, m_rows * a.Dm * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.w + (size_t)n0 * a.Dm), 0, n_rows * a.Dm * 2, 0x00020000);
-  int voff[8];
+  int voff[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int slot = (wave * 8 + t) * 64 + lane;    // 0 .. 2047
+  for (int t = 0; t < 4; ++t) {
+    const int slot = (wave * 4 + t) * 64 + lane;    // 0 .. 2047
     const int r = slot >> 3, pc = slot & 7;
     voff[t] = r * a.Dm * 2 + ((pc ^ swz(r)) << 4);
   }
   auto issue = [&](int kk, int stage) {
     char* base = smem + stage * STAGE_BYTES;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void*)(base + (wave * 8 + t) * 1024), 16,
+    for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void*)(base + (wave * 4 + t) * 1024), 16,
                                                voff[t], kk * 2, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wres, (lds_void*)(base + SLICE_BYTES + (wave * 8 + t) * 1024), 16, voff[t], kk * 2, 0, 0);
+          wres, (lds_void*)(base + SLICE_BYTES + (wave * 4 + t) * 1024), 16, voff[t], kk * 2, 0, 0);
     }
   };
 
-  f32x4 acc[8][8];                                  // [feature block][token block]
+  f32x4 acc[4][8];                                  // [feature block][token block]
 #pragma unroll
-  for (int fb = 0; fb < 8; ++fb)
+  for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
     for (int tb = 0; tb < 8; ++tb) acc[fb][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment offsets: row (wave block + 16 * blk + l16), chunk 4u + grp
-  const int hrow0 = wm * 128 + l16, wrow0 = wn * 128 + l16;
+  // fragment offsets: row (wave block + 16 * blk + l16), chunk 4u + grp;
+  // rows 16 apart keep the same swizzle ((r >> 1) & 7 repeats every 16)
+  const int hrow0 = wm * 128 + l16, wrow0 = wn * 64 + l16;
   int hoff[2], woff[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     hoff[u] = hrow0 * ROW_BYTES + (((4 * u + grp) ^ swz(hrow0)) << 4);
     woff[u] = SLICE_BYTES + wrow0 * ROW_BYTES + (((4 * u + grp) ^ swz(wrow0)) << 4);
   }
-  // rows 16 apart keep the same swizzle ((r >> 1) & 7 repeats every 16)
 
   const int n_k = a.Dm / BK;
   issue(0, 0);
@@ -118,33 +120,21 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
     __syncthreads();
     if (ks + 1 < n_k) issue((ks + 1) * BK, (ks + 1) & 1);
     const char* base = smem + (ks & 1) * STAGE_BYTES;
-    // H fragments stay in registers for a k-substep; W fragments stream one
-    // feature block ahead of the MFMAs that use them, and the next
-    // substep's H fragments are read during the last two feature blocks
-    bf16x8 hf[8], hn[8], wf[2];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) hf[b] = *reinterpret_cast<const bf16x8*>(base + hoff[0] + b * 16 * ROW_BYTES);
-    wf[0] = *reinterpret_cast<const bf16x8*>(base + woff[0]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      // the k-substep's four W fragments stay in registers; the H
+      // fragments stream one token block ahead of the MFMAs that use them
+      bf16x8 wf[4], hf[2];
 #pragma unroll
-      for (int fb = 0; fb < 8; ++fb) {
-        if (fb + 1 < 8)
-          wf[(fb + 1) & 1] =
-              *reinterpret_cast<const bf16x8*>(base + woff[u] + (fb + 1) * 16 * ROW_BYTES);
-        else if (u == 0)
-          wf[0] = *reinterpret_cast<const bf16x8*>(base + woff[1]);
-        if (u == 0 && fb >= 6) {
+      for (int fb = 0; fb < 4; ++fb)
+        wf[fb] = *reinterpret_cast<const bf16x8*>(base + woff[u] + fb * 16 * ROW_BYTES);
+      hf[0] = *reinterpret_cast<const bf16x8*>(base + hoff[u]);
 #pragma unroll
-          for (int b = (fb - 6) * 4; b < (fb - 5) * 4; ++b)
-            hn[b] = *reinterpret_cast<const bf16x8*>(base + hoff[1] + b * 16 * ROW_BYTES);
-        }
+      for (int tb = 0; tb < 8; ++tb) {
+        if (tb + 1 < 8)
+          hf[(tb + 1) & 1] = *reinterpret_cast<const bf16x8*>(base + hoff[u] + (tb + 1) * 16 * ROW_BYTES);
 #pragma unroll
-        for (int tb = 0; tb < 8; ++tb) acc[fb][tb] = OP::mma(wf[fb & 1], hf[tb], acc[fb][tb]);
-      }
-      if (u == 0) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) hf[b] = hn[b];
+        for (int fb = 0; fb < 4; ++fb) acc[fb][tb] = OP::mma(wf[fb], hf[tb & 1], acc[fb][tb]);
       }
     }
   }
@@ -155,8 +145,8 @@ __global__ __launch_bounds__(256, 1) void kv_bridge_kernel(BridgeArgs a) {
     const int m = m0 + wm * 128 + tb * 16 + l16;
     if (m >= a.M) continue;
 #pragma unroll
-    for (int fb = 0; fb < 8; ++fb) {
-      const int n = n0 + wn * 128 + fb * 16 + 4 * grp;
+    for (int fb = 0; fb < 4; ++fb) {
+      const int n = n0 + wn * 64 + fb * 16 + 4 * grp;
       if (n >= N) continue;
       __bf16* dst = n < a.F ? a.k + (size_t)m * a.F + n : a.v + (size_t)m * a.F + (n - a.F);
       __attribute__((ext_vector_type(4))) __bf16 w4;
@@ -182,7 +172,7 @@ hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)((size_t)a.n_mt * a.n_nt));
-  hipLaunchKernelGGL(kv_bridge_kernel, grid, dim3(256), SMEM_BYTES, st, a);
+  hipLaunchKernelGGL(kv_bridge_kernel, grid, dim3(512), SMEM_BYTES, st, a);
   return hipGetLastError();
 }
 
