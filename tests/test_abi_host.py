@@ -335,3 +335,18 @@ def test_paged_prefill_workspace_and_rejections():
     assert call(k_new=None) == 1 and call(v_pool=None) == 1
     assert call(idx=FAKE + 4) == 5
     assert call(ws=FAKE + 8) == 5
+
+
+def test_paged_prefill_without_new_tokens_launches_nothing():
+    # a batch where no sequence appends anything is a no-op: OK without a
+    # workspace, before any device work
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+    p = base_problem(batch=2, n_kv=64 * 10)
+    pages = hs2.KvPages(FAKE, 64, 10, 20)
+    cu_q = (ctypes.c_int32 * 3)(0, 0, 0)
+    lens = (ctypes.c_int32 * 2)(100, 0)
+    assert hs2.workspace_size_paged(p, pages, [0, 0, 0], [100, 0]) == (0, 0)
+    st = lib.hs2_block_forward_paged(ctypes.byref(p), ctypes.byref(pages), 2, cu_q, lens,
+                                     *[vp(FAKE)] * 9, None, None, 0, None)
+    assert st == 0, lib.hs2_last_error().decode()
