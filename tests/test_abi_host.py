@@ -214,11 +214,16 @@ def test_backward_workspace_and_rejections():
     lib = hs2.load()
     vp = ctypes.c_void_p
     p = base_problem()
-    # Delta rows, then two fp32 K/V accumulators when there are sparse layers
+    # Delta rows, a bf16 K^T copy (bf16, head dim 128), then two fp32 K/V
+    # accumulators when there are sparse layers
     delta = 1 * 8 * 256 * 4
+    kt = 1 * 2 * 1024 * 128 * 2
     acc = 1 * 1024 * 2 * 128 * 4
-    assert hs2.backward_workspace_size(p, 0) == delta
-    assert hs2.backward_workspace_size(p, 3) == delta + 2 * acc
+    assert hs2.backward_workspace_size(p, 0) == delta + kt
+    assert hs2.backward_workspace_size(p, 3) == delta + kt + 2 * acc
+    # the K^T copy serves only the bf16, head-dim-128 dQ kernel
+    assert hs2.backward_workspace_size(base_problem(head_dim=64), 0) == 1 * 8 * 256 * 4
+    assert hs2.backward_workspace_size(base_problem(dtype=hs2.FP32), 0) == delta
     ws = hs2.backward_workspace_size(p, 2)
 
     def call(L=2, ws_bytes=ws, **over):

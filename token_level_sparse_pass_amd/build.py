@@ -16,7 +16,8 @@ LIB = os.path.join(HERE, "libhs2.so")
 SOURCES = ["hs2_api.hip", "attn_fwd.hip", "attn_fwd_bf16.hip", "attn_decode_bf16.hip",
            "score.hip", "score_bf16.hip",
            "select.hip", "kv_append.hip", "kv_bridge.hip",
-           "sparse_attn.hip", "sparse_attn_bf16.hip", "attn_bwd.hip", "sparse_bwd.hip"]
+           "sparse_attn.hip", "sparse_attn_bf16.hip", "attn_bwd.hip", "attn_bwd_bf16.hip",
+           "sparse_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -564,10 +564,12 @@ hs2_status hs2_kv_bridge(const hs2_problem* p, int32_t d_model, const void* hidd
 
 namespace {
 
-// Backward workspace: Delta [B][h_q][n_q] floats, then (with sparse layers)
-// the fp32 K and V gradient accumulators, [B][n_kv][h_kv][head_dim] each.
+// Backward workspace: Delta [B][h_q][n_q] floats; for bf16 / head_dim 128
+// the transposed K copy the dQ kernel reads ([B][h_kv][tile][d][64 keys]);
+// then (with sparse layers) the fp32 K and V gradient accumulators,
+// [B][n_kv][h_kv][head_dim] each.
 struct BwdLayout {
-  size_t delta = 0, acc_k = 0, acc_v = 0, acc_elems = 0, total = 0;
+  size_t delta = 0, kt = 0, kt_bytes = 0, acc_k = 0, acc_v = 0, acc_elems = 0, total = 0;
 };
 
 BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
@@ -575,6 +577,11 @@ BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
   size_t off = 0;
   L.delta = off;
   off += align_up((size_t)p.batch * p.h_q * p.n_q * sizeof(float));
+  if (hs2::bwd_dq_uses_bf16_kernel(shape_of(p))) {
+    L.kt = off;
+    L.kt_bytes = (size_t)p.batch * p.h_kv * hs2::vt_keys_for(p.n_kv) * p.head_dim * 2;
+    off += align_up(L.kt_bytes);
+  }
   if (n_sparse > 0) {
     L.acc_elems = (size_t)p.batch * p.n_kv * p.h_kv * p.head_dim;
     L.acc_k = off;
@@ -644,6 +651,16 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
   {
     PassTimer t(st, HS2_PASS_BWD_PREP);
     HIP_TRY(hs2::launch_bwd_delta(bp, st), "backward Delta");
+    if (L.kt_bytes) {
+      // K in the tile-major transposed layout of the dQ kernel's K^T operand
+      hs2::FwdPlan tp;
+      tp.s = shape_of(*p);
+      tp.v = k;
+      tp.vt = (char*)workspace + L.kt;
+      tp.vt_keys = hs2::vt_keys_for(p->n_kv);
+      HIP_TRY(hs2::launch_v_transpose(tp, st), "K transpose");
+      bp.kt = tp.vt;
+    }
     if (sparse) {
       HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");
       HIP_TRY(hs2::launch_zero_f32(acc_v, L.acc_elems, st), "zero accumulators");

@@ -234,7 +234,12 @@ struct BwdPlan {
   float* delta;
   const float* acc_k; const float* acc_v;
   void* dq; void* dk; void* dv;
+  // bf16 / head_dim 128: K transposed to [batch][h_kv][tile][head_dim][64]
+  // (as launch_v_transpose lays out V), read by the dQ kernel; NULL selects
+  // the generic dQ kernel
+  const void* kt = nullptr;
 };
+bool bwd_dq_uses_bf16_kernel(const Shape& s);
 hipError_t launch_bwd_delta(const BwdPlan& p, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st);   // after the delta
 hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st);     // after the delta
