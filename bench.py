@@ -291,6 +291,11 @@ def backward_work(w):
     S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q and dQ += dS K, 2 d
     flops each. The dK/dV kernel performs the first four; the dQ kernel's
     own share is dQ (it recomputes S and dP, which is not counted).
+    Preparation: Delta = rowsum(dO * O) (O, dO read, Delta written), the
+    sparse layers' fp32 accumulators cleared and, for bf16 at head dim 128,
+    K, Q and dO copied into the transposed tile layouts the dQ and dK/dV
+    kernels read (each read once and written once, plus lse and Delta read
+    and written again per row).
     Sparse layers: the K and V rows each query selects, gathered once per KV
     head; Q, O, dO read and dQ written for every layer; the fp32 K/V
     gradient rows read and written once per selected key.
@@ -300,9 +305,12 @@ def backward_work(w):
     pos = [nkv - nq + i for i in range(nq)]
     pairs = sum(p + 1 for p in pos) * B
     sel = sum(min(p + 1, w.top_k + w.window) for p in pos) * B
+    prep = 2.0 * B * nq * hq * d * esz + 4.0 * B * hq * nq + (2.0 * B * nkv * hkv * d * 4 if L else 0.0)
+    if w.dtype == "bf16" and d == 128:
+        # K^T copy, and Q / dO with their row statistics in transposed tiles
+        prep += 2.0 * B * nkv * hkv * d * esz + 4.0 * B * nq * hq * d * esz + 16.0 * B * hq * nq
     return {
-        "bwd_prep": ("hbm", 2.0 * B * nq * hq * d * esz + 4.0 * B * hq * nq +
-                     (2.0 * B * nkv * hkv * d * 4 if L else 0.0)),
+        "bwd_prep": ("hbm", prep),
         "bwd_sparse": ("hbm", sel * hkv * d * 2.0 * esz + 4.0 * L * B * nq * hq * d * esz +
                        sel * hkv * d * 2.0 * 4 * 2),
         "bwd_dkdv": ("mfma", 8.0 * hq * d * pairs),

@@ -214,10 +214,12 @@ def test_backward_workspace_and_rejections():
     lib = hs2.load()
     vp = ctypes.c_void_p
     p = base_problem()
-    # Delta rows, a bf16 K^T copy (bf16, head dim 128), then two fp32 K/V
+    # Delta rows; for bf16 at head dim 128 a K^T copy and the Q / dO rows in
+    # transposed 64-row tiles with their statistics; then two fp32 K/V
     # accumulators when there are sparse layers
     delta = 1 * 8 * 256 * 4
-    kt = 1 * 2 * 1024 * 128 * 2
+    tiles = 2 * (256 * 4 // 64)                      # KV heads x 64-row tiles
+    kt = 1 * 2 * 1024 * 128 * 2 + 2 * tiles * 64 * 128 * 2 + tiles * 128 * 4
     acc = 1 * 1024 * 2 * 128 * 4
     assert hs2.backward_workspace_size(p, 0) == delta + kt
     assert hs2.backward_workspace_size(p, 3) == delta + kt + 2 * acc

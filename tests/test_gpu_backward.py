@@ -79,6 +79,8 @@ BWD_CASES = [
     small("b_bf16_decode", "bf16", 3, 1, 900, 8, 2, 128, 64, 32, L=2),
     # 64 rows per work-group in the sparse backward: 8 layers x 8 heads
     small("b_bf16_64rows", "bf16", 1, 90, 300, 16, 2, 128, 40, 16, L=8),
+    # six heads per KV head: 64-row tiles start mid-query (64 = 10 * 6 + 4)
+    small("b_bf16_g6_chunk", "bf16", 2, 150, 420, 12, 2, 128, 40, 16, L=2),
 ]
 
 

@@ -518,7 +518,11 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st) {
 }
 
 hipError_t launch_bwd_delta(const BwdPlan& p, hipStream_t st) { return dispatch<DeltaF>(p, st); }
-hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st) { return dispatch<DkdvF>(p, st); }
+hipError_t launch_bwd_dkdv_bf16(const BwdPlan& p, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st) {
+  if (p.qt && bwd_dq_uses_bf16_kernel(p.s)) return launch_bwd_dkdv_bf16(p, st);
+  return dispatch<DkdvF>(p, st);
+}
 hipError_t launch_bwd_dq_bf16(const BwdPlan& p, hipStream_t st);
 
 hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st) {

@@ -1,12 +1,14 @@
-// dQ of the full layer's backward pass, specialised for bf16 and head dim
-// 128 (fine-tuning at long context; HySparse2 pages: "Xiaomi Unveils
-// HySparse2 for Faster Long-Context AI", section "Performance Gains: Cost,
-// Speed, and Long-Context Capabilities"). Same contract as the dQ kernel of
-// attn_bwd.hip:
-//   P = 2^(t * c - lse2),  dP = dO V^T,  dS = P * (dP - Delta),  dQ = scale dS K
+// dQ and dK/dV of the full layer's backward pass, specialised for bf16 and
+// head dim 128 (fine-tuning at long context; HySparse2 pages: "Xiaomi
+// Unveils HySparse2 for Faster Long-Context AI", section "Performance
+// Gains: Cost, Speed, and Long-Context Capabilities"). Same contract as the
+// kernels of attn_bwd.hip:
+//   P = 2^(t * c - lse2),  dP = dO V^T,  dS = P * (dP - Delta),
+//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
 // with t the raw logit q.k, c = scale * log2(e) and lse2 = lse * log2(e).
+// The dK/dV kernel and its row-layout kernel follow the dQ kernel below.
 //
-// Laid out like the forward pass-1 kernel: a work-group owns 256 rows
+// The dQ kernel is laid out like the forward pass-1 kernel: a work-group owns 256 rows
 // (query, head-of-group pairs) of one (sequence, KV head), eight waves of
 // two 16-row MFMA blocks, two waves per SIMD; each 64-key tile of K, V and
 // of a transposed copy of K (Kt[b][g][tile][d][64 keys], written once per
@@ -22,6 +24,10 @@
 #include "hs2_launch.h"
 
 #include <type_traits>
+
+#ifndef BWD_BF16_KB
+#define BWD_BF16_KB 1
+#endif
 
 namespace hs2 {
 
@@ -281,6 +287,396 @@ hipError_t launch_bwd_dq_bf16(const BwdPlan& p, hipStream_t st) {
   }
   const dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
   hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<RBW, NWV>), grid, dim3(64 * NWV), smem_bytes, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV of the full layer (bf16, head dim 128). A work-group owns 16 KB
+// keys per wave of one (sequence, KV head), their K and V rows held in
+// registers with the dK^T and dV^T accumulators, and walks the rows
+// (query, head-of-group pairs) that see them in 64-row tiles, from the last
+// tile down. Per tile four tensors come straight into a two-stage LDS ring:
+// the Q and dO rows (for S = Q K^T and dP = dO V^T, A = rows, B = keys) and
+// their transposed copies Qt, dOt [d][64 rows] written once per call by
+// bwd_rows_layout_kernel, so that the row contractions
+//   dV^T += dO^T P,   dK^T += Q^T dS          (A = Qt / dOt, B = P / dS)
+// read one 16-byte fragment per MFMA with no register transposes. Within
+// each 32-row half of a tile the transposed copies hold row
+// 16 (x / 4) + 4 q + x % 4 at position 8 q + x: the rows a lane of group q
+// holds in its S accumulators, in slot order.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int TR = 64;                               // rows per tile
+constexpr int ROWS_T_BYTES = TR * D * 2;             // 16 KB per tensor tile
+constexpr int DK_QR = 0, DK_DR = ROWS_T_BYTES, DK_QT = 2 * ROWS_T_BYTES, DK_DT = 3 * ROWS_T_BYTES;
+constexpr int DK_STAGE = 4 * ROWS_T_BYTES;           // stats of both stages follow the ring
+constexpr int DK_STATS = 2 * DK_STAGE;
+constexpr int DK_SMEM = DK_STATS + 2 * 2 * TR * 4;
+
+// tile row (in 0 .. 63) stored at position pos of a transposed tile
+__device__ __forceinline__ int trow_of_pos(int pos) {
+  const int x = pos & 7, q = (pos >> 3) & 3;
+  return (pos & 32) + 16 * (x >> 2) + 4 * q + (x & 3);
+}
+
+struct RowsArgs {
+  const __bf16* q; const __bf16* dout;
+  const float* lse; const float* delta;
+  __bf16* qt; __bf16* dot; float* rst;
+  int n_q, h_q, h_kv, n_rt;
+};
+
+struct DkdvArgs {
+  const __bf16* q; const __bf16* dout; const __bf16* k; const __bf16* v;
+  const __bf16* qt; const __bf16* dot; const float* rst;
+  const float* acc_k; const float* acc_v;
+  __bf16* dk; __bf16* dv;
+  int B, n_q, n_kv, h_q, h_kv, n_rt, n_kt;
+  int q64, r64;                                       // 64 = q64 * G + r64
+  float scale, c;
+};
+
+}  // namespace
+
+// Q and dO of one (sequence, KV head, 64-row tile) transposed to [d][64]
+// (position order above, zero past the last row), and the tile's
+// lse * log2(e) (+inf past the last row) and Delta, as rst[tile][2][64].
+__global__ __launch_bounds__(256) void bwd_rows_layout_kernel(RowsArgs a) {
+  __shared__ uint16_t tile[TR][D + 8];
+  const int G = a.h_q / a.h_kv;
+  const int R = a.n_q * G;
+  const int t = blockIdx.x % a.n_rt;
+  const int bg = blockIdx.x / a.n_rt;
+  const int g = bg % a.h_kv;
+  const int b = bg / a.h_kv;
+  const size_t tile_id = (size_t)bg * a.n_rt + t;
+#pragma unroll 1
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(which ? a.dout : a.q);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = threadIdx.x + 256 * it;
+      const int rr = u >> 4, c = u & 15;
+      const int r = t * TR + rr;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (r < R) {
+        const int i = r / G, h = r - (r / G) * G;
+        val = *reinterpret_cast<const uint4*>(src + (((size_t)b * a.n_q + i) * a.h_q + g * G + h) * D +
+                                              c * 8);
+      }
+      *reinterpret_cast<uint4*>(&tile[rr][c * 8]) = val;
+    }
+    __syncthreads();
+    uint16_t* dst = reinterpret_cast<uint16_t*>(which ? a.dot : a.qt) + tile_id * (D * TR);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int u = threadIdx.x + 256 * it;          // 1024 chunks of 8 positions
+      const int d = u >> 3, c = u & 7;
+      uint16_t e[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) e[x] = tile[trow_of_pos(8 * c + x)][d];
+      uint4 w;
+      w.x = e[0] | ((uint32_t)e[1] << 16);
+      w.y = e[2] | ((uint32_t)e[3] << 16);
+      w.z = e[4] | ((uint32_t)e[5] << 16);
+      w.w = e[6] | ((uint32_t)e[7] << 16);
+      *reinterpret_cast<uint4*>(dst + d * TR + c * 8) = w;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < TR) {
+    const int r = t * TR + threadIdx.x;
+    float l2 = INFINITY, dl = 0.f;                    // P = 0 past the last row
+    if (r < R) {
+      const int i = r / G, h = r - (r / G) * G;
+      const size_t si = ((size_t)b * a.h_q + g * G + h) * a.n_q + i;
+      l2 = a.lse[si] * LOG2E;
+      dl = a.delta[si];
+    }
+    a.rst[tile_id * (2 * TR) + threadIdx.x] = l2;
+    a.rst[tile_id * (2 * TR) + TR + threadIdx.x] = dl;
+  }
+}
+
+template <int KB, int NWV>
+__global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArgs a) {
+  using OP = Op<__bf16, D>;
+  constexpr int KT = 16 * KB * NWV;                   // keys per work-group
+  constexpr int CPT = 1024 / (64 * NWV);              // 16-byte chunks per thread per tensor
+  static_assert(CPT * 64 * NWV == 1024, "tile chunks must split evenly over the threads");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int G = a.h_q / a.h_kv;
+  const int R = a.n_q * G;
+  const int q_off = a.n_kv - a.n_q;
+  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int kt = (int)(lid % a.n_kt);                 // low key tiles (most rows) first
+  const int bg = (int)(lid / a.n_kt);
+  const int b = bg % a.B;
+  const int g = bg / a.B;
+  const int j0 = kt * KT;
+  const int jw = j0 + wave * KB * 16;
+
+  // ---- the wave's keys: K and V rows as B operands, gradient accumulators ----
+  const size_t kstride = (size_t)a.h_kv * D;
+  Frag<__bf16, D> kf[KB], vf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int j = jw + kb * 16 + l16;
+    if (j < a.n_kv) {
+      const size_t off = ((size_t)b * a.n_kv + j) * kstride + (size_t)g * D;
+      load_slice<__bf16, D>(kf[kb], a.k + off, lane);
+      load_slice<__bf16, D>(vf[kb], a.v + off, lane);
+    } else {
+      zero_slice<__bf16, D>(kf[kb]);
+      zero_slice<__bf16, D>(vf[kb]);
+    }
+  }
+  f32x4 dk[KB][8], dv[KB][8];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      dk[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // ---- row tiles: rows that see key j0 onwards, the last tile first ----
+  const int rt_begin = (max(0, j0 - q_off) * G) / TR;
+  const int i_need = j0 + KT - 1 - q_off;             // a tile is unmasked when its
+  int t_u = i_need <= 0 ? 0 : (int)(((int64_t)i_need * G + TR - 1) / TR);   // first row sees all keys
+  t_u = min(max(t_u, rt_begin), a.n_rt);
+  const int n_tiles = a.n_rt - rt_begin;
+  const int n_unm = a.n_rt - t_u;
+
+  // per-slot (query, head) of the row chunks this thread loads, for the
+  // tile issued next; stepped down by 64 rows per tile
+  const size_t tile0 = (size_t)(b * a.h_kv + g) * a.n_rt;
+  int si_[CPT], sh_[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int slot = (wave * CPT + c) * 64 + lane;
+    const int r = (a.n_rt - 1) * TR + (slot >> 4);
+    si_[c] = r / G;
+    sh_[c] = r - si_[c] * G;
+  }
+  const __bf16* qseq = a.q + ((size_t)b * a.n_q * a.h_q + (size_t)g * G) * D;
+  const __bf16* dseq = a.dout + ((size_t)b * a.n_q * a.h_q + (size_t)g * G) * D;
+
+  auto issue = [&](int tile, int stage) {
+    char* base = smem + stage * DK_STAGE;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int slot = (wave * CPT + c) * 64 + lane;
+      const int rr = slot >> 4, pc = slot & 15;
+      const int ch = pc ^ kswz(rr);
+      const size_t row = ((size_t)min(si_[c], a.n_q - 1) * a.h_q + sh_[c]) * D + ch * 8;
+      const __bf16* qs = qseq + row;
+      const __bf16* ds = dseq + row;
+      __builtin_amdgcn_global_load_lds(qs, (lds_void*)(base + DK_QR + (wave * CPT + c) * 1024), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds(ds, (lds_void*)(base + DK_DR + (wave * CPT + c) * 1024), 16, 0,
+                                       0);
+      // the same slot, 64 rows lower, for the next tile
+      sh_[c] -= a.r64;
+      si_[c] -= a.q64;
+      if (sh_[c] < 0) { sh_[c] += G; si_[c] -= 1; }
+    }
+    const size_t toff_g = (tile0 + tile) * (size_t)(D * TR);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int slot = (wave * CPT + c) * 64 + lane;
+      const int d = slot >> 3, pc = slot & 7;
+      const int ch = pc ^ tswz(d);
+      const __bf16* qs = a.qt + toff_g + d * TR + ch * 8;
+      const __bf16* ds = a.dot + toff_g + d * TR + ch * 8;
+      __builtin_amdgcn_global_load_lds(qs, (lds_void*)(base + DK_QT + (wave * CPT + c) * 1024), 16, 0,
+                                       0);
+      __builtin_amdgcn_global_load_lds(ds, (lds_void*)(base + DK_DT + (wave * CPT + c) * 1024), 16, 0,
+                                       0);
+    }
+    if (wave == 0 && lane < 32) {
+      const float* ss = a.rst + (tile0 + tile) * (size_t)(2 * TR) + lane * 4;
+      __builtin_amdgcn_global_load_lds(ss, (lds_void*)(smem + DK_STATS + stage * (2 * TR * 4)), 16, 0,
+                                       0);
+    }
+  };
+
+  // per-lane LDS offsets: row blocks 0, 1 (blocks 2, 3 are 8 KB on with the
+  // same swizzle); transposed rows d = 16 db + l16 (db * 2 KB on)
+  int roff[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = 16 * rb + l16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) roff[rb][u] = row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
+  }
+  int toff[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) toff[st] = l16 * 128 + (((4 * st + grp) ^ tswz(l16)) << 4);
+
+  if (n_tiles > 0) issue(a.n_rt - 1, 0);
+  auto step = [&](int u, auto stage_c, auto masked_c) {
+    constexpr int STAGE_C = decltype(stage_c)::value;     // -1: runtime
+    constexpr bool masked = decltype(masked_c)::value;
+    const int stage = STAGE_C >= 0 ? STAGE_C : (u & 1);
+    const int t = a.n_rt - 1 - u;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    // the other stage held the previous tile, which every wave finished
+    // reading before the barrier above
+    if (u + 1 < n_tiles) issue(t - 1, stage ^ 1);
+    const char* base = smem + stage * DK_STAGE;
+    const char* stats = smem + DK_STATS + stage * (2 * TR * 4);
+
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // P and dS of rows 32 st .. +31 for the wave's keys, packed as the B
+      // operands of the row contractions
+      bf16x8 pu[KB], du[KB];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int rb = 2 * st + h2;
+        const f32x4 l2v = *reinterpret_cast<const f32x4*>(stats + (16 * rb + 4 * grp) * 4);
+        const f32x4 dlv = *reinterpret_cast<const f32x4*>(stats + TR * 4 + (16 * rb + 4 * grp) * 4);
+        f32x4 sv[KB], dp[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const bf16x8 qa =
+              *reinterpret_cast<const bf16x8*>(base + DK_QR + roff[rb & 1][uu] + (rb >> 1) * 8192);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sv[kb] = OP::mma(qa, kf[kb].u[uu], sv[kb]);
+        }
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          const bf16x8 da =
+              *reinterpret_cast<const bf16x8*>(base + DK_DR + roff[rb & 1][uu] + (rb >> 1) * 8192);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) dp[kb] = OP::mma(da, vf[kb].u[uu], dp[kb]);
+        }
+        // lane: rows 16 rb + 4 grp + e, key jw + 16 kb + l16
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pv = fast_exp2(fmaf(sv[kb][e], a.c, -l2v[e]));
+            if constexpr (masked) {
+              const int pos = q_off + (t * TR + 16 * rb + 4 * grp + e) / G;
+              if (jw + 16 * kb + l16 > pos) pv = 0.f;
+            }
+            pu[kb][4 * h2 + e] = (__bf16)pv;
+            du[kb][4 * h2 + e] = (__bf16)(pv * (dp[kb][e] - dlv[e]));
+          }
+      }
+      // dV^T += dOt . P and dK^T += Qt . dS over the half's 32 rows
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(base + DK_DT + toff[st] + db * 2048);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dv[kb][db] = OP::mma(ta, pu[kb], dv[kb][db]);
+      }
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(base + DK_QT + toff[st] + db * 2048);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) dk[kb][db] = OP::mma(ta, du[kb], dk[kb][db]);
+      }
+    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int u = 0;
+  for (; u + 1 < n_unm; u += 2) {
+    step(u, S0{}, std::false_type{});
+    step(u + 1, S1{}, std::false_type{});
+  }
+  if (u < n_unm) step(u++, S0{}, std::false_type{});
+  for (; u < n_tiles; ++u) step(u, std::integral_constant<int, -1>{}, std::true_type{});
+
+  // lane holds dK^T / dV^T at d = 16 db + 4 grp + e for key jw + 16 kb + l16
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int j = jw + 16 * kb + l16;
+    if (j >= a.n_kv) continue;
+    const size_t off = ((size_t)b * a.n_kv + j) * kstride + (size_t)g * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      f32x4 xk = dk[kb][db] * a.scale, xv = dv[kb][db];
+      if (a.acc_k) {
+        xk += *reinterpret_cast<const f32x4*>(a.acc_k + off + 16 * db);
+        xv += *reinterpret_cast<const f32x4*>(a.acc_v + off + 16 * db);
+      }
+      __attribute__((ext_vector_type(4))) __bf16 wk, wv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wk[e] = (__bf16)xk[e];
+        wv[e] = (__bf16)xv[e];
+      }
+      *reinterpret_cast<decltype(wk)*>(a.dk + off + 16 * db) = wk;
+      *reinterpret_cast<decltype(wv)*>(a.dv + off + 16 * db) = wv;
+    }
+  }
+}
+
+size_t bwd_rows_layout_tiles(const Shape& s) {
+  const int G = s.h_q / s.h_kv;
+  return (size_t)s.batch * s.h_kv * (((size_t)s.n_q * G + TR - 1) / TR);
+}
+
+hipError_t launch_bwd_rows_layout(const BwdPlan& p, hipStream_t st) {
+  RowsArgs a;
+  a.q = reinterpret_cast<const __bf16*>(p.q);
+  a.dout = reinterpret_cast<const __bf16*>(p.dout);
+  a.lse = p.lse; a.delta = p.delta;
+  a.qt = reinterpret_cast<__bf16*>(p.qt);
+  a.dot = reinterpret_cast<__bf16*>(p.dot);
+  a.rst = p.rst;
+  a.n_q = p.s.n_q; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
+  const int G = a.h_q / a.h_kv;
+  a.n_rt = (int)(((size_t)a.n_q * G + TR - 1) / TR);
+  hipLaunchKernelGGL(bwd_rows_layout_kernel, dim3((unsigned)bwd_rows_layout_tiles(p.s)), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdPlan& p, hipStream_t st) {
+  constexpr int KB = BWD_BF16_KB, NWV = 8;
+  DkdvArgs a;
+  a.q = reinterpret_cast<const __bf16*>(p.q);
+  a.dout = reinterpret_cast<const __bf16*>(p.dout);
+  a.k = reinterpret_cast<const __bf16*>(p.k);
+  a.v = reinterpret_cast<const __bf16*>(p.v);
+  a.qt = reinterpret_cast<const __bf16*>(p.qt);
+  a.dot = reinterpret_cast<const __bf16*>(p.dot);
+  a.rst = p.rst;
+  a.acc_k = p.acc_k; a.acc_v = p.acc_v;
+  a.dk = reinterpret_cast<__bf16*>(p.dk);
+  a.dv = reinterpret_cast<__bf16*>(p.dv);
+  a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
+  const int G = a.h_q / a.h_kv;
+  a.n_rt = (int)(((size_t)a.n_q * G + TR - 1) / TR);
+  a.n_kt = (a.n_kv + 16 * KB * NWV - 1) / (16 * KB * NWV);
+  a.q64 = TR / G; a.r64 = TR % G;
+  a.scale = p.scale; a.c = p.s.scale_log2;
+  struct DkdvLdsTag {};
+  {
+    const hipError_t e = ensure_dynamic_lds<DkdvLdsTag>(
+        (const void*)attn_bwd_dkdv_bf16_kernel<KB, NWV>, DK_SMEM);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)((size_t)a.n_kt * a.B * a.h_kv));
+  hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<KB, NWV>), grid, dim3(64 * NWV), DK_SMEM, st, a);
   return hipGetLastError();
 }
 

@@ -570,6 +570,7 @@ namespace {
 // [B][n_kv][h_kv][head_dim] each.
 struct BwdLayout {
   size_t delta = 0, kt = 0, kt_bytes = 0, acc_k = 0, acc_v = 0, acc_elems = 0, total = 0;
+  size_t qt = 0, dot = 0, rst = 0, rows_tiles = 0;
 };
 
 BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
@@ -581,6 +582,14 @@ BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
     L.kt = off;
     L.kt_bytes = (size_t)p.batch * p.h_kv * hs2::vt_keys_for(p.n_kv) * p.head_dim * 2;
     off += align_up(L.kt_bytes);
+    L.rows_tiles = hs2::bwd_rows_layout_tiles(shape_of(p));
+    const size_t tile_bytes = (size_t)64 * p.head_dim * 2;
+    L.qt = off;
+    off += align_up(L.rows_tiles * tile_bytes);
+    L.dot = off;
+    off += align_up(L.rows_tiles * tile_bytes);
+    L.rst = off;
+    off += align_up(L.rows_tiles * 128 * sizeof(float));
   }
   if (n_sparse > 0) {
     L.acc_elems = (size_t)p.batch * p.n_kv * p.h_kv * p.head_dim;
@@ -660,6 +669,11 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
       tp.vt_keys = hs2::vt_keys_for(p->n_kv);
       HIP_TRY(hs2::launch_v_transpose(tp, st), "K transpose");
       bp.kt = tp.vt;
+      // Q and dO in the dK/dV kernel's transposed tile layout
+      bp.qt = (char*)workspace + L.qt;
+      bp.dot = (char*)workspace + L.dot;
+      bp.rst = fptr(workspace, L.rst);
+      HIP_TRY(hs2::launch_bwd_rows_layout(bp, st), "row layout");
     }
     if (sparse) {
       HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");

@@ -238,8 +238,19 @@ struct BwdPlan {
   // (as launch_v_transpose lays out V), read by the dQ kernel; NULL selects
   // the generic dQ kernel
   const void* kt = nullptr;
+  // bf16 / head_dim 128: Q and dO transposed per (sequence, KV head, tile of
+  // 64 rows) to [head_dim][64], and the tiles' rows' lse * log2(e) and Delta
+  // ([tile][2][64]); written by launch_bwd_rows_layout, read by the dK/dV
+  // kernel; NULL selects the generic dK/dV kernel
+  void* qt = nullptr;
+  void* dot = nullptr;
+  float* rst = nullptr;
 };
 bool bwd_dq_uses_bf16_kernel(const Shape& s);
+// tiles of the transposed row layout (each 64 x head_dim elements of qt and
+// of dot, 128 floats of rst)
+size_t bwd_rows_layout_tiles(const Shape& s);
+hipError_t launch_bwd_rows_layout(const BwdPlan& p, hipStream_t st);   // after the delta
 hipError_t launch_bwd_delta(const BwdPlan& p, hipStream_t st);
 hipError_t launch_bwd_dkdv(const BwdPlan& p, hipStream_t st);   // after the delta
 hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st);     // after the delta
