@@ -25,9 +25,6 @@
 
 #include <type_traits>
 
-#ifndef BWD_BF16_KB
-#define BWD_BF16_KB 1
-#endif
 
 namespace hs2 {
 
@@ -291,13 +288,12 @@ hipError_t launch_bwd_dq_bf16(const BwdPlan& p, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV of the full layer (bf16, head dim 128). A work-group owns 16 KB
-// keys per wave of one (sequence, KV head), their K and V rows held in
-// registers with the dK^T and dV^T accumulators, and walks the rows
-// (query, head-of-group pairs) that see them in 64-row tiles, from the last
-// tile down. Per tile four tensors come straight into a two-stage LDS ring:
-// the Q and dO rows (for S = Q K^T and dP = dO V^T, A = rows, B = keys) and
-// their transposed copies Qt, dOt [d][64 rows] written once per call by
+// dK, dV of the full layer (bf16, head dim 128). A work-group owns 128 keys
+// of one (sequence, KV head) and walks the rows (query, head-of-group pairs)
+// that see them in 64-row tiles, from the last tile down. Per tile four
+// tensors come straight into a two-stage LDS ring: the Q and dO rows (for
+// S = Q K^T and dP = dO V^T, A = rows, B = keys) and their transposed
+// copies Qt, dOt [d][64 rows] written once per call by
 // bwd_rows_layout_kernel, so that the row contractions
 //   dV^T += dO^T P,   dK^T += Q^T dS          (A = Qt / dOt, B = P / dS)
 // read one 16-byte fragment per MFMA with no register transposes. Within
@@ -400,20 +396,33 @@ __global__ __launch_bounds__(256) void bwd_rows_layout_kernel(RowsArgs a) {
   }
 }
 
-template <int KB, int NWV>
-__global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArgs a) {
+// dK, dV with paired waves: waves 0..3 hold the K rows of 32 keys each and
+// accumulate dV^T, waves 4..7 hold the V rows of the same keys and
+// accumulate dK^T, so each wave keeps 32 keys' operands and one set of
+// accumulators (96 registers) where one wave holding both would need 192.
+// Per 64-row tile, a K wave forms S = Q K^T and P, hands P (bf16, in its
+// accumulator lane order) to its V wave through LDS and adds dO^T P; the V
+// wave forms dP = dO V^T, then dS = P (dP - Delta) and adds Q^T dS. Each
+// LDS fragment read then feeds two key blocks' MFMAs.
+constexpr int DKP_X = DK_SMEM;                        // P hand-over: [pair][st][kb][lane] x 16 B
+constexpr int DKP_SMEM = DKP_X + 4 * 2 * 2 * 64 * 16;
+constexpr int DKP_KEYS = 128;                         // keys per work-group
+
+__global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArgs a) {
   using OP = Op<__bf16, D>;
-  constexpr int KT = 16 * KB * NWV;                   // keys per work-group
-  constexpr int CPT = 1024 / (64 * NWV);              // 16-byte chunks per thread per tensor
-  static_assert(CPT * 64 * NWV == 1024, "tile chunks must split evenly over the threads");
+  constexpr int NWV = 8, KB = 2;
+  constexpr int KT = 16 * KB * (NWV / 2);
+  static_assert(KT == DKP_KEYS, "keys per work-group");
+  constexpr int CPT = 1024 / (64 * NWV);
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int grp = lane >> 4;
   const int l16 = lane & 15;
+  const bool vwave = wave >= 4;                       // V rows, dK; else K rows, dV
+  const int pair = wave & 3;
   const int G = a.h_q / a.h_kv;
-  const int R = a.n_q * G;
   const int q_off = a.n_kv - a.n_q;
   const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int kt = (int)(lid % a.n_kt);                 // low key tiles (most rows) first
@@ -421,31 +430,26 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
   const int b = bg % a.B;
   const int g = bg / a.B;
   const int j0 = kt * KT;
-  const int jw = j0 + wave * KB * 16;
+  const int jw = j0 + pair * KB * 16;
 
-  // ---- the wave's keys: K and V rows as B operands, gradient accumulators ----
+  // ---- the pair's keys: K (or V) rows as B operands, one accumulator set ----
   const size_t kstride = (size_t)a.h_kv * D;
-  Frag<__bf16, D> kf[KB], vf[KB];
+  Frag<__bf16, D> kv[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int j = jw + kb * 16 + l16;
     if (j < a.n_kv) {
       const size_t off = ((size_t)b * a.n_kv + j) * kstride + (size_t)g * D;
-      load_slice<__bf16, D>(kf[kb], a.k + off, lane);
-      load_slice<__bf16, D>(vf[kb], a.v + off, lane);
+      load_slice<__bf16, D>(kv[kb], (vwave ? a.v : a.k) + off, lane);
     } else {
-      zero_slice<__bf16, D>(kf[kb]);
-      zero_slice<__bf16, D>(vf[kb]);
+      zero_slice<__bf16, D>(kv[kb]);
     }
   }
-  f32x4 dk[KB][8], dv[KB][8];
+  f32x4 acc[KB][8];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      dk[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int db = 0; db < 8; ++db) acc[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- row tiles: rows that see key j0 onwards, the last tile first ----
   const int rt_begin = (max(0, j0 - q_off) * G) / TR;
@@ -508,8 +512,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
     }
   };
 
-  // per-lane LDS offsets: row blocks 0, 1 (blocks 2, 3 are 8 KB on with the
-  // same swizzle); transposed rows d = 16 db + l16 (db * 2 KB on)
   int roff[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -520,10 +522,16 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
   int toff[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) toff[st] = l16 * 128 + (((4 * st + grp) ^ tswz(l16)) << 4);
+  // this lane's P slot of (st, kb) in the pair's hand-over buffer
+  char* xp = smem + DKP_X + pair * (2 * 2 * 64 * 16) + lane * 16;
+  // the row operand of S (Q, K waves) or dP (dO, V waves), and the
+  // transposed operand of the row contraction (dO^T for dV, Q^T for dK)
+  const int row_src = vwave ? DK_DR : DK_QR;
+  const int t_src = vwave ? DK_QT : DK_DT;
 
   if (n_tiles > 0) issue(a.n_rt - 1, 0);
   auto step = [&](int u, auto stage_c, auto masked_c) {
-    constexpr int STAGE_C = decltype(stage_c)::value;     // -1: runtime
+    constexpr int STAGE_C = decltype(stage_c)::value;
     constexpr bool masked = decltype(masked_c)::value;
     const int stage = STAGE_C >= 0 ? STAGE_C : (u & 1);
     const int t = a.n_rt - 1 - u;
@@ -535,64 +543,77 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
     const char* base = smem + stage * DK_STAGE;
     const char* stats = smem + DK_STATS + stage * (2 * TR * 4);
 
+    // logits S (K waves) or dP (V waves) of the tile's 64 rows
+    f32x4 x[2][2][KB];                                // [st][h2][kb]
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // P and dS of rows 32 st .. +31 for the wave's keys, packed as the B
-      // operands of the row contractions
-      bf16x8 pu[KB], du[KB];
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int rb = 2 * st + h2;
-        const f32x4 l2v = *reinterpret_cast<const f32x4*>(stats + (16 * rb + 4 * grp) * 4);
-        const f32x4 dlv = *reinterpret_cast<const f32x4*>(stats + TR * 4 + (16 * rb + 4 * grp) * 4);
-        f32x4 sv[KB], dp[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int kb = 0; kb < KB; ++kb) x[st][h2][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int uu = 0; uu < 4; ++uu) {
-          const bf16x8 qa =
-              *reinterpret_cast<const bf16x8*>(base + DK_QR + roff[rb & 1][uu] + (rb >> 1) * 8192);
+          const bf16x8 ra =
+              *reinterpret_cast<const bf16x8*>(base + row_src + roff[rb & 1][uu] + (rb >> 1) * 8192);
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sv[kb] = OP::mma(qa, kf[kb].u[uu], sv[kb]);
+          for (int kb = 0; kb < KB; ++kb) x[st][h2][kb] = OP::mma(ra, kv[kb].u[uu], x[st][h2][kb]);
+        }
+      }
+    bf16x8 pk[2][KB];                                 // P (K waves) / dS (V waves), packed
+    if (!vwave) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rb = 2 * st + h2;
+          const f32x4 l2v = *reinterpret_cast<const f32x4*>(stats + (16 * rb + 4 * grp) * 4);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pv = fast_exp2(fmaf(x[st][h2][kb][e], a.c, -l2v[e]));
+              if constexpr (masked) {
+                const int pos = q_off + (t * TR + 16 * rb + 4 * grp + e) / G;
+                if (jw + 16 * kb + l16 > pos) pv = 0.f;
+              }
+              pk[st][kb][4 * h2 + e] = (__bf16)pv;
+            }
         }
 #pragma unroll
-        for (int uu = 0; uu < 4; ++uu) {
-          const bf16x8 da =
-              *reinterpret_cast<const bf16x8*>(base + DK_DR + roff[rb & 1][uu] + (rb >> 1) * 8192);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) dp[kb] = OP::mma(da, vf[kb].u[uu], dp[kb]);
-        }
-        // lane: rows 16 rb + 4 grp + e, key jw + 16 kb + l16
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
+          *reinterpret_cast<bf16x8*>(xp + (st * 2 + kb) * 1024) = pk[st][kb];
+    }
+    __syncthreads();                                  // P of every pair handed over
+    if (vwave) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float pv = fast_exp2(fmaf(sv[kb][e], a.c, -l2v[e]));
-            if constexpr (masked) {
-              const int pos = q_off + (t * TR + 16 * rb + 4 * grp + e) / G;
-              if (jw + 16 * kb + l16 > pos) pv = 0.f;
-            }
-            pu[kb][4 * h2 + e] = (__bf16)pv;
-            du[kb][4 * h2 + e] = (__bf16)(pv * (dp[kb][e] - dlv[e]));
-          }
-      }
-      // dV^T += dOt . P and dK^T += Qt . dS over the half's 32 rows
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 pv[KB];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(base + DK_DT + toff[st] + db * 2048);
+        for (int kb = 0; kb < KB; ++kb) pv[kb] = *reinterpret_cast<const bf16x8*>(xp + (st * 2 + kb) * 1024);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dv[kb][db] = OP::mma(ta, pu[kb], dv[kb][db]);
-      }
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int rb = 2 * st + h2;
+          const f32x4 dlv = *reinterpret_cast<const f32x4*>(stats + TR * 4 + (16 * rb + 4 * grp) * 4);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(base + DK_QT + toff[st] + db * 2048);
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) dk[kb][db] = OP::mma(ta, du[kb], dk[kb][db]);
+            for (int e = 0; e < 4; ++e)
+              pk[st][kb][4 * h2 + e] = (__bf16)((float)pv[kb][4 * h2 + e] * (x[st][h2][kb][e] - dlv[e]));
+        }
       }
     }
+    // dV^T += dOt . P (K waves) or dK^T += Qt . dS (V waves)
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 ta = *reinterpret_cast<const bf16x8*>(base + t_src + toff[st] + db * 2048);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc[kb][db] = OP::mma(ta, pk[st][kb], acc[kb][db]);
+      }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -604,7 +625,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
   if (u < n_unm) step(u++, S0{}, std::false_type{});
   for (; u < n_tiles; ++u) step(u, std::integral_constant<int, -1>{}, std::true_type{});
 
-  // lane holds dK^T / dV^T at d = 16 db + 4 grp + e for key jw + 16 kb + l16
+  // lane holds dV^T (K waves) or dK^T (V waves) at d = 16 db + 4 grp + e
+  // for key jw + 16 kb + l16
+  const float mul = vwave ? a.scale : 1.f;
+  const float* add = vwave ? a.acc_k : a.acc_v;
+  __bf16* out = vwave ? a.dk : a.dv;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int j = jw + 16 * kb + l16;
@@ -612,19 +637,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dkdv_bf16_kernel(DkdvArg
     const size_t off = ((size_t)b * a.n_kv + j) * kstride + (size_t)g * D + 4 * grp;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      f32x4 xk = dk[kb][db] * a.scale, xv = dv[kb][db];
-      if (a.acc_k) {
-        xk += *reinterpret_cast<const f32x4*>(a.acc_k + off + 16 * db);
-        xv += *reinterpret_cast<const f32x4*>(a.acc_v + off + 16 * db);
-      }
-      __attribute__((ext_vector_type(4))) __bf16 wk, wv;
+      f32x4 xo = acc[kb][db] * mul;
+      if (add) xo += *reinterpret_cast<const f32x4*>(add + off + 16 * db);
+      __attribute__((ext_vector_type(4))) __bf16 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wk[e] = (__bf16)xk[e];
-        wv[e] = (__bf16)xv[e];
-      }
-      *reinterpret_cast<decltype(wk)*>(a.dk + off + 16 * db) = wk;
-      *reinterpret_cast<decltype(wv)*>(a.dv + off + 16 * db) = wv;
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)xo[e];
+      *reinterpret_cast<decltype(w)*>(out + off + 16 * db) = w;
     }
   }
 }
@@ -651,7 +669,6 @@ hipError_t launch_bwd_rows_layout(const BwdPlan& p, hipStream_t st) {
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdPlan& p, hipStream_t st) {
-  constexpr int KB = BWD_BF16_KB, NWV = 8;
   DkdvArgs a;
   a.q = reinterpret_cast<const __bf16*>(p.q);
   a.dout = reinterpret_cast<const __bf16*>(p.dout);
@@ -666,17 +683,17 @@ hipError_t launch_bwd_dkdv_bf16(const BwdPlan& p, hipStream_t st) {
   a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   const int G = a.h_q / a.h_kv;
   a.n_rt = (int)(((size_t)a.n_q * G + TR - 1) / TR);
-  a.n_kt = (a.n_kv + 16 * KB * NWV - 1) / (16 * KB * NWV);
+  a.n_kt = (a.n_kv + DKP_KEYS - 1) / DKP_KEYS;
   a.q64 = TR / G; a.r64 = TR % G;
   a.scale = p.scale; a.c = p.s.scale_log2;
   struct DkdvLdsTag {};
   {
     const hipError_t e = ensure_dynamic_lds<DkdvLdsTag>(
-        (const void*)attn_bwd_dkdv_bf16_kernel<KB, NWV>, DK_SMEM);
+        (const void*)attn_bwd_dkdv_bf16_pair_kernel, DKP_SMEM);
     if (e != hipSuccess) return e;
   }
   const dim3 grid((unsigned)((size_t)a.n_kt * a.B * a.h_kv));
-  hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<KB, NWV>), grid, dim3(64 * NWV), DK_SMEM, st, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_bf16_pair_kernel, grid, dim3(512), DKP_SMEM, st, a);
   return hipGetLastError();
 }
 
