@@ -81,6 +81,9 @@ BWD_CASES = [
     small("b_bf16_64rows", "bf16", 1, 90, 300, 16, 2, 128, 40, 16, L=8),
     # six heads per KV head: 64-row tiles start mid-query (64 = 10 * 6 + 4)
     small("b_bf16_g6_chunk", "bf16", 2, 150, 420, 12, 2, 128, 40, 16, L=2),
+    # one query head per KV head, and a single partial 64-row tile (15 rows)
+    small("b_bf16_g1", "bf16", 1, 100, 260, 4, 4, 128, 40, 16, L=2),
+    small("b_bf16_g3_tiny", "bf16", 1, 5, 70, 6, 2, 128, 16, 8, L=1),
 ]
 
 
