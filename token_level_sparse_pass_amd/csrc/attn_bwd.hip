@@ -135,9 +135,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int R = a.n_q * G;
   const int q_off = a.n_kv - a.n_q;
 
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int kt = (int)(lid % a.n_tiles);              // low key tiles (most rows) first
-  const int bg = (int)(lid / a.n_tiles);
+  // longest first over the whole grid: key tile 0 (seen by the most rows)
+  // of every (sequence, KV head), then tile 1, ...
+  const int kt = (int)(blockIdx.x / (a.B * a.h_kv));
+  const int bg = (int)(blockIdx.x % (a.B * a.h_kv));
   const int b = bg % a.B;
   const int g = bg / a.B;
   const int j0 = kt * KT;
@@ -316,9 +317,9 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdArgs a) {
   const int R = a.n_q * G;
   const int q_off = a.n_kv - a.n_q;
 
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int rt = a.n_tiles - 1 - (int)(lid % a.n_tiles);   // heavy tiles first
-  const int bg = (int)(lid / a.n_tiles);
+  // longest first over the whole grid (row tile descending)
+  const int rt = a.n_tiles - 1 - (int)(blockIdx.x / (a.B * a.h_kv));
+  const int bg = (int)(blockIdx.x % (a.B * a.h_kv));
   const int b = bg % a.B;
   const int g = bg / a.B;
   const int r0 = rt * ROWS;

@@ -74,9 +74,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_bwd_dq_bf16_kernel(DqArgs a)
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.h_q / a.h_kv;
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int rt = a.n_rt - 1 - (int)(lid % a.n_rt);      // heavy tiles first
-  const int bg = lid / a.n_rt;
+  // longest first over the whole grid (row tile descending, every
+  // (sequence, KV head) at each step), as in the forward kernel
+  const int rt = a.n_rt - 1 - (int)(blockIdx.x / (a.B * a.h_kv));
+  const int bg = blockIdx.x % (a.B * a.h_kv);
   const int b = bg % a.B;
   const int g = bg / a.B;
 
@@ -424,9 +425,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArg
   const int pair = wave & 3;
   const int G = a.h_q / a.h_kv;
   const int q_off = a.n_kv - a.n_q;
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int kt = (int)(lid % a.n_kt);                 // low key tiles (most rows) first
-  const int bg = (int)(lid / a.n_kt);
+  // longest first over the whole grid: key tile 0 (seen by the most rows)
+  // of every (sequence, KV head), then tile 1, ...
+  const int kt = (int)(blockIdx.x / (a.B * a.h_kv));
+  const int bg = (int)(blockIdx.x % (a.B * a.h_kv));
   const int b = bg % a.B;
   const int g = bg / a.B;
   const int j0 = kt * KT;

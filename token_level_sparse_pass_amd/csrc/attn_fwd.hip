@@ -98,9 +98,10 @@ __global__ __launch_bounds__(256) void attn_fwd_prefill_kernel(FwdArgs a) {
   const int R = a.n_q * G;
   const int q_off = a.n_kv - a.n_q;
 
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int rt = a.n_rt - 1 - (int)(lid % a.n_rt);      // heavy tiles first
-  const int bg = lid / a.n_rt;
+  // longest first over the whole grid (row tile descending, every
+  // (sequence, KV head) at each step): balances causal work
+  const int rt = a.n_rt - 1 - (int)(blockIdx.x / (a.B * a.h_kv));
+  const int bg = blockIdx.x % (a.B * a.h_kv);
   const int b = bg % a.B;
   const int g = bg / a.B;
   const int r0 = rt * ROWS;

@@ -152,8 +152,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     st0 = (size_t)3 * a.h_q * a.vl.q0[s];
     plane = (size_t)a.h_q * nq;
   } else {
-    rt = a.n_rt - 1 - (int)(lid % a.n_rt);              // heavy tiles first
-    const int bg = lid / a.n_rt;
+    // longest first over the whole grid: row tile n_rt - 1 of every
+    // (sequence, KV head), then n_rt - 2, ...; the dispatcher fills
+    // whichever CU frees up, so this balances causal work (grouping one KV
+    // head's tiles per XCD instead left the XCDs with the heavy tiles
+    // running long after the others had finished)
+    rt = a.n_rt - 1 - (int)(blockIdx.x / (a.B * a.h_kv));
+    const int bg = blockIdx.x % (a.B * a.h_kv);
     const int b = bg % a.B;
     g = bg / a.B;
     nq = a.n_q;
