@@ -126,7 +126,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.h_q / a.h_kv;
-  const uint32_t lid = xcd_swizzle(blockIdx.x, gridDim.x);
 
   // this work-group's sequence: its lengths, token offsets into the packed
   // tensors, transposed-V block, and its statistics block (3 planes of
@@ -135,11 +134,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   size_t qtok0, ktok0, vt_tile0, st0, plane;
   int vt_tiles;
   if (a.vl.n > 0) {
-    // row tiles fastest, KV head slowest: neighbouring ids (one XCD, one
-    // L2) share a sequence's K/V head
-    const int n_t = a.vl.tile0[a.vl.n];
-    g = (int)(lid / n_t);
-    const int t = (int)(lid - (uint32_t)g * n_t);
+    // KV head fastest, then the table's tiles in order (sequences longest
+    // context first, each heaviest tile first), as the dispatcher starts
+    // them: longest first over the whole grid
+    g = (int)(blockIdx.x % a.h_kv);
+    const int t = (int)(blockIdx.x / a.h_kv);
     int s = 0;
     while (s + 1 < a.vl.n && t >= a.vl.tile0[s + 1]) ++s;
     nq = a.vl.nq[s];

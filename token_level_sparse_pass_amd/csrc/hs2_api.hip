@@ -873,10 +873,14 @@ hs2_status run_varlen_prefill(const hs2_problem& p, int32_t n_sparse_layers,
     PassTimer t(st, HS2_PASS_LAYOUT);
     HIP_TRY(hs2::launch_v_transpose(tf, st), "V transpose");
   }
-  // sequences in batch order: the work-groups of one sequence then run
-  // together and share its K/V in L2 (dispatching the longest contexts
-  // first measured 15 % slower on a batch of agent turns)
-  const std::vector<int>& order = seqs;
+  // longest context first: a row tile's work grows with its sequence's
+  // key count, and the kernel hands out tiles in table order (every KV
+  // head of a tile together), so the long tiles start first and the tail
+  // is short
+  std::vector<int> order = seqs;
+  std::stable_sort(order.begin(), order.end(), [&](int x, int y) {
+    return cu_kv[x + 1] - cu_kv[x] > cu_kv[y + 1] - cu_kv[y];
+  });
   for (size_t g0 = 0; g0 < order.size(); g0 += hs2::VARLEN_MAX_SEQS) {
     hs2::VarlenSeqs d;
     d.n = (int)std::min<size_t>(hs2::VARLEN_MAX_SEQS, order.size() - g0);
