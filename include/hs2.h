@@ -298,8 +298,10 @@ hs2_status hs2_block_forward_paged(const hs2_problem* p, const hs2_kv_pages* pag
  * deterministic. With n_sparse_layers = 0, q_sparse, o_sparse, idx,
  * do_sparse and dq_sparse may be NULL.
  * Workspace: hs2_backward_workspace_size bytes (Delta = rowsum(dO * O) per
- * row; for bf16 at head dim 128 a tiled K^T copy that the dQ kernel reads;
- * the sparse layers' fp32 K/V accumulators), 16-byte aligned. */
+ * row; for bf16 at head dim 128 a tiled K^T copy that the dQ kernel reads,
+ * and Q and dO in transposed 64-row tiles with their rows' lse and Delta,
+ * which the dK/dV kernel reads; the sparse layers' fp32 K/V accumulators),
+ * 16-byte aligned. */
 hs2_status hs2_backward_workspace_size(const hs2_problem* p, int32_t n_sparse_layers,
                                        size_t* bytes);
 hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
@@ -330,7 +332,8 @@ typedef enum {
   HS2_PASS_SELECT = 2,
   HS2_PASS_SPARSE = 3,
   HS2_PASS_LAYOUT = 4,
-  HS2_PASS_BWD_PREP = 5,    /* backward: Delta, K^T copy, accumulators clear */
+  HS2_PASS_BWD_PREP = 5,    /* backward: Delta, K^T and Q/dO tile copies,
+                               accumulators cleared                        */
   HS2_PASS_BWD_SPARSE = 6,  /* backward: the sparse layers                   */
   HS2_PASS_BWD_DKDV = 7,    /* backward: the full layer's dK, dV             */
   HS2_PASS_BWD_DQ = 8,      /* backward: the full layer's dQ                 */
