@@ -8,10 +8,14 @@
 // The pass is bound by the gather from HBM, so the design keeps many gathers
 // in flight without spending registers on them: one work-group serves one
 // (sequence, query, KV head); its waves gather 32-key tiles of the selected
-// K and V rows straight into a 4-stage LDS ring (global_load_lds, three tiles
-// in flight while one is used), and each wave then computes one 16-row block
-// of (layer, head-of-group) rows from LDS. Every selected row is read from
-// HBM once for all heads and layers of the group.
+// K and V rows straight into a two-stage LDS ring (global_load_lds, the
+// next tile in flight while one is used), and each wave then computes one
+// 16-row block of (layer, head-of-group) rows from LDS. Every selected row
+// is read from HBM once for all heads and layers of the group. The ring is
+// kept shallow so that four work-groups fit a CU (36.6 KB of LDS with a
+// 1152-entry index row): more independent work-groups in flight beat a
+// deeper ring per work-group (at the 32K prefill 8.4 ms with two stages,
+// 9.3 ms with three, 12.6 ms with four, 23.8 ms with five).
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -23,7 +27,7 @@ constexpr int D = 128;
 constexpr int TK = 32;                       // keys per tile
 constexpr int HALF = TK * D * 2;             // 8 KB: K (or V) rows of a tile
 constexpr int TILE_BYTES = 2 * HALF;
-constexpr int NS = 4;                        // ring stages
+constexpr int NS = 2;                        // ring stages (see the kernel comment)
 constexpr float RESCALE_GAP = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -43,6 +47,19 @@ __device__ __forceinline__ int kswz(int row) { return row & 15; }
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (other counters untouched)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// wait until at most K * L_ of this wave's vector-memory operations are
+// outstanding, for the run-time `ahead` in 0 .. K (the immediate must be a
+// constant)
+template <int K, int L_>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (K < 0) {
+    return;
+  } else {
+    if (ahead == K) __builtin_amdgcn_s_waitcnt(vmcnt_imm(K * L_));
+    else wait_ahead<K - 1, L_>(ahead);
+  }
+}
 
 }  // namespace
 
@@ -143,10 +160,8 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   for (int t = 0; t < n_tiles; ++t) {
     // own loads of tile t done (later tiles may stay in flight), then all waves'
     const int ahead = min(NS - 2, n_tiles - 1 - t);
-    static_assert(NS - 2 == 2, "wait ladder below assumes two tiles ahead");
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    static_assert((NS - 2) * LPW <= 63, "vmcnt range");
+    wait_ahead<NS - 2, LPW>(ahead);
     __syncthreads();
     if (t + NS - 1 < n_tiles) {
       issue((t + NS - 1) % NS);
