@@ -152,6 +152,11 @@ def select_block(S_row, p: int, block_size: int, top_blocks: int,
 
 
 def block_scores(S_row, p: int, block_size: int, window: int) -> np.ndarray:
+    """Score of each block of candidates: the largest candidate score in it.
+
+    Block b holds keys b*block_size .. (b+1)*block_size - 1; only its keys
+    j <= p - window count (a block that reaches into the window is scored on
+    its candidate keys alone)."""
     n_cand = max(0, p - window + 1)
     n_blocks = (n_cand + block_size - 1) // block_size
     return np.array([np.asarray(S_row[bi * block_size:min(n_cand, (bi + 1) * block_size)],
@@ -159,12 +164,24 @@ def block_scores(S_row, p: int, block_size: int, window: int) -> np.ndarray:
 
 
 def kth_candidate_score(S_row, p: int, top_k: int, window: int) -> float:
-    """tau_p: the score of the k-th ranked candidate (the selection threshold)."""
+    """tau_p: the score of the k-th ranked candidate (the selection threshold).
+
+    With fewer than k candidates it is the lowest candidate score; with none,
+    +inf."""
     n_cand = max(0, p - window + 1)
     if n_cand == 0:
         return np.inf
     vals = np.sort(np.asarray(S_row[:n_cand], dtype=np.float64))[::-1]
     return float(vals[min(top_k, n_cand) - 1])
+
+
+def kth_block_score(S_row, p: int, block_size: int, top_blocks: int, window: int) -> float:
+    """Block-mode threshold: the block score of the top_blocks-th ranked block
+    (the lowest one when fewer blocks exist; +inf with no candidates)."""
+    bs = block_scores(S_row, p, block_size, window)
+    if len(bs) == 0:
+        return np.inf
+    return float(np.sort(bs)[::-1][min(top_blocks, len(bs)) - 1])
 
 
 def pad_index_row(idx_row, width: int) -> np.ndarray:
@@ -225,9 +242,7 @@ def block_forward(q_full, q_sparse, k, v, top_k=1024, window=128,
                 tau[b, i] = kth_candidate_score(S[b, i], p, top_k, window)
             else:
                 row = select_block(S[b, i], p, block_size, top_blocks, window)
-                bs = block_scores(S[b, i], p, block_size, window)
-                tau[b, i] = (np.sort(bs)[::-1][min(top_blocks, len(bs)) - 1]
-                             if len(bs) else np.inf)
+                tau[b, i] = kth_block_score(S[b, i], p, block_size, top_blocks, window)
             idx[b, i, :len(row)] = row
     q_sparse = np.asarray(q_sparse)
     o_sparse = np.stack([sparse_layer(q_sparse[l], k, v, idx, scale)
@@ -427,8 +442,7 @@ def block_rows(q_full, q_sparse, k, v, b: int, rows, top_k=1024, window=128,
             tau[r] = kth_candidate_score(S[r], p, top_k, window)
         else:
             row = select_block(S[r], p, block_size, top_blocks, window)
-            bs = block_scores(S[r], p, block_size, window)
-            tau[r] = np.sort(bs)[::-1][min(top_blocks, len(bs)) - 1] if len(bs) else np.inf
+            tau[r] = kth_block_score(S[r], p, block_size, top_blocks, window)
         idx[r, :len(row)] = row
     L = q_sparse.shape[0]
     o_sparse = np.zeros((L, R, hq, d))

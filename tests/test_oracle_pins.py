@@ -105,6 +105,32 @@ def test_worked_example_d1():
         got = res["idx"][0, p]
         assert list(got[got >= 0]) == want["idx"]
         assert abs(res["o_sparse"][0, 0, p, 0, 0] - float(Fraction(want["o_sparse_h0"]))) < 1e-13
+        # the selection threshold, hand-derived as the top_k-th candidate score
+        tau = float(want["tau"]) if want["tau"] == "inf" else float(Fraction(want["tau"]))
+        assert res["tau"][0, p] == tau or abs(res["tau"][0, p] - tau) < 1e-14
+        assert O.kth_candidate_score(res["S"][0, p], p, ex["top_k"], ex["window"]) == \
+            res["tau"][0, p]
+
+    # block mode on the same inputs: hand-derived block scores (candidates
+    # only), thresholds and index sets
+    bm = ex["block_mode"]
+    res = O.block_forward(q, q[None], k, v, top_k=ex["top_k"], window=ex["window"],
+                          select="block", block_size=bm["block_size"],
+                          top_blocks=bm["top_blocks"], scale=1.0)
+    for p_str, want in bm["expected"].items():
+        p = int(p_str)
+        bs = O.block_scores(res["S"][0, p], p, bm["block_size"], ex["window"])
+        np.testing.assert_allclose(bs, [float(Fraction(x)) for x in want["block_scores"]],
+                                   rtol=0, atol=1e-14)
+        tau = float(Fraction(want["tau"]))
+        assert abs(O.kth_block_score(res["S"][0, p], p, bm["block_size"], bm["top_blocks"],
+                                     ex["window"]) - tau) < 1e-14
+        assert abs(res["tau"][0, p] - tau) < 1e-14
+        got = res["idx"][0, p]
+        assert list(got[got >= 0]) == want["idx"]
+    for p in (0, 1):                    # no candidates: no block, no threshold
+        assert len(O.block_scores(res["S"][0, p], p, bm["block_size"], ex["window"])) == 0
+        assert res["tau"][0, p] == np.inf
 
 
 # --------------------------------------------------------------------------
@@ -138,6 +164,42 @@ def test_token_topk_brute_force(seed):
     for j in cand:
         rank = np.sum(S[:n_cand] > S[j]) + np.sum((S[:n_cand] == S[j]) & (cand < j))
         assert (j in got) == (rank < k)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_threshold_is_lowest_score_of_the_brute_force_set(seed):
+    # tau is fixed by the chosen set itself: the lowest score in the top-k
+    # subset found by enumeration, at least the best score left out; +inf when
+    # there is no candidate. Distinct scores make the k-th and (k+1)-th differ.
+    rng = np.random.default_rng(500 + seed)
+    n_cand = int(rng.integers(0, 12))
+    k = int(rng.integers(1, 5))
+    w = int(rng.integers(1, 4))
+    p = n_cand + w - 1
+    S = rng.permutation(p + 1).astype(np.float64) / 16 if seed % 2 else \
+        rng.integers(0, 4, size=p + 1).astype(np.float64) / 4
+    tau = O.kth_candidate_score(S, p, k, w)
+    if n_cand == 0:
+        assert tau == np.inf
+        return
+    chosen = brute_force_topk(S[:n_cand], k)
+    assert tau == min(S[j] for j in chosen)
+    rest = [j for j in range(n_cand) if j not in chosen]
+    if rest:
+        assert tau >= max(S[j] for j in rest)
+
+
+def test_threshold_literal_values():
+    # hand-written rows: the threshold is the k-th largest candidate score,
+    # not the (k+1)-th, and window scores never count
+    S = np.array([0.1, 0.7, 0.4, 0.9, 0.2, 0.05, 5.0, 6.0])   # p = 7, window 2: j <= 5
+    assert O.kth_candidate_score(S, 7, 1, 2) == 0.9
+    assert O.kth_candidate_score(S, 7, 2, 2) == 0.7
+    assert O.kth_candidate_score(S, 7, 3, 2) == 0.4
+    assert O.kth_candidate_score(S, 7, 6, 2) == 0.05
+    assert O.kth_candidate_score(S, 7, 9, 2) == 0.05            # fewer than k: lowest
+    assert O.kth_candidate_score(S, 1, 3, 2) == np.inf          # no candidate
+    assert O.kth_candidate_score(np.array([2.0, 2.0, 1.0, 0.0]), 3, 2, 1) == 2.0
 
 
 def test_exact_ties_take_lowest_indices():
@@ -239,6 +301,24 @@ def test_block_selection_brute_force(seed):
     chosen = brute_force_topk(np.array(bmax), tb) if n_blocks else []
     toks = [j for b in chosen for j in range(b * bsz, min(n_cand, (b + 1) * bsz))]
     assert list(got) == toks + list(range(max(0, p - w + 1), p + 1))
+    # block scores are the per-block maxima over candidates, and the block
+    # threshold is the lowest score among the enumerated best blocks
+    assert list(O.block_scores(S, p, bsz, w)) == bmax
+    tau = O.kth_block_score(S, p, bsz, tb, w)
+    assert tau == (min(bmax[b] for b in chosen) if n_blocks else np.inf)
+
+
+def test_block_scores_literal_values():
+    # block 2 reaches into the window (p = 10, window 2: candidates j <= 8);
+    # its window key 9 has the row's largest score and must not count
+    S = np.array([0.1, 0.3, 0.2, 0.0,  0.5, 0.4, 0.45, 0.6,  0.05, 0.9, 0.8])
+    np.testing.assert_array_equal(O.block_scores(S, 10, 4, 2), [0.3, 0.6, 0.05])
+    assert O.kth_block_score(S, 10, 4, 1, 2) == 0.6
+    assert O.kth_block_score(S, 10, 4, 2, 2) == 0.3
+    assert O.kth_block_score(S, 10, 4, 3, 2) == 0.05
+    assert O.kth_block_score(S, 10, 4, 5, 2) == 0.05
+    assert list(O.select_block(S, 10, 4, 1, 2)) == [4, 5, 6, 7, 9, 10]
+    assert list(O.select_block(S, 10, 4, 3, 2)) == [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
 
 
 # --------------------------------------------------------------------------
@@ -289,6 +369,62 @@ def test_compare_selection_rule():
     assert ok and n == 2
     ok, _, why = O.compare_selection([0, 1, 2, 7, 9], ref, S, p, w, tau)
     assert not ok and why == "window"
+
+
+def test_compare_selection_band_sits_on_the_kth_score():
+    # candidates 0..4 (p = 6, window 2), k = 3. Key 1 sits 9e-7 above the
+    # k-th score 0.3 (key 2) and key 3 sits 9e-7 below it: both are within
+    # 1e-6 of tau = 0.3, so a row that keeps 3 instead of 1 is an excused
+    # near-tie. A band around the (k+1)-th score (key 3) would reject it.
+    p, w, k = 6, 2, 3
+    S = np.array([0.5, 0.3 * (1 + 9e-7), 0.3, 0.3 * (1 - 9e-7), 0.1, 0.0, 0.0])
+    ref = O.select_token(S, p, k, w)
+    assert list(ref) == [0, 1, 2, 5, 6]
+    tau = O.kth_candidate_score(S, p, k, w)
+    assert tau == 0.3
+    ok, n, _ = O.compare_selection([0, 2, 3, 5, 6], ref, S, p, w, tau)
+    assert ok and n == 2
+    ok, _, why = O.compare_selection([0, 2, 3, 5, 6], ref, S, p, w, S[3])
+    assert not ok and why == "beyond-tie"
+    # a swap with key 4, far below tau, is never excused
+    ok, _, why = O.compare_selection([0, 1, 4, 5, 6], ref, S, p, w, tau)
+    assert not ok and why == "beyond-tie"
+
+
+def test_compare_selection_block_rule():
+    # blocks of 4. First p = 12, window 2: candidates j <= 10, so block 2
+    # holds candidates 8..10 only; window key 11 (score 0.9) lies in its span
+    # and must not raise its score.
+    w, bsz, tb = 2, 4, 2
+    S = np.full(14, 0.01)
+    S[1] = 0.5                         # block 0: max 0.5
+    S[5] = 0.3 * (1 + 6e-7)            # block 1: max 0.3(1 + 6e-7)
+    S[9] = 0.3                         # block 2: max 0.3, its other keys 0.01
+    S[11] = 0.9
+    ref = O.select_block(S, 12, bsz, tb, w)
+    assert list(ref) == [0, 1, 2, 3, 4, 5, 6, 7, 11, 12]
+    assert O.kth_block_score(S, 12, bsz, tb, w) == S[5]
+    # Then p = 13: block 2 = keys 8..11, all candidates, with key 11 lowered.
+    S[11] = 0.2
+    p = 13
+    ref = O.select_block(S, p, bsz, tb, w)
+    assert list(ref) == [0, 1, 2, 3, 4, 5, 6, 7, 12, 13]
+    tau = O.kth_block_score(S, p, bsz, tb, w)
+    assert tau == S[5]
+    # blocks 0 and 2 instead of 0 and 1: block 2's max (not its min) is
+    # within 1e-6 of tau, so the swap is an excused near-tie
+    gpu = [0, 1, 2, 3, 8, 9, 10, 11, 12, 13]
+    ok, n, _ = O.compare_selection(gpu, ref, S, p, w, tau, block_size=bsz)
+    assert ok and n == 8
+    # the same swap when block 2's max is far from tau is not excused
+    S3 = S.copy()
+    S3[9] = 0.2
+    ok, _, why = O.compare_selection(gpu, O.select_block(S3, p, bsz, tb, w), S3, p, w,
+                                     O.kth_block_score(S3, p, bsz, tb, w), block_size=bsz)
+    assert not ok and why == "beyond-tie"
+    # a row of another size (a block cut at the window edge) never agrees
+    ok, _, why = O.compare_selection(gpu[:-3] + [13], ref, S, p, w, tau, block_size=bsz)
+    assert not ok and why == "size"
 
 
 def test_pages_constants():
