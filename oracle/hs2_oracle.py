@@ -40,7 +40,11 @@ What it computes, step by step (the pages describe the method in prose only):
 Inputs may be float32/float64 arrays or raw bf16 bit patterns (uint16); they
 are widened exactly to fp64.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+from threadpoolctl import threadpool_limits
 
 NEG_INF = -np.inf
 
@@ -406,32 +410,54 @@ def block_rows(q_full, q_sparse, k, v, b: int, rows, top_k=1024, window=128,
     Q = widen(q_full[b, rows])                               # [R, hq, d]
     groups = np.array([group_of(h, hq, hkv) for h in range(hq)])
     lse = np.full((R, hq), NEG_INF)
-    last = int(pos.max()) + 1 if R else 0
-    for c0 in range(0, last, chunk):
-        c1 = min(last, c0 + chunk)
-        keep = np.arange(c0, c1)[None, :] <= pos[:, None]    # [R, c]
-        for g in range(hkv):
-            Kg = widen(k[b, c0:c1, g])                       # [c, d]
-            for h in np.nonzero(groups == g)[0]:
-                s = (Q[:, h, :] @ Kg.T) * scale              # [R, c]
-                s = np.where(keep, s, NEG_INF)
-                m = s.max(axis=1)
-                ok = np.isfinite(m)
-                part = np.full(R, NEG_INF)
-                part[ok] = m[ok] + np.log(np.exp(s[ok] - m[ok, None]).sum(axis=1))
-                lse[:, h] = np.logaddexp(lse[:, h], part)
     o_full = np.zeros((R, hq, d))
     S = np.zeros((R, nkv))
-    for c0 in range(0, last, chunk):
-        c1 = min(last, c0 + chunk)
-        keep = np.arange(c0, c1)[None, :] <= pos[:, None]
-        for g in range(hkv):
-            Kg, Vg = widen(k[b, c0:c1, g]), widen(v[b, c0:c1, g])
-            for h in np.nonzero(groups == g)[0]:
-                s = (Q[:, h, :] @ Kg.T) * scale
-                p = np.where(keep, np.exp(np.where(keep, s, 0.0) - lse[:, h, None]), 0.0)
-                o_full[:, h, :] += p @ Vg
-                S[:, c0:c1] += p
+    last = int(pos.max()) + 1 if R else 0
+    first = int(pos.min()) if R else 0
+
+    def chunk_logits(hs, c0, c1):
+        # s_h = scale * Q_h K_g^T for the heads hs of one group over keys
+        # c0..c1-1, as one matrix product over (row, head) pairs: [R, G, c];
+        # keys past a row's position get -inf (a chunk that lies wholly at or
+        # before every row's position needs no mask)
+        g = groups[hs[0]]
+        s = (Q[:, hs, :].reshape(R * len(hs), d) @ widen(k[b, c0:c1, g]).T) * scale
+        s = s.reshape(R, len(hs), c1 - c0)
+        if c1 - 1 > first:
+            keep = (np.arange(c0, c1)[None, :] <= pos[:, None])[:, None, :]
+            s = np.where(keep, s, NEG_INF)
+        return s
+
+    def group_rows(g):
+        # both sweeps for the heads of KV group g: their LSE, O and their
+        # share of the score rows (groups are independent until S is summed)
+        hs = np.nonzero(groups == g)[0]
+        lse_g = np.full((R, len(hs)), NEG_INF)
+        for c0 in range(0, last, chunk):
+            s = chunk_logits(hs, c0, min(last, c0 + chunk))
+            m = s.max(axis=2)                                       # [R, G]
+            ok = np.isfinite(m)
+            part = np.full(m.shape, NEG_INF)
+            e = np.exp(s - np.where(ok, m, 0.0)[:, :, None])       # exp(-inf) = 0
+            part[ok] = m[ok] + np.log(e.sum(axis=2)[ok])
+            lse_g = np.logaddexp(lse_g, part)
+        o_g = np.zeros((R, len(hs), d))
+        S_g = np.zeros((R, last))
+        for c0 in range(0, last, chunk):
+            c1 = min(last, c0 + chunk)
+            p = np.exp(chunk_logits(hs, c0, c1) - lse_g[:, :, None])  # 0 past each row's p
+            o_g += (p.reshape(-1, c1 - c0) @ widen(v[b, c0:c1, g])).reshape(R, len(hs), d)
+            S_g[:, c0:c1] = p.sum(axis=1)
+        return hs, lse_g, o_g, S_g
+
+    # one thread per group, each running single-threaded BLAS
+    with threadpool_limits(limits=1, user_api="blas"), \
+            ThreadPoolExecutor(max_workers=max(1, min(hkv, os.cpu_count() or 1))) as ex:
+        parts = list(ex.map(group_rows, range(hkv)))
+    for hs, lse_g, o_g, S_g in parts:                      # fixed group order
+        lse[:, hs] = lse_g
+        o_full[:, hs] = o_g
+        S[:, :last] += S_g
     width = top_k + window if select == "token" else top_blocks * block_size + window
     idx = np.full((R, width), -1, dtype=np.int64)
     tau = np.zeros(R)
@@ -484,7 +510,7 @@ def sparse_rows(q_sparse, k, v, b: int, rows, idx_rows, scale=None):
 # ----------------------------------------------------------------------------
 # step 6: backward pass with the index sets held fixed
 # ----------------------------------------------------------------------------
-def attention_grads(q, k, v, keep, dout, scale):
+def attention_grads(q, k, v, keep, dout, scale, with_mag=False):
     """Gradients of one softmax-attention head, the textbook way.
 
     q [n, d], k/v [m, d], keep [n, m] bool (which keys each query sees; every
@@ -495,6 +521,15 @@ def attention_grads(q, k, v, keep, dout, scale):
       ds = P * (dP - rowsum(P * dP))     (the softmax Jacobian applied to dP)
       dq = scale ds k,   dk = scale ds^T q.
     Returns (dq, dk, dv) in fp64.
+
+    with_mag=True also returns, as a fourth item, the magnitudes of the
+    summands behind every gradient element (an error-bound helper for
+    comparisons, not part of the method): with Delta = rowsum(P * dP) =
+    rowsum(dout * O) and A = rowsum(|dout| * |O|) >= |Delta|, the weight
+    W = P * (|dP| + A) bounds |ds| termwise, and
+      mag_dq = scale W |k|,  mag_dk = scale W^T |q|,  mag_dv = P^T |dout|,
+    so |dq| <= mag_dq, |dk| <= mag_dk, |dv| <= mag_dv elementwise, with
+    equality for dv when dout >= 0.
     """
     s = np.where(keep, (q @ k.T) * scale, NEG_INF)
     m = s.max(axis=1, keepdims=True)
@@ -503,16 +538,24 @@ def attention_grads(q, k, v, keep, dout, scale):
     dv = P.T @ dout
     dP = dout @ v.T
     ds = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-    return scale * ds @ k, scale * ds.T @ q, dv
+    grads = (scale * ds @ k, scale * ds.T @ q, dv)
+    if not with_mag:
+        return grads
+    A = (np.abs(dout) * np.abs(P @ v)).sum(axis=1, keepdims=True)
+    W = P * (np.abs(dP) + A)
+    return grads + ((scale * W @ np.abs(k), scale * W.T @ np.abs(q), P.T @ np.abs(dout)),)
 
 
-def block_backward(q_full, q_sparse, k, v, idx, do_full, do_sparse, scale=None):
+def block_backward(q_full, q_sparse, k, v, idx, do_full, do_sparse, scale=None,
+                   with_mag=False):
     """Backward of the whole block for given output gradients, dense.
 
     q_full / do_full [B, n_q, h_q, d], q_sparse / do_sparse [L, B, n_q, h_q, d],
     k/v [B, n_kv, h_kv, d], idx [B, n_q, W] (-1 padded; the sparse layers'
     index sets, held fixed). Returns dict(dq_full, dq_sparse, dk, dv) in fp64;
     dk and dv sum the full layer's and every sparse layer's contributions.
+    with_mag=True adds "mag", a dict of the same four keys holding each
+    element's summand magnitude (attention_grads), summed like the gradients.
     """
     qf, kk, vv, dof = widen(q_full), widen(k), widen(v), widen(do_full)
     qs, dos = widen(q_sparse), widen(do_sparse)
@@ -523,10 +566,19 @@ def block_backward(q_full, q_sparse, k, v, idx, do_full, do_sparse, scale=None):
     idx = np.asarray(idx)
     pos = np.arange(nq) + (nkv - nq)
     causal = np.arange(nkv)[None, :] <= pos[:, None]
-    dq_full = np.zeros_like(qf)
-    dq_sparse = np.zeros_like(qs)
-    dk = np.zeros_like(kk)
-    dv = np.zeros_like(vv)
+    out = dict(dq_full=np.zeros_like(qf), dq_sparse=np.zeros_like(qs), dk=np.zeros_like(kk),
+               dv=np.zeros_like(vv))
+    mag = {n: np.zeros_like(a) for n, a in out.items()}
+
+    def add(dst, res, b, h, g, layer):
+        # res = (dq, dk, dv): dq belongs to (layer, b, :, h), dk/dv sum into group g
+        if layer is None:
+            dst["dq_full"][b, :, h] = res[0]
+        else:
+            dst["dq_sparse"][layer, b, :, h] = res[0]
+        dst["dk"][b, :, g] += res[1]
+        dst["dv"][b, :, g] += res[2]
+
     for b in range(B):
         chosen = np.zeros((nq, nkv), dtype=bool)
         for i in range(nq):
@@ -534,22 +586,20 @@ def block_backward(q_full, q_sparse, k, v, idx, do_full, do_sparse, scale=None):
             chosen[i, sel] = True
         for h in range(hq):
             g = group_of(h, hq, hkv)
-            a, bk, bv = attention_grads(qf[b, :, h], kk[b, :, g], vv[b, :, g], causal,
-                                        dof[b, :, h], scale)
-            dq_full[b, :, h] = a
-            dk[b, :, g] += bk
-            dv[b, :, g] += bv
-            for l in range(L):
-                a, bk, bv = attention_grads(qs[l, b, :, h], kk[b, :, g], vv[b, :, g], chosen,
-                                            dos[l, b, :, h], scale)
-                dq_sparse[l, b, :, h] = a
-                dk[b, :, g] += bk
-                dv[b, :, g] += bv
-    return dict(dq_full=dq_full, dq_sparse=dq_sparse, dk=dk, dv=dv)
+            passes = [(None, qf[b, :, h], causal, dof[b, :, h])] + \
+                [(l, qs[l, b, :, h], chosen, dos[l, b, :, h]) for l in range(L)]
+            for layer, qh, keep, doh in passes:
+                res = attention_grads(qh, kk[b, :, g], vv[b, :, g], keep, doh, scale, with_mag)
+                add(out, res[:3], b, h, g, layer)
+                if with_mag:
+                    add(mag, res[3], b, h, g, layer)
+    if with_mag:
+        out["mag"] = mag
+    return out
 
 
 def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int, j_lo: int,
-                        scale=None):
+                        scale=None, with_mag=False):
     """block_backward for large contexts, restricted to what a tail of keys
     decides: the K/V gradient rows j >= j_lo and the query gradients of every
     query at position p >= j_lo. Only those queries can reach such a key
@@ -558,7 +608,8 @@ def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int,
     n_q x n_kv is formed, only (queries in the tail) x n_kv per KV group.
 
     Returns dict(rows (query indices i), dq_full [R, h_q, d],
-    dq_sparse [L, R, h_q, d], dk, dv [n_kv - j_lo, h_kv, d]).
+    dq_sparse [L, R, h_q, d], dk, dv [n_kv - j_lo, h_kv, d]); with_mag=True
+    adds "mag" with the summand magnitudes of the same elements.
     """
     nq, hq, d = q_full.shape[1], q_full.shape[2], q_full.shape[3]
     nkv, hkv = k.shape[1], k.shape[2]
@@ -575,10 +626,20 @@ def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int,
     for r, i in enumerate(rows):
         sel = idx[b, i][idx[b, i] >= 0]
         chosen[r, sel] = True
-    dq_full = np.zeros((R, hq, d))
-    dq_sparse = np.zeros((L, R, hq, d))
-    dk = np.zeros((nkv - j_lo, hkv, d))
-    dv = np.zeros((nkv - j_lo, hkv, d))
+    def zeros():
+        return dict(dq_full=np.zeros((R, hq, d)), dq_sparse=np.zeros((L, R, hq, d)),
+                    dk=np.zeros((nkv - j_lo, hkv, d)), dv=np.zeros((nkv - j_lo, hkv, d)))
+    out, mag = zeros(), zeros()
+
+    def add(dst, res, layer, heads, g):
+        a, bk, bv = res
+        if layer is None:
+            dst["dq_full"][:, heads] = a.reshape(R, G, d)
+        else:
+            dst["dq_sparse"][layer][:, heads] = a.reshape(R, G, d)
+        dst["dk"][:, g] += bk[j_lo:]
+        dst["dv"][:, g] += bv[j_lo:]
+
     for g in range(hkv):
         heads = [h for h in range(hq) if group_of(h, hq, hkv) == g]
         Kg, Vg = widen(k[b, :, g]), widen(v[b, :, g])
@@ -589,14 +650,14 @@ def block_backward_tail(q_full, q_sparse, k, v, idx, do_full, do_sparse, b: int,
             dsrc = do_full[b, rows] if layer is None else np.asarray(do_sparse)[layer, b, rows]
             Q = widen(qsrc)[:, heads].reshape(R * G, d)
             dO = widen(dsrc)[:, heads].reshape(R * G, d)
-            a, bk, bv = attention_grads(Q, Kg, Vg, np.repeat(keep, G, axis=0), dO, scale)
-            if layer is None:
-                dq_full[:, heads] = a.reshape(R, G, d)
-            else:
-                dq_sparse[layer][:, heads] = a.reshape(R, G, d)
-            dk[:, g] += bk[j_lo:]
-            dv[:, g] += bv[j_lo:]
-    return dict(rows=rows, dq_full=dq_full, dq_sparse=dq_sparse, dk=dk, dv=dv)
+            res = attention_grads(Q, Kg, Vg, np.repeat(keep, G, axis=0), dO, scale, with_mag)
+            add(out, res[:3], layer, heads, g)
+            if with_mag:
+                add(mag, res[3], layer, heads, g)
+    out["rows"] = rows
+    if with_mag:
+        out["mag"] = mag
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -357,3 +357,103 @@ def test_paged_prefill_without_new_tokens_launches_nothing():
     st = lib.hs2_block_forward_paged(ctypes.byref(p), ctypes.byref(pages), 2, cu_q, lens,
                                      *[vp(FAKE)] * 9, None, None, 0, None)
     assert st == 0, lib.hs2_last_error().decode()
+
+
+# --------------------------------------------------------------------------
+# the Python binding checks every tensor's shape before any device call (the
+# C ABI sees raw pointers only); CPU tensors reach these checks, then fail as
+# non-device tensors, so nothing here touches a GPU
+# --------------------------------------------------------------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _shape_error(fn, *args, match="shape", **kw):
+    with pytest.raises(ValueError, match=match):
+        fn(*args, **kw)
+
+
+def test_binding_rejects_mis_shaped_block_forward():
+    import torch
+    B, nq, nkv, hq, hkv, d, L = 1, 8, 32, 4, 2, 64, 2
+    q, qs = _t(B, nq, hq, d), _t(L, B, nq, hq, d)
+    k, v = _t(B, nkv, hkv, d), _t(B, nkv, hkv, d)
+    kw = dict(top_k=4, window=4)
+    _shape_error(hs2.block_forward, q, _t(L, B, nq, hq + 1, d), k, v, **kw)     # q_sparse heads
+    _shape_error(hs2.block_forward, q, _t(L, B, nq - 1, hq, d), k, v, **kw)     # q_sparse rows
+    _shape_error(hs2.block_forward, q, qs, k, _t(B, nkv - 1, hkv, d), **kw)     # v != k
+    _shape_error(hs2.block_forward, q, qs, _t(B, nkv, hkv, d // 2), v, **kw)    # head dim
+    out = dict(o_full=_t(B, nq, hq, d), o_sparse=_t(L, B, nq, hq, d),
+               idx=torch.zeros((B, nq, 7), dtype=torch.int32), lse=None)
+    _shape_error(hs2.block_forward, q, qs, k, v, out=out, **kw)                 # idx width
+    out["idx"] = torch.zeros((B, nq, 8), dtype=torch.int64)
+    _shape_error(hs2.block_forward, q, qs, k, v, out=out, match="int32", **kw)  # idx dtype
+    # every shape right: the next check is the device
+    _shape_error(hs2.block_forward, q, qs, k, v, match="device tensor", **kw)
+
+
+def test_binding_rejects_mis_shaped_sparse_and_full_calls():
+    import torch
+    B, nq, nkv, hq, hkv, d, L = 2, 8, 32, 4, 2, 64, 3
+    qs, k, v = _t(L, B, nq, hq, d), _t(B, nkv, hkv, d), _t(B, nkv, hkv, d)
+    kw = dict(top_k=4, window=4)
+    idx = torch.zeros((B, nq, 8), dtype=torch.int32)
+    _shape_error(hs2.sparse_attn, qs, k, v, torch.zeros((B, nq - 1, 8), dtype=torch.int32), **kw)
+    _shape_error(hs2.sparse_attn, qs, k, v, torch.zeros((1, nq, 8), dtype=torch.int32), **kw)
+    _shape_error(hs2.sparse_attn, qs, _t(B + 1, nkv, hkv, d), v, idx, **kw)
+    _shape_error(hs2.sparse_attn, qs, k, v, idx, match="device tensor", **kw)
+    _shape_error(hs2.full_attn_select, _t(B, nq, hq, d), k, _t(B, nkv, hkv + 1, d), **kw)
+    _shape_error(hs2.full_attn_select, _t(B, nq, hq, d), _t(B, nkv, hkv, d + 1), v, **kw)
+
+
+def test_binding_rejects_mis_shaped_decode_and_bridge_calls():
+    import torch
+    B, cap, hq, hkv, d, L = 2, 64, 4, 2, 64, 2
+    q, qs = _t(B, 1, hq, d), _t(L, B, 1, hq, d)
+    kn, vn = _t(B, 1, hkv, d), _t(B, 1, hkv, d)
+    kc, vc = _t(B, cap, hkv, d), _t(B, cap, hkv, d)
+    kw = dict(top_k=4, window=4)
+    _shape_error(hs2.decode_step, q, qs, kn, _t(B, 2, hkv, d), kc, vc, [3, 4], **kw)
+    _shape_error(hs2.decode_step, q, qs, kn, vn, kc, _t(B, cap, hkv, d + 8), [3, 4], **kw)
+    _shape_error(hs2.decode_step, q, qs, kn, vn, kc, vc, [3], match="lens", **kw)
+    pool = _t(4 * 32, hkv, d)
+    table = torch.zeros((B, 2), dtype=torch.int32)
+    _shape_error(hs2.decode_step_paged, q, qs, kn, vn, pool, _t(4 * 32, hkv, d // 2), table, 32,
+                 [3, 4], **kw)
+    _shape_error(hs2.decode_step_paged, q, qs, kn, vn, pool, pool.clone(),
+                 torch.zeros((B + 1, 2), dtype=torch.int32), 32, [3, 4], **kw)
+    _shape_error(hs2.kv_bridge, _t(1, 16, 256), _t(2, 128, 255), 2)
+    _shape_error(hs2.kv_bridge, _t(1, 16, 256), _t(3, 128, 256), 2)
+    _shape_error(hs2.kv_bridge, _t(1, 16, 256), _t(2, 128, 256), 3, match="multiple")
+
+
+def test_binding_rejects_mis_shaped_packed_and_backward_calls():
+    import torch
+    hq, hkv, d, L = 4, 2, 64, 2
+    q, qs = _t(10, hq, d), _t(L, 10, hq, d)
+    k, v = _t(40, hkv, d), _t(40, hkv, d)
+    kw = dict(top_k=4, window=4)
+    _shape_error(hs2.block_forward_varlen, q, qs, k, _t(41, hkv, d), [0, 4, 10], [0, 20, 40],
+                 **kw)
+    _shape_error(hs2.block_forward_varlen, q, _t(L, 10, hq + 2, d), k, v, [0, 4, 10],
+                 [0, 20, 40], **kw)
+    _shape_error(hs2.block_forward_varlen, q, qs, k, v, [0, 4, 10], [0, 40], match="cu_seqlens",
+                 **kw)
+    pool = _t(4 * 32, hkv, d)
+    table = torch.zeros((2, 4), dtype=torch.int32)
+    _shape_error(hs2.block_forward_paged, q, qs, _t(10, hkv, d), _t(9, hkv, d), pool, pool.clone(),
+                 table, 32, [0, 4, 10], [5, 6], **kw)
+    B, nq, nkv = 1, 8, 32
+    qf, kk, vv = _t(B, nq, hq, d), _t(B, nkv, hkv, d), _t(B, nkv, hkv, d)
+    qsp = _t(L, B, nq, hq, d)
+    lse = torch.zeros((B, hq, nq), dtype=torch.float32)
+    idx = torch.zeros((B, nq, 8), dtype=torch.int32)
+    args = [qf, qsp, kk, vv, qf.clone(), qsp.clone(), lse, idx, qf.clone(), qsp.clone()]
+    bad = list(args)
+    bad[6] = torch.zeros((B, hq, nq + 1), dtype=torch.float32)            # lse
+    _shape_error(hs2.block_backward, *bad, **kw)
+    bad = list(args)
+    bad[9] = _t(L + 1, B, nq, hq, d)                                     # do_sparse
+    _shape_error(hs2.block_backward, *bad, **kw)
+    _shape_error(hs2.block_backward, *args, match="device tensor", **kw)

@@ -301,60 +301,140 @@ def test_config1_full(gpu_lib):
         assert np.abs(og[:, 0, tied] - alt).max() <= TOL["fp32"]
 
 
-def sampled_rows(w: Workload, n):
+BOUNDARY_POSITIONS = (0, 1, 126, 127, 128, 1150, 1151, 1152, 1153)
+
+
+def sampled_rows(w: Workload, n, must=()):
+    """Query rows checked against the oracle at a workload's full size: the
+    first and last row, the rows at the selection boundaries (first candidate
+    at p = 128, the set reaching k + w at p = 1151..1153) when the chunk
+    holds them, every row in `must`, and n further uniform rows. Every one of
+    those is kept."""
     nq = w.n_q
-    base = [0, nq - 1]
-    for p in (127, 128, 1151, 1152, 1153):
-        i = p - w.q_off
-        if 0 <= i < nq:
-            base.append(i)
-    rng = np.random.default_rng(w.cid)
-    extra = rng.choice(nq, size=min(nq, n), replace=False).tolist()
-    return sorted(set(base + extra))[:max(n, len(base))]
+    base = {0, nq - 1} | {int(i) for i in must}
+    for p in BOUNDARY_POSITIONS:
+        if 0 <= p - w.q_off < nq:
+            base.add(p - w.q_off)
+    rng = np.random.default_rng(1000 + w.cid)
+    pool = np.setdiff1d(np.arange(nq), np.fromiter(base, dtype=np.int64))
+    extra = rng.choice(pool, size=min(len(pool), n), replace=False).tolist()
+    return sorted(base | set(int(x) for x in extra))
 
 
-@pytest.mark.parametrize("cid,n_rows", [(2, 6), (3, 4), (4, 3), (5, 2)])
+def needle_target_rows(w: Workload, meta):
+    return sorted(set(int(t) - w.q_off for t in meta["needle_target"]))
+
+
+def check_rows(w, gi_b, of_b, osg_b, inp_host, b, rows, select="token", ref=None):
+    """Oracle rows of batch entry b against the GPU's index rows and outputs.
+
+    gi_b [n_q, W] GPU index rows; of_b / osg_b the GPU's O_full [n_q, h_q, d]
+    and O_sparse [L, n_q, h_q, d] of this batch entry (host arrays, any rows
+    outside `rows` ignored). Near-tie rows compare with the oracle's sparse
+    layers on the GPU's own index row. Returns (oracle dict, tied rows)."""
+    q, qs, kb, vb = inp_host
+    kw = dict(top_k=w.top_k, window=w.window, select=select, block_size=w.block_size,
+              top_blocks=w.top_blocks)
+    if ref is None:
+        ref = O.block_rows(q, qs, kb, vb, 0, rows, **kw)
+    bsz = w.block_size if select == "block" else 0
+    tied = compare_index_rows(gi_b[rows], ref["S"], ref["pos"], ref["idx"], ref["tau"],
+                              w.window, block_size=bsz)
+    tol = TOL[w.dtype]
+    err_full = np.abs(of_b[rows] - ref["o_full"]).max()
+    assert err_full <= tol, f"o_full err {err_full}"
+    err_sparse = 0.0
+    for r, row in enumerate(rows):
+        want = ref["o_sparse"][:, r] if r not in tied else \
+            O.sparse_rows(qs, kb, vb, 0, [row], gi_b[row][None])[:, 0]
+        e = np.abs(osg_b[:, row] - want).max() if want.size else 0.0
+        err_sparse = max(err_sparse, e)
+        assert e <= tol, f"row {row}: o_sparse err {e}"
+    say(f"  batch {b}: {len(rows)} rows checked, {len(tied)} near-tie rows, "
+        f"o_full err {err_full:.2e}, o_sparse err {err_sparse:.2e}")
+    return ref, tied
+
+
+def host_batch(inp, b):
+    return (host(inp["q_full"][b:b + 1]), host(inp["q_sparse"][:, b:b + 1]),
+            host(inp["k"][b:b + 1]), host(inp["v"][b:b + 1]))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid,n_rows", [(2, 64), (4, 32), (5, 16)])
 def test_config_sampled(gpu_lib, cid, n_rows):
+    """Full-size parity on sampled rows of the three prefill-shaped
+    workloads (the 32K prefill also checks every needle's target row), plus
+    the index-set invariants on every row."""
     w = CONFIGS[cid]
     say("config", w.name)
     inp = make_inputs(w, device="cuda")
     out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
                                 top_k=w.top_k, window=w.window)
     torch.cuda.synchronize()
-    say("gpu done")
+    check_invariants(out["idx"], w)
+    must = needle_target_rows(w, inp["meta"]) if w.structure == "needles" else ()
+    rows = sampled_rows(w, n_rows, must)
+    say("rows", len(rows), rows)
+    gi = out["idx"].cpu().numpy()
+    of, osg = as_np(out["o_full"][0]), as_np(out["o_sparse"][:, 0])
+    ref, _ = check_rows(w, gi[0], of, osg, host_batch(inp, 0), 0, rows)
+    if w.structure == "needles":
+        # quality sanity on the planted structure (not parity): each needle
+        # is selected by its target query, in the oracle's set and the GPU's
+        meta = inp["meta"]
+        where = {row: r for r, row in enumerate(rows)}
+        hits_ref = hits_gpu = 0
+        for j, t in zip(meta["needle_pos"], meta["needle_target"]):
+            i = int(t) - w.q_off
+            hits_ref += int(j in set(ref["idx"][where[i]].tolist()))
+            hits_gpu += int(j in set(gi[0, i].tolist()))
+        say("needle hits: oracle", hits_ref, "gpu", hits_gpu, "of", len(meta["needle_pos"]))
+        assert hits_gpu == hits_ref == len(meta["needle_pos"])
+
+
+@pytest.mark.timeout(600)
+def test_config_decode_all_sequences(gpu_lib):
+    """The 64 x 128K decode workload: every sequence's query against the
+    oracle."""
+    w = CONFIGS[3]
+    say("config", w.name)
+    inp = make_inputs(w, device="cuda")
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
+                                top_k=w.top_k, window=w.window)
+    torch.cuda.synchronize()
     check_invariants(out["idx"], w)
     gi = out["idx"].cpu().numpy()
-    o_full = out["o_full"]
-    o_sparse = out["o_sparse"]
-    tol = TOL[w.dtype]
-    batches = [0, w.batch - 1] if w.batch > 1 else [0]
-    for b in batches:
-        rows = sampled_rows(w, n_rows) if w.n_q > 1 else [0]
-        q = host(inp["q_full"][b:b + 1])
-        qs = host(inp["q_sparse"][:, b:b + 1])
-        kb, vb = host(inp["k"][b:b + 1]), host(inp["v"][b:b + 1])
-        ref = O.block_rows(q, qs, kb, vb, 0, rows, top_k=w.top_k, window=w.window)
-        say("oracle rows done", b, rows)
-        tied = compare_index_rows(gi[b, rows], ref["S"], ref["pos"], ref["idx"], ref["tau"],
-                                  w.window)
-        of = as_np(o_full[b, rows])
-        assert np.abs(of - ref["o_full"]).max() <= tol
-        osg = as_np(o_sparse[:, b, rows])
-        for r in range(len(rows)):
-            want = ref["o_sparse"][:, r] if r not in tied else \
-                O.sparse_rows(qs, kb, vb, 0, [rows[r]], gi[b, rows[r]][None])[:, 0]
-            assert np.abs(osg[:, r] - want).max() <= tol
-        say("batch", b, "tied rows", len(tied))
-    if w.structure == "needles":
-        # quality sanity (not parity): each needle is chosen by its target query
-        meta = inp["meta"]
-        hits = 0
-        for j, t in zip(meta["needle_pos"], meta["needle_target"]):
-            hits += int(j in set(gi[0, t - w.q_off].tolist()))
-        say("needle hits", hits, "of", len(meta["needle_pos"]))
+    of, osg = as_np(out["o_full"]), as_np(out["o_sparse"])
+    n_tied = 0
+    for b in range(w.batch):
+        _, tied = check_rows(w, gi[b], of[b], osg[:, b], host_batch(inp, b), b, [0])
+        n_tied += len(tied)
+    say("decode sequences checked", w.batch, "near-tie rows", n_tied)
 
 
-@pytest.mark.parametrize("cid,n_rows", [(2, 4), (4, 3)])
+@pytest.mark.timeout(600)
+def test_config_block_ablation_sampled(gpu_lib):
+    """The 8K-on-262K chunk in the block-selection variant (64-token blocks,
+    top 16) at full size: sampled rows against the oracle, invariants on
+    every row."""
+    w = CONFIGS[4]
+    say("config", w.name, "block selection")
+    inp = make_inputs(w, device="cuda")
+    out = gpu_lib.block_forward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"],
+                                top_k=w.top_k, window=w.window, select="block",
+                                block_size=w.block_size, top_blocks=w.top_blocks)
+    torch.cuda.synchronize()
+    check_invariants(out["idx"], w.with_(top_k=w.block_size * w.top_blocks), block_mode=True)
+    rows = sampled_rows(w, 32)
+    say("rows", len(rows), rows)
+    gi = out["idx"].cpu().numpy()
+    check_rows(w, gi[0], as_np(out["o_full"][0]), as_np(out["o_sparse"][:, 0]),
+               host_batch(inp, 0), 0, rows, select="block")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid,n_rows", [(2, 4), (4, 3), (5, 4)])
 def test_score_precision_sampled(gpu_lib, cid, n_rows):
     """Precision budget of the scores that decide the selection: the GPU's
     S(p, j) rows exported through the debug hook against the oracle's, at the
@@ -382,11 +462,43 @@ def test_score_precision_sampled(gpu_lib, cid, n_rows):
         rels.append(np.abs(g[r, :n_c][keep] - s_ref[keep]) / s_ref[keep])
     rel = np.concatenate(rels)
     mx, p999 = float(rel.max()), float(np.quantile(rel, 0.999))
-    say(f"score rel err over {rel.size} candidates: max {mx:.3e}, p99.9 {p999:.3e}")
+    say(f"score rel err over {rel.size} candidates of rows {rows}: max {mx:.3e}, "
+        f"p99.9 {p999:.3e}")
     assert p999 <= 5e-7
     assert mx <= 5e-6
     compare_index_rows(idx[0, rows].cpu().numpy(), ref["S"], ref["pos"], ref["idx"], ref["tau"],
                        w.window)
+
+
+# ---------------------------------------------------------------------------
+# the many-query sparse kernel on oracle index sets: every row of every layer
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", [
+    # 16 rows per (query, KV head): one wave per work-group
+    small("spk_nwv1", "bf16", 1, 1024, 1536, 8, 2, 128, 128, 32, L=4),
+    # 24 rows: two waves
+    small("spk_nwv2", "bf16", 2, 512, 900, 16, 2, 128, 96, 16, L=3),
+    # 40 rows: four waves, a ragged last row block
+    small("spk_nwv4", "bf16", 1, 1024, 1400, 16, 2, 128, 100, 20, L=5),
+    # 72 rows: more than 64, so two launches (64 + 8 rows)
+    small("spk_multi_launch", "bf16", 1, 1024, 1300, 16, 2, 128, 64, 16, L=9),
+    # an index row too wide for the kernel's LDS: the generic kernel runs
+    small("spk_wide_rows", "bf16", 1, 2048, 9000, 2, 1, 128, 4096, 4200, L=1),
+], ids=lambda c: c.name)
+def test_many_query_sparse_kernel_on_oracle_indices(gpu_lib, case):
+    say("case", case)
+    assert case.batch * case.n_q * case.h_kv >= 2048       # the many-query kernel's range
+    inp = make_inputs(case, device="cuda")
+    q, k, v, qs = (host(inp[n]) for n in ("q_full", "k", "v", "q_sparse"))
+    ref = O.block_forward(q, qs, k, v, top_k=case.top_k, window=case.window)
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+    out = gpu_lib.sparse_attn(inp["q_sparse"], inp["k"], inp["v"], idx,
+                              top_k=case.top_k, window=case.window)
+    torch.cuda.synchronize()
+    err = np.abs(as_np(out) - ref["o_sparse"]).max()
+    say("max abs err over", out.numel(), "outputs:", err)
+    assert err <= TOL[case.dtype]
 
 
 # ---------------------------------------------------------------------------

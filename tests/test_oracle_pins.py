@@ -660,6 +660,37 @@ def test_backward_tail_matches_dense(j_lo):
         np.testing.assert_allclose(t["dq_sparse"], dense["dq_sparse"][:, b, rows], atol=1e-12)
         np.testing.assert_allclose(t["dk"], dense["dk"][b, j_lo:], atol=1e-12)
         np.testing.assert_allclose(t["dv"], dense["dv"][b, j_lo:], atol=1e-12)
+    # the summand magnitudes agree the same way
+    dense = O.block_backward(**c, with_mag=True)["mag"]
+    t = O.block_backward_tail(c["q_full"], c["q_sparse"], c["k"], c["v"], c["idx"],
+                              c["do_full"], c["do_sparse"], 1, j_lo, with_mag=True)
+    m, rows = t["mag"], t["rows"]
+    np.testing.assert_allclose(m["dq_full"], dense["dq_full"][1, rows], atol=1e-12)
+    np.testing.assert_allclose(m["dq_sparse"], dense["dq_sparse"][:, 1, rows], atol=1e-12)
+    np.testing.assert_allclose(m["dk"], dense["dk"][1, j_lo:], atol=1e-12)
+    np.testing.assert_allclose(m["dv"], dense["dv"][1, j_lo:], atol=1e-12)
+
+
+def test_backward_summand_magnitudes():
+    # the per-element error bound of the GPU comparison scales with these:
+    # every gradient element is at most its magnitude (triangle inequality),
+    # dV equals its magnitude when every output gradient is nonnegative (all
+    # its summands P * dO are then >= 0), magnitudes are linear in |dO|, and
+    # the gradients themselves do not change when magnitudes are requested
+    c = _bwd_case(150, B=2, nq=7, nkv=11, hq=4, hkv=2, d=5, L=2, top_k=3, window=2)
+    plain = O.block_backward(**c)
+    r = O.block_backward(**c, with_mag=True)
+    for n in ("dq_full", "dq_sparse", "dk", "dv"):
+        np.testing.assert_array_equal(r[n], plain[n])
+        assert np.all(np.abs(r[n]) <= r["mag"][n] + 1e-13), n
+        assert np.all(r["mag"][n] >= 0), n
+    c2 = dict(c, do_full=np.abs(c["do_full"]), do_sparse=np.abs(c["do_sparse"]))
+    r2 = O.block_backward(**c2, with_mag=True)
+    np.testing.assert_allclose(r2["mag"]["dv"], r2["dv"], rtol=1e-13, atol=1e-14)
+    c3 = dict(c, do_full=-3 * c["do_full"], do_sparse=-3 * c["do_sparse"])
+    r3 = O.block_backward(**c3, with_mag=True)
+    for n in ("dq_full", "dq_sparse", "dk", "dv"):
+        np.testing.assert_allclose(r3["mag"][n], 3 * r["mag"][n], rtol=1e-12, atol=1e-14)
 
 
 # ----------------------------------------------------------------------------

@@ -252,8 +252,16 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   for (int e = 0; e < 4; ++e) reinterpret_cast<bf16x8*>(orow)[e] = outv[e];
 }
 
+// Dynamic LDS of one work-group: the ring plus the index row. Wider index
+// rows than fit the default 64 KB per work-group (more than 8192 entries)
+// go to the generic kernel, which keeps no index row in LDS.
+constexpr size_t SPARSE_LDS_LIMIT = 64 * 1024;
+
+size_t sparse_bf16_lds_bytes(int width) { return (size_t)NS * TILE_BYTES + (size_t)width * sizeof(int); }
+
 bool sparse_uses_bf16_kernel(const SparsePlan& p) {
-  return p.bf16 && p.head_dim == D && (size_t)p.batch * p.n_q * p.h_kv >= 2048;
+  return p.bf16 && p.head_dim == D && (size_t)p.batch * p.n_q * p.h_kv >= 2048 &&
+         p.layers * (p.h_q / p.h_kv) <= 64 && sparse_bf16_lds_bytes(p.width) <= SPARSE_LDS_LIMIT;
 }
 
 hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
@@ -269,7 +277,8 @@ hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
   const int G = p.h_q / p.h_kv;
   const int rb = (p.layers * G + 15) / 16;
   const dim3 grid((unsigned)((size_t)p.batch * p.n_q * p.h_kv));
-  const size_t smem = NS * TILE_BYTES + (size_t)p.width * sizeof(int);
+  const size_t smem = sparse_bf16_lds_bytes(p.width);
+  if (smem > SPARSE_LDS_LIMIT) return hipErrorInvalidValue;
   if (rb <= 1) hipLaunchKernelGGL(sparse_bf16_kernel<1>, grid, dim3(64), smem, st, a);
   else if (rb <= 2) hipLaunchKernelGGL(sparse_bf16_kernel<2>, grid, dim3(128), smem, st, a);
   else if (rb <= 4) hipLaunchKernelGGL(sparse_bf16_kernel<4>, grid, dim3(256), smem, st, a);

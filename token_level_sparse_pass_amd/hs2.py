@@ -160,6 +160,38 @@ def _check_tensor(t, name, dtype=None):
         raise ValueError(f"{name} must be {dtype}")
 
 
+def _validate(specs):
+    """Check every tensor argument against the shape the call implies.
+
+    specs: (tensor or None, name, expected shape, dtype or None) tuples; a
+    None tensor is skipped. The C ABI receives raw pointers and cannot see a
+    mis-shaped tensor, which would become an out-of-bounds device access, so
+    every shape, dtype and device is checked here first: shapes and dtypes
+    before anything touches a device (so these checks also run without a
+    GPU), then that all tensors are contiguous device tensors on one device.
+    """
+    live = [s for s in specs if s[0] is not None]
+    for t, name, shape, dtype in live:
+        if tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} is {t.dtype}, expected {dtype}")
+    dev = live[0][0].device if live else None
+    for t, name, _, _ in live:
+        _check_tensor(t, name)
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _ws_bytes(ws, device):
+    """Byte size of a caller workspace (any dtype), after checking it."""
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace must be a device tensor on {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def alloc_workspace(p: Problem, device, nbytes=None):
     mn, pref = workspace_size(p)
     n = pref if nbytes is None else max(nbytes, mn)
@@ -169,10 +201,12 @@ def alloc_workspace(p: Problem, device, nbytes=None):
 def full_attn_select(q, k, v, *, workspace=None, debug_rows=None, want_lse=True, **kw):
     """Full layer + scoring + selection. Returns (o, idx, lse, scores|None)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, q.dtype)
-    p = _problem_from(q, k, kw)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, n_q, h_q, d] and k [B, n_kv, h_kv, d]")
     B, nq, hq, d = q.shape
+    _validate([(q, "q", q.shape, q.dtype), (k, "k", (B, k.shape[1], k.shape[2], d), q.dtype),
+               (v, "v", k.shape, q.dtype)])
+    p = _problem_from(q, k, kw)
     width = index_width(p)
     o = torch.empty_like(q)
     idx = torch.empty((B, nq, width), dtype=torch.int32, device=q.device)
@@ -185,22 +219,22 @@ def full_attn_select(q, k, v, *, workspace=None, debug_rows=None, want_lse=True,
         dbg = Debug(rows, len(debug_rows), scores.data_ptr())
         dbg_ref = ctypes.byref(dbg)
     _check(lib.hs2_full_attn_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                    _ptr(idx), _ptr(lse), dbg_ref, _ptr(ws), ws.numel(),
-                                    _stream(q.device)))
+                                    _ptr(idx), _ptr(lse), dbg_ref, _ptr(ws),
+                                    _ws_bytes(ws, q.device), _stream(q.device)))
     return o, idx, lse, scores
 
 
 def sparse_attn(q_layers, k, v, idx, **kw):
     """Sparse layers over the given index rows. q_layers [L, B, n_q, h_q, d]."""
     lib = load()
-    for t, n in ((q_layers, "q_layers"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, q_layers.dtype)
-    _check_tensor(idx, "idx", torch.int32)
-    L = q_layers.shape[0]
-    p = _problem_from(q_layers[0] if L else q_layers.new_empty((1,) + q_layers.shape[1:])[0],
-                      k, kw)
-    if idx.shape[-1] != index_width(p):
-        raise ValueError(f"idx width {idx.shape[-1]} != {index_width(p)}")
+    if q_layers.dim() != 5 or k.dim() != 4:
+        raise ValueError("q_layers must be [L, B, n_q, h_q, d] and k [B, n_kv, h_kv, d]")
+    L, B, nq, hq, d = q_layers.shape
+    p = problem(q_layers.dtype, B, nq, k.shape[1], hq, k.shape[2], d, **kw)
+    width = index_width(p)
+    _validate([(q_layers, "q_layers", q_layers.shape, q_layers.dtype),
+               (k, "k", (B, k.shape[1], k.shape[2], d), q_layers.dtype),
+               (v, "v", k.shape, q_layers.dtype), (idx, "idx", (B, nq, width), torch.int32)])
     o = torch.empty_like(q_layers)
     _check(lib.hs2_sparse_attn(ctypes.byref(p), L, _ptr(q_layers), _ptr(k), _ptr(v),
                                _ptr(idx), _ptr(o), _stream(k.device)))
@@ -210,21 +244,33 @@ def sparse_attn(q_layers, k, v, idx, **kw):
 def block_forward(q_full, q_sparse, k, v, *, workspace=None, want_lse=True, out=None, **kw):
     """The whole Hybrid Block. Returns dict(o_full, o_sparse, idx, lse)."""
     lib = load()
-    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, q_full.dtype)
-    p = _problem_from(q_full, k, kw)
+    if q_full.dim() != 4 or k.dim() != 4 or q_sparse.dim() != 5:
+        raise ValueError("q_full must be [B, n_q, h_q, d], q_sparse [L, B, n_q, h_q, d] "
+                         "and k [B, n_kv, h_kv, d]")
     B, nq, hq, d = q_full.shape
+    L = q_sparse.shape[0]
+    p = _problem_from(q_full, k, kw)
     width = index_width(p)
+    kshape = (B, k.shape[1], k.shape[2], d)
+    specs = [(q_full, "q_full", q_full.shape, q_full.dtype),
+             (q_sparse, "q_sparse", (L,) + tuple(q_full.shape), q_full.dtype),
+             (k, "k", kshape, q_full.dtype), (v, "v", kshape, q_full.dtype)]
+    if out is not None:
+        specs += [(out["o_full"], "o_full", q_full.shape, q_full.dtype),
+                  (out["o_sparse"], "o_sparse", q_sparse.shape, q_full.dtype),
+                  (out["idx"], "idx", (B, nq, width), torch.int32),
+                  (out.get("lse"), "lse", (B, hq, nq), torch.float32)]
+    _validate(specs)
     if out is None:
         out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
                    idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
                    lse=torch.empty((B, hq, nq), dtype=torch.float32, device=q_full.device)
                    if want_lse else None)
     ws = alloc_workspace(p, q_full.device) if workspace is None else workspace
-    _check(lib.hs2_block_forward(ctypes.byref(p), q_sparse.shape[0], _ptr(q_full),
+    _check(lib.hs2_block_forward(ctypes.byref(p), L, _ptr(q_full),
                                  _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out["o_full"]),
-                                 _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
-                                 _ptr(ws), ws.numel(), _stream(q_full.device)))
+                                 _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out.get("lse")),
+                                 _ptr(ws), _ws_bytes(ws, q_full.device), _stream(q_full.device)))
     return out
 
 
@@ -239,13 +285,28 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, *, works
     o_sparse, idx, lse); the caller advances lens.
     """
     lib = load()
-    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
-                 (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _check_tensor(t, n, q_full.dtype)
-    p = _problem_from(q_full, k_cache, kw)
+    if q_full.dim() != 4 or k_cache.dim() != 4 or q_sparse.dim() != 5:
+        raise ValueError("q_full must be [B, 1, h_q, d], q_sparse [L, B, 1, h_q, d] and "
+                         "k_cache [B, capacity, h_kv, d]")
     B, nq, hq, d = q_full.shape
-    lens_h = (ctypes.c_int32 * B)(*[int(x) for x in lens])
+    hkv = k_cache.shape[2]
+    if len(lens) != B:
+        raise ValueError(f"lens has {len(lens)} entries, expected {B}")
+    p = _problem_from(q_full, k_cache, kw)
     width = index_width(p)
+    cshape = (B, k_cache.shape[1], hkv, d)
+    specs = [(q_full, "q_full", q_full.shape, q_full.dtype),
+             (q_sparse, "q_sparse", (q_sparse.shape[0],) + tuple(q_full.shape), q_full.dtype),
+             (k_new, "k_new", (B, nq, hkv, d), q_full.dtype),
+             (v_new, "v_new", (B, nq, hkv, d), q_full.dtype),
+             (k_cache, "k_cache", cshape, q_full.dtype), (v_cache, "v_cache", cshape, q_full.dtype)]
+    if out is not None:
+        specs += [(out["o_full"], "o_full", q_full.shape, q_full.dtype),
+                  (out["o_sparse"], "o_sparse", q_sparse.shape, q_full.dtype),
+                  (out["idx"], "idx", (B, nq, width), torch.int32),
+                  (out.get("lse"), "lse", (B, hq, nq), torch.float32)]
+    _validate(specs)
+    lens_h = (ctypes.c_int32 * B)(*[int(x) for x in lens])
     if out is None:
         out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
                    idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
@@ -255,7 +316,8 @@ def decode_step(q_full, q_sparse, k_new, v_new, k_cache, v_cache, lens, *, works
     _check(lib.hs2_decode_step(ctypes.byref(p), q_sparse.shape[0], _ptr(q_full), _ptr(q_sparse),
                                _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), lens_h,
                                _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]),
-                               _ptr(out["lse"]), _ptr(ws), ws.numel(), _stream(q_full.device)))
+                               _ptr(out.get("lse")), _ptr(ws), _ws_bytes(ws, q_full.device),
+                               _stream(q_full.device)))
     return out
 
 
@@ -268,17 +330,32 @@ def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table
     pool row page_table[b, j // page_size] * page_size + j % page_size.
     """
     lib = load()
-    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
-                 (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
-        _check_tensor(t, n, q_full.dtype)
-    _check_tensor(page_table, "page_table", torch.int32)
+    if q_full.dim() != 4 or k_pool.dim() != 3 or q_sparse.dim() != 5 or page_table.dim() != 2:
+        raise ValueError("q_full must be [B, 1, h_q, d], q_sparse [L, B, 1, h_q, d], k_pool "
+                         "[rows, h_kv, d] and page_table [B, max_pages]")
     B, nq, hq, d = q_full.shape
+    hkv = k_pool.shape[1]
+    if len(lens) != B:
+        raise ValueError(f"lens has {len(lens)} entries, expected {B}")
     max_pages = page_table.shape[1]
     n_pages = k_pool.shape[0] // page_size
-    p = problem(q_full.dtype, B, nq, max_pages * page_size, hq, k_pool.shape[1], d, **kw)
+    p = problem(q_full.dtype, B, nq, max_pages * page_size, hq, hkv, d, **kw)
+    width = index_width(p)
+    pshape = (k_pool.shape[0], hkv, d)
+    specs = [(q_full, "q_full", q_full.shape, q_full.dtype),
+             (q_sparse, "q_sparse", (q_sparse.shape[0],) + tuple(q_full.shape), q_full.dtype),
+             (k_new, "k_new", (B, nq, hkv, d), q_full.dtype),
+             (v_new, "v_new", (B, nq, hkv, d), q_full.dtype),
+             (k_pool, "k_pool", pshape, q_full.dtype), (v_pool, "v_pool", pshape, q_full.dtype),
+             (page_table, "page_table", (B, max_pages), torch.int32)]
+    if out is not None:
+        specs += [(out["o_full"], "o_full", q_full.shape, q_full.dtype),
+                  (out["o_sparse"], "o_sparse", q_sparse.shape, q_full.dtype),
+                  (out["idx"], "idx", (B, nq, width), torch.int32),
+                  (out.get("lse"), "lse", (B, hq, nq), torch.float32)]
+    _validate(specs)
     pages = KvPages(page_table.data_ptr(), page_size, max_pages, n_pages)
     lens_h = (ctypes.c_int32 * B)(*[int(x) for x in lens])
-    width = index_width(p)
     if out is None:
         out = dict(o_full=torch.empty_like(q_full), o_sparse=torch.empty_like(q_sparse),
                    idx=torch.empty((B, nq, width), dtype=torch.int32, device=q_full.device),
@@ -288,8 +365,9 @@ def decode_step_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_table
     _check(lib.hs2_decode_step_paged(ctypes.byref(p), ctypes.byref(pages), q_sparse.shape[0],
                                      _ptr(q_full), _ptr(q_sparse), _ptr(k_new), _ptr(v_new),
                                      _ptr(k_pool), _ptr(v_pool), lens_h, _ptr(out["o_full"]),
-                                     _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
-                                     _ptr(ws), ws.numel(), _stream(q_full.device)))
+                                     _ptr(out["o_sparse"]), _ptr(out["idx"]),
+                                     _ptr(out.get("lse")), _ptr(ws), _ws_bytes(ws, q_full.device),
+                                     _stream(q_full.device)))
     return out
 
 
@@ -297,11 +375,19 @@ def kv_bridge(hidden, w_kv, h_kv, *, out=None):
     """hs2_kv_bridge: K, V [B, n, h_kv, d] from hidden [B, n, d_model] and
     w_kv [2, h_kv * d, d_model] (bf16). Returns (k, v)."""
     lib = load()
-    _check_tensor(hidden, "hidden", torch.bfloat16)
-    _check_tensor(w_kv, "w_kv", torch.bfloat16)
+    if hidden.dim() != 3 or w_kv.dim() != 3:
+        raise ValueError("hidden must be [B, n, d_model] and w_kv [2, h_kv * d, d_model]")
     B, n, dm = hidden.shape
     feats = w_kv.shape[1]
+    if h_kv <= 0 or feats % h_kv:
+        raise ValueError(f"w_kv has {feats} output features, not a multiple of h_kv = {h_kv}")
     d = feats // h_kv
+    specs = [(hidden, "hidden", hidden.shape, torch.bfloat16),
+             (w_kv, "w_kv", (2, feats, dm), torch.bfloat16)]
+    if out is not None:
+        specs += [(out[0], "k", (B, n, h_kv, d), torch.bfloat16),
+                  (out[1], "v", (B, n, h_kv, d), torch.bfloat16)]
+    _validate(specs)
     p = problem(torch.bfloat16, B, 1, n, h_kv, h_kv, d, top_k=1, window=1)
     if out is None:
         out = (torch.empty((B, n, h_kv, d), dtype=torch.bfloat16, device=hidden.device),
@@ -325,18 +411,25 @@ def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, 
     gradients; returns dict(dq_full, dq_sparse, dk, dv)."""
     lib = load()
     dt = q_full.dtype
-    for t, n in ((q_full, "q_full"), (k, "k"), (v, "v"), (o_full, "o_full"),
-                 (do_full, "do_full")):
-        _check_tensor(t, n, dt)
-    _check_tensor(lse, "lse", torch.float32)
+    if q_full.dim() != 4 or k.dim() != 4:
+        raise ValueError("q_full must be [B, n_q, h_q, d] and k [B, n_kv, h_kv, d]")
+    B, nq, hq, d = q_full.shape
     L = 0 if q_sparse is None else q_sparse.shape[0]
-    if L:
-        for t, n in ((q_sparse, "q_sparse"), (o_sparse, "o_sparse"), (do_sparse, "do_sparse")):
-            _check_tensor(t, n, dt)
-        _check_tensor(idx, "idx", torch.int32)
     p = _problem_from(q_full, k, kw)
-    if L and idx.shape[-1] != index_width(p):
-        raise ValueError(f"idx width {idx.shape[-1]} != {index_width(p)}")
+    kshape = (B, k.shape[1], k.shape[2], d)
+    specs = [(q_full, "q_full", q_full.shape, dt), (k, "k", kshape, dt), (v, "v", kshape, dt),
+             (o_full, "o_full", q_full.shape, dt), (do_full, "do_full", q_full.shape, dt),
+             (lse, "lse", (B, hq, nq), torch.float32)]
+    if L:
+        lshape = (L,) + tuple(q_full.shape)
+        specs += [(q_sparse, "q_sparse", lshape, dt), (o_sparse, "o_sparse", lshape, dt),
+                  (do_sparse, "do_sparse", lshape, dt),
+                  (idx, "idx", (B, nq, index_width(p)), torch.int32)]
+    if out is not None:
+        specs += [(out["dq_full"], "dq_full", q_full.shape, dt),
+                  (out["dq_sparse"] if L else None, "dq_sparse", (L,) + tuple(q_full.shape), dt),
+                  (out["dk"], "dk", kshape, dt), (out["dv"], "dv", kshape, dt)]
+    _validate(specs)
     if out is None:
         out = dict(dq_full=torch.empty_like(q_full),
                    dq_sparse=torch.empty_like(q_sparse) if L else None,
@@ -349,7 +442,7 @@ def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, 
         _ptr(o_full), _ptr(o_sparse if L else None), _ptr(lse), _ptr(idx if L else None),
         _ptr(do_full), _ptr(do_sparse if L else None), _ptr(out["dq_full"]),
         _ptr(out["dq_sparse"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(workspace),
-        workspace.numel(), _stream(q_full.device)))
+        _ws_bytes(workspace, q_full.device), _stream(q_full.device)))
     return out
 
 
@@ -375,15 +468,20 @@ def block_forward_varlen(q_full, q_sparse, k, v, cu_q, cu_kv, *, workspace=None,
     Returns dict(o_full, o_sparse, idx [total_q, W], lse (h_q * total_q
     floats, sequence b's [h_q][n_q(b)] block at h_q * cu_q[b]))."""
     lib = load()
-    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k, "k"), (v, "v")):
-        _check_tensor(t, n, q_full.dtype)
+    if q_full.dim() != 3 or k.dim() != 3 or q_sparse.dim() != 4:
+        raise ValueError("q_full must be [total_q, h_q, d], q_sparse [L, total_q, h_q, d] and "
+                         "k [total_kv, h_kv, d]")
     cq, vq = _cu(cu_q)
     ck, vk = _cu(cu_kv)
     batch = len(vq) - 1
     total_q, hq, d = q_full.shape
     hkv = k.shape[1]
-    if vq[-1] != total_q or vk[-1] != k.shape[0]:
+    if len(vk) != len(vq) or vq[-1] != total_q or vk[-1] != k.shape[0]:
         raise ValueError("cu_seqlens do not match the packed tensors")
+    kshape = (k.shape[0], hkv, d)
+    _validate([(q_full, "q_full", q_full.shape, q_full.dtype),
+               (q_sparse, "q_sparse", (q_sparse.shape[0],) + tuple(q_full.shape), q_full.dtype),
+               (k, "k", kshape, q_full.dtype), (v, "v", kshape, q_full.dtype)])
     p = problem(q_full.dtype, batch, 1, 1, hq, hkv, d, **kw)
     width = index_width(p)
     mn, pref = workspace_size_varlen(p, cq, ck)
@@ -396,7 +494,7 @@ def block_forward_varlen(q_full, q_sparse, k, v, cu_q, cu_kv, *, workspace=None,
     _check(lib.hs2_block_forward_varlen(
         ctypes.byref(p), q_sparse.shape[0], cq, ck, _ptr(q_full), _ptr(q_sparse), _ptr(k),
         _ptr(v), _ptr(out["o_full"]), _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]),
-        _ptr(workspace), workspace.numel(), _stream(q_full.device)))
+        _ptr(workspace), _ws_bytes(workspace, q_full.device), _stream(q_full.device)))
     return out
 
 
@@ -428,18 +526,25 @@ def block_forward_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_tab
     lengths before the call (host ints; the caller advances them). Returns
     dict(o_full, o_sparse, idx [total_q, W], lse) as block_forward_varlen."""
     lib = load()
-    for t, n in ((q_full, "q_full"), (q_sparse, "q_sparse"), (k_new, "k_new"),
-                 (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
-        _check_tensor(t, n, q_full.dtype)
-    _check_tensor(page_table, "page_table", torch.int32)
+    if q_full.dim() != 3 or k_pool.dim() != 3 or q_sparse.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q_full must be [total_q, h_q, d], q_sparse [L, total_q, h_q, d], "
+                         "k_pool [rows, h_kv, d] and page_table [B, max_pages]")
     cq, vq = _cu(cu_q)
     ln, vl = _cu(lens)
     batch = len(vq) - 1
     total_q, hq, d = q_full.shape
-    if vq[-1] != total_q or k_new.shape[0] != total_q or len(vl) != batch:
+    hkv = k_pool.shape[1]
+    if vq[-1] != total_q or len(vl) != batch:
         raise ValueError("cu_q / lens do not match the packed tensors")
     if page_table.shape[0] != batch:
         raise ValueError("page_table needs one row per sequence")
+    pshape = (k_pool.shape[0], hkv, d)
+    _validate([(q_full, "q_full", q_full.shape, q_full.dtype),
+               (q_sparse, "q_sparse", (q_sparse.shape[0],) + tuple(q_full.shape), q_full.dtype),
+               (k_new, "k_new", (total_q, hkv, d), q_full.dtype),
+               (v_new, "v_new", (total_q, hkv, d), q_full.dtype),
+               (k_pool, "k_pool", pshape, q_full.dtype), (v_pool, "v_pool", pshape, q_full.dtype),
+               (page_table, "page_table", page_table.shape, torch.int32)])
     p, pages = _paged_problem(q_full, k_pool, page_table, page_size, batch, kw)
     width = index_width(p)
     if workspace is None:
@@ -453,5 +558,5 @@ def block_forward_paged(q_full, q_sparse, k_new, v_new, k_pool, v_pool, page_tab
         ctypes.byref(p), ctypes.byref(pages), q_sparse.shape[0], cq, ln, _ptr(q_full),
         _ptr(q_sparse), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out["o_full"]),
         _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out["lse"]), _ptr(workspace),
-        workspace.numel(), _stream(q_full.device)))
+        _ws_bytes(workspace, q_full.device), _stream(q_full.device)))
     return out
