@@ -77,18 +77,218 @@ KERNEL_SOURCES = {
 }
 
 
-def measured_traffic(pass_name, workload):
-    """HBM bytes per launch from the committed counter summary, if current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def committed_counters(kind, pass_name, workload):
+    """A pass's record from profiles/<kind>.json (kind "traffic": HBM bytes
+    from FETCH_SIZE / WRITE_SIZE; kind "mfma": MFMA counters) for this
+    workload, or None when there is none or the pass's kernel sources have
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", kind + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(pass_name)
-    if not rec or rec.get("workload") != workload:
+        rec = json.load(f).get("passes", {}).get(pass_name, {}).get(workload)
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[pass_name]):
         return None
-    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[pass_name]):
-        return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(pass_name, workload):
+    """HBM bytes per launch of the pass's kernels from the committed counters."""
+    rec = committed_counters("traffic", pass_name, workload)
+    return None if rec is None else rec["bytes_per_launch"]
+
+
+# kernels of each pass, by name prefix (as rocprofv3 reports them)
+PASS_KERNELS = {
+    "full_attention": ("hs2::attn_fwd_bf16_kernel", "hs2::attn_fwd_prefill_kernel",
+                       "hs2::attn_decode_bf16_kernel", "hs2::attn_fwd_decode_kernel",
+                       "hs2::decode_combine_kernel"),
+    "score": ("hs2::score_bf16_kernel", "hs2::score_prefill_kernel", "hs2::decode_score_kernel"),
+    "select": ("hs2::select_token_kernel", "hs2::select_block_kernel"),
+    "sparse_attention": ("hs2::sparse_bf16_kernel", "hs2::sparse_attn_kernel"),
+    "v_layout": ("hs2::transpose_v_kernel",),
+}
+COUNTER_REGEX = "attn_fwd|attn_decode|decode_|score|sparse|select|transpose"
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+                 "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def _read_counter_csv(path):
+    """{(dispatch id, kernel name): {counter: value}} from a rocprofv3 csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = _kernel_base_name(r["Kernel_Name"])
+            key = (int(r["Dispatch_Id"]), name)
+            out.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def _kernel_base_name(name):
+    """'hs2::name' from a demangled signature or an Itanium-mangled name
+    (_ZN<len><part>...: the nested-name prefix, template arguments dropped)."""
+    if name.startswith("_ZN"):
+        parts, i = [], 3
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            parts.append(name[j:j + n])
+            i = j + n
+        return "::".join(parts)
+    name = name.split("(")[0]
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("<")[0]
+
+
+def _pass_of(kernel):
+    for name, prefixes in PASS_KERNELS.items():
+        if kernel in prefixes:
+            return name
+    return None
+
+
+def counters_summary(pmc_dir, steps_profiled=2):
+    """Summarise rocprofv3 --pmc runs into profiles/traffic.json,
+    profiles/mfma.json and one markdown file per workload (host only).
+
+    pmc_dir holds the runs made by the commands this function writes into
+    the markdown (directories mfma_c<N>, fetch_c<N>, write_c<N> for
+    workload N, fetch_copy / write_copy for the copy calibration), each with
+    rocprofv3's run_counter_collection.csv and run_agent_info.csv. Each
+    workload run is `bench.py --steps 1 --warmup 0`: two block_forward
+    calls, so per-step figures are totals / 2."""
+    import csv
+    from synth import CONFIGS
+
+    def csv_of(sub):
+        path = os.path.join(pmc_dir, sub, "run_counter_collection.csv")
+        return _read_counter_csv(path) if os.path.exists(path) else None
+
+    n_xcc = 8
+    agent = os.path.join(pmc_dir, "fetch_copy", "run_agent_info.csv")
+    if os.path.exists(agent):
+        with open(agent) as f:
+            for r in csv.DictReader(f):
+                if r.get("Agent_Type") == "GPU" or r.get("Name", "").startswith("gfx"):
+                    n_xcc = int(r.get("Num_Xcc", n_xcc))
+    # copy calibration: a 2 GiB elementwise copy (2 GiB read, 2 GiB written)
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = csv_of(("fetch" if c == "FETCH_SIZE" else "write") + "_copy")
+        vals = [v[c] for v in d.values()]
+        cal[c] = sum(vals) / len(vals)
+    size_kib = 2048 * 1024
+    scale = {"fetch": size_kib / cal["FETCH_SIZE"], "write": size_kib / cal["WRITE_SIZE"]}
+
+    traffic, mfma = {}, {}
+    md = {}
+    cmd_base = ("cd /tmp && export TMPDIR=/tmp  # then, from there, with R = the repository root:\n")
+    for cid, w in CONFIGS.items():
+        fetch, write, mf = csv_of(f"fetch_c{cid}"), csv_of(f"write_c{cid}"), csv_of(f"mfma_c{cid}")
+        if fetch is None and mf is None:
+            continue
+        run = f"python3 $R/bench.py --config {cid} --steps 1 --warmup 0 --no-cpu-baseline"
+        cmds = []
+        lines = []
+        if fetch is not None and write is not None:
+            for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+                cmds.append(f"rocprofv3 --pmc {c} --kernel-include-regex \"{COUNTER_REGEX}\" -f csv "
+                            f"-d $R/gpurun_out/pmc/{sub}_c{cid} -o run -- {run}")
+            # the two runs launch the same kernels in the same order: pair the
+            # n-th dispatch of each kernel in one with the n-th in the other
+            per = {}
+            for kern in sorted({k[1] for k in fetch if _pass_of(k[1])}):
+                fk = sorted(k for k in fetch if k[1] == kern)
+                wk = sorted(k for k in write if k[1] == kern)
+                assert len(fk) == len(wk), (kern, len(fk), len(wk))
+                ps = _pass_of(kern)
+                e = per.setdefault(ps, {"kernels": set(), "dispatches": 0, "fetch": 0.0,
+                                        "write": 0.0})
+                e["kernels"].add(kern)
+                e["dispatches"] += len(fk)
+                e["fetch"] += sum(fetch[k]["FETCH_SIZE"] for k in fk)
+                e["write"] += sum(write[k]["WRITE_SIZE"] for k in wk)
+            lines += ["", "HBM traffic (FETCH_SIZE and WRITE_SIZE in KiB, summed over the "
+                      f"{steps_profiled} profiled steps; bytes scaled by the copy calibration):", "",
+                      "| pass | kernels | dispatches per step | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) "
+                      "| HBM bytes per step | per launch |", "|---|---|---|---|---|---|---|"]
+            for ps, e in per.items():
+                byts = (e["fetch"] * scale["fetch"] + e["write"] * scale["write"]) * 1024
+                step = byts / steps_profiled
+                launches = e["dispatches"] / steps_profiled
+                traffic.setdefault(ps, {})[w.name] = {
+                    "kernels": sorted(e["kernels"]), "launches_per_step": launches,
+                    "fetch_kib": round(e["fetch"], 1), "write_kib": round(e["write"], 1),
+                    "bytes_per_step": round(step), "bytes_per_launch": round(step / launches),
+                    "source_sha": source_sha(KERNEL_SOURCES[ps])}
+                lines.append(f"| {ps} | {', '.join('`' + k + '`' for k in sorted(e['kernels']))} "
+                             f"| {launches:g} | {e['fetch']:.0f} | {e['write']:.0f} "
+                             f"| {step / 2**30:.3f} GiB | {step / launches / 2**30:.4f} GiB |")
+        if mf is not None:
+            cmds.append(f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-include-regex "
+                        f"\"{COUNTER_REGEX}\" -f csv -d $R/gpurun_out/pmc/mfma_c{cid} -o run -- {run}")
+            per = {}
+            for (disp, kern), v in mf.items():
+                ps = _pass_of(kern)
+                if ps is None:
+                    continue
+                e = per.setdefault(ps, {"kernels": set(), "dispatches": 0})
+                e["kernels"].add(kern)
+                e["dispatches"] += 1
+                for c, x in v.items():
+                    e[c] = e.get(c, 0.0) + x
+            lines += ["", "MFMA counters (summed over the dispatches of the profiled steps; "
+                      f"GRBM_GUI_ACTIVE is reported summed over the {n_xcc} XCDs, so one XCD's "
+                      f"active cycles are that sum / {n_xcc}):", "",
+                      "| pass | dispatches per step | MFMA flops per step (MOPS_BF16 x 512) "
+                      "| MFMA busy (BUSY_CYCLES / (GUI_ACTIVE/XCDs x 1024 SIMDs)) "
+                      "| active cycles per launch (one XCD) | VALU instr per MFMA "
+                      "| LDS instr per MFMA |", "|---|---|---|---|---|---|---|"]
+            for ps, e in per.items():
+                if e.get("SQ_INSTS_MFMA", 0) == 0:
+                    continue
+                gui = e["GRBM_GUI_ACTIVE"] / n_xcc
+                busy = e["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * 1024)
+                flops_step = e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / steps_profiled
+                launches = e["dispatches"] / steps_profiled
+                rec = {"kernels": sorted(e["kernels"]), "launches_per_step": launches,
+                       "mfma_flops_per_step": flops_step, "mfma_busy": round(busy, 4),
+                       "active_cycles_per_launch": round(gui / e["dispatches"]),
+                       "valu_per_mfma": round(e["SQ_INSTS_VALU"] / e["SQ_INSTS_MFMA"], 3),
+                       "lds_per_mfma": round(e["SQ_INSTS_LDS"] / e["SQ_INSTS_MFMA"], 3),
+                       "source_sha": source_sha(KERNEL_SOURCES[ps])}
+                mfma.setdefault(ps, {})[w.name] = rec
+                lines.append(f"| {ps} | {launches:g} | {flops_step:.4e} | {100 * busy:.1f} % "
+                             f"| {rec['active_cycles_per_launch']:.4e} | {rec['valu_per_mfma']:.2f} "
+                             f"| {rec['lds_per_mfma']:.2f} |")
+        md[w.name] = (cmds, lines)
+    cal_cmds = [f"rocprofv3 --pmc {c} --kernel-include-regex \"neg\" -f csv -d "
+                f"$R/gpurun_out/pmc/{sub}_copy -o run -- python3 $R/bench.py --copy-calibration 2048"
+                for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
+    cal_line = (f"Copy calibration: a plain elementwise copy of 2 GiB (2 GiB read, 2 GiB written) "
+                f"reads FETCH_SIZE = {cal['FETCH_SIZE']:.0f} KiB and WRITE_SIZE = "
+                f"{cal['WRITE_SIZE']:.0f} KiB per dispatch, so fetch counts are scaled by "
+                f"{scale['fetch']:.4f} and write counts by {scale['write']:.4f}.")
+    prof = os.path.join(ROOT, "profiles")
+    note = ("rocprofv3 --pmc counters per pass and workload; bytes are FETCH_SIZE and WRITE_SIZE "
+            "scaled by a plain copy's readings; MFMA flops are SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; "
+            "records hold for the kernel sources whose hash they carry")
+    with open(os.path.join(prof, "traffic.json"), "w") as f:
+        json.dump({"_note": note, "scale": scale, "passes": traffic}, f, indent=1)
+    with open(os.path.join(prof, "mfma.json"), "w") as f:
+        json.dump({"_note": note, "xcds": n_xcc, "passes": mfma}, f, indent=1)
+    for wname, (cmds, lines) in md.items():
+        with open(os.path.join(prof, f"counters_{wname}.md"), "w") as f:
+            f.write(f"# rocprofv3 counters: Hybrid Block step, {wname}\n\n"
+                    "Commands (one pass per counter set; each run's program is bench.py of this "
+                    "repository; summarised by `python bench.py --counters-summary "
+                    "gpurun_out/pmc`):\n\n```\n" + cmd_base + "\n".join(cmds + cal_cmds) +
+                    "\n```\n\n" + cal_line + "\n" + "\n".join(lines) + "\n")
+    print(json.dumps({"workloads": sorted(md), "scale": scale}))
 
 
 def host_cpu():
@@ -602,6 +802,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=0,
                     help="with --decode-loop: keep the cache in a pool of pages of this many "
                          "rows, handed out in shuffled order (hs2_decode_step_paged)")
+    ap.add_argument("--counters-summary", metavar="DIR", default=None,
+                    help="host only: summarise rocprofv3 --pmc runs under DIR into profiles/ "
+                         "and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read MIB, write MIB) "
                          "three times, to scale HBM byte counters, and exit")
@@ -611,6 +814,9 @@ def main():
               "single-GPU build (no collectives); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.counters_summary:
+        counters_summary(args.counters_summary)
+        return
     import torch
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -687,25 +893,47 @@ def main():
         bound, amount = work[name]
         per_step_ms = ms[i] / args.steps
         launches = nl[i] // args.steps
+        secs = per_step_ms / 1e3 if per_step_ms > 0 else float("inf")
         if bound == "mfma":
-            ach = amount / (per_step_ms / 1e3) / 1e12 if per_step_ms > 0 else 0.0
+            ach = amount / secs / 1e12
             passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
                             "bound": "mfma", "achieved": round(ach, 2), "unit": "TFLOP/s",
                             "frac": round(ach / peak_mfma, 4)}
+            mc = committed_counters("mfma", name, w.name)
+            if mc is not None:
+                # rocprof's own count of the MFMA flops this pass executes,
+                # over the live time, and its MFMA-busy fraction
+                rate = mc["mfma_flops_per_step"] / secs / 1e12
+                passes[name]["rocprof"] = {
+                    "mfma_tflops": round(rate, 2), "mfma_frac": round(rate / peak_mfma, 4),
+                    "mfma_busy": mc["mfma_busy"], "valu_per_mfma": mc["valu_per_mfma"]}
         else:
-            ach = amount / (per_step_ms / 1e3) / 1e9 if per_step_ms > 0 else 0.0
+            # HBM fraction from the committed FETCH/WRITE counters (null without
+            # them); "effective" counts every algorithmic byte, including those
+            # that the caches serve, so it can exceed the HBM peak
+            eff = amount / secs / 1e9
+            tr = committed_counters("traffic", name, w.name)
+            ach = None if tr is None else tr["bytes_per_step"] / secs / 1e9
             passes[name] = {"ms": round(per_step_ms, 4), "launches_per_step": int(launches),
-                            "bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s",
-                            "frac": round(ach / PEAK_HBM_GBS, 4)}
+                            "bound": "hbm",
+                            "achieved": None if ach is None else round(ach, 1), "unit": "GB/s",
+                            "frac": None if ach is None else round(ach / PEAK_HBM_GBS, 4),
+                            "effective_GBs": round(eff, 1),
+                            "effective_frac": round(eff / PEAK_HBM_GBS, 4)}
     dom = max(passes, key=lambda n: passes[n]["ms"])
     d = passes[dom]
     per_launch = work[dom][1] / max(1, d["launches_per_step"])
     traffic = measured_traffic(dom, w.name)
-    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"],
-                "peak": peak_mfma if d["bound"] == "mfma" else PEAK_HBM_GBS,
-                "unit": d["unit"], "frac": d["frac"],
+    # the dominant kernel: algorithmic work per launch over its live time
+    ach = per_launch * d["launches_per_step"] / (d["ms"] / 1e3) / (1e12 if d["bound"] == "mfma"
+                                                                  else 1e9)
+    peak = peak_mfma if d["bound"] == "mfma" else PEAK_HBM_GBS
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": round(ach, 2),
+                "peak": peak, "unit": d["unit"], "frac": round(ach / peak, 4),
                 "algorithmic_per_launch": per_launch,
                 "traffic": traffic}
+    if "rocprof" in d:
+        roofline["rocprof"] = d["rocprof"]
 
     cpu = None
     if not args.no_cpu_baseline:
