@@ -137,6 +137,30 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * hs2_block_forward with its workspace taken from a buffer the library
+ * holds in device memory, HS2_STATIC_WORKSPACE_BYTES on each GPU it runs
+ * on, reserved when the library's device code is loaded onto that GPU and
+ * held until the process ends. The call allocates nothing.
+ *   Arguments, layouts and results are those of hs2_block_forward, without
+ *   the workspace; the device is the calling thread's current HIP device.
+ *   A problem whose minimum workspace (hs2_workspace_size) exceeds
+ *   HS2_STATIC_WORKSPACE_BYTES returns HS2_ERR_WORKSPACE, like every other
+ *   argument error, before any device call.
+ *   Every call on one GPU uses that GPU's one buffer, which keeps what the
+ *   last call left in it: calls on one GPU that overlap in time (on
+ *   different streams, or from threads without ordering) race and give
+ *   undefined results; calls ordered on one stream are safe. No part of the
+ *   buffer has to start at zero (each pass writes what the next one reads),
+ *   so nothing is cleared between calls. */
+#define HS2_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+hs2_status hs2_block_forward_static(const hs2_problem* p, int32_t n_sparse_layers,
+                                    const void* q_full, const void* q_sparse,
+                                    const void* k, const void* v, void* o_full,
+                                    void* o_sparse, int32_t* idx, float* lse,
+                                    void* stream);
+
 /* One decode step of the whole block over a growing KV cache, for a batch
  * of sequences of different lengths (the block's deployment shape: decode
  * is where the Cross-Decoder's hybrid blocks run, bound by memory bandwidth;

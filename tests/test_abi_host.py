@@ -457,3 +457,26 @@ def test_binding_rejects_mis_shaped_packed_and_backward_calls():
     bad[9] = _t(L + 1, B, nq, hq, d)                                     # do_sparse
     _shape_error(hs2.block_backward, *bad, **kw)
     _shape_error(hs2.block_backward, *args, match="device tensor", **kw)
+
+
+def test_static_workspace_entry_point_rejects_on_the_host():
+    lib = hs2.load()
+    vp = ctypes.c_void_p
+
+    def call(p, ptrs=None):
+        a = dict(q=FAKE, qs=FAKE, k=FAKE, v=FAKE, o=FAKE, os=FAKE, idx=FAKE, lse=None)
+        a.update(ptrs or {})
+        return lib.hs2_block_forward_static(ctypes.byref(p), 2, vp(a["q"]), vp(a["qs"]),
+                                            vp(a["k"]), vp(a["v"]), vp(a["o"]), vp(a["os"]),
+                                            vp(a["idx"]), vp(a["lse"]), None)
+    # the 1M-token context needs far more than the static workspace's 64 MiB
+    big = base_problem(n_q=16384, n_kv=1048576, h_q=64, h_kv=8, top_k=1024, window=128)
+    assert hs2.workspace_size(big)[0] > hs2.STATIC_WORKSPACE_BYTES
+    assert call(big) == 4                                      # HS2_ERR_WORKSPACE
+    assert "static" in lib.hs2_last_error().decode()
+    small = base_problem()
+    assert hs2.workspace_size(small)[0] <= hs2.STATIC_WORKSPACE_BYTES
+    assert call(small, dict(q=None)) == 1                      # HS2_ERR_NULL
+    assert call(small, dict(os=None)) == 1
+    assert call(small, dict(idx=FAKE + 4)) == 5                # HS2_ERR_ALIGN
+    assert call(base_problem(h_q=6, h_kv=4)) == 2              # HS2_ERR_SHAPE

@@ -454,6 +454,67 @@ hs2_status hs2_block_forward(const hs2_problem* p, int32_t n_sparse_layers, cons
   return run_sparse(*p, n_sparse_layers, q_sparse, k, v, idx, o_sparse, st);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace of hs2_block_forward_static: one copy of this array on each
+// GPU the library runs on. In host code its name is only a stand-in, so the
+// device address of each GPU's copy is looked up once, with that GPU
+// current, and every launch receives that address.
+static __device__ __align__(256) char scratch[HS2_STATIC_WORKSPACE_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+hs2_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(HS2_ERR_DEVICE, "device %d: the static workspace serves devices 0..%d", dev,
+                MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "static workspace address");
+    if (!ptr) return fail(HS2_ERR_DEVICE, "static workspace has no device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_block_forward_static(const hs2_problem* p, int32_t n_sparse_layers,
+                                    const void* q_full, const void* q_sparse, const void* k,
+                                    const void* v, void* o_full, void* o_sparse, int32_t* idx,
+                                    float* lse, void* stream) {
+  g_err.clear();
+  // every host check first: nothing touches a device before they pass
+  HS2_TRY(check_problem(p));
+  size_t mn = 0;
+  if (plan(*p, SIZE_MAX, nullptr, &mn, nullptr) != HS2_OK) return fail(HS2_ERR_SHAPE, "plan");
+  if (mn > HS2_STATIC_WORKSPACE_BYTES)
+    return fail(HS2_ERR_WORKSPACE,
+                "the problem needs a workspace of at least %zu bytes; the static one holds %zu",
+                mn, (size_t)HS2_STATIC_WORKSPACE_BYTES);
+  HS2_TRY(check_ptr(q_full, "q_full"));
+  HS2_TRY(check_ptr(k, "k"));
+  HS2_TRY(check_ptr(v, "v"));
+  HS2_TRY(check_ptr(o_full, "o_full"));
+  HS2_TRY(check_ptr(idx, "idx"));
+  HS2_TRY(check_ptr(lse, "lse", false));
+  HS2_TRY(check_sparse_args(p, n_sparse_layers, q_sparse, k, v, idx, o_sparse));
+  void* ws = nullptr;
+  HS2_TRY(scratch_of_current_device(&ws));
+  return hs2_block_forward(p, n_sparse_layers, q_full, q_sparse, k, v, o_full, o_sparse, idx, lse,
+                           ws, HS2_STATIC_WORKSPACE_BYTES, stream);
+}
+
 namespace {
 
 // A paged pool's geometry; p.n_kv must be its per-sequence capacity.

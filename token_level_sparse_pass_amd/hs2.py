@@ -71,6 +71,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_sparse_attn.restype = i32
     lib.hs2_block_forward.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hs2_block_forward.restype = i32
+    lib.hs2_block_forward_static.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hs2_block_forward_static.restype = i32
     lib.hs2_decode_step.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp,
                                     vp, vp, vp, sz, vp]
     lib.hs2_decode_step.restype = i32
@@ -271,6 +273,37 @@ def block_forward(q_full, q_sparse, k, v, *, workspace=None, want_lse=True, out=
                                  _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out["o_full"]),
                                  _ptr(out["o_sparse"]), _ptr(out["idx"]), _ptr(out.get("lse")),
                                  _ptr(ws), _ws_bytes(ws, q_full.device), _stream(q_full.device)))
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 64 << 20      # HS2_STATIC_WORKSPACE_BYTES
+
+
+def block_forward_static(q_full, q_sparse, k, v, *, out, **kw):
+    """hs2_block_forward_static: the whole block with the library's static
+    device workspace, for callers that cannot allocate. `out` holds the
+    caller's output tensors (o_full, o_sparse, idx, lse or None); the call
+    allocates nothing. Calls that overlap in time on one GPU race."""
+    lib = load()
+    if q_full.dim() != 4 or k.dim() != 4 or q_sparse.dim() != 5:
+        raise ValueError("q_full must be [B, n_q, h_q, d], q_sparse [L, B, n_q, h_q, d] "
+                         "and k [B, n_kv, h_kv, d]")
+    B, nq, hq, d = q_full.shape
+    L = q_sparse.shape[0]
+    p = _problem_from(q_full, k, kw)
+    width = index_width(p)
+    kshape = (B, k.shape[1], k.shape[2], d)
+    _validate([(q_full, "q_full", q_full.shape, q_full.dtype),
+               (q_sparse, "q_sparse", (L,) + tuple(q_full.shape), q_full.dtype),
+               (k, "k", kshape, q_full.dtype), (v, "v", kshape, q_full.dtype),
+               (out["o_full"], "o_full", q_full.shape, q_full.dtype),
+               (out["o_sparse"], "o_sparse", q_sparse.shape, q_full.dtype),
+               (out["idx"], "idx", (B, nq, width), torch.int32),
+               (out.get("lse"), "lse", (B, hq, nq), torch.float32)])
+    _check(lib.hs2_block_forward_static(ctypes.byref(p), L, _ptr(q_full), _ptr(q_sparse),
+                                        _ptr(k), _ptr(v), _ptr(out["o_full"]),
+                                        _ptr(out["o_sparse"]), _ptr(out["idx"]),
+                                        _ptr(out.get("lse")), _stream(q_full.device)))
     return out
 
 
