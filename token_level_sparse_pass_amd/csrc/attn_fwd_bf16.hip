@@ -3,20 +3,25 @@
 // attention over the shared K/V plus per-(query, head) statistics
 // (m2, l) and LSE.
 //
-// Differences from the generic kernel, all aimed at keeping the SIMD's
-// issue slots on MFMAs (with two waves per SIMD issuing both, every VALU
-// instruction in the loop costs MFMA time: about 2-3 cycles each, measured
-// with MFMA and FMA streams interleaved in each wave):
+// Differences from the generic kernel, all aimed at keeping the MFMA pipe
+// fed with as few instructions around it as possible:
 //  * V is transposed once per call into a tile-major copy in the workspace,
 //    Vt[b][g][tile][d][64 keys], so the PV product reads its operands with
 //    16-byte LDS loads instead of transposing in registers;
 //  * K and Vt tiles go straight from global memory into LDS
-//    (global_load_lds_dwordx4) through a two-stage ring (the next tile
-//    loads while this one is used), with XOR-swizzled 16-byte chunks so
-//    the MFMA operand reads are free of bank conflicts; the tile loop is
-//    unrolled by two so each stage's LDS offsets are immediates of the
-//    read instructions, and tiles that need no causal mask run a copy of
-//    the loop body without one;
+//    (global_load_lds_dwordx4) through two-stage rings, with XOR-swizzled
+//    16-byte chunks so the MFMA operand reads are free of bank conflicts;
+//    the tile loop is unrolled by two so each stage's LDS offsets are
+//    immediates of the read instructions, and tiles that need no causal
+//    mask run a copy of the loop body without one;
+//  * the eight waves form two groups half a tile apart (waves w and w + 4
+//    share a SIMD): a tile step is an MFMA phase (the previous tile's PV
+//    product, then this tile's logits) and a VALU phase (this tile's
+//    softmax), and the groups pass the tile barrier at different points of
+//    it, so one wave's MFMAs run beside its SIMD partner's softmax (1-2 %
+//    faster than all eight waves in step; counters put both the MFMA and the
+//    VALU pipe near half busy, so the loop is latency bound at two waves per
+//    SIMD rather than bound by either pipe);
 //  * row maxima use three-input max instructions and the gfx950 permlane
 //    swaps (no LDS round trip for the cross-row step); this file is built
 //    with -fno-honor-nans so that fmaxf does not first quiet every operand
@@ -30,8 +35,8 @@
 // Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
 // 16-row MFMA blocks per wave, eight waves (two per SIMD) per work-group,
 // all sharing each tile in LDS. Each wave reads a whole K and V^T tile from
-// LDS per 64 keys (512 B per MFMA); the counters put the LDS pipe at under
-// half of its cycles, so the loop is bound by instruction issue, not LDS.
+// LDS per 64 keys (512 B per MFMA); the LDS pipe is busy under half of its
+// cycles.
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -118,7 +123,6 @@ template <int RBW, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
   using OP = Op<__bf16, D>;
   constexpr int ROWS = 16 * RBW * NWV;                  // rows per work-group
-  constexpr int CPT = 1024 / (64 * NWV);                // 16-byte chunks per thread per tensor
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -203,8 +207,25 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     }
   }
 
-  // ---- tile loads straight into LDS ----
-  auto issue = [&](int tile, int stage) {
+  // ---- two groups of four waves, half a tile apart ----
+  // Waves w and w + 4 share a SIMD. Each wave's tile step is an MFMA phase
+  // (the previous tile's PV product, then this tile's logits) followed by a
+  // VALU phase (the softmax that forms this tile's P). The leading group
+  // (waves 0-3) passes tile barrier t before its MFMA phase of tile t, the
+  // other group between its MFMA and VALU phases of tile t - 1, so on every
+  // SIMD one wave's MFMAs run beside the other wave's softmax arithmetic
+  // instead of both waves reaching each phase together.
+  // Tiles move through two-stage rings: right after barrier t every wave
+  // issues its share of K(t + 1) (into the stage of K(t - 1), whose logits
+  // both groups formed before barrier t) and of Vt(t) (into the stage of
+  // Vt(t - 2), whose PV product both groups finished before barrier t); a
+  // wave waits for its own loads before its next barrier, so both tiles are
+  // in LDS for every wave after barrier t + 1, before either is read.
+  const bool lead = __builtin_amdgcn_readfirstlane(wave) < 4;
+  static_assert(NWV == 8, "two groups of four waves");
+  constexpr int CPT = 1024 / (64 * NWV);                // 16-byte chunks per thread per tensor
+
+  auto issue_k = [&](int tile, int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE_BYTES;
     const int j0 = tile * TK;
 #pragma unroll
@@ -216,6 +237,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       const __bf16* src = kseq + (size_t)key * kstride + c * 8;
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
     }
+  };
+  auto issue_v = [&](int tile, int stage) __attribute__((always_inline)) {
+    char* base = smem + stage * STAGE_BYTES;
     const __bf16* vsrc = vtseq + (size_t)tile * (D * TK);
 #pragma unroll
     for (int t = 0; t < CPT; ++t) {
@@ -239,52 +263,50 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // per-lane LDS offsets that do not change between tiles
-  int koff[4][4];                                       // [kb][unit] byte offset in K tile
+  // per-lane LDS offsets that do not change between tiles. The K row of
+  // key block kb held by lane (grp, l16) is tile_key(kb, l16), whose swizzle
+  // kswz() is l16 for every kb, so the block moves the row by a constant
+  // (KB_OFF[kb], an immediate of the read); likewise the Vt row of head-dim
+  // block db is db * 16 + l16, whose swizzle does not depend on db.
+  int koff[4];                                          // [unit] byte offset, key block 0
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int row = tile_key(kb, l16);
+  for (int u = 0; u < 4; ++u) koff[u] = tile_key(0, l16) * 256 + (((4 * grp + u) ^ l16) << 4);
+  int voff[2];                                          // [step] byte offset, head-dim block 0
 #pragma unroll
-    for (int u = 0; u < 4; ++u) koff[kb][u] = row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
-  }
-  int voff[2][8];                                       // [step][db] byte offset in Vt tile
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
+  for (int st = 0; st < 2; ++st) voff[st] = KT_BYTES + l16 * 128 + (((4 * st + grp) ^ vswz(l16)) << 4);
+
+  f32x4 s[RBW][4];                                      // this tile's logits^T
+  bf16x8 pu[RBW][2];                                    // the previous tile's P^T operands
+
+  // O^T += V^T . P^T for the tile whose P is in pu (its Vt rows at vbase)
+  auto pv = [&](auto stage_c) __attribute__((always_inline)) {
+    const char* vbase = smem + decltype(stage_c)::value * STAGE_BYTES;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int d = db * 16 + l16;
-      voff[st][db] = KT_BYTES + d * 128 + (((4 * st + grp) ^ vswz(d)) << 4);
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vbase + voff[0] + db * 2048);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vbase + voff[1] + db * 2048);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        acc[rb][db] = OP::mma(v0, pu[rb][0], acc[rb][db]);
+        acc[rb][db] = OP::mma(v1, pu[rb][1], acc[rb][db]);
+      }
     }
-
-  // two-stage ring: tile t + 1 is loaded into the other stage while tile t
-  // is used; the loop is unrolled by two so each stage's LDS offsets are
-  // compile-time constants folded into the LDS read instructions
-  if (n_tiles > 0) issue(0, 0);
-  auto step = [&](int t, auto stage_c, auto masked_c) {
-    constexpr int STAGE_C = decltype(stage_c)::value;       // -1: runtime
-    constexpr bool masked = decltype(masked_c)::value;
-    const int STAGE = STAGE_C >= 0 ? STAGE_C : (t & 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    // the other stage held tile t - 1, which every wave finished reading
-    // before the barrier above
-    if (t + 1 < n_tiles) issue(t + 1, STAGE ^ 1);
-    const char* base = smem + STAGE * STAGE_BYTES;
-    const int j0 = t * TK;
-
-    // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
-    // kb + 1 are read from LDS while block kb's MFMAs run
-    f32x4 s[RBW][4];
+  };
+  // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
+  // kb + 1 are read from LDS while block kb's MFMAs run
+  auto qk = [&](auto stage_c) __attribute__((always_inline)) {
+    const char* kbase = smem + decltype(stage_c)::value * STAGE_BYTES;
     bf16x8 kf[2][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(base + koff[0][u]);
+    for (int u = 0; u < 4; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(kbase + koff[u]);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int cur = kb & 1;
       if (kb + 1 < 4) {
+        const int kb_off = (tile_key(kb + 1, 0) - tile_key(0, 0)) * 256;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          kf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(base + koff[kb + 1][u]);
+          kf[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(kbase + koff[u] + kb_off);
       }
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
@@ -294,12 +316,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
         s[rb][kb] = x;
       }
     }
-    // V fragments of the first PV step, read during the softmax arithmetic
-    bf16x8 vf0[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) vf0[db] = *reinterpret_cast<const bf16x8*>(base + voff[0][db]);
-
-    bf16x8 pu[RBW][2];
+  };
+  // softmax of tile t: row maxima, lazy rescale, P = 2^(s c - m), row sums,
+  // P^T operands in bf16
+  auto softmax = [&](int t, auto masked_c) __attribute__((always_inline)) {
+    constexpr bool masked = decltype(masked_c)::value;
+    const int j0 = t * TK;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       if constexpr (masked) {
@@ -351,32 +373,74 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
           pu[rb][st][4 + e] = (__bf16)s[rb][2 * st + 1][e];
         }
     }
-
-    // O^T += V^T . P^T (step 1's V fragments are read during step 0)
-    bf16x8 vf1[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      vf1[db] = *reinterpret_cast<const bf16x8*>(base + voff[1][db]);
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf0[db], pu[rb][0], acc[rb][db]);
-    }
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = OP::mma(vf1[db], pu[rb][1], acc[rb][db]);
   };
-  // tiles below n_full have no key past any row here: no causal mask
+
+  // one tile step; stage_c = t % 2 (known at compile time in the unrolled
+  // loop over open tiles, at run time on the few diagonal tiles): K(t) and
+  // Vt(t) live in stage t % 2, Vt(t - 1) in the other one
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using SR = std::integral_constant<int, -1>;
+  // a wave's share of the loads issued right after barrier t
+  auto loads = [&](int t, int st) __attribute__((always_inline)) {
+    if (t + 1 < n_tiles) issue_k(t + 1, st ^ 1);
+    issue_v(t, st);
+  };
+  auto step = [&](int t, auto stage_c, auto masked_c, auto first_c) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
+    const int ST = SC >= 0 ? SC : (t & 1);
+    if (lead) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();                                  // barrier t
+      loads(t, ST);
+    } else if (decltype(first_c)::value) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();                                  // barrier 0
+      loads(0, 0);
+    }
+    if constexpr (!decltype(first_c)::value) {
+      if constexpr (SC >= 0) pv(std::integral_constant<int, SC ^ 1>{});   // tile t - 1
+      else if (ST) pv(S0{});
+      else pv(S1{});
+    }
+    if constexpr (SC >= 0) qk(stage_c);
+    else if (ST) qk(S1{});
+    else qk(S0{});
+    if (!lead) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();                                  // barrier t + 1
+      if (t + 1 < n_tiles) loads(t + 1, ST ^ 1);
+    }
+    softmax(t, masked_c);
+  };
   using Open = std::false_type;
   using Diag = std::true_type;
-  int t = 0;
-  for (; t + 1 < n_full; t += 2) {
-    step(t, S0{}, Open{});
-    step(t + 1, S1{}, Open{});
+  using First = std::true_type;
+  using Later = std::false_type;
+  // tiles below n_full have no key past any row here: no causal mask
+  if (n_tiles > 0) {
+    issue_k(0, 0);
+    if (n_full > 0) step(0, S0{}, Open{}, First{});
+    else step(0, S0{}, Diag{}, First{});
   }
-  if (t < n_full) step(t++, S0{}, Open{});
-  for (; t < n_tiles; ++t) step(t, std::integral_constant<int, -1>{}, Diag{});
+  int t = 1;
+  if (t < n_full && (t & 1)) step(t++, S1{}, Open{}, Later{});
+  for (; t + 1 < n_full; t += 2) {
+    step(t, S0{}, Open{}, Later{});
+    step(t + 1, S1{}, Open{}, Later{});
+  }
+  if (t < n_full) step(t++, S0{}, Open{}, Later{});
+  for (; t < n_tiles; ++t) step(t, SR{}, Diag{}, Later{});
+  // the last tile's PV product, after barrier n_tiles (the leading group's
+  // here, the other group's in its last step)
+  if (n_tiles > 0) {
+    if (lead) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();
+    }
+    if ((n_tiles - 1) & 1) pv(S1{});
+    else pv(S0{});
+  }
 
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
