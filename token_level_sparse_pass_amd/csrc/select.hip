@@ -11,7 +11,8 @@
 // so the bits order like the values): three histogram passes (12 + 12 + 8
 // bits) fix the k-th largest key tau, one pass collects every key > tau and
 // the lowest-index keys == tau, and a bitonic sort in LDS puts the chosen
-// indices in ascending order. One 1024-thread work-group per query row.
+// indices in ascending order. One work-group (512 or 1024 threads, see
+// token_threads) per query row.
 // Long rows first take a fast path that reads the row once: a threshold
 // from 8192 sampled keys (2048 runs of 4, aimed at about 3k keys above
 // the threshold), one pass
@@ -23,7 +24,7 @@
 
 namespace hs2 {
 
-constexpr int SEL_THREADS = 1024;
+constexpr int SEL_THREADS = 1024;   // block mode, and the default of the shared helpers
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int LIST_CAP = 4096;       // top_k limit
 constexpr int EQ_CAP = 2048;         // keys equal to the threshold sorted in LDS
@@ -38,7 +39,8 @@ struct SelArgs {
   int block_size, top_blocks;
 };
 
-// Inclusive prefix sum over the 1024 threads of the block.
+// Inclusive prefix sum over the NT threads of the block.
+template <int NT = SEL_THREADS>
 __device__ __forceinline__ int block_inclusive_scan(int v, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -64,15 +66,16 @@ __device__ __forceinline__ void write_window_and_pad(int32_t* out, int n_sel, in
 
 // Find the digit holding the `need`-th largest key among hist[0..nbins) and
 // return (digit, how many of the needed keys are still inside that digit).
+template <int NT = SEL_THREADS>
 __device__ void find_digit(const int* hist, int nbins, int need, int* wsum, int* res) {
-  const int per = nbins / SEL_THREADS > 0 ? nbins / SEL_THREADS : 1;
+  const int per = nbins / NT > 0 ? nbins / NT : 1;
   const int t = threadIdx.x;
-  const int rt = SEL_THREADS - 1 - t;                 // thread rt owns the high bins
+  const int rt = NT - 1 - t;                          // thread rt owns the high bins
   int v = 0;
   const int lo = rt * per;
   if (lo < nbins)
     for (int x = 0; x < per; ++x) v += hist[lo + x];
-  const int incl = block_inclusive_scan(v, wsum);     // bins above and including mine
+  const int incl = block_inclusive_scan<NT>(v, wsum); // bins above and including mine
   const int above = incl - v;
   if (lo < nbins && above < need && need <= incl) {
     int acc = above;
@@ -89,10 +92,11 @@ __device__ void find_digit(const int* hist, int nbins, int need, int* wsum, int*
   __syncthreads();
 }
 
+template <int NT = SEL_THREADS>
 __device__ void bitonic_sort(int* arr, int n_pow2) {
   for (int k = 2; k <= n_pow2; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n_pow2; i += SEL_THREADS) {
+      for (int i = threadIdx.x; i < n_pow2; i += NT) {
         const int ixj = i ^ j;
         if (ixj > i) {
           const bool asc = (i & k) == 0;
@@ -109,6 +113,7 @@ __device__ void bitonic_sort(int* arr, int n_pow2) {
 
 // Keys of a full score row (index = position) ...
 struct RowSrc {
+  static constexpr bool kRow = true;
   const uint32_t* row;
   int n;
   __device__ __forceinline__ uint32_t key(int j) const { return row[j]; }
@@ -116,6 +121,7 @@ struct RowSrc {
 };
 // ... or of the candidates gathered into LDS (index stored beside the key).
 struct CandSrc {
+  static constexpr bool kRow = false;
   const uint32_t* keys;
   const int* idx;
   int n;
@@ -126,7 +132,7 @@ struct CandSrc {
 // Exact k-th largest key of src (12 + 12 + 8-bit radix passes with LDS
 // histograms). Returns tau, how many keys == tau must be taken, and how many
 // keys == tau exist.
-template <class S>
+template <int NT, class S>
 __device__ void radix_kth(const S& src, int k, int* hist, int* wsum, int* res, uint32_t* tau,
                           int* need_eq, int* n_eq_total) {
   uint32_t prefix = 0, pmask = 0;
@@ -135,56 +141,35 @@ __device__ void radix_kth(const S& src, int k, int* hist, int* wsum, int* res, u
   const int widths[3] = {12, 12, 8};
   for (int pass = 0; pass < 3; ++pass) {
     const int sh = shifts[pass], nbins = 1 << widths[pass];
-    for (int x = threadIdx.x; x < nbins; x += SEL_THREADS) hist[x] = 0;
+    for (int x = threadIdx.x; x < nbins; x += NT) hist[x] = 0;
     __syncthreads();
-    for (int j = threadIdx.x; j < src.n; j += SEL_THREADS) {
-      const uint32_t kk = src.key(j);
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & (nbins - 1)], 1);
-    }
-    __syncthreads();
-    find_digit(hist, nbins, need, wsum, res);
-    const int digit = res[0];
-    need = res[1];
-    if (pass == 2) *n_eq_total = hist[digit];
-    prefix |= (uint32_t)digit << sh;
-    pmask |= (uint32_t)(nbins - 1) << sh;
-    __syncthreads();
-  }
-  *tau = prefix;
-  *need_eq = need;
-}
-
-// Row specialisation of the histogram passes with 16-byte loads.
-template <>
-__device__ void radix_kth<RowSrc>(const RowSrc& src, int k, int* hist, int* wsum, int* res,
-                                  uint32_t* tau, int* need_eq, int* n_eq_total) {
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  const int n_c = src.n;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nbins = 1 << widths[pass];
-    for (int x = threadIdx.x; x < nbins; x += SEL_THREADS) hist[x] = 0;
-    __syncthreads();
-    constexpr int STRIDE = SEL_THREADS * 4;
-    for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
-      uint4 kv[4];
+    if constexpr (S::kRow) {
+      // whole score rows: batched 16-byte loads
+      constexpr int STRIDE = NT * 4;
+      const int n_c = src.n;
+      for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
+        uint4 kv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
+        for (int u = 0; u < 4; ++u)
+          kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = jb + u * STRIDE;
-        const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+        for (int u = 0; u < 4; ++u) {
+          const int j = jb + u * STRIDE;
+          const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (j + e < n_c && (ks[e] & pmask) == prefix)
-            atomicAdd(&hist[(ks[e] >> sh) & (nbins - 1)], 1);
+          for (int e = 0; e < 4; ++e)
+            if (j + e < n_c && (ks[e] & pmask) == prefix)
+              atomicAdd(&hist[(ks[e] >> sh) & (nbins - 1)], 1);
+        }
+      }
+    } else {
+      for (int j = threadIdx.x; j < src.n; j += NT) {
+        const uint32_t kk = src.key(j);
+        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & (nbins - 1)], 1);
       }
     }
     __syncthreads();
-    find_digit(hist, nbins, need, wsum, res);
+    find_digit<NT>(hist, nbins, need, wsum, res);
     const int digit = res[0];
     need = res[1];
     if (pass == 2) *n_eq_total = hist[digit];
@@ -197,43 +182,38 @@ __device__ void radix_kth<RowSrc>(const RowSrc& src, int k, int* hist, int* wsum
 }
 
 // Every key > tau into list, every key == tau into eqlist (when they fit).
-template <class S>
+// Whole score rows are read with batched 16-byte loads (rows are padded to
+// a multiple of 256 floats, so a clamped quad never leaves the row).
+template <int NT, class S>
 __device__ void collect_above(const S& src, uint32_t tau, bool eq_fits, int* list, int* eqlist,
                               int* counters) {
   if (threadIdx.x < 2) counters[threadIdx.x] = 0;
   __syncthreads();
-  for (int j = threadIdx.x; j < src.n; j += SEL_THREADS) {
-    const uint32_t kk = src.key(j);
-    if (kk > tau) list[atomicAdd(&counters[0], 1)] = src.index(j);
-    else if (kk == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = src.index(j);
-  }
-  __syncthreads();
-}
-
-// Row specialisation: batched 16-byte loads (rows are padded to a multiple
-// of 256 floats, so a clamped quad never leaves the row's allocation).
-template <>
-__device__ void collect_above<RowSrc>(const RowSrc& src, uint32_t tau, bool eq_fits, int* list,
-                                      int* eqlist, int* counters) {
-  if (threadIdx.x < 2) counters[threadIdx.x] = 0;
-  __syncthreads();
-  const int n_c = src.n;
-  constexpr int STRIDE = SEL_THREADS * 4;
-  for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
-    uint4 kv[4];
+  if constexpr (S::kRow) {
+    const int n_c = src.n;
+    constexpr int STRIDE = NT * 4;
+    for (int jb = threadIdx.x * 4; jb < n_c; jb += 4 * STRIDE) {
+      uint4 kv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
+      for (int u = 0; u < 4; ++u)
+        kv[u] = *reinterpret_cast<const uint4*>(src.row + min(jb + u * STRIDE, (n_c - 1) & ~3));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = jb + u * STRIDE;
-      const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + u * STRIDE;
+        const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (j + e >= n_c) continue;
-        if (ks[e] > tau) list[atomicAdd(&counters[0], 1)] = j + e;
-        else if (ks[e] == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = j + e;
+        for (int e = 0; e < 4; ++e) {
+          if (j + e >= n_c) continue;
+          if (ks[e] > tau) list[atomicAdd(&counters[0], 1)] = j + e;
+          else if (ks[e] == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = j + e;
+        }
       }
+    }
+  } else {
+    for (int j = threadIdx.x; j < src.n; j += NT) {
+      const uint32_t kk = src.key(j);
+      if (kk > tau) list[atomicAdd(&counters[0], 1)] = src.index(j);
+      else if (kk == tau && eq_fits) eqlist[atomicAdd(&counters[1], 1)] = src.index(j);
     }
   }
   __syncthreads();
@@ -241,37 +221,40 @@ __device__ void collect_above<RowSrc>(const RowSrc& src, uint32_t tau, bool eq_f
 
 // Sort the tie list, append its need_eq lowest indices, sort the whole
 // selection ascending and write it, followed by the window.
+template <int NT>
 __device__ void finish_selection(int* list, int* eqlist, int n_gt, int need_eq, int n_eq_total,
                                  bool eq_sorted_needed, int top_k, int32_t* out, int p,
                                  int window, int width) {
   if (eq_sorted_needed) {
     int n2 = 1;
     while (n2 < n_eq_total) n2 <<= 1;
-    for (int x = n_eq_total + threadIdx.x; x < n2; x += SEL_THREADS) eqlist[x] = 0x7FFFFFFF;
+    for (int x = n_eq_total + threadIdx.x; x < n2; x += NT) eqlist[x] = 0x7FFFFFFF;
     __syncthreads();
-    if (n_eq_total > 1) bitonic_sort(eqlist, n2);
-    for (int x = threadIdx.x; x < need_eq; x += SEL_THREADS) list[n_gt + x] = eqlist[x];
+    if (n_eq_total > 1) bitonic_sort<NT>(eqlist, n2);
+    for (int x = threadIdx.x; x < need_eq; x += NT) list[n_gt + x] = eqlist[x];
   }
   __syncthreads();
   int n2 = 1;
   while (n2 < top_k) n2 <<= 1;
-  for (int x = top_k + threadIdx.x; x < n2; x += SEL_THREADS) list[x] = 0x7FFFFFFF;
+  for (int x = top_k + threadIdx.x; x < n2; x += NT) list[x] = 0x7FFFFFFF;
   __syncthreads();
-  bitonic_sort(list, n2);
-  for (int t = threadIdx.x; t < top_k; t += SEL_THREADS) out[t] = list[t];
+  bitonic_sort<NT>(list, n2);
+  for (int t = threadIdx.x; t < top_k; t += NT) out[t] = list[t];
   write_window_and_pad(out, top_k, p, window, width);
 }
 
 constexpr int NSAMP = 8192;      // sampled keys per row (fast path)
 constexpr int CAND_CAP = 4096;   // candidates gathered into LDS (fast path)
 
-__global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
+template <int NT>
+__global__ __launch_bounds__(NT, 2048 / NT) void select_token_kernel(SelArgs a) {
+  constexpr int NW = NT / 64;
   __shared__ int hist[4096];
   __shared__ int list[LIST_CAP];
   __shared__ int eqlist[EQ_CAP];
   __shared__ uint32_t ckey[CAND_CAP];
   __shared__ int cidx[CAND_CAP];
-  __shared__ int wsum[SEL_WAVES];
+  __shared__ int wsum[NW];
   __shared__ int res[2];
   __shared__ int counters[2];
 
@@ -285,7 +268,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
   const uint32_t* row = reinterpret_cast<const uint32_t*>(a.scores + (size_t)r * a.stride);
 
   if (n_c <= a.top_k) {
-    for (int t = threadIdx.x; t < n_c; t += SEL_THREADS) out[t] = t;
+    for (int t = threadIdx.x; t < n_c; t += NT) out[t] = t;
     write_window_and_pad(out, n_c, p, a.window, a.width);
     return;
   }
@@ -295,19 +278,29 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
   // Exact whenever at least top_k keys were gathered (then the top_k-th
   // largest key, and every key equal to it, is among them).
   if (n_c >= 4 * a.top_k && n_c >= 16384) {
-    for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+    for (int x = threadIdx.x; x < 4096; x += NT) hist[x] = 0;
     if (threadIdx.x == 0) counters[0] = 0;
     __syncthreads();
     // 8192 sampled keys: 2048 runs of 4 spread over the row (short runs keep
     // clustered structure from skewing the sample); two histogram levels
     // place the threshold at 24-bit precision
-    const int sj0 = (int)(((long long)(2 * threadIdx.x) * (n_c - 4)) / 2047) / 4 * 4;
-    const int sj1 = (int)(((long long)(2 * threadIdx.x + 1) * (n_c - 4)) / 2047) / 4 * 4;
-    const uint4 s0 = *reinterpret_cast<const uint4*>(row + sj0);
-    const uint4 s1 = *reinterpret_cast<const uint4*>(row + sj1);
-    const uint32_t sk[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    constexpr int RPT = 2048 / NT;                    // runs per thread
+    constexpr int SK = 4 * RPT;
+    uint32_t sk[SK];
+    // (re)read this thread's sampled keys: they are not kept in registers
+    // across the gather pass, a retry reads them again
+    auto load_sample = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
+      for (int q = 0; q < RPT; ++q) {
+        const int run = RPT * threadIdx.x + q;
+        const int sj = (int)(((long long)run * (n_c - 4)) / 2047) / 4 * 4;
+        const uint4 sv = *reinterpret_cast<const uint4*>(row + sj);
+        sk[4 * q] = sv.x; sk[4 * q + 1] = sv.y; sk[4 * q + 2] = sv.z; sk[4 * q + 3] = sv.w;
+      }
+    };
+    load_sample();
+#pragma unroll
+    for (int e = 0; e < SK; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
     __syncthreads();
     // up to two attempts: a gather that overflows retries with a higher
     // threshold, one that catches fewer than top_k keys with a lower one
@@ -317,27 +310,28 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
     if (attempt > 0) {
       if (n_cand > CAND_CAP) rank = max(1, rank * 3 / 5);
       else rank = min(NSAMP, rank * 2);
-      for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+      for (int x = threadIdx.x; x < 4096; x += NT) hist[x] = 0;
       if (threadIdx.x == 0) counters[0] = 0;
       __syncthreads();
+      load_sample();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
+      for (int e = 0; e < SK; ++e) atomicAdd(&hist[sk[e] >> 20], 1);
       __syncthreads();
     }
-    find_digit(hist, 4096, rank, wsum, res);
+    find_digit<NT>(hist, 4096, rank, wsum, res);
     const uint32_t top12 = (uint32_t)res[0];
     const int rank2 = res[1];
     __syncthreads();
-    for (int x = threadIdx.x; x < 4096; x += SEL_THREADS) hist[x] = 0;
+    for (int x = threadIdx.x; x < 4096; x += NT) hist[x] = 0;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < SK; ++e)
       if ((sk[e] >> 20) == top12) atomicAdd(&hist[(sk[e] >> 8) & 4095], 1);
     __syncthreads();
-    find_digit(hist, 4096, rank2, wsum, res);
+    find_digit<NT>(hist, 4096, rank2, wsum, res);
     const uint32_t v_s = (top12 << 20) | ((uint32_t)res[0] << 8);
     // eight 16-byte loads in flight per thread
-    constexpr int STRIDE = SEL_THREADS * 4;
+    constexpr int STRIDE = NT * 4;
     for (int jb = threadIdx.x * 4; jb < n_c; jb += 8 * STRIDE) {
       // branch-free loads so all eight stay in flight: a position past the
       // row is clamped to its last aligned quad and masked below (rows are
@@ -378,11 +372,11 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
       const CandSrc cs{ckey, cidx, n_cand};
       uint32_t tau;
       int need_eq, n_eq_total = 0;
-      radix_kth(cs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
+      radix_kth<NT>(cs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
       if (n_eq_total <= EQ_CAP) {
-        collect_above(cs, tau, true, list, eqlist, counters);
-        finish_selection(list, eqlist, a.top_k - need_eq, need_eq, n_eq_total, true, a.top_k,
-                         out, p, a.window, a.width);
+        collect_above<NT>(cs, tau, true, list, eqlist, counters);
+        finish_selection<NT>(list, eqlist, a.top_k - need_eq, need_eq, n_eq_total, true, a.top_k,
+                             out, p, a.window, a.width);
         return;
       }
     }
@@ -393,26 +387,26 @@ __global__ __launch_bounds__(SEL_THREADS) void select_token_kernel(SelArgs a) {
   const RowSrc rs{row, n_c};
   uint32_t tau;
   int need_eq, n_eq_total = 0;
-  radix_kth(rs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
+  radix_kth<NT>(rs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
   const int n_gt = a.top_k - need_eq;
   const bool eq_fits = n_eq_total <= EQ_CAP;
-  collect_above(rs, tau, eq_fits, list, eqlist, counters);
+  collect_above<NT>(rs, tau, eq_fits, list, eqlist, counters);
   if (!eq_fits) {
     // many exact ties: walk the row in index order and keep the first need_eq
     int taken = 0;
-    for (int base = 0; base < n_c && taken < need_eq; base += SEL_THREADS) {
+    for (int base = 0; base < n_c && taken < need_eq; base += NT) {
       const int j = base + threadIdx.x;
       const int f = (j < n_c && row[j] == tau) ? 1 : 0;
-      const int incl = block_inclusive_scan(f, wsum);
+      const int incl = block_inclusive_scan<NT>(f, wsum);
       if (f && taken + incl - 1 < need_eq) list[n_gt + taken + incl - 1] = j;
-      if (threadIdx.x == SEL_THREADS - 1) res[0] = incl;
+      if (threadIdx.x == NT - 1) res[0] = incl;
       __syncthreads();
       taken += res[0];
       __syncthreads();
     }
   }
-  finish_selection(list, eqlist, n_gt, need_eq, n_eq_total, eq_fits, a.top_k, out, p, a.window,
-                   a.width);
+  finish_selection<NT>(list, eqlist, n_gt, need_eq, n_eq_total, eq_fits, a.top_k, out, p,
+                       a.window, a.width);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,6 +499,18 @@ __global__ __launch_bounds__(SEL_THREADS) void select_block_kernel(SelArgs a) {
   write_window_and_pad(out, n_sel, p, a.window, a.width);
 }
 
+// Work-group size of a token-select launch. Two 512-thread work-groups fit
+// a CU (one 1024-thread one does), so one row's serial steps (threshold,
+// radix passes over the gathered keys, sorts) overlap another row's read;
+// that measured faster for launches of many rows of moderate length (32K
+// prefill 3.5 -> 2.3 ms, 8K chunk on 262K 2.5 -> 2.2 ms). Rows of a million
+// candidates (24.4 vs 21.3 ms) and launches of few rows (decode) keep 1024
+// threads per row.
+int token_threads(const SelectPlan& p) {
+  const long long longest = (long long)p.n_kv - p.window;
+  return (p.rows >= 512 && longest < (1 << 19)) ? 512 : 1024;
+}
+
 hipError_t launch_select(const SelectPlan& p, hipStream_t st) {
   if (p.rows <= 0) return hipSuccess;
   SelArgs a;
@@ -514,8 +520,10 @@ hipError_t launch_select(const SelectPlan& p, hipStream_t st) {
   a.block_size = p.block_size; a.top_blocks = p.top_blocks;
   if (p.block_mode)
     hipLaunchKernelGGL(select_block_kernel, dim3(p.rows), dim3(SEL_THREADS), 0, st, a);
+  else if (token_threads(p) == 512)
+    hipLaunchKernelGGL(select_token_kernel<512>, dim3(p.rows), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL(select_token_kernel, dim3(p.rows), dim3(SEL_THREADS), 0, st, a);
+    hipLaunchKernelGGL(select_token_kernel<1024>, dim3(p.rows), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 
