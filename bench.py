@@ -151,6 +151,65 @@ def _pass_of(kernel):
     return None
 
 
+def trace_summary(trace_dir, cid):
+    """Summarise a `rocprofv3 --kernel-trace --stats` run of `bench.py
+    --config cid --steps 3 --warmup 1 --no-cpu-baseline` (host only) into
+    profiles/block_step_<workload>.md: the per-kernel statistics and the
+    bench line the same run printed (run.log beside the trace)."""
+    import csv
+    import glob
+    from synth import CONFIGS
+    w = CONFIGS[cid]
+    stats = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
+    dbs = sorted(glob.glob(os.path.join(trace_dir, "**", "*results.db"), recursive=True))
+    if stats:
+        with open(stats[0]) as f:
+            rows = list(csv.DictReader(f))
+    elif dbs:
+        # rocprofv3's database output: its top_kernels view holds the same
+        # statistics (durations in microseconds there)
+        import sqlite3
+        con = sqlite3.connect(dbs[0])
+        rows = [{"Name": n, "Calls": c, "TotalDurationNs": t * 1e3, "AverageNs": a * 1e3,
+                 "Percentage": pc}
+                for n, c, t, a, pc in con.execute(
+                    "select name, total_calls, total_duration, average, percentage "
+                    "from top_kernels order by total_duration desc")]
+        con.close()
+    else:
+        raise SystemExit(f"no kernel statistics under {trace_dir}")
+    bench_line = None
+    log_path = trace_dir.rstrip("/") + ".log"
+    if os.path.exists(log_path):
+        for line in open(log_path):
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    lines = [f"# Kernel trace: Hybrid Block step, {w.name}", "",
+             "Command (from /tmp, with R = the repository root, on one MI355X; summarised by "
+             "`python bench.py --trace-summary DIR --config N`):", "", "```",
+             f"rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/trace_c{cid} -o run -- "
+             f"python3 $R/bench.py --config {cid} --steps 3 --warmup 1 --no-cpu-baseline", "```", "",
+             "Kernel trace statistics (durations in microseconds; the bench runs 1 warm-up and "
+             "3 timed steps, so each launch slot of a step is counted 4 times):", "",
+             "| kernel | calls | total (us) | average (us) | % of GPU time |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        calls = int(float(r.get("Calls", 0)))
+        tot = float(r.get("TotalDurationNs", 0)) / 1e3
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        lines.append(f"| `{name.split('(')[0][:90]}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.2f} |")
+    if bench_line:
+        ps = bench_line.get("passes", {})
+        lines += ["", "The same run's bench line (HIP events on the library's stream): "
+                  f"{bench_line['ms_per_step']:.3f} ms per step, {bench_line['value']:.1f} tokens/s; "
+                  "per pass: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in ps.items()) + "."]
+    out = os.path.join(ROOT, "profiles", f"block_step_{w.name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def counters_summary(pmc_dir, steps_profiled=2):
     """Summarise rocprofv3 --pmc runs into profiles/traffic.json,
     profiles/mfma.json and one markdown file per workload (host only).
@@ -802,6 +861,9 @@ def main():
     ap.add_argument("--page-size", type=int, default=0,
                     help="with --decode-loop: keep the cache in a pool of pages of this many "
                          "rows, handed out in shuffled order (hs2_decode_step_paged)")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="host only: summarise a rocprofv3 --kernel-trace --stats run of "
+                         "--config N under DIR into profiles/ and exit")
     ap.add_argument("--counters-summary", metavar="DIR", default=None,
                     help="host only: summarise rocprofv3 --pmc runs under DIR into profiles/ "
                          "and exit")
@@ -816,6 +878,9 @@ def main():
 
     if args.counters_summary:
         counters_summary(args.counters_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.config)
         return
     import torch
     if args.copy_calibration > 0:
