@@ -40,6 +40,19 @@ def algorithmic_work(w):
     cand = sum(max(0, p - w.window + 1) for p in pos) * B       # candidate pairs
     sel = sum(min(p + 1, w.top_k + w.window) for p in pos) * B  # selected keys
     L = w.n_sparse
+    # selection reads each candidate score once, except on rows of more than
+    # 128 * top_k candidates with the bf16 score pass: those read the row's
+    # 64-key segment maxima and then top_k whole segments (the keys at or
+    # above the top_k-th largest maximum lie in at least that many)
+    seg = nq > 1 and w.dtype == "bf16" and d == 128
+    sel_read = 0.0
+    for p in pos:
+        n_c = max(0, p - w.window + 1)
+        if seg and n_c >= 128 * w.top_k:
+            sel_read += 4.0 * ((n_c + 63) // 64) + 256.0 * w.top_k
+        else:
+            sel_read += 4.0 * n_c
+    sel_read *= B
     if nq == 1:
         # decode: one query per sequence, so pass 1 streams K and V once
         # (8 flop/B) and the score pass reads the stored logits
@@ -51,7 +64,7 @@ def algorithmic_work(w):
     return {
         "full_attention": full,
         "score": score,
-        "select": ("hbm", 4.0 * cand + 4.0 * B * nq * (w.top_k + w.window)),
+        "select": ("hbm", sel_read + 4.0 * B * nq * (w.top_k + w.window)),
         "sparse_attention": ("hbm", sel * hkv * d * 2.0 * esz + 2.0 * L * B * nq * hq * d * esz),
         # V read once, written once in key-tile-major transposed order
         "v_layout": ("hbm", 2.0 * B * nkv * hkv * d * esz),

@@ -198,6 +198,75 @@ def test_exact_ties_long_rows(gpu_lib, nq, B):
             assert list(row) == list(range(top_k)) + list(range(p - w + 1, p + 1)), (b, i)
 
 
+def exact_rule_on_own_scores(gi_rows, scores, pos, top_k, window):
+    """Each GPU index row must be exactly the (-S, j) top-k (plus the window)
+    of the GPU's own exported fp32 score row: the selection rule itself,
+    ties included, independent of score precision."""
+    for r, p in enumerate(pos):
+        want = O.select_token(scores[r].cpu().numpy(), int(p), top_k, window)
+        got = gi_rows[r][gi_rows[r] >= 0]
+        assert np.array_equal(got, want), f"row {r} (p={p})"
+
+
+# Rows of more than 128 * top_k candidates select through the row's 64-key
+# segment maxima written by the score pass (the top_k-th largest maximum
+# bounds tau from below; only keys at or above it are gathered).
+SEG_N_KV = 140000
+
+
+def dense_block_keys(q_full, k, start, n_keys, alpha=30.0, noise=0.3, seed=7):
+    """k with keys [start, start + n_keys) pointing along the sum of each KV
+    group's query vectors (scaled by alpha, plus noise): every query row then
+    puts nearly all of its probability on that run of keys."""
+    B, nq, hq, d = q_full.shape
+    hkv = k.shape[2]
+    G = hq // hkv
+    qs = q_full[0].float().sum(0).reshape(hkv, G, d).sum(1)          # [hkv, d]
+    u = qs / qs.norm(dim=-1, keepdim=True)
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    eps = torch.randn((n_keys, hkv, d), generator=gen).to(k.device)
+    k = k.clone()
+    k[0, start:start + n_keys] = (alpha * u[None] + noise * eps).to(k.dtype)
+    return k
+
+
+@pytest.mark.parametrize("pattern", ["repeat", "dense", "ties"])
+def test_segment_path_selection(gpu_lib, pattern):
+    # repeat: key rows recur with period 3000, so each score value recurs
+    #   about 47 times (tau has many exact ties) and the segment path takes
+    #   them by index;
+    # dense: 120 consecutive segments of strong keys, so the keys at or above
+    #   the segment bound overflow the gathered set and the row falls back to
+    #   the sampled and full passes;
+    # ties: every score equal (K = 0), through every fallback.
+    nq, top_k, w = 3, 1024, 128
+    case = small("seg_" + pattern, "bf16", 1, nq, SEG_N_KV, 8, 2, 128, top_k, w)
+    inp = make_inputs(case, device="cuda")
+    k = inp["k"]
+    if pattern == "repeat":
+        reps = (SEG_N_KV + 2999) // 3000
+        k = k[:, :3000].repeat(1, reps, 1, 1)[:, :SEG_N_KV].contiguous()
+    elif pattern == "dense":
+        k = dense_block_keys(inp["q_full"], k, 50000, 120 * 64)
+    else:
+        k = torch.zeros_like(k)
+    rows = list(range(nq))
+    o, idx, lse, scores = gpu_lib.full_attn_select(inp["q_full"], k, inp["v"], top_k=top_k,
+                                                   window=w, debug_rows=rows)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    pos = np.arange(nq) + SEG_N_KV - nq
+    exact_rule_on_own_scores(gi, scores, pos, top_k, w)
+    if pattern == "dense":
+        assert all(((gi[r][:top_k] >= 50000) & (gi[r][:top_k] < 50000 + 120 * 64)).all()
+                   for r in rows)
+    q, kh, v = host(inp["q_full"]), host(k), host(inp["v"])
+    ref = O.block_forward(q, np.zeros((0,) + q.shape, dtype=q.dtype), kh, v, top_k=top_k,
+                          window=w)
+    tied = compare_index_rows(gi, ref["S"][0], pos, ref["idx"][0], ref["tau"][0], w)
+    say(pattern, "near-tie rows", len(tied))
+
+
 @pytest.mark.parametrize("case", [
     small("blk_bf16", "bf16", 1, 300, 2000, 8, 2, 128, 0, 16),
     small("blk_fp32_unit", "fp32", 1, 120, 400, 4, 1, 64, 0, 8),

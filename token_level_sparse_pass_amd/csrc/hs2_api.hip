@@ -121,6 +121,7 @@ struct Layout {
   size_t logits_stride = 0;  // floats per logits row (decode)
   size_t lens = 0;           // [B] int32 keys per sequence (decode step)
   size_t stride = 0;         // floats per score row
+  size_t seg_off = 0;        // prefill: float offset of the segment maxima in a row, 0 = none
   int chunk_rows = 0;        // prefill query rows per chunk
   int n_split = 0, kps = 0;  // decode split
   size_t total = 0;
@@ -158,6 +159,11 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
       off += align_up((size_t)p.batch * p.h_kv * p.head_dim * l.vt_keys * 2);
     }
     l.scores = off;
+    if (hs2::score_uses_bf16_kernel(shape_of(p)) && l.stride >= 256) {
+      // each row carries the maxima of its 64-key segments after the scores
+      l.seg_off = l.stride;
+      l.stride += l.stride / 64;
+    }
     const size_t row_b = std::max<size_t>(l.stride, 1) * sizeof(float);
     const size_t mn = off + align_up(row_b);
     size_t pref_rows = std::max<size_t>(128, CHUNK_TARGET / row_b / 128 * 128);
@@ -344,6 +350,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
       hs2::ScorePlan sc;
       sc.s = s; sc.b = b; sc.q0 = q0; sc.rows = rows; sc.window = p.window;
       sc.q = q; sc.k = k; sc.stats = stats; sc.scores = scores; sc.score_stride = L.stride;
+      sc.seg_off = L.seg_off;
       {
         PassTimer t(st, HS2_PASS_SCORE);
         HIP_TRY(hs2::launch_score_prefill(sc, st), "score");
@@ -354,7 +361,7 @@ hs2_status run_full(const hs2_problem& p, const void* q, const void* k, const vo
       sp.rows = rows; sp.flat0 = flat0; sp.n_q = p.n_q; sp.n_kv = p.n_kv;
       sp.top_k = p.top_k; sp.window = p.window; sp.width = width;
       sp.block_mode = block_mode; sp.block_size = p.block_size; sp.top_blocks = p.top_blocks;
-      sp.scores = scores; sp.score_stride = L.stride; sp.idx = idx;
+      sp.scores = scores; sp.score_stride = L.stride; sp.seg_off = L.seg_off; sp.idx = idx;
       {
         PassTimer t(st, HS2_PASS_SELECT);
         HIP_TRY(hs2::launch_select(sp, st), "select");

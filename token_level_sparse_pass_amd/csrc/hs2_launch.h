@@ -149,8 +149,15 @@ struct ScorePlan {
   const void* q; const void* k;
   const float* stats;
   float* scores; size_t score_stride;   // floats between rows
+  // When nonzero, the row also holds, from float seg_off on, the maximum of
+  // S over the candidate keys of each 64-key segment (segment s covers keys
+  // [64 s, 64 s + 63]); written by the bf16 head-dim-128 kernel only.
+  size_t seg_off = 0;
 };
 hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st);
+// True when launch_score_prefill uses the bf16 head-dim-128 kernel (the one
+// that writes segment maxima).
+bool score_uses_bf16_kernel(const Shape& s);
 
 // Selection for `rows` score rows: row r is flattened query flat0 + r
 // (flattened query = b * n_q + i).
@@ -159,6 +166,7 @@ struct SelectPlan {
   int top_k, window, width;
   bool block_mode; int block_size, top_blocks;
   const float* scores; size_t score_stride;
+  size_t seg_off = 0;                 // segment maxima after each row (see ScorePlan), 0 = none
   int32_t* idx;                       // [batch, n_q, width]
   const int32_t* seq_len = nullptr;   // decode rows (n_q == 1): keys per sequence
 };

@@ -52,6 +52,7 @@ struct Score2Args {
   int n_qt, n_kt;
   int swizzle;          // 0: ids in launch order (launches that are mostly causal triangle)
   float c;
+  size_t seg_off;       // segment maxima offset within a row, 0 = do not write them
 };
 
 }  // namespace
@@ -225,6 +226,25 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<f32x4*>(out + kb * 16) = sacc[qb][kb];
   }
+  // the wave's 64 keys are one segment: per query, the maximum of its
+  // candidate keys there (the row's lanes l16 + 16 grp hold 16 keys each)
+  if (a.seg_off) {
+    const int s0 = kj0 + wk * 64;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int r = r_lo + srow0 + qb * 16;
+      const int lim = q_off + a.q0 + r - a.window;    // last candidate key of row r
+      float m = -1.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s0 + kb * 16 + 4 * grp + e <= lim) m = max2f(m, sacc[qb][kb][e]);
+      m = row_group_max(m);
+      if (grp == 0 && r < a.rows && s0 <= lim)
+        a.scores[(size_t)r * a.stride + a.seg_off + (s0 >> 6)] = m;
+    }
+  }
 }
 
 bool score_uses_bf16_kernel(const Shape& s) { return s.bf16 && s.head_dim == D; }
@@ -239,6 +259,7 @@ hipError_t launch_score_prefill(const ScorePlan& p, hipStream_t st) {
   a.stats = p.stats; a.scores = p.scores; a.stride = p.score_stride;
   a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.b = p.b; a.q0 = p.q0; a.rows = p.rows; a.window = p.window; a.c = p.s.scale_log2;
+  a.seg_off = p.seg_off;
   const int q_off = a.n_kv - a.n_q;
   const int n_cand_max = q_off + p.q0 + p.rows - p.window;
   if (n_cand_max <= 0) return hipSuccess;

@@ -37,6 +37,7 @@ struct SelArgs {
   int flat0, n_q, n_kv, top_k, window, width;
   const int32_t* seq_len;            // keys per sequence (decode rows), or NULL
   int block_size, top_blocks;
+  size_t seg_off;                    // 64-key segment maxima after each row, 0 = none
 };
 
 // Inclusive prefix sum over the NT threads of the block.
@@ -273,6 +274,96 @@ __global__ __launch_bounds__(NT, 2048 / NT) void select_token_kernel(SelArgs a) 
     return;
   }
 
+  // ---- segment path: the row's 64-key segment maxima bound tau from below.
+  // T = the top_k-th largest maximum: the top_k segments reaching it hold a
+  // key >= T each, so tau >= T, and every key >= tau (ties included) lies in
+  // a segment whose maximum is >= T. Gather the keys >= T of those segments
+  // into LDS and select exactly there; only about top_k segments of the row
+  // are read. Falls through when the segment list or the gathered keys do
+  // not fit.
+  if (a.seg_off && n_c >= 128 * a.top_k) {
+    const int n_seg = (n_c + 63) >> 6;
+    const uint32_t* srow = row + a.seg_off;
+    uint32_t T;
+    {
+      int need_s, n_eq_s = 0;
+      const RowSrc ms{srow, n_seg};
+      radix_kth<NT>(ms, a.top_k, hist, wsum, res, &T, &need_s, &n_eq_s);
+    }
+    if (threadIdx.x == 0) counters[0] = 0;
+    __syncthreads();
+    // list[] <- ids of the segments whose maximum is >= T (in no set order)
+    for (int sb = 0; sb < n_seg; sb += NT) {
+      const int sg = sb + threadIdx.x;
+      const bool f = sg < n_seg && srow[sg] >= T;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+      if (m) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&counters[0], __popcll(m));
+        base = __shfl(base, 0, 64);
+        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (f && pos < LIST_CAP) list[pos] = sg;
+      }
+    }
+    __syncthreads();
+    const int n_list = counters[0];
+    __syncthreads();
+    if (n_list <= LIST_CAP) {
+      if (threadIdx.x == 0) counters[0] = 0;
+      __syncthreads();
+      // 16 lanes per segment (one 16-byte quad each), four segments per
+      // wave and four waves' worth of loads in flight per lane
+      const int wave = threadIdx.x >> 6;
+      constexpr int U = 4;
+      for (int sb = wave * 4; sb < n_list; sb += NW * 4 * U) {
+        uint4 kv[U];
+        int j0[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int t = sb + u * NW * 4 + (lane >> 4);
+          const int sg = list[min(t, n_list - 1)];
+          j0[u] = t < n_list ? sg * 64 + (lane & 15) * 4 : n_c;
+          kv[u] = *reinterpret_cast<const uint4*>(row + sg * 64 + (lane & 15) * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool f = (j0[u] + e < n_c) && ks[e] >= T;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+            if (m) {
+              int base = 0;
+              if (lane == 0) base = atomicAdd(&counters[0], __popcll(m));
+              base = __shfl(base, 0, 64);
+              const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+              if (f && pos < CAND_CAP) {
+                ckey[pos] = ks[e];
+                cidx[pos] = j0[u] + e;
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int n_cand = counters[0];
+      __syncthreads();
+      if (n_cand <= CAND_CAP) {
+        const CandSrc cs{ckey, cidx, n_cand};
+        uint32_t tau;
+        int need_eq, n_eq_total = 0;
+        radix_kth<NT>(cs, a.top_k, hist, wsum, res, &tau, &need_eq, &n_eq_total);
+        if (n_eq_total <= EQ_CAP) {
+          collect_above<NT>(cs, tau, true, list, eqlist, counters);
+          finish_selection<NT>(list, eqlist, a.top_k - need_eq, need_eq, n_eq_total, true,
+                               a.top_k, out, p, a.window, a.width);
+          return;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
   // ---- fast path: a conservative threshold from a strided sample, one pass
   // that gathers every key at or above it into LDS, exact selection there.
   // Exact whenever at least top_k keys were gathered (then the top_k-th
@@ -440,7 +531,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_block_kernel(SelArgs a) {
     return;
   }
 
-  // block maxima (as order-preserving keys + 1, so 0 can mean "taken")
+  // block maxima (as order-preserving keys + 1, so 0 can mean "taken"); for
+  // 64-token blocks the score pass already wrote them after the row
+  if (a.seg_off && bs == 64) {
+    const uint32_t* srow = row + a.seg_off;
+    for (int beta = threadIdx.x; beta < n_blocks; beta += SEL_THREADS) bkey[beta] = srow[beta] + 1u;
+  } else
   for (int beta = wave; beta < n_blocks; beta += SEL_WAVES) {
     const int lo = beta * bs, hi = min(n_c, lo + bs);
     uint32_t m = 0;
@@ -518,6 +614,7 @@ hipError_t launch_select(const SelectPlan& p, hipStream_t st) {
   a.flat0 = p.flat0; a.n_q = p.n_q; a.n_kv = p.n_kv; a.seq_len = p.seq_len;
   a.top_k = p.top_k; a.window = p.window; a.width = p.width;
   a.block_size = p.block_size; a.top_blocks = p.top_blocks;
+  a.seg_off = p.seg_off;
   if (p.block_mode)
     hipLaunchKernelGGL(select_block_kernel, dim3(p.rows), dim3(SEL_THREADS), 0, st, a);
   else if (token_threads(p) == 512)
