@@ -132,12 +132,11 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
   Frag<__bf16, D> qf;
   if (row_ok) load_slice<__bf16, D>(qf, a.q + ((size_t)b * a.h_q + g * G + hh) * D, lane);
   else zero_slice<__bf16, D>(qf);
-  // logits of this (sequence, KV head): [key][G], one 32-key tile = 32 * G
-  // floats, staged in the K half of the tile's own ring stage (free once the
-  // logits are computed) and stored as whole 16-byte chunks
-  float* lgt = a.logits + ((size_t)b * a.h_kv + g) * a.lstride * G;
-  const int n_vec = 8 * G;                      // 16-byte chunks per tile
-  const int spt = (n_vec + 63) / 64;            // store instructions per tile
+  // raw logits of this lane's query head: one row of lstride floats per
+  // (sequence, head); lane (grp, hh) holds keys 4 grp .. 4 grp + 3 of each
+  // 16-key block, so a tile leaves as two 16-byte stores per lane
+  float* lgt = a.logits + ((size_t)b * a.h_q + g * G + min(l16, G - 1)) * a.lstride;
+  constexpr int SPT = 2;                        // store instructions per tile
 
   float m_run = -1e30f, l_run = 0.f;
   f32x4 acc[8];
@@ -151,8 +150,8 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
   for (int t = 0; t < n_tiles; ++t) {
     // tile t has landed once at most the later tiles' loads (issued after
     // it) and the logit stores of the tiles since are in flight
-    static_assert(LPT * (NS - 2) + 2 * (NS - 1) <= 63, "vmcnt holds at most 63");
-    wait_vm(LPT * min(NS - 2, n_tiles - 1 - t) + spt * min(t, NS - 1));
+    static_assert(LPT * (NS - 2) + SPT * (NS - 1) <= 63, "vmcnt holds at most 63");
+    wait_vm(LPT * min(NS - 2, n_tiles - 1 - t) + SPT * min(t, NS - 1));
     __syncthreads();
     // the stage refilled below was read in the previous iteration, whose
     // LDS reads all completed before their MFMAs could issue
@@ -182,28 +181,14 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
     }
 
     const int kbase = k_begin + t * TK;
-    // raw logits of the valid heads for the score step, through LDS so the
-    // tile leaves as whole contiguous 16-byte chunks: exactly `spt` store
-    // instructions per tile (rows are padded to whole tiles, and keys past
-    // n_kv are never read back)
-    // (LDS operations of one wave run in order, so these writes land after
-    // every read of the K half above)
-    float* stage_lg = reinterpret_cast<float*>(smem + (t % NS) * TILE_BYTES);
+    // raw logits of the valid heads for the score step (rows are padded to
+    // whole tiles, and keys past the sequence's length are never read back);
+    // lanes 0..G-1 of every lane group store, so each tile issues exactly
+    // SPT store instructions
     if (row_ok) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) stage_lg[(kb * 16 + 4 * grp + e) * G + hh] = s[kb][e];
-    }
-    {
-      float* dst = lgt + (size_t)kbase * G;
-      // moved as bf16x8 bit patterns: an LDS read typed like the ring's
-      // data keeps the compiler from waiting on the gathers in flight
-      for (int i = 0; i < spt; ++i) {
-        const int c = i * 64 + lane;
-        if (c < n_vec)
-          reinterpret_cast<bf16x8*>(dst)[c] = reinterpret_cast<const bf16x8*>(stage_lg)[c];
-      }
+        *reinterpret_cast<f32x4*>(lgt + kbase + kb * 16 + 4 * grp) = s[kb];
     }
 
     if (kbase + TK > k_end) {
@@ -280,7 +265,6 @@ hipError_t launch_attn_decode_bf16(const DecodePlan& p, hipStream_t st) {
   a.B = p.s.batch; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.kps = p.keys_per_split; a.n_split = p.n_split; a.c = p.s.scale_log2;
   const dim3 grid((unsigned)((size_t)a.B * a.h_kv * a.n_split));
-  static_assert(TK * 16 * 4 <= HALF, "logits of 16 heads fit the K half of a stage");
   hipLaunchKernelGGL(attn_decode_bf16_kernel, grid, dim3(64), NS * TILE_BYTES, st, a);
   return hipGetLastError();
 }

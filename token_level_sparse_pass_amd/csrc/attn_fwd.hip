@@ -406,11 +406,11 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
         // keep the raw logits (q.k) of valid heads for the scoring step
         const int hh = rb * 16 + (lane & 15);
         if (hh < G) {
-          float* lg = a.logits + ((size_t)b * a.h_kv + g) * a.lstride * G + hh;
+          float* lg = a.logits + ((size_t)b * a.h_q + g * G + hh) * a.lstride;
           const int jb = j0 + kb * 16 + 4 * grp;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (jb + e < k_end) lg[(size_t)(jb + e) * G] = xs[e];
+            if (jb + e < k_end) lg[jb + e] = xs[e];
         }
       }
       tmax = xor_max(tmax, 16);
@@ -552,7 +552,8 @@ hipError_t launch_attn_fwd_decode(const DecodePlan& p, hipStream_t st) {
 }
 
 // S[b][j] = sum over heads (in order) of 2^(c * logit - m2) / l, candidates only.
-// The logits of KV head g's query heads are contiguous per key.
+// Logits are one row per (sequence, query head), so each head's read is
+// contiguous across the threads of a block.
 __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   extern __shared__ float sh[];                  // m2[h_q], inv_l[h_q]
   const int b = blockIdx.y;
@@ -565,15 +566,10 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   const int n_cand = a.seq_len ? a.seq_len[b] - a.window : a.n_cand;
   if (j >= n_cand) return;
-  const int G = a.h_q / a.h_kv;
+  const float* lg = a.logits + (size_t)b * a.h_q * a.logits_stride + j;
   float s = 0.f;
-  for (int g = 0; g < a.h_kv; ++g) {
-    const float* lg = a.logits + (((size_t)b * a.h_kv + g) * a.logits_stride + j) * G;
-    for (int hh = 0; hh < G; ++hh) {
-      const int h = g * G + hh;
-      s = fmaf(fast_exp2(fmaf(lg[hh], a.c, -sh[h])), sh[a.h_q + h], s);
-    }
-  }
+  for (int h = 0; h < a.h_q; ++h)
+    s = fmaf(fast_exp2(fmaf(lg[(size_t)h * a.logits_stride], a.c, -sh[h])), sh[a.h_q + h], s);
   a.scores[(size_t)b * a.score_stride + j] = s;
 }
 

@@ -100,10 +100,9 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st);
 // Decode (n_q == 1): split-KV pass 1 that also stores every raw logit (q.k)
 // so the score needs no second read of K; partials are merged by
 // the combine step. part: [batch][h_q][n_split][head_dim + 2] floats,
-// logits: [batch][h_kv][logits_stride][G] floats (G = h_q / h_kv: the raw
-// logits q.k of a KV head's query heads are contiguous per key), with
-// logits_stride a multiple of 64 that is >= n_kv, so whole tiles of a ragged
-// last split stay inside.
+// logits: [batch][h_q][logits_stride] floats (one row of raw logits q.k per
+// sequence and query head), with logits_stride a multiple of 64 that is
+// >= n_kv, so whole tiles of a ragged last split stay inside.
 struct DecodePlan {
   Shape s;
   const void* q; const void* k; const void* v;
