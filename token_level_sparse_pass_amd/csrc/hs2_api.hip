@@ -166,7 +166,10 @@ hs2_status plan(const hs2_problem& p, size_t ws_bytes, Layout* L, size_t* min_by
     }
     const size_t row_b = std::max<size_t>(l.stride, 1) * sizeof(float);
     const size_t mn = off + align_up(row_b);
-    size_t pref_rows = std::max<size_t>(128, CHUNK_TARGET / row_b / 128 * 128);
+    // the preferred chunk holds CHUNK_TARGET bytes of scores (the segment
+    // maxima come on top of it)
+    const size_t score_b = std::max<size_t>(l.seg_off ? l.seg_off : l.stride, 1) * sizeof(float);
+    size_t pref_rows = std::max<size_t>(128, CHUNK_TARGET / score_b / 128 * 128);
     pref_rows = std::min<size_t>(pref_rows, ((size_t)p.n_q + 127) / 128 * 128);
     const size_t pref = off + align_up(pref_rows * row_b);
     if (min_bytes) *min_bytes = mn;
