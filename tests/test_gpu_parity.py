@@ -267,6 +267,35 @@ def test_segment_path_selection(gpu_lib, pattern):
     say(pattern, "near-tie rows", len(tied))
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("pattern", ["plain", "repeat"])
+def test_segment_path_many_rows(gpu_lib, pattern):
+    # 512 query rows of 140K candidates: the launch size at which the
+    # segment path runs 512-thread work-groups. Every row is checked
+    # exactly against the selection rule on the GPU's own score row, and
+    # sampled rows against the streamed oracle.
+    nq, top_k, w = 512, 1024, 128
+    case = small("segrows_" + pattern, "bf16", 1, nq, SEG_N_KV, 8, 2, 128, top_k, w)
+    inp = make_inputs(case, device="cuda")
+    k = inp["k"]
+    if pattern == "repeat":
+        reps = (SEG_N_KV + 2999) // 3000
+        k = k[:, :3000].repeat(1, reps, 1, 1)[:, :SEG_N_KV].contiguous()
+    rows = list(range(nq))
+    _, idx, _, scores = gpu_lib.full_attn_select(inp["q_full"], k, inp["v"], top_k=top_k,
+                                                 window=w, debug_rows=rows)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[0]
+    pos = np.arange(nq) + SEG_N_KV - nq
+    exact_rule_on_own_scores(gi, scores, pos, top_k, w)
+    sample = [0, 1, 255, 510, 511]
+    q, kh, v = host(inp["q_full"]), host(k), host(inp["v"])
+    ref = O.block_rows(q, np.zeros((0,) + q.shape, dtype=q.dtype), kh, v, 0, sample,
+                       top_k=top_k, window=w)
+    tied = compare_index_rows(gi[sample], ref["S"], ref["pos"], ref["idx"], ref["tau"], w)
+    say(pattern, "rows", nq, "exact on own scores; oracle rows", len(sample), "near-tie", len(tied))
+
+
 @pytest.mark.parametrize("case", [
     small("blk_bf16", "bf16", 1, 300, 2000, 8, 2, 128, 0, 16),
     small("blk_fp32_unit", "fp32", 1, 120, 400, 4, 1, 64, 0, 8),

@@ -14,7 +14,11 @@
 // Chunks are XOR-swizzled so the MFMA operand reads are conflict-free; no
 // global load in the loop writes a register, so nothing waits on the
 // prefetches until the end of each head. Each probability costs one FMA
-// (logit * c - m2), one exp2 and one FMA into the running sum.
+// (logit * c - m2), one exp2 and one FMA into the running sum. With a
+// segment offset the kernel also writes, after each row's scores, the
+// maximum of S over the candidate keys of every 64-key segment (one per
+// wave and row), which the selection uses to read only the segments that
+// can hold a selected key.
 //
 // Work-groups are ordered in blocks of 32 key tiles x all query tiles of
 // the chunk, so a K tile is reused by every query tile from cache, and

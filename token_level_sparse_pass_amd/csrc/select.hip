@@ -13,12 +13,18 @@
 // the lowest-index keys == tau, and a bitonic sort in LDS puts the chosen
 // indices in ascending order. One work-group (512 or 1024 threads, see
 // token_threads) per query row.
-// Long rows first take a fast path that reads the row once: a threshold
-// from 8192 sampled keys (2048 runs of 4, aimed at about 3k keys above
-// the threshold), one pass
+// Rows of more than 128 * top_k candidates whose score pass also wrote the
+// maxima of their 64-key segments take the segment path: the top_k-th
+// largest maximum T bounds tau from below, so only the segments whose
+// maximum reaches T (about top_k of them) are read, their keys >= T are
+// gathered into LDS and the exact radix select runs there. Other long rows
+// take a path that reads the row once: a threshold from 8192 sampled keys
+// (2048 runs of 4, aimed at about 3k keys above the threshold), one pass
 // gathering every key at or above it into LDS, and the exact radix select
-// on that small set; it falls back to the full passes when it gathered
-// fewer than k keys or more than fit.
+// on that small set. Both fall back to the full passes when the gathered
+// set is too small or does not fit; all paths select the same keys.
+// Block mode with 64-token blocks takes its block maxima from the segment
+// maxima as well.
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -599,12 +605,16 @@ __global__ __launch_bounds__(SEL_THREADS) void select_block_kernel(SelArgs a) {
 // a CU (one 1024-thread one does), so one row's serial steps (threshold,
 // radix passes over the gathered keys, sorts) overlap another row's read;
 // that measured faster for launches of many rows of moderate length (32K
-// prefill 3.5 -> 2.3 ms, 8K chunk on 262K 2.5 -> 2.2 ms). Rows of a million
-// candidates (24.4 vs 21.3 ms) and launches of few rows (decode) keep 1024
+// prefill 3.5 -> 2.3 ms, 8K chunk on 262K 2.5 -> 2.2 ms), and for rows that
+// take the segment path, which read only about top_k segments (16K chunk on
+// 1M 3.5 -> 2.95 ms). Other rows of a million candidates (24.4 vs 21.3 ms
+// when they read the whole row) and launches of few rows (decode) keep 1024
 // threads per row.
 int token_threads(const SelectPlan& p) {
   const long long longest = (long long)p.n_kv - p.window;
-  return (p.rows >= 512 && longest < (1 << 19)) ? 512 : 1024;
+  if (p.rows < 512) return 1024;
+  if (p.seg_off && !p.block_mode && longest >= 128LL * p.top_k) return 512;
+  return longest < (1 << 19) ? 512 : 1024;
 }
 
 hipError_t launch_select(const SelectPlan& p, hipStream_t st) {
