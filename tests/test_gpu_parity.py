@@ -268,32 +268,56 @@ def test_segment_path_selection(gpu_lib, pattern):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("pattern", ["plain", "repeat"])
-def test_segment_path_many_rows(gpu_lib, pattern):
-    # 512 query rows of 140K candidates: the launch size at which the
-    # segment path runs 512-thread work-groups. Every row is checked
-    # exactly against the selection rule on the GPU's own score row, and
-    # sampled rows against the streamed oracle.
+@pytest.mark.parametrize("pattern,B", [("plain", 1), ("repeat", 1), ("plain", 2)])
+def test_segment_path_many_rows(gpu_lib, pattern, B):
+    # 512 query rows per sequence of 140K candidates: the launch size at
+    # which the segment path runs 512-thread work-groups. Every row is
+    # checked exactly against the selection rule on the GPU's own score
+    # row, and sampled rows against the streamed oracle.
     nq, top_k, w = 512, 1024, 128
-    case = small("segrows_" + pattern, "bf16", 1, nq, SEG_N_KV, 8, 2, 128, top_k, w)
+    case = small("segrows_" + pattern, "bf16", B, nq, SEG_N_KV, 8, 2, 128, top_k, w)
     inp = make_inputs(case, device="cuda")
     k = inp["k"]
     if pattern == "repeat":
         reps = (SEG_N_KV + 2999) // 3000
         k = k[:, :3000].repeat(1, reps, 1, 1)[:, :SEG_N_KV].contiguous()
-    rows = list(range(nq))
+    rows = list(range(B * nq))
     _, idx, _, scores = gpu_lib.full_attn_select(inp["q_full"], k, inp["v"], top_k=top_k,
                                                  window=w, debug_rows=rows)
     torch.cuda.synchronize()
-    gi = idx.cpu().numpy()[0]
+    gi = idx.cpu().numpy()
     pos = np.arange(nq) + SEG_N_KV - nq
-    exact_rule_on_own_scores(gi, scores, pos, top_k, w)
+    for b in range(B):
+        exact_rule_on_own_scores(gi[b], scores[b * nq:(b + 1) * nq], pos, top_k, w)
     sample = [0, 1, 255, 510, 511]
     q, kh, v = host(inp["q_full"]), host(k), host(inp["v"])
-    ref = O.block_rows(q, np.zeros((0,) + q.shape, dtype=q.dtype), kh, v, 0, sample,
-                       top_k=top_k, window=w)
-    tied = compare_index_rows(gi[sample], ref["S"], ref["pos"], ref["idx"], ref["tau"], w)
-    say(pattern, "rows", nq, "exact on own scores; oracle rows", len(sample), "near-tie", len(tied))
+    for b in range(B):
+        ref = O.block_rows(q, np.zeros((0,) + q.shape, dtype=q.dtype), kh, v, b, sample,
+                           top_k=top_k, window=w)
+        tied = compare_index_rows(gi[b][sample], ref["S"], ref["pos"], ref["idx"], ref["tau"], w)
+        say(pattern, "batch", b, "rows", nq, "exact on own scores; oracle rows", len(sample),
+            "near-tie", len(tied))
+
+
+@pytest.mark.timeout(300)
+def test_segment_path_chunked_matches(gpu_lib):
+    # a workspace of 128 score rows (with their segment maxima) splits the
+    # 300 queries into chunks; the selection and outputs must not change
+    nq, top_k, w = 300, 1024, 128
+    case = small("segchunks", "bf16", 1, nq, SEG_N_KV, 8, 2, 128, top_k, w, L=1)
+    inp = make_inputs(case, device="cuda")
+    p = gpu_lib.problem(torch.bfloat16, 1, nq, SEG_N_KV, 8, 2, 128, top_k=top_k, window=w)
+    mn, pref = gpu_lib.workspace_size(p)
+    s_floats = (SEG_N_KV - w + 255) // 256 * 256
+    row = (s_floats + s_floats // 64) * 4              # one score row and its segment maxima
+    small_ws = torch.empty(mn + 127 * row, dtype=torch.uint8, device="cuda")
+    args = (inp["q_full"], inp["q_sparse"], inp["k"], inp["v"])
+    a = gpu_lib.block_forward(*args, top_k=top_k, window=w)
+    b = gpu_lib.block_forward(*args, top_k=top_k, window=w, workspace=small_ws)
+    torch.cuda.synchronize()
+    assert small_ws.numel() < pref
+    for key in ("o_full", "o_sparse", "idx", "lse"):
+        assert torch.equal(a[key], b[key]), key
 
 
 @pytest.mark.parametrize("case", [
