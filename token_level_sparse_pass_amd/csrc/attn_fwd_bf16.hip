@@ -13,7 +13,9 @@
 //    16-byte chunks so the MFMA operand reads are free of bank conflicts;
 //    the tile loop is unrolled by two so each stage's LDS offsets are
 //    immediates of the read instructions, and tiles that need no causal
-//    mask run a copy of the loop body without one;
+//    mask run a copy of the loop body without one; a load's global address
+//    is a uniform tile base plus a lane offset computed once, and its LDS
+//    target is uniform, so the loads cost almost no vector instructions;
 //  * the eight waves form two groups half a tile apart (waves w and w + 4
 //    share a SIMD): a tile step is an MFMA phase (the previous tile's PV
 //    product, then this tile's logits) and a VALU phase (this tile's
@@ -125,10 +127,12 @@ template <int RBW, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) {
   using OP = Op<__bf16, D>;
   constexpr int ROWS = 16 * RBW * NWV;                  // rows per work-group
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // a fixed-size array: its address is a constant, so stage and row offsets
+  // fold into the immediates of the LDS instructions
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS targets stay scalar
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.h_q / a.h_kv;
@@ -223,34 +227,50 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   // Vt(t - 2), whose PV product both groups finished before barrier t); a
   // wave waits for its own loads before its next barrier, so both tiles are
   // in LDS for every wave after barrier t + 1, before either is read.
-  const bool lead = __builtin_amdgcn_readfirstlane(wave) < 4;
+  const bool lead = wave < 4;
   static_assert(NWV == 8, "two groups of four waves");
   constexpr int CPT = 1024 / (64 * NWV);                // 16-byte chunks per thread per tensor
 
+  // The chunks a lane moves sit at fixed byte offsets from the tile's start
+  // (K row r of the tile, Vt row d), so a load is a uniform tile base plus a
+  // per-lane 32-bit offset computed once here, and the LDS targets are
+  // uniform: no per-tile vector address arithmetic. Only a tile that runs
+  // past n_kv clamps its K rows (to row n_kv - 1, whose logits are masked).
+  int k_row[CPT];
+  uint32_t k_off[CPT], k_col[CPT], v_off[CPT];
+#pragma unroll
+  for (int t = 0; t < CPT; ++t) {
+    const int slot = (wave * CPT + t) * 64 + lane;
+    const int r = slot >> 4, c = (slot & 15) ^ kswz(r);
+    k_row[t] = r;
+    k_col[t] = (uint32_t)c * 16;
+    k_off[t] = (uint32_t)((size_t)r * kstride * 2) + k_col[t];
+    const int d = slot >> 3, cv = (slot & 7) ^ vswz(d);
+    v_off[t] = (uint32_t)(d * TK + cv * 8) * 2;
+  }
   auto issue_k = [&](int tile, int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE_BYTES;
     const int j0 = tile * TK;
+    if (j0 + TK <= nkv) {
+      const char* src = reinterpret_cast<const char*>(kseq + (size_t)j0 * kstride);
 #pragma unroll
-    for (int t = 0; t < CPT; ++t) {
-      const int slot = (wave * CPT + t) * 64 + lane;
-      const int r = slot >> 4, pc = slot & 15;
-      const int c = pc ^ kswz(r);
-      const int key = min(j0 + r, nkv - 1);
-      const __bf16* src = kseq + (size_t)key * kstride + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
+      for (int t = 0; t < CPT; ++t)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(src + k_off[t]), (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int t = 0; t < CPT; ++t) {
+        const int key = min(j0 + k_row[t], nkv - 1);
+        const char* src = reinterpret_cast<const char*>(kseq + (size_t)key * kstride) + k_col[t];
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(src), (lds_void*)(base + (wave * CPT + t) * 1024), 16, 0, 0);
+      }
     }
   };
   auto issue_v = [&](int tile, int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE_BYTES;
-    const __bf16* vsrc = vtseq + (size_t)tile * (D * TK);
+    const char* vsrc = reinterpret_cast<const char*>(vtseq + (size_t)tile * (D * TK));
 #pragma unroll
-    for (int t = 0; t < CPT; ++t) {
-      const int slot = (wave * CPT + t) * 64 + lane;
-      const int d = slot >> 3, pc = slot & 7;
-      const int c = pc ^ vswz(d);
-      __builtin_amdgcn_global_load_lds(
-          vsrc + d * TK + c * 8, (lds_void*)(base + KT_BYTES + (wave * CPT + t) * 1024), 16, 0, 0);
-    }
+    for (int t = 0; t < CPT; ++t)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(vsrc + v_off[t]), (lds_void*)(base + KT_BYTES + (wave * CPT + t) * 1024), 16, 0, 0);
   };
 
   float m_run[RBW];
@@ -526,13 +546,7 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
   // sharing each tile beat four waves by about 3 %
   constexpr int RBW = 2, NWV = FWD_WAVES;
   constexpr int rows = 16 * RBW * NWV;
-  constexpr int smem_bytes = 2 * STAGE_BYTES;
-  struct FwdLdsTag {};
-  if (smem_bytes > 65536) {
-    const hipError_t e = ensure_dynamic_lds<FwdLdsTag>(
-        (const void*)attn_fwd_bf16_kernel<RBW, NWV>, smem_bytes);
-    if (e != hipSuccess) return e;
-  }
+  static_assert(2 * STAGE_BYTES <= 65536, "the two-stage ring is a static LDS array");
   a.n_rt = (a.n_q * G + rows - 1) / rows;
   dim3 grid((unsigned)((size_t)a.n_rt * a.B * a.h_kv));
   if (p.vl) {
@@ -540,8 +554,7 @@ hipError_t launch_attn_fwd_prefill(const FwdPlan& p, hipStream_t st) {
     grid = dim3((unsigned)((size_t)a.vl.tile0[a.vl.n] * a.h_kv));
     if (a.vl.tile0[a.vl.n] == 0) return hipSuccess;
   }
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV>), grid, dim3(64 * NWV), smem_bytes, st,
-                     a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<RBW, NWV>), grid, dim3(64 * NWV), 0, st, a);
   return hipGetLastError();
 }
 

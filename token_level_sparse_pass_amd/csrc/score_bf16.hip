@@ -13,7 +13,8 @@
 // (64 KB) are staged in LDS the same way while the current one is in use.
 // Chunks are XOR-swizzled so the MFMA operand reads are conflict-free; no
 // global load in the loop writes a register, so nothing waits on the
-// prefetches until the end of each head. Each probability costs one FMA
+// prefetches until the end of each head, and each load is a uniform
+// per-head base plus a lane offset computed once per tile. Each probability costs one FMA
 // (logit * c - m2), one exp2 and one FMA into the running sum. With a
 // segment offset the kernel also writes, after each row's scores, the
 // maximum of S over the candidate keys of every 64-key segment (one per
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS targets stay scalar
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int wq = wave >> 2, wk = wave & 3;
@@ -92,39 +93,44 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
   const __bf16* kseq = a.k + (size_t)a.b * a.n_kv * a.h_kv * D;
   const size_t plane = (size_t)a.B * a.h_q * a.n_q;
 
+  // The per-lane parts of the Q and statistics addresses (tile row, clamped
+  // to the last row; 16-byte chunk) are the same for every head: a load is a
+  // uniform per-head base plus a 32-bit lane offset computed once here.
+  const int r_last = a.rows - 1 - r_lo;                 // last real row of the tile
+  const __bf16* qtile = qseq + (size_t)(a.q0 + r_lo) * a.h_q * D;
+  uint32_t q_lane[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int slot = (wave * 4 + t) * 64 + lane;
+    const int r = slot >> 4, c = (slot & 15) ^ qswz(r);
+    q_lane[t] = (uint32_t)(min(r, r_last) * a.h_q * D + c * 8) * 2;
+  }
+  // waves 0,1: m2 of rows 0..63, 64..127; waves 2,3: 1/l
+  const float* st_tile = a.stats + ((wave >> 1) ? 2 : 0) * plane + (size_t)a.b * a.h_q * a.n_q + a.q0 + r_lo;
+  const uint32_t st_lane = (uint32_t)min((wave & 1) * 64 + lane, r_last) * 4;
   auto issue = [&](int h, int stage) {
     char* base = smem + stage * QT_BYTES;
+    const char* src = reinterpret_cast<const char*>(qtile + h * D);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int slot = (wave * 4 + t) * 64 + lane;
-      const int r = slot >> 4, pc = slot & 15;
-      const int c = pc ^ qswz(r);
-      const int qi = a.q0 + min(r_lo + r, a.rows - 1);
-      __builtin_amdgcn_global_load_lds(qseq + ((size_t)qi * a.h_q + h) * D + c * 8,
-                                       (lds_void*)(base + (wave * 4 + t) * 1024), 16, 0, 0);
-    }
-    if (wave < 4) {
-      // waves 0,1: m2 of rows 0..63, 64..127; waves 2,3: 1/l
-      const int pl = (wave >> 1) ? 2 : 0;
-      const int r = (wave & 1) * 64 + lane;
-      const int qi = a.q0 + min(r_lo + r, a.rows - 1);
-      const float* src = a.stats + pl * plane + ((size_t)a.b * a.h_q + h) * a.n_q + qi;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + ST_BASE + stage * ST_BYTES + wave * 256),
-                                       4, 0, 0);
-    }
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(src + q_lane[t]), (lds_void*)(base + (wave * 4 + t) * 1024), 16, 0, 0);
+    if (wave < 4)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const float*>(reinterpret_cast<const char*>(st_tile + (size_t)h * a.n_q) + st_lane),
+                                       (lds_void*)(smem + ST_BASE + stage * ST_BYTES + wave * 256), 4, 0, 0);
   };
 
   // K rows of the tile's 256 keys for KV head g, into the K buffer
+  // (the tile's key rows clamped to the last key, which no row reads back)
   auto issue_k = [&](int g) {
     char* base = smem + K_BASE;
+    const char* src = reinterpret_cast<const char*>(kseq + ((size_t)kj0 * a.h_kv + g) * D);
+    const int j_last = a.n_kv - 1 - kj0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int slot = (wave * 8 + t) * 64 + lane;
-      const int r = slot >> 4, pc = slot & 15;
-      const int c = pc ^ kswz(r);
-      const int j = min(kj0 + r, a.n_kv - 1);
-      __builtin_amdgcn_global_load_lds(kseq + ((size_t)j * a.h_kv + g) * D + c * 8,
-                                       (lds_void*)(base + (wave * 8 + t) * 1024), 16, 0, 0);
+      const int r = slot >> 4, c = (slot & 15) ^ kswz(r);
+      const uint32_t off = (uint32_t)(min(r, j_last) * a.h_kv * D + c * 8) * 2;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(src + off), (lds_void*)(base + (wave * 8 + t) * 1024), 16, 0, 0);
     }
   };
 
