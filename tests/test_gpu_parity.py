@@ -80,6 +80,12 @@ def check_invariants(idx, w: Workload, block_mode=False):
     small("sp_fp32", "fp32", 1, 200, 260, 4, 1, 64, 40, 8, L=3),
     small("sp_bf16_d64_L5", "bf16", 1, 150, 400, 16, 2, 64, 100, 20, L=5),
     small("sp_decode", "bf16", 5, 1, 3000, 32, 4, 128, 1024, 128, L=3),
+    # few lists of 16 rows: the partitioned decode kernel, one wave per
+    # partition, 750-entry rows (24 tiles, and shorter rows for early queries)
+    small("sp_decode_rows16", "bf16", 3, 2, 2000, 16, 4, 128, 700, 50, L=4),
+    # few lists of 40 rows: more than the partitioned kernel takes, so the
+    # generic split kernel runs
+    small("sp_decode_rows40", "bf16", 2, 64, 700, 16, 2, 128, 100, 20, L=5),
     small("sp_fp32_d128", "fp32", 1, 64, 300, 8, 4, 128, 50, 10, L=2),
 ], ids=lambda c: c.name)
 def test_sparse_attn_on_oracle_indices(gpu_lib, case):

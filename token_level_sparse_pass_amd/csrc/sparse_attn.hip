@@ -8,8 +8,8 @@
 // all (layer, query head of group g) pairs, so each selected K/V row is
 // gathered from HBM once and used by G heads x L layers. The index list is
 // walked in tiles of 32 keys; NW waves split the list and merge their
-// online-softmax states through LDS at the end (NW > 1 is the decode shape,
-// where there are few queries to fill the chip).
+// online-softmax states through LDS at the end (NW > 1 serves few queries,
+// as in decode, where the bf16 head-dim-128 kernels do not apply).
 //
 // Per 32-key tile, in MFMA terms (16x16 tiles, see hs2_device.h):
 //   logits^T (keys x rows) = K_sel . Q^T        A = gathered K rows, B = Q rows
@@ -337,9 +337,12 @@ static hipError_t launch_sparse_t(const SparseArgs& a, int rb, bool split, hipSt
 
 bool sparse_uses_bf16_kernel(const SparsePlan& p);
 hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st);
+bool sparse_uses_bf16_split_kernel(const SparsePlan& p);
+hipError_t launch_sparse_attn_bf16_split(const SparsePlan& p, hipStream_t st);
 
 hipError_t launch_sparse_attn(const SparsePlan& p, hipStream_t st) {
   if (sparse_uses_bf16_kernel(p)) return launch_sparse_attn_bf16(p, st);
+  if (sparse_uses_bf16_split_kernel(p)) return launch_sparse_attn_bf16_split(p, st);
   SparseArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.idx = p.idx; a.o = p.o;
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;

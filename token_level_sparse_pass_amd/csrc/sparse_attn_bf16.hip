@@ -1,5 +1,6 @@
-// Sparse layers with KV Reuse, specialised for bf16 and head dim 128 on
-// many queries (prefill-shaped calls). Same contract as sparse_attn.hip:
+// Sparse layers with KV Reuse, specialised for bf16 and head dim 128: one
+// kernel for many queries (prefill-shaped calls) and, further down, one for
+// few index lists (decode-shaped calls). Same contract as sparse_attn.hip:
 // every sparse layer attends, with one softmax, over the same index set and
 // the same K/V as the full layer (HySparse2 pages: "Xiaomi Unveils HySparse2
 // for Faster Long-Context AI", sections "Two-Level KV Sharing" and
@@ -257,6 +258,240 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   for (int e = 0; e < 4; ++e) reinterpret_cast<bf16x8*>(orow)[e] = outv[e];
 }
 
+// Decode-shaped calls (few index lists, fewer work-groups than the chip
+// holds): one work-group serves one (sequence, query, KV head) list with NP
+// key partitions. Each partition is a group of NWV row-block waves with its
+// own two-stage ring over a contiguous NP-th of the list's tiles, so NP
+// tiles' gathers are in flight per work-group instead of one. At the end
+// the partitions' online-softmax states (maximum, sum, O^T) go through LDS
+// and the first partition's waves merge them in partition order, so the
+// result does not depend on timing.
+// (three partitions of three stages, or two of four, keep more tiles in
+// flight per partition but measured the same on the 64 x 128K decode: the
+// gathers, not their latency, set the time)
+constexpr int NP = 4;
+constexpr int NSS = 2;
+constexpr size_t SPLIT_RING_BYTES = (size_t)NP * NSS * TILE_BYTES;   // 128 KB
+
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV * NP) void sparse_bf16_split_kernel(Sp2Args a) {
+  using OP = Op<__bf16, D>;
+  constexpr int KPW = TK / NWV;              // keys gathered per wave per tile
+  constexpr int IPW = KPW / 4;               // 1 KB load instructions per half
+  constexpr int LPW = 2 * IPW;               // load instructions per wave per tile
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wid / NWV;                // key partition
+  const int wave = wid - part * NWV;         // row block (and gather share) within it
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const int G = a.h_q / a.h_kv;
+  const int rows_total = a.L * G;
+
+  const uint32_t wg = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int nbq = a.B * a.n_q;
+  const int g = wg / nbq;
+  const int bi = wg - g * nbq;                // b * n_q + i
+  const int b = bi / a.n_q;
+  const int i = bi - b * a.n_q;
+  const int32_t* irow = a.idx + (size_t)bi * a.W;
+
+  // the index row (as K/V buffer rows) after the rings
+  int* sidx = reinterpret_cast<int*>(smem + SPLIT_RING_BYTES);
+  for (int t = threadIdx.x; t < a.W; t += 64 * NWV * NP) {
+    const int j = irow[t];
+    sidx[t] = j >= 0 ? (int)a.kv.row(b, j) : -1;
+  }
+  __syncthreads();
+  int n_valid = 0;
+  for (int t = lane; t < a.W; t += 64) n_valid += (sidx[t] >= 0) ? 1 : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
+  const int n_tiles = (n_valid + TK - 1) / TK;
+  const int fallback = n_valid > 0 ? sidx[0] : 0;
+  // this partition's tiles [t_lo, t_lo + n_mine); every wave runs `steps`
+  // barrier steps, the largest partition's tile count
+  const int t_lo = n_tiles * part / NP;
+  const int n_mine = n_tiles * (part + 1) / NP - t_lo;
+  const int steps = (n_tiles + NP - 1) / NP;
+
+  const size_t kvs = (size_t)a.h_kv * D;
+  const __bf16* kseq = a.k + (size_t)g * D;             // + buffer row * kvs
+  const __bf16* vseq = a.v + (size_t)g * D;
+  char* ring = smem + (size_t)part * NSS * TILE_BYTES;
+
+  int nidx[IPW];
+  auto read_idx = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int pos = (t_lo + t) * TK + wave * KPW + j * 4 + grp;
+      nidx[j] = pos < n_valid ? sidx[pos] : fallback;
+    }
+  };
+  auto issue = [&](int stage) {
+    char* base = ring + stage * TILE_BYTES;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int key = wave * KPW + j * 4 + grp;        // tile-local key of this lane
+      const size_t row = (size_t)nidx[j] * kvs;
+      const int slot_base = (wave * KPW + j * 4) * 16;
+      __builtin_amdgcn_global_load_lds(kseq + row + ((l16 ^ kswz(key)) << 3),
+                                       (lds_void*)(base + slot_base * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vseq + row + (l16 << 3),
+                                       (lds_void*)(base + HALF + slot_base * 16), 16, 0, 0);
+    }
+  };
+
+  const int r = wave * 16 + l16;
+  const bool wave_active = wave * 16 < rows_total;
+  Frag<__bf16, D> qf;
+  if (r < rows_total) {
+    const int layer = r / G, hh = r - (r / G) * G;
+    load_slice<__bf16, D>(qf, a.q + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D),
+                          lane);
+  } else {
+    zero_slice<__bf16, D>(qf);
+  }
+  float m_run = -1e30f, l_run = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: tiles 0 .. NSS-2 in flight
+#pragma unroll
+  for (int t = 0; t < NSS - 1; ++t) {
+    if (t < n_mine) {
+      read_idx(t);
+      issue(t);
+    }
+  }
+  if (NSS - 1 < n_mine) read_idx(NSS - 1);
+
+  for (int t = 0; t < steps; ++t) {
+    // own loads of tile t done (later tiles may stay in flight), then all waves'
+    const int ahead = max(0, min(NSS - 2, n_mine - 1 - t));
+    static_assert((NSS - 2) * LPW <= 63, "vmcnt range");
+    wait_ahead<NSS - 2, LPW>(ahead);
+    __syncthreads();
+    if (t + NSS - 1 < n_mine) {
+      issue((t + NSS - 1) % NSS);
+      if (t + NSS < n_mine) read_idx(t + NSS);
+    }
+    if (t >= n_mine || !wave_active) continue;
+    const char* base = ring + (t % NSS) * TILE_BYTES;
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kb * 16 + l16;
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(base + key * 256 + (((4 * grp + u) ^ kswz(key)) << 4));
+        x = OP::mma(kf, qf.u[u], x);
+      }
+      s[kb] = x;
+    }
+    bf16x8 vraw[8];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int key = sl < 4 ? 4 * grp + sl : 16 + 4 * grp + (sl - 4);
+      vraw[sl] = *reinterpret_cast<const bf16x8*>(base + HALF + key * 256 + l16 * 16);
+    }
+
+    const int kbase = (t_lo + t) * TK;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (kbase + kb * 16 + 4 * grp + e >= n_valid) s[kb][e] = -INFINITY;
+        tmax = fmaxf(tmax, s[kb][e]);
+      }
+    tmax = xor_max(tmax, 16);
+    tmax = xor_max(tmax, 32);
+    const float m_tile = tmax * a.c;
+    const bool grow = m_tile > m_run + RESCALE_GAP;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+    }
+    float psum = 0.f;
+    bf16x8 pu;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = fast_exp2(fmaf(s[kb][e], a.c, -m_run));
+        psum += pe;
+        pu[kb * 4 + e] = (__bf16)pe;
+      }
+    l_run += psum;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      bf16x8 vu;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) vu[sl] = vraw[sl][db];
+      acc[db] = OP::mma(vu, pu, acc[db]);
+    }
+  }
+
+  // merge: every partition's state into LDS (the rings are free after this
+  // barrier), then the first partition's waves combine them in order
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(smem);           // [NP][NWV][32][64] partial O^T
+  float* mm = mo + NP * NWV * 32 * 64;                  // [NP][NWV][16] row maxima
+  float* ml = mm + NP * NWV * 16;                       // [NP][NWV][16] row sums
+  const int slot = part * NWV + wave;
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mo[(slot * 32 + db * 4 + e) * 64 + lane] = acc[db][e];
+  if (grp == 0) {
+    mm[slot * 16 + l16] = m_run;
+    ml[slot * 16 + l16] = l;
+  }
+  __syncthreads();
+  if (part != 0 || r >= rows_total) return;
+  float M = -1e30f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) M = fmaxf(M, mm[(p * NWV + wave) * 16 + l16]);
+  float L = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int sp = p * NWV + wave;
+    const float w = fast_exp2(mm[sp * 16 + l16] - M);
+    L += ml[sp * 16 + l16] * w;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[db][e] += mo[(sp * 32 + db * 4 + e) * 64 + lane] * w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int layer = r / G, hh = r - (r / G) * G;
+  __bf16* orow = a.o + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D) + grp * 32;
+  bf16x8 outv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) outv[e][db] = (__bf16)(o[db][e] * inv);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) reinterpret_cast<bf16x8*>(orow)[e] = outv[e];
+}
+
 // Dynamic LDS of one work-group: the ring plus the index row. Wider index
 // rows than fit the default 64 KB per work-group (more than 8192 entries)
 // go to the generic kernel, which keeps no index row in LDS.
@@ -267,6 +502,22 @@ size_t sparse_bf16_lds_bytes(int width) { return (size_t)NS * TILE_BYTES + (size
 bool sparse_uses_bf16_kernel(const SparsePlan& p) {
   return p.bf16 && p.head_dim == D && (size_t)p.batch * p.n_q * p.h_kv >= 2048 &&
          p.layers * (p.h_q / p.h_kv) <= 64 && sparse_bf16_lds_bytes(p.width) <= SPARSE_LDS_LIMIT;
+}
+
+// The decode-shaped kernel needs the NP rings plus the index row, and after
+// the loop the partitions' states; at most a work-group's 160 KB.
+constexpr size_t SPLIT_LDS_LIMIT = 160 * 1024;
+
+static size_t sparse_bf16_split_lds_bytes(int width, int nwv) {
+  const size_t merge = (size_t)NP * nwv * (32 * 64 + 2 * 16) * sizeof(float);
+  const size_t ring = SPLIT_RING_BYTES + (size_t)width * sizeof(int);
+  return ring > merge ? ring : merge;
+}
+
+bool sparse_uses_bf16_split_kernel(const SparsePlan& p) {
+  const int rows = p.layers * (p.h_q / p.h_kv);
+  return p.bf16 && p.head_dim == D && (size_t)p.batch * p.n_q * p.h_kv < 2048 && rows <= 32 &&
+         sparse_bf16_split_lds_bytes(p.width, rows <= 16 ? 1 : 2) <= SPLIT_LDS_LIMIT;
 }
 
 hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
@@ -288,6 +539,39 @@ hipError_t launch_sparse_attn_bf16(const SparsePlan& p, hipStream_t st) {
   else if (rb <= 2) hipLaunchKernelGGL(sparse_bf16_kernel<2>, grid, dim3(128), smem, st, a);
   else if (rb <= 4) hipLaunchKernelGGL(sparse_bf16_kernel<4>, grid, dim3(256), smem, st, a);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_bf16_split(const SparsePlan& p, hipStream_t st) {
+  Sp2Args a;
+  a.q = reinterpret_cast<const __bf16*>(p.q);
+  a.k = reinterpret_cast<const __bf16*>(p.k);
+  a.v = reinterpret_cast<const __bf16*>(p.v);
+  a.idx = p.idx;
+  a.o = reinterpret_cast<__bf16*>(p.o);
+  a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv;
+  a.h_q = p.h_q; a.h_kv = p.h_kv; a.W = p.width; a.c = p.scale_log2; a.kv = p.kv;
+  a.layer_stride = p.layer_stride ? p.layer_stride : (size_t)p.batch * p.n_q * p.h_q * D;
+  const int rows = p.layers * (p.h_q / p.h_kv);
+  const dim3 grid((unsigned)((size_t)p.batch * p.n_q * p.h_kv));
+  if (grid.x == 0) return hipSuccess;
+  struct Split1Tag {};
+  struct Split2Tag {};
+  if (rows <= 16) {
+    const size_t smem = sparse_bf16_split_lds_bytes(p.width, 1);
+    if (smem > SPLIT_LDS_LIMIT) return hipErrorInvalidValue;
+    const hipError_t e = ensure_dynamic_lds<Split1Tag>((const void*)sparse_bf16_split_kernel<1>, (int)SPLIT_LDS_LIMIT);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sparse_bf16_split_kernel<1>, grid, dim3(64 * NP), smem, st, a);
+  } else if (rows <= 32) {
+    const size_t smem = sparse_bf16_split_lds_bytes(p.width, 2);
+    if (smem > SPLIT_LDS_LIMIT) return hipErrorInvalidValue;
+    const hipError_t e = ensure_dynamic_lds<Split2Tag>((const void*)sparse_bf16_split_kernel<2>, (int)SPLIT_LDS_LIMIT);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sparse_bf16_split_kernel<2>, grid, dim3(128 * NP), smem, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
