@@ -118,7 +118,7 @@ PASS_KERNELS = {
                        "hs2::decode_combine_kernel"),
     "score": ("hs2::score_bf16_kernel", "hs2::score_prefill_kernel", "hs2::decode_score_kernel"),
     "select": ("hs2::select_token_kernel", "hs2::select_block_kernel"),
-    "sparse_attention": ("hs2::sparse_bf16_kernel", "hs2::sparse_attn_kernel"),
+    "sparse_attention": ("hs2::sparse_bf16_kernel", "hs2::sparse_bf16_split_kernel", "hs2::sparse_attn_kernel"),
     "v_layout": ("hs2::transpose_v_kernel",),
 }
 COUNTER_REGEX = "attn_fwd|attn_decode|decode_|score|sparse|select|transpose"
