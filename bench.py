@@ -648,20 +648,21 @@ def backward_bench(args):
     ws = torch.empty(hs2.backward_workspace_size(p, w.n_sparse), dtype=torch.uint8, device=dev)
     args_ = (inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], fwd["o_full"], fwd["o_sparse"],
              fwd["lse"], fwd["idx"], grads["do_full"], grads["do_sparse"])
+    bkw = dict(kw, deterministic=args.deterministic)
     out = None
     for s in range(args.warmup):
-        out = hs2.block_backward(*args_, workspace=ws, out=out, **kw)
+        out = hs2.block_backward(*args_, workspace=ws, out=out, **bkw)
         torch.cuda.synchronize()
         log(f"warmup step {s + 1}/{args.warmup} done")
     if out is None:
-        out = hs2.block_backward(*args_, workspace=ws, **kw)
+        out = hs2.block_backward(*args_, workspace=ws, **bkw)
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     lib.hs2_profile_enable(1)
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        hs2.block_backward(*args_, workspace=ws, out=out, **kw)
+        hs2.block_backward(*args_, workspace=ws, out=out, **bkw)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = (ctypes.c_double * len(PASSES))()
@@ -707,7 +708,8 @@ def backward_bench(args):
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
            "data": "synthetic (seeded; shapes and structure of the workload, no datasets)",
-           "config": {"workload": w.name + "_backward", "batch": w.batch, "n_q": w.n_q,
+           "config": {"workload": w.name + ("_backward_deterministic" if args.deterministic
+                                            else "_backward"), "batch": w.batch, "n_q": w.n_q,
                       "n_kv": w.n_kv, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
                       "top_k": w.top_k, "window": w.window, "sparse_layers": w.n_sparse,
                       "parallelism": "single GPU"},
@@ -878,6 +880,8 @@ def main():
                          "prefill over 256-row pages) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fixed index sets) instead")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="with --backward: time hs2_block_backward_deterministic")
     ap.add_argument("--bwd-config", type=int, default=2,
                     help="with --backward: the workload (default 2, the 32K-token prefill)")
     ap.add_argument("--page-size", type=int, default=0,

@@ -318,14 +318,15 @@ hs2_status hs2_block_forward_paged(const hs2_problem* p, const hs2_kv_pages* pag
  * Outputs (DEVICE, dtype, overwritten): dq_full, dq_sparse (shapes of
  * q_full, q_sparse), dk, dv (shape of k). Gradients are accumulated in fp32
  * and rounded once. The sparse layers' K/V sums use fp32 atomic adds, so
- * their last bits may differ from run to run; everything else is
- * deterministic. With n_sparse_layers = 0, q_sparse, o_sparse, idx,
- * do_sparse and dq_sparse may be NULL.
+ * their last bits may differ from run to run (hs2_block_backward_deterministic
+ * below avoids that); everything else is deterministic. With
+ * n_sparse_layers = 0, q_sparse, o_sparse, idx, do_sparse and dq_sparse may
+ * be NULL.
  * Workspace: hs2_backward_workspace_size bytes (Delta = rowsum(dO * O) per
  * row; for bf16 at head dim 128 a tiled K^T copy that the dQ kernel reads,
  * and Q and dO in transposed 64-row tiles with their rows' lse and Delta,
- * which the dK/dV kernel reads; the sparse layers' fp32 K/V accumulators),
- * 16-byte aligned. */
+ * which the dK/dV kernel reads; the sparse layers' K/V accumulators, sized
+ * for either entry point), 16-byte aligned. */
 hs2_status hs2_backward_workspace_size(const hs2_problem* p, int32_t n_sparse_layers,
                                        size_t* bytes);
 hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
@@ -336,6 +337,27 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers,
                               const void* do_full, const void* do_sparse,
                               void* dq_full, void* dq_sparse, void* dk, void* dv,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* hs2_block_backward with bit-reproducible results: same arguments, same
+ * workspace. The sparse layers' K/V sums are kept as 64-bit fixed point
+ * (integer atomic adds, whose result does not depend on the order in which
+ * they land) with a scale derived on the device from the inputs: a key's
+ * sums over all rows of its KV head are bounded by R max|dO| (dV) and
+ * softmax_scale * 2 R max||dO|| max||V|| max|Q| (dK), R the rows per
+ * (sequence, KV head) over all sparse layers, and the scale is the largest
+ * power of two that keeps those bounds below 2^61. The resolution is far
+ * finer than fp32 sums keep (2^-39 for dV, 2^-34 for dK on a 32K-token
+ * prefill with unit-variance inputs). Costs one extra read of q_sparse,
+ * do_sparse and v, and 64-bit instead of 32-bit atomics. */
+hs2_status hs2_block_backward_deterministic(const hs2_problem* p, int32_t n_sparse_layers,
+                                            const void* q_full, const void* q_sparse,
+                                            const void* k, const void* v,
+                                            const void* o_full, const void* o_sparse,
+                                            const float* lse, const int32_t* idx,
+                                            const void* do_full, const void* do_sparse,
+                                            void* dq_full, void* dq_sparse, void* dk, void* dv,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 /* Optional pass timing, a profiling aid. While enabled, every call records
  * HIP events on its stream around each pass: HS2_PASS_FULL (full attention,

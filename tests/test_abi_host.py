@@ -215,35 +215,39 @@ def test_backward_workspace_and_rejections():
     vp = ctypes.c_void_p
     p = base_problem()
     # Delta rows; for bf16 at head dim 128 a K^T copy and the Q / dO rows in
-    # transposed 64-row tiles with their statistics; then two fp32 K/V
-    # accumulators when there are sparse layers
+    # transposed 64-row tiles with their statistics; then, when there are
+    # sparse layers, two K/V accumulators sized for 64-bit fixed point (the
+    # deterministic entry point; the default one uses their first half as
+    # fp32) and a 256-byte block for their bounds and scales
     delta = 1 * 8 * 256 * 4
     tiles = 2 * (256 * 4 // 64)                      # KV heads x 64-row tiles
     kt = 1 * 2 * 1024 * 128 * 2 + 2 * tiles * 64 * 128 * 2 + tiles * 128 * 4
-    acc = 1 * 1024 * 2 * 128 * 4
+    acc = 1 * 1024 * 2 * 128 * 8
     assert hs2.backward_workspace_size(p, 0) == delta + kt
-    assert hs2.backward_workspace_size(p, 3) == delta + kt + 2 * acc
+    assert hs2.backward_workspace_size(p, 3) == delta + kt + 2 * acc + 256
     # the K^T copy serves only the bf16, head-dim-128 dQ kernel
     assert hs2.backward_workspace_size(base_problem(head_dim=64), 0) == 1 * 8 * 256 * 4
     assert hs2.backward_workspace_size(base_problem(dtype=hs2.FP32), 0) == delta
     ws = hs2.backward_workspace_size(p, 2)
 
-    def call(L=2, ws_bytes=ws, **over):
-        names = ["q_full", "q_sparse", "k", "v", "o_full", "o_sparse", "lse", "idx", "do_full",
-                 "do_sparse", "dq_full", "dq_sparse", "dk", "dv", "ws"]
-        a = {n: FAKE for n in names}
-        a.update(over)
-        ptrs = [vp(a[n]) for n in names]
-        return lib.hs2_block_backward(ctypes.byref(p), L, *ptrs[:-1], ptrs[-1], ws_bytes, None)
+    # both entry points validate alike (the deterministic one shares the code)
+    for fn in (lib.hs2_block_backward, lib.hs2_block_backward_deterministic):
+        def call(L=2, ws_bytes=ws, **over):
+            names = ["q_full", "q_sparse", "k", "v", "o_full", "o_sparse", "lse", "idx",
+                     "do_full", "do_sparse", "dq_full", "dq_sparse", "dk", "dv", "ws"]
+            a = {n: FAKE for n in names}
+            a.update(over)
+            ptrs = [vp(a[n]) for n in names]
+            return fn(ctypes.byref(p), L, *ptrs[:-1], ptrs[-1], ws_bytes, None)
 
-    assert call(L=-1) == 2
-    for n in ("q_full", "k", "v", "o_full", "lse", "do_full", "dq_full", "dk", "dv", "ws"):
-        assert call(**{n: None}) == 1, n
-        assert call(**{n: FAKE + 4}) == 5, n
-    for n in ("q_sparse", "o_sparse", "idx", "do_sparse", "dq_sparse"):
-        assert call(**{n: None}) == 1, n
-    assert call(ws_bytes=ws - 1) == 4
-    assert b"workspace" in lib.hs2_last_error()
+        assert call(L=-1) == 2
+        for n in ("q_full", "k", "v", "o_full", "lse", "do_full", "dq_full", "dk", "dv", "ws"):
+            assert call(**{n: None}) == 1, n
+            assert call(**{n: FAKE + 4}) == 5, n
+        for n in ("q_sparse", "o_sparse", "idx", "do_sparse", "dq_sparse"):
+            assert call(**{n: None}) == 1, n
+        assert call(ws_bytes=ws - 1) == 4
+        assert b"workspace" in lib.hs2_last_error()
     bad = base_problem(h_q=6, h_kv=4)
     assert lib.hs2_backward_workspace_size(ctypes.byref(bad), 1, ctypes.byref(ctypes.c_size_t())) == 2
 

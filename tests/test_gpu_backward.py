@@ -72,7 +72,7 @@ def gpu_forward_outputs(lib, inp, idx, case, select="token"):
     return o_full, lse, o_sparse
 
 
-def run_backward(lib, case, idx_source="oracle", select="token"):
+def run_backward(lib, case, idx_source="oracle", select="token", deterministic=False):
     inp = make_inputs(case, device="cuda")
     grads = grad_inputs(case, device="cuda")
     host = {n: to_host(inp[n]) for n in ("q_full", "k", "v", "q_sparse")}
@@ -88,7 +88,7 @@ def run_backward(lib, case, idx_source="oracle", select="token"):
     L = case.n_sparse
     out = lib.block_backward(inp["q_full"], inp["q_sparse"] if L else None, inp["k"], inp["v"],
                              o_full, o_sparse, lse, idx if L else None, grads["do_full"],
-                             grads["do_sparse"] if L else None, **kw)
+                             grads["do_sparse"] if L else None, deterministic=deterministic, **kw)
     torch.cuda.synchronize()
     return inp, grads, host, idx, out
 
@@ -145,12 +145,54 @@ def test_backward_block_mode_indices(gpu_lib):
         check_grad(name, as_np(out[name]), ref[name], ref["mag"][name], "bf16")
 
 
-def test_backward_full_layer_deterministic(gpu_lib):
-    case = small("b_det", "bf16", 1, 300, 300, 8, 2, 128, 32, 16, L=0)
-    a = run_backward(gpu_lib, case)[4]
-    b = run_backward(gpu_lib, case)[4]
-    for name in ("dq_full", "dk", "dv"):
+@pytest.mark.parametrize("L", [0, 3], ids=["full_layer", "with_sparse_layers"])
+def test_backward_deterministic(gpu_lib, L):
+    """Two runs of the deterministic entry point give bit-identical
+    gradients. With sparse layers the K/V sums come from atomics landing in
+    any order; 1024 queries with 128-key windows make many of them add into
+    the same keys."""
+    case = small("b_det", "bf16", 1, 1024, 1024, 16, 2, 128, 128, 32, L=L)
+    a = run_backward(gpu_lib, case, deterministic=True)[4]
+    b = run_backward(gpu_lib, case, deterministic=True)[4]
+    for name in ("dq_full", "dk", "dv") + (("dq_sparse",) if L else ()):
         assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("case", [BWD_CASES[0], BWD_CASES[1], BWD_CASES[2], BWD_CASES[7]],
+                         ids=lambda c: c.name)
+def test_backward_deterministic_parity(gpu_lib, case):
+    """The deterministic entry point (fixed-point K/V sums) meets the same
+    per-element bound as the default one."""
+    say("case", case)
+    inp, grads, host, idx, out = run_backward(gpu_lib, case, deterministic=True)
+    L = case.n_sparse
+    ref = O.block_backward(host["q_full"], host["q_sparse"], host["k"], host["v"], to_host(idx),
+                           to_host(grads["do_full"]), to_host(grads["do_sparse"]), with_mag=True)
+    for name in ("dq_full", "dk", "dv") + (("dq_sparse",) if L else ()):
+        check_grad(name, as_np(out[name]), ref[name], ref["mag"][name], case.dtype)
+
+
+@pytest.mark.parametrize("mul", [1e-6, 1e3], ids=["tiny_grads", "large_grads"])
+def test_backward_gradient_magnitudes(gpu_lib, mul):
+    """The sparse layers' K/V sums are fixed point with a scale derived from
+    the inputs: gradients scaled by 1e-6 or 1e3 keep the same relative
+    accuracy (the oracle is linear in dO)."""
+    case = small("b_mag", "bf16", 1, 400, 900, 8, 2, 128, 96, 32, L=3)
+    inp = make_inputs(case, device="cuda")
+    grads = grad_inputs(case, device="cuda")
+    grads = {n: (g.float() * mul).to(g.dtype) for n, g in grads.items()}
+    host = {n: to_host(inp[n]) for n in ("q_full", "k", "v", "q_sparse")}
+    idx = random_index_rows(case, device="cuda")
+    kw = dict(top_k=case.top_k, window=case.window)
+    o_full, lse, o_sparse = gpu_forward_outputs(gpu_lib, inp, idx, case)
+    out = gpu_lib.block_backward(inp["q_full"], inp["q_sparse"], inp["k"], inp["v"], o_full,
+                                 o_sparse, lse, idx, grads["do_full"], grads["do_sparse"],
+                                 deterministic=True, **kw)
+    torch.cuda.synchronize()
+    ref = O.block_backward(host["q_full"], host["q_sparse"], host["k"], host["v"], to_host(idx),
+                           to_host(grads["do_full"]), to_host(grads["do_sparse"]), with_mag=True)
+    for name in ("dq_full", "dq_sparse", "dk", "dv"):
+        check_grad(name, as_np(out[name]), ref[name], ref["mag"][name], "bf16")
 
 
 def test_backward_32k_prefill_tail_and_invariants(gpu_lib):

@@ -61,8 +61,10 @@ struct BwdArgs {
   const void* q; const void* k; const void* v; const void* o; const void* dout;
   const float* lse;       // [B][h_q][n_q], natural log
   float* delta;           // [B][h_q][n_q]
-  const float* acc_k;     // [B][n_kv][h_kv][D] sparse-layer sums, or NULL
-  const float* acc_v;
+  const void* acc_k;      // [B][n_kv][h_kv][D] sparse-layer sums, or NULL
+  const void* acc_v;
+  bool acc_fixed;         // 64-bit fixed point times acc_scale[2] (K), [3] (V)
+  const float* acc_scale;
   void* dq; void* dk; void* dv;
   int B, n_q, n_kv, h_q, h_kv;
   int n_tiles;            // key tiles (dK/dV) or row tiles (dQ)
@@ -283,8 +285,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const int j = jw + kb * 16 + l16;
     if (j >= a.n_kv) continue;
     const size_t off = (((size_t)b * a.n_kv + j) * a.h_kv + g) * D;
-    store_t_row<T, D>(dkb + off, dk[kb], a.scale, a.acc_k ? a.acc_k + off : nullptr, grp);
-    store_t_row<T, D>(dvb + off, dv[kb], 1.f, a.acc_v ? a.acc_v + off : nullptr, grp);
+    const AccIn ak{a.acc_k, a.acc_fixed, a.acc_k && a.acc_fixed ? a.acc_scale[2] : 0.f};
+    const AccIn av{a.acc_v, a.acc_fixed, a.acc_v && a.acc_fixed ? a.acc_scale[3] : 0.f};
+    store_t_row<T, D>(dkb + off, dk[kb], a.scale, ak, off, grp);
+    store_t_row<T, D>(dvb + off, dv[kb], 1.f, av, off, grp);
   }
 }
 
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdArgs a) {
     const int r = r0 + wave * RBW * 16 + rb * 16 + l16;
     if (r >= R) continue;
     const int i = r / G, h = g * G + (r - (r / G) * G);
-    store_t_row<T, D>(dqb + (((size_t)b * a.n_q + i) * a.h_q + h) * D, acc[rb], a.scale, nullptr,
+    store_t_row<T, D>(dqb + (((size_t)b * a.n_q + i) * a.h_q + h) * D, acc[rb], a.scale, AccIn{}, 0,
                       grp);
   }
 }
@@ -451,6 +455,7 @@ BwdArgs args_of(const BwdPlan& p) {
   BwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout;
   a.lse = p.lse; a.delta = p.delta; a.acc_k = p.acc_k; a.acc_v = p.acc_v;
+  a.acc_fixed = p.acc_fixed; a.acc_scale = p.acc_scale;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
   a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;
   a.n_tiles = 0;

@@ -328,7 +328,8 @@ struct RowsArgs {
 struct DkdvArgs {
   const __bf16* q; const __bf16* dout; const __bf16* k; const __bf16* v;
   const __bf16* qt; const __bf16* dot; const float* rst;
-  const float* acc_k; const float* acc_v;
+  const void* acc_k; const void* acc_v;
+  bool acc_fixed; const float* acc_scale;
   __bf16* dk; __bf16* dv;
   int B, n_q, n_kv, h_q, h_kv, n_rt, n_kt;
   int q64, r64;                                       // 64 = q64 * G + r64
@@ -630,7 +631,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArg
   // lane holds dV^T (K waves) or dK^T (V waves) at d = 16 db + 4 grp + e
   // for key jw + 16 kb + l16
   const float mul = vwave ? a.scale : 1.f;
-  const float* add = vwave ? a.acc_k : a.acc_v;
+  const void* add = vwave ? a.acc_k : a.acc_v;
+  const float add_scale = add && a.acc_fixed ? a.acc_scale[vwave ? 2 : 3] : 0.f;
   __bf16* out = vwave ? a.dk : a.dv;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -640,7 +642,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArg
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       f32x4 xo = acc[kb][db] * mul;
-      if (add) xo += *reinterpret_cast<const f32x4*>(add + off + 16 * db);
+      if (add && a.acc_fixed) {
+        const long long* ap = static_cast<const long long*>(add) + off + 16 * db;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[e] += (float)((double)ap[e] * add_scale);
+      } else if (add) {
+        xo += *reinterpret_cast<const f32x4*>(static_cast<const float*>(add) + off + 16 * db);
+      }
       __attribute__((ext_vector_type(4))) __bf16 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (__bf16)xo[e];
@@ -679,7 +687,7 @@ hipError_t launch_bwd_dkdv_bf16(const BwdPlan& p, hipStream_t st) {
   a.qt = reinterpret_cast<const __bf16*>(p.qt);
   a.dot = reinterpret_cast<const __bf16*>(p.dot);
   a.rst = p.rst;
-  a.acc_k = p.acc_k; a.acc_v = p.acc_v;
+  a.acc_k = p.acc_k; a.acc_v = p.acc_v; a.acc_fixed = p.acc_fixed; a.acc_scale = p.acc_scale;
   a.dk = reinterpret_cast<__bf16*>(p.dk);
   a.dv = reinterpret_cast<__bf16*>(p.dv);
   a.B = p.s.batch; a.n_q = p.s.n_q; a.n_kv = p.s.n_kv; a.h_q = p.s.h_q; a.h_kv = p.s.h_kv;

@@ -637,10 +637,13 @@ namespace {
 
 // Backward workspace: Delta [B][h_q][n_q] floats; for bf16 / head_dim 128
 // the transposed K copy the dQ kernel reads ([B][h_kv][tile][d][64 keys]);
-// then (with sparse layers) the fp32 K and V gradient accumulators,
-// [B][n_kv][h_kv][head_dim] each.
+// then (with sparse layers) the K and V gradient accumulators,
+// [B][n_kv][h_kv][head_dim] each, sized for 64-bit fixed point so that one
+// workspace serves both backward entry points (fp32 sums use the first
+// half), and the fixed-point bounds and scales (16 floats).
 struct BwdLayout {
   size_t delta = 0, kt = 0, kt_bytes = 0, acc_k = 0, acc_v = 0, acc_elems = 0, total = 0;
+  size_t bounds = 0;
   size_t qt = 0, dot = 0, rst = 0, rows_tiles = 0;
 };
 
@@ -665,9 +668,11 @@ BwdLayout bwd_layout(const hs2_problem& p, int n_sparse) {
   if (n_sparse > 0) {
     L.acc_elems = (size_t)p.batch * p.n_kv * p.h_kv * p.head_dim;
     L.acc_k = off;
-    off += align_up(L.acc_elems * sizeof(float));
+    off += align_up(L.acc_elems * sizeof(long long));
     L.acc_v = off;
-    off += align_up(L.acc_elems * sizeof(float));
+    off += align_up(L.acc_elems * sizeof(long long));
+    L.bounds = off;
+    off += align_up(16 * sizeof(float));
   }
   L.total = off;
   return L;
@@ -687,12 +692,18 @@ hs2_status hs2_backward_workspace_size(const hs2_problem* p, int32_t n_sparse_la
   return HS2_OK;
 }
 
-hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
-                              const void* q_sparse, const void* k, const void* v,
-                              const void* o_full, const void* o_sparse, const float* lse,
-                              const int32_t* idx, const void* do_full, const void* do_sparse,
-                              void* dq_full, void* dq_sparse, void* dk, void* dv,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both backward entry points: `fixed` selects the sparse layers' 64-bit
+// fixed-point K/V sums (deterministic) over fp32 atomics.
+hs2_status block_backward(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                          const void* q_sparse, const void* k, const void* v,
+                          const void* o_full, const void* o_sparse, const float* lse,
+                          const int32_t* idx, const void* do_full, const void* do_sparse,
+                          void* dq_full, void* dq_sparse, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream, bool fixed) {
   g_err.clear();
   HS2_TRY(check_problem(p));
   if (n_sparse_layers < 0) return fail(HS2_ERR_SHAPE, "n_sparse_layers %d", n_sparse_layers);
@@ -719,14 +730,16 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
 
   const hipStream_t st = (hipStream_t)stream;
   const float scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  float* acc_k = sparse ? fptr(workspace, L.acc_k) : nullptr;
-  float* acc_v = sparse ? fptr(workspace, L.acc_v) : nullptr;
+  void* acc_k = sparse ? (char*)workspace + L.acc_k : nullptr;
+  void* acc_v = sparse ? (char*)workspace + L.acc_v : nullptr;
+  float* bounds = sparse ? fptr(workspace, L.bounds) : nullptr;   // 4 maxima, then 4 scales
   hs2::BwdPlan bp;
   bp.s = shape_of(*p);
   bp.scale = p->softmax_scale;
   bp.q = q_full; bp.k = k; bp.v = v; bp.o = o_full; bp.dout = do_full;
   bp.lse = lse; bp.delta = fptr(workspace, L.delta);
   bp.acc_k = acc_k; bp.acc_v = acc_v;
+  bp.acc_fixed = sparse && fixed; bp.acc_scale = sparse ? bounds + 4 : nullptr;
   bp.dq = dq_full; bp.dk = dk; bp.dv = dv;
   {
     PassTimer t(st, HS2_PASS_BWD_PREP);
@@ -747,8 +760,24 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
       HIP_TRY(hs2::launch_bwd_rows_layout(bp, st), "row layout");
     }
     if (sparse) {
-      HIP_TRY(hs2::launch_zero_f32(acc_k, L.acc_elems, st), "zero accumulators");
-      HIP_TRY(hs2::launch_zero_f32(acc_v, L.acc_elems, st), "zero accumulators");
+      const size_t words = fixed ? 2 * L.acc_elems : L.acc_elems;
+      HIP_TRY(hs2::launch_zero_f32(static_cast<float*>(acc_k), words, st), "zero accumulators");
+      HIP_TRY(hs2::launch_zero_f32(static_cast<float*>(acc_v), words, st), "zero accumulators");
+      if (fixed) {
+        // fixed-point scales of the accumulators, from every sparse layer
+        HIP_TRY(hs2::launch_zero_f32(bounds, 16, st), "zero bounds");
+        hs2::SparseBwdBoundPlan bb;
+        bb.q = q_sparse; bb.dout = do_sparse; bb.v = v;
+        bb.q_rows = (size_t)n_sparse_layers * p->batch * p->n_q * p->h_q;
+        bb.v_rows = (size_t)p->batch * p->n_kv * p->h_kv;
+        bb.head_dim = p->head_dim;
+        bb.bf16 = p->dtype == HS2_BF16;
+        bb.rows = (double)n_sparse_layers * p->n_q * (p->h_q / p->h_kv);
+        bb.scale = p->softmax_scale;
+        bb.maxima = reinterpret_cast<unsigned*>(bounds);
+        bb.scales = bounds + 4;
+        HIP_TRY(hs2::launch_sparse_bwd_bounds(bb, st), "accumulator bounds");
+      }
     }
   }
   if (sparse) {
@@ -765,6 +794,7 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
       sp.dout = (const char*)do_sparse + l0 * layer_bytes;
       sp.dq = (char*)dq_sparse + l0 * layer_bytes;
       sp.k = k; sp.v = v; sp.idx = idx; sp.acc_k = acc_k; sp.acc_v = acc_v;
+      sp.fixed = fixed; sp.acc_scale = bounds + 4;
       sp.batch = p->batch; sp.n_q = p->n_q; sp.n_kv = p->n_kv; sp.h_q = p->h_q;
       sp.h_kv = p->h_kv; sp.head_dim = p->head_dim; sp.width = index_width(*p);
       sp.scale = p->softmax_scale; sp.scale_log2 = scale_log2;
@@ -781,6 +811,31 @@ hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, con
     HIP_TRY(hs2::launch_bwd_dq(bp, st), "full-layer dQ");
   }
   return HS2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs2_status hs2_block_backward(const hs2_problem* p, int32_t n_sparse_layers, const void* q_full,
+                              const void* q_sparse, const void* k, const void* v,
+                              const void* o_full, const void* o_sparse, const float* lse,
+                              const int32_t* idx, const void* do_full, const void* do_sparse,
+                              void* dq_full, void* dq_sparse, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return block_backward(p, n_sparse_layers, q_full, q_sparse, k, v, o_full, o_sparse, lse, idx,
+                        do_full, do_sparse, dq_full, dq_sparse, dk, dv, workspace,
+                        workspace_bytes, stream, false);
+}
+
+hs2_status hs2_block_backward_deterministic(
+    const hs2_problem* p, int32_t n_sparse_layers, const void* q_full, const void* q_sparse,
+    const void* k, const void* v, const void* o_full, const void* o_sparse, const float* lse,
+    const int32_t* idx, const void* do_full, const void* do_sparse, void* dq_full,
+    void* dq_sparse, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_backward(p, n_sparse_layers, q_full, q_sparse, k, v, o_full, o_sparse, lse, idx,
+                        do_full, do_sparse, dq_full, dq_sparse, dk, dv, workspace,
+                        workspace_bytes, stream, true);
 }
 
 }  // extern "C"

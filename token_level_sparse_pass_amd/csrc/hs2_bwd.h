@@ -78,11 +78,23 @@ __device__ __forceinline__ void mma_t(f32x4 (&acc)[D / 16], const TRows<T, D>& x
   }
 }
 
+// The sparse layers' K/V sums that the full layer's dK/dV kernels add in:
+// none, fp32, or 64-bit fixed point times `scale`.
+struct AccIn {
+  const void* base = nullptr;
+  bool fixed = false;
+  float scale = 0.f;
+  __device__ __forceinline__ float at(size_t i) const {
+    return fixed ? (float)((double)static_cast<const long long*>(base)[i] * scale)
+                 : static_cast<const float*>(base)[i];
+  }
+};
+
 // Store a transposed accumulator set (d = DV*(4*grp + e) + db) as row `dst`,
-// times `mul`, plus the fp32 row `add` (nullable).
+// times `mul`, plus the row of `add` that starts at element add_off (if any).
 template <typename T, int D>
 __device__ __forceinline__ void store_t_row(T* dst, const f32x4 (&acc)[D / 16], float mul,
-                                            const float* add, int grp) {
+                                            const AccIn& add, size_t add_off, int grp) {
   constexpr int DV = D / 16;
   T outv[4 * DV];
 #pragma unroll
@@ -90,7 +102,7 @@ __device__ __forceinline__ void store_t_row(T* dst, const f32x4 (&acc)[D / 16], 
 #pragma unroll
     for (int db = 0; db < DV; ++db) {
       float x = acc[db][e] * mul;
-      if (add) x += add[(4 * grp + e) * DV + db];
+      if (add.base) x += add.at(add_off + (4 * grp + e) * DV + db);
       outv[e * DV + db] = to_elem<T>(x);
     }
   constexpr int BYTES = 4 * DV * sizeof(T);

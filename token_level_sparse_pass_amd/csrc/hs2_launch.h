@@ -231,15 +231,19 @@ hipError_t launch_kv_bridge(const BridgePlan& p, hipStream_t st);
 // Backward pass of the full layer: Delta = rowsum(dO * O) into `delta`
 // ([batch][h_q][n_q] floats), then dK/dV and dQ, in that order on a stream. lse is the
 // forward's natural-log LSE. acc_k / acc_v (nullable) hold the sparse
-// layers' fp32 K/V gradient sums in the K/V layout; they are added into dK,
-// dV, so launch_sparse_bwd must run first on the same stream.
+// layers' K/V gradient sums in the K/V layout, fp32, or with acc_fixed 64-bit
+// fixed point to be multiplied by acc_scale[2] (K) and acc_scale[3] (V);
+// they are added into dK, dV, so launch_sparse_bwd must run first on the
+// same stream.
 struct BwdPlan {
   Shape s;
   float scale;                         // softmax scale
   const void* q; const void* k; const void* v; const void* o; const void* dout;
   const float* lse;
   float* delta;
-  const float* acc_k; const float* acc_v;
+  const void* acc_k; const void* acc_v;
+  bool acc_fixed = false;
+  const float* acc_scale = nullptr;
   void* dq; void* dk; void* dv;
   // bf16 / head_dim 128: K transposed to [batch][h_kv][tile][head_dim][64]
   // (as launch_v_transpose lays out V), read by the dQ kernel; NULL selects
@@ -264,18 +268,43 @@ hipError_t launch_bwd_dq(const BwdPlan& p, hipStream_t st);     // after the del
 
 // Backward of `layers` sparse layers (layers * h_q / h_kv <= 64) over a
 // fixed index set: writes dq and ADDS the K/V gradients into acc_k / acc_v
-// (fp32, [batch][n_kv][h_kv][head_dim], zeroed by the caller) with atomics.
+// ([batch][n_kv][h_kv][head_dim], zeroed by the caller) with atomics: fp32
+// adds, or with `fixed` 64-bit integer adds of round(x * acc_scale[0]) (K)
+// and round(x * acc_scale[1]) (V), whose sums do not depend on the order in
+// which the adds land.
 struct SparseBwdPlan {
   const void* q; const void* o; const void* dout;
   const void* k; const void* v;
   const int32_t* idx;
   void* dq;
-  float* acc_k; float* acc_v;
+  void* acc_k; void* acc_v;
+  bool fixed = false;
+  const float* acc_scale = nullptr;
   int layers, batch, n_q, n_kv, h_q, h_kv, head_dim, width;
   float scale, scale_log2;
   bool bf16;
 };
 hipError_t launch_sparse_bwd(const SparseBwdPlan& p, hipStream_t st);
+
+// The fixed-point scales of the sparse layers' K/V sums, from bounds on what
+// any sum can reach (every row's probabilities add up to one):
+//   |dV| <= R max|dO|,   |dK| <= scale * 2 R max||dO|| max||V|| max|Q|,
+// R = layers * n_q * h_q / h_kv rows per (sequence, KV head), norms over
+// head-dim rows. Reads q / dout ([q_rows][head_dim], every sparse layer) and
+// v ([v_rows][head_dim]) once; writes 4 maxima into `maxima` (zeroed by the
+// caller) and scales[0..3] = 2^F_K, 2^F_V, 2^-F_K, 2^-F_V with the largest F
+// that keeps every scaled sum below 2^61.
+struct SparseBwdBoundPlan {
+  const void* q; const void* dout; const void* v;
+  size_t q_rows, v_rows;
+  int head_dim;
+  bool bf16;
+  double rows;                         // R
+  float scale;                         // softmax scale
+  unsigned* maxima;
+  float* scales;
+};
+hipError_t launch_sparse_bwd_bounds(const SparseBwdBoundPlan& p, hipStream_t st);
 
 // p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned)
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t st);

@@ -15,9 +15,15 @@
 // and put P^T and dS^T into LDS, while contraction waves 4..7 take the
 // previous tile and contract over the rows:
 //   dK_sel = scale dS^T Q,  dV_sel = P^T dO      (32 keys x D each)
-// adding the results to fp32 accumulators [B][n_kv][h_kv][D] with atomics:
-// a key appears in the index sets of many queries, and the accumulators are
-// folded into dK and dV by the full layer's dK/dV kernel. Keeping the
+// adding the results to accumulators [B][n_kv][h_kv][D] with atomics: a key
+// appears in the index sets of many queries, and the accumulators are
+// folded into dK and dV by the full layer's dK/dV kernel. The accumulators
+// are fp32 (fastest; the order in which the adds land changes the last
+// bits), or, for the deterministic entry point, 64-bit fixed point: each
+// addend is rounded to a multiple of 2^-F, F from a bound on what any sum
+// can reach (launch_sparse_bwd_bounds), and integer sums do not depend on
+// the order of the adds. Their resolution (2^-39 for dV and 2^-34 for dK at
+// the 32K prefill) is far finer than fp32 sums keep. Keeping the
 // atomics on waves that issue no loads matters: a wave's vector memory
 // operations complete in order, so a load issued after a burst of atomics
 // would wait for all of them. Each atomic instruction covers four keys x 16
@@ -29,6 +35,9 @@
 #include "hs2_bwd.h"
 #include "hs2_device.h"
 #include "hs2_launch.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace hs2 {
 
@@ -44,8 +53,9 @@ struct SparseBwdArgs {
   const void* v;
   const int32_t* idx;   // [B, n_q, W]
   void* dq;             // [L, B, n_q, h_q, D]
-  float* acc_k;         // [B, n_kv, h_kv, D]
-  float* acc_v;
+  void* acc_k;          // [B, n_kv, h_kv, D]: fp32, or 64-bit fixed point
+  void* acc_v;
+  const float* acc_scale;   // fixed point: [0] = 2^F_K, [1] = 2^F_V
   int L, B, n_q, n_kv, h_q, h_kv, W;
   float scale, scale_log2;
 };
@@ -58,8 +68,9 @@ __device__ __forceinline__ int slot_pos(int rr) {
 
 }  // namespace
 
-template <typename T, int D>
+template <typename T, int D, bool FIXED>
 __global__ __launch_bounds__(512) void sparse_bwd_kernel(SparseBwdArgs a) {
+  using Acc = std::conditional_t<FIXED, long long, float>;
   using OP = Op<T, D>;
   constexpr int DB = D / 16;                 // 16-wide head-dim blocks
   constexpr int DBW = DB / 2;                // per contraction wave
@@ -220,8 +231,11 @@ __global__ __launch_bounds__(512) void sparse_bwd_kernel(SparseBwdArgs a) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) dq[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float* accb = (for_dk ? a.acc_k : a.acc_v) + (size_t)b * a.n_kv * a.h_kv * D + (size_t)g * D;
+  Acc* accb = static_cast<Acc*>(for_dk ? a.acc_k : a.acc_v) + (size_t)b * a.n_kv * a.h_kv * D +
+              (size_t)g * D;
   const float mul = for_dk ? a.scale : 1.f;
+  double fix = 0.0;
+  if constexpr (FIXED) fix = a.acc_scale[for_dk ? 0 : 1];
 
   // Software pipeline over the tiles: in step t the row waves work on tile t
   // (buffer t & 1) while the contraction waves contract tile t - 1 (the
@@ -314,10 +328,17 @@ __global__ __launch_bounds__(512) void sparse_bwd_kernel(SparseBwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int key = s_key[buf][kb * 16 + 4 * grp + e];
           if (key < 0) continue;
-          float* dst = accb + (size_t)key * kstride + l16;
+          Acc* dst = accb + (size_t)key * kstride + l16;
 #pragma unroll
-          for (int bk = 0; bk < DBW; ++bk)
-            unsafeAtomicAdd(dst + 16 * (dbk0 + bk), c[bk][e] * mul);
+          for (int bk = 0; bk < DBW; ++bk) {
+            if constexpr (FIXED) {
+              const long long q = (long long)rint((double)(c[bk][e] * mul) * fix);
+              atomicAdd(reinterpret_cast<unsigned long long*>(dst + 16 * (dbk0 + bk)),
+                        (unsigned long long)q);
+            } else {
+              unsafeAtomicAdd(dst + 16 * (dbk0 + bk), c[bk][e] * mul);
+            }
+          }
         }
       }
     }
@@ -326,16 +347,17 @@ __global__ __launch_bounds__(512) void sparse_bwd_kernel(SparseBwdArgs a) {
 
   if (row_ok) {
     T* dst = reinterpret_cast<T*>(a.dq) + row_off(my_row);
-    store_t_row<T, D>(dst, dq, a.scale, nullptr, grp);
+    store_t_row<T, D>(dst, dq, a.scale, AccIn{}, 0, grp);
   }
 }
 
 namespace {
 
 template <typename T, int D>
-hipError_t launch_sparse_bwd_t(const SparseBwdArgs& a, hipStream_t st) {
+hipError_t launch_sparse_bwd_t(const SparseBwdArgs& a, bool fixed, hipStream_t st) {
   const dim3 grid((unsigned)((size_t)a.B * a.n_q * a.h_kv));
-  hipLaunchKernelGGL((sparse_bwd_kernel<T, D>), grid, dim3(512), 0, st, a);
+  if (fixed) hipLaunchKernelGGL((sparse_bwd_kernel<T, D, true>), grid, dim3(512), 0, st, a);
+  else hipLaunchKernelGGL((sparse_bwd_kernel<T, D, false>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
@@ -344,16 +366,124 @@ hipError_t launch_sparse_bwd_t(const SparseBwdArgs& a, hipStream_t st) {
 hipError_t launch_sparse_bwd(const SparseBwdPlan& p, hipStream_t st) {
   SparseBwdArgs a;
   a.q = p.q; a.o = p.o; a.dout = p.dout; a.k = p.k; a.v = p.v; a.idx = p.idx;
-  a.dq = p.dq; a.acc_k = p.acc_k; a.acc_v = p.acc_v;
+  a.dq = p.dq; a.acc_k = p.acc_k; a.acc_v = p.acc_v; a.acc_scale = p.acc_scale;
+  if (p.fixed && !p.acc_scale) return hipErrorInvalidValue;
   a.L = p.layers; a.B = p.batch; a.n_q = p.n_q; a.n_kv = p.n_kv; a.h_q = p.h_q;
   a.h_kv = p.h_kv; a.W = p.width; a.scale = p.scale; a.scale_log2 = p.scale_log2;
   if (p.layers * (p.h_q / p.h_kv) > MAX_ROWS) return hipErrorInvalidValue;
   if (p.bf16) {
-    if (p.head_dim == 128) return launch_sparse_bwd_t<__bf16, 128>(a, st);
-    if (p.head_dim == 64) return launch_sparse_bwd_t<__bf16, 64>(a, st);
+    if (p.head_dim == 128) return launch_sparse_bwd_t<__bf16, 128>(a, p.fixed, st);
+    if (p.head_dim == 64) return launch_sparse_bwd_t<__bf16, 64>(a, p.fixed, st);
   } else {
-    if (p.head_dim == 128) return launch_sparse_bwd_t<float, 128>(a, st);
-    if (p.head_dim == 64) return launch_sparse_bwd_t<float, 64>(a, st);
+    if (p.head_dim == 128) return launch_sparse_bwd_t<float, 128>(a, p.fixed, st);
+    if (p.head_dim == 64) return launch_sparse_bwd_t<float, 64>(a, p.fixed, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// bounds for the fixed-point accumulators
+// ---------------------------------------------------------------------------
+namespace {
+
+// Largest |Q| and |dO| entry and largest squared row norm of dO and of V.
+// Sixteen lanes share a head-dim row (coalesced loads); non-negative floats
+// order like their bit patterns, so integer atomicMax combines the waves.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_bound_kernel(const T* q, const T* dout, size_t q_rows,
+                                                         const T* v, size_t v_rows, unsigned* mx) {
+  constexpr int E = D / 16;                           // elements per lane of a row
+  const int sub = threadIdx.x & 15;
+  const size_t n = q_rows + v_rows;
+  const size_t step = ((size_t)gridDim.x * blockDim.x) / 16;
+  float mq = 0.f, mdo = 0.f, ndo = 0.f, nv = 0.f;
+  for (size_t r = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 16; r < n; r += step) {
+    float s = 0.f;
+    if (r < q_rows) {
+      const T* qr = q + r * D + sub * E;
+      const T* dr = dout + r * D + sub * E;
+#pragma unroll
+      for (int x = 0; x < E; ++x) {
+        const float b = to_f32(dr[x]);
+        mq = fmaxf(mq, fabsf(to_f32(qr[x])));
+        mdo = fmaxf(mdo, fabsf(b));
+        s = fmaf(b, b, s);
+      }
+    } else {
+      const T* vr = v + (r - q_rows) * D + sub * E;
+#pragma unroll
+      for (int x = 0; x < E; ++x) {
+        const float b = to_f32(vr[x]);
+        s = fmaf(b, b, s);
+      }
+    }
+    // the row's sum of squares over its sixteen lanes (one row per group)
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (r < q_rows) ndo = fmaxf(ndo, s);
+    else nv = fmaxf(nv, s);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, m, 64));
+    mdo = fmaxf(mdo, __shfl_xor(mdo, m, 64));
+    ndo = fmaxf(ndo, __shfl_xor(ndo, m, 64));
+    nv = fmaxf(nv, __shfl_xor(nv, m, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&mx[0], __float_as_uint(mq));
+    atomicMax(&mx[1], __float_as_uint(mdo));
+    atomicMax(&mx[2], __float_as_uint(ndo));
+    atomicMax(&mx[3], __float_as_uint(nv));
+  }
+}
+
+// b = m 2^e with m < 1, so addends bounded by b, summed, stay below 2^61
+// once scaled by 2^(61 - e); the rounding of each addend adds at most half a
+// unit, far inside the two spare bits. Clamped so that 2^F and 2^-F stay
+// finite in fp32 (an all-zero bound takes the finest scale).
+__device__ int fixed_exponent(double b) {
+  if (!(b > 0.0)) return 100;
+  int e = 0;
+  frexp(b, &e);
+  return max(-64, min(100, 61 - e));
+}
+
+__global__ void bwd_scale_kernel(const unsigned* mx, float* scales, double rows, float softmax_scale) {
+  const double mq = __uint_as_float(mx[0]), mdo = __uint_as_float(mx[1]);
+  const double ndo = sqrt((double)__uint_as_float(mx[2])), nv = sqrt((double)__uint_as_float(mx[3]));
+  // |dS| = P |dP - Delta| <= 2 P ||dO|| ||V||, and a key's P summed over all
+  // rows of its KV head is at most the row count
+  const int fk = fixed_exponent((double)softmax_scale * 2.0 * rows * ndo * nv * mq);
+  const int fv = fixed_exponent(rows * mdo);
+  scales[0] = ldexpf(1.f, fk);
+  scales[1] = ldexpf(1.f, fv);
+  scales[2] = ldexpf(1.f, -fk);
+  scales[3] = ldexpf(1.f, -fv);
+}
+
+template <typename T, int D>
+hipError_t launch_bounds_t(const SparseBwdBoundPlan& p, hipStream_t st) {
+  const size_t n = p.q_rows + p.v_rows;
+  const unsigned blocks = (unsigned)std::max<size_t>(1, std::min<size_t>((n * 16 + 255) / 256, 4096));
+  hipLaunchKernelGGL((bwd_bound_kernel<T, D>), dim3(blocks), dim3(256), 0, st,
+                     reinterpret_cast<const T*>(p.q), reinterpret_cast<const T*>(p.dout), p.q_rows,
+                     reinterpret_cast<const T*>(p.v), p.v_rows, p.maxima);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scale_kernel, dim3(1), dim3(1), 0, st, p.maxima, p.scales, p.rows, p.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_bwd_bounds(const SparseBwdBoundPlan& p, hipStream_t st) {
+  if (p.bf16) {
+    if (p.head_dim == 128) return launch_bounds_t<__bf16, 128>(p, st);
+    if (p.head_dim == 64) return launch_bounds_t<__bf16, 64>(p, st);
+  } else {
+    if (p.head_dim == 128) return launch_bounds_t<float, 128>(p, st);
+    if (p.head_dim == 64) return launch_bounds_t<float, 64>(p, st);
   }
   return hipErrorInvalidValue;
 }

@@ -96,6 +96,8 @@ def load(path: str = LIB_PATH):
     lib.hs2_backward_workspace_size.restype = i32
     lib.hs2_block_backward.argtypes = [P, i32] + [vp] * 14 + [vp, sz, vp]
     lib.hs2_block_backward.restype = i32
+    lib.hs2_block_backward_deterministic.argtypes = [P, i32] + [vp] * 14 + [vp, sz, vp]
+    lib.hs2_block_backward_deterministic.restype = i32
     lib.hs2_status_string.argtypes = [i32]
     lib.hs2_status_string.restype = ctypes.c_char_p
     lib.hs2_last_error.restype = ctypes.c_char_p
@@ -438,10 +440,11 @@ def backward_workspace_size(p: Problem, n_sparse_layers: int) -> int:
 
 
 def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, do_sparse, *,
-                   workspace=None, out=None, **kw):
+                   workspace=None, out=None, deterministic=False, **kw):
     """Backward of the whole block with the index sets held fixed. Takes the
     forward's inputs and outputs (lse: natural log, required) and the output
-    gradients; returns dict(dq_full, dq_sparse, dk, dv)."""
+    gradients; returns dict(dq_full, dq_sparse, dk, dv). deterministic=True
+    calls hs2_block_backward_deterministic (bit-reproducible K/V sums)."""
     lib = load()
     dt = q_full.dtype
     if q_full.dim() != 4 or k.dim() != 4:
@@ -470,7 +473,8 @@ def block_backward(q_full, q_sparse, k, v, o_full, o_sparse, lse, idx, do_full, 
     if workspace is None:
         workspace = torch.empty(max(16, backward_workspace_size(p, L)), dtype=torch.uint8,
                                 device=q_full.device)
-    _check(lib.hs2_block_backward(
+    fn = lib.hs2_block_backward_deterministic if deterministic else lib.hs2_block_backward
+    _check(fn(
         ctypes.byref(p), L, _ptr(q_full), _ptr(q_sparse if L else None), _ptr(k), _ptr(v),
         _ptr(o_full), _ptr(o_sparse if L else None), _ptr(lse), _ptr(idx if L else None),
         _ptr(do_full), _ptr(do_sparse if L else None), _ptr(out["dq_full"]),
