@@ -81,8 +81,11 @@ def source_sha(paths):
 
 _CSRC = "token_level_sparse_pass_amd/csrc/"
 KERNEL_SOURCES = {
-    "full_attention": [_CSRC + "attn_fwd_bf16.hip", _CSRC + "attn_fwd.hip", _CSRC + "hs2_device.h"],
-    "score": [_CSRC + "score_bf16.hip", _CSRC + "score.hip", _CSRC + "hs2_device.h"],
+    "full_attention": [_CSRC + "attn_fwd_bf16.hip", _CSRC + "attn_fwd.hip",
+                       _CSRC + "attn_decode_bf16.hip", _CSRC + "hs2_device.h"],
+    # decode's score step (decode_score_kernel) lives in attn_fwd.hip
+    "score": [_CSRC + "score_bf16.hip", _CSRC + "score.hip", _CSRC + "attn_fwd.hip",
+              _CSRC + "hs2_device.h"],
     "select": [_CSRC + "select.hip"],
     "sparse_attention": [_CSRC + "sparse_attn_bf16.hip", _CSRC + "sparse_attn.hip",
                          _CSRC + "hs2_device.h"],

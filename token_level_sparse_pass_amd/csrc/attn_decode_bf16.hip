@@ -119,10 +119,14 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(Dec2Args a) {
     for (int j = 0; j < TK / 4; ++j) {
       const int key = j * 4 + grp;
       const size_t row = (row0 + (size_t)(min(j0 + key, k_end - 1) - j0)) * kvs;
+      // K and V are read once: non-temporal (nt) loads, which leave the
+      // caches to the logits this kernel writes and the score step reads
+      // back (pass 1 3.67 -> 3.53 ms, score step 0.185 -> 0.173 ms at the
+      // 64 x 128K decode)
       __builtin_amdgcn_global_load_lds(kseq + row + ((l16 ^ kswz(key)) << 3),
-                                       (lds_void*)(base + j * 1024), 16, 0, 0);
+                                       (lds_void*)(base + j * 1024), 16, 0, 2);
       __builtin_amdgcn_global_load_lds(vseq + row + (l16 << 3),
-                                       (lds_void*)(base + HALF + j * 1024), 16, 0, 0);
+                                       (lds_void*)(base + HALF + j * 1024), 16, 0, 2);
     }
   };
 

@@ -569,7 +569,9 @@ __global__ __launch_bounds__(256) void decode_score_kernel(DecodeScorePlan a) {
   const float* lg = a.logits + (size_t)b * a.h_q * a.logits_stride + j;
   float s = 0.f;
   for (int h = 0; h < a.h_q; ++h)
-    s = fmaf(fast_exp2(fmaf(lg[(size_t)h * a.logits_stride], a.c, -sh[h])), sh[a.h_q + h], s);
+    // each logit is read once: non-temporal loads
+    s = fmaf(fast_exp2(fmaf(__builtin_nontemporal_load(lg + (size_t)h * a.logits_stride), a.c, -sh[h])),
+             sh[a.h_q + h], s);
   a.scores[(size_t)b * a.score_stride + j] = s;
 }
 
