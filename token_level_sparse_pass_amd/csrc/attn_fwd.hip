@@ -481,20 +481,41 @@ __global__ __launch_bounds__(256) void attn_fwd_decode_kernel(DecArgs a) {
 }
 
 template <typename T, int D>
-__global__ void decode_combine_kernel(const float* part, int n_split, T* o, float* stats,
-                                      float* lse, size_t plane) {
-  // one work-group per (b, head); thread d owns output element d
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* part, int n_split, T* o,
+                                                           float* stats, float* lse, size_t plane) {
+  // one work-group per (b, head); thread d owns output element d. The
+  // splits' maxima, weights 2^(m_s - M) and row sums are read by all
+  // threads together into LDS, a chunk of splits at a time, so each thread's
+  // loop over splits only loads its own element of every split (loads that
+  // do not depend on one another); the sums still run in split order.
+  constexpr int CH = 512;
+  __shared__ float w_sh[CH], l_sh[CH], red[D / 64];
   const size_t bh = blockIdx.x;
   const float* rec = part + bh * n_split * (D + 2);
-  float M = -1e30f;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, rec[(size_t)s * (D + 2)]);
-  float L = 0.f, acc = 0.f;
   const int d = threadIdx.x;
-  for (int s = 0; s < n_split; ++s) {
-    const float* r = rec + (size_t)s * (D + 2);
-    const float w = fast_exp2(r[0] - M);
-    L += r[1] * w;
-    acc += r[2 + d] * w;
+  float M = -1e30f;
+  for (int s = d; s < n_split; s += D) M = fmaxf(M, rec[(size_t)s * (D + 2)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if ((d & 63) == 0) red[d >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) M = fmaxf(M, red[i]);
+  float L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += CH) {
+    const int n = min(CH, n_split - s0);
+    __syncthreads();                              // the previous chunk's weights are used
+    for (int s = d; s < n; s += D) {
+      const float* r = rec + (size_t)(s0 + s) * (D + 2);
+      w_sh[s] = fast_exp2(r[0] - M);
+      l_sh[s] = r[1];
+    }
+    __syncthreads();
+    const float* r = rec + (size_t)s0 * (D + 2) + 2 + d;
+#pragma unroll 8
+    for (int s = 0; s < n; ++s) acc += r[(size_t)s * (D + 2)] * w_sh[s];
+    // every thread forms the same L from the broadcast LDS values
+    for (int s = 0; s < n; ++s) L += l_sh[s] * w_sh[s];
   }
   o[bh * D + d] = to_elem<T>(acc / L);
   if (d == 0) {
