@@ -67,8 +67,17 @@ constexpr float LN2 = 0.69314718055994530942f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// chunk swizzles: K tile rows are 256 B (16 chunks), Vt rows 128 B (8 chunks)
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+// chunk swizzles: K tile rows are 256 B (16 chunks), Vt rows 128 B (8 chunks).
+// A 16-byte read of 64 lanes is served 32 lanes at a time from 128 banks
+// (512 B), so two rows of equal parity share banks: the K swizzle makes the
+// 32 chunks that a half wave reads from 16 rows (lane groups 0-1 or 2-3,
+// one row per l16) land on distinct bank groups. It is built from row bits
+// 0, 1, 3 and 4 only (the bits l16 sets in tile_key), with row bits 0 and 3
+// in swapped places: for fixed row parity, chunks 4 grp + u and
+// 4 (grp + 1) + u then never meet (halves the LDS cycles of the K reads).
+__device__ __forceinline__ int kswz(int row) {
+  return ((row >> 3) & 1) | (row & 2) | ((row & 1) << 2) | (((row >> 4) & 1) << 3);
+}
 __device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
 
 // key held in MFMA row m of key block kb: lane group q of the P^T operand
@@ -291,12 +300,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
 
   // per-lane LDS offsets that do not change between tiles. The K row of
   // key block kb held by lane (grp, l16) is tile_key(kb, l16), whose swizzle
-  // kswz() is l16 for every kb, so the block moves the row by a constant
+  // kswz() does not depend on kb, so the block moves the row by a constant
   // (KB_OFF[kb], an immediate of the read); likewise the Vt row of head-dim
   // block db is db * 16 + l16, whose swizzle does not depend on db.
   int koff[4];                                          // [unit] byte offset, key block 0
 #pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = tile_key(0, l16) * 256 + (((4 * grp + u) ^ l16) << 4);
+  for (int u = 0; u < 4; ++u) koff[u] = tile_key(0, l16) * 256 + (((4 * grp + u) ^ kswz(tile_key(0, l16))) << 4);
   int voff[2];                                          // [step] byte offset, head-dim block 0
 #pragma unroll
   for (int st = 0; st < 2; ++st) voff[st] = KT_BYTES + l16 * 128 + (((4 * st + grp) ^ vswz(l16)) << 4);

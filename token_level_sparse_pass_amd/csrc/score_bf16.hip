@@ -51,8 +51,15 @@ constexpr int KT_BLOCK = 32;                  // key tiles per scheduling block
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int qswz(int row) { return row & 15; }
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
+// Q and K rows are 256 B (16 chunks). A 16-byte read of 64 lanes is served
+// 32 lanes at a time from 128 banks (512 B), so rows of equal parity share
+// banks; with bits 0 and 2 of the row's low four bits swapped in the
+// swizzle, the 32 chunks a half wave reads (lane groups 0-1 or 2-3, one row
+// per l16) land on distinct bank groups (the plain low four bits put chunks
+// 4 grp + u and 4 (grp + 1) + u of rows l16 and l16 ^ 4 on the same banks).
+__device__ __forceinline__ int row_swz(int row) { return (row & 10) | ((row & 1) << 2) | ((row >> 2) & 1); }
+__device__ __forceinline__ int qswz(int row) { return row_swz(row); }
+__device__ __forceinline__ int kswz(int row) { return row_swz(row); }
 
 struct Score2Args {
   const __bf16* q; const __bf16* k;
@@ -149,8 +156,8 @@ __global__ __launch_bounds__(512, 2) void score_bf16_kernel(Score2Args a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sacc[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Q rows wq * 64 + 16 qb + l16 all have swizzle l16 (the row's low four
-  // bits), so query block qb sits a constant 16 rows (4 KB) past block 0 and
+  // Q rows wq * 64 + 16 qb + l16 all have the swizzle of l16 (it reads only
+  // the row's low four bits), so query block qb sits a constant 16 rows (4 KB) past block 0 and
   // one offset per unit serves all four blocks; likewise the statistics
   const int srow0 = wq * 64 + l16;
   int qoff[4];                                        // [unit] byte offset in Q tile, block 0
