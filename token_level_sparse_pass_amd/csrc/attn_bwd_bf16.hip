@@ -40,8 +40,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// chunk swizzles: K and V tile rows are 256 B (16 chunks), Kt rows 128 B (8)
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+// chunk swizzles: K and V tile rows are 256 B (16 chunks), Kt rows 128 B (8).
+// A 16-byte read of 64 lanes is served 32 lanes at a time from 128 banks
+// (512 B), so rows of equal parity share banks. kswz (rows tile_key(kb, l16),
+// built from row bits 0, 1, 3, 4 with bits 0 and 3 in swapped places) and
+// rswz (rows 16 rb + l16: the low four bits with bits 0 and 2 swapped) put
+// the 32 chunks a half wave reads on distinct bank groups.
+__device__ __forceinline__ int kswz(int row) {
+  return ((row >> 3) & 1) | (row & 2) | ((row & 1) << 2) | (((row >> 4) & 1) << 3);
+}
+__device__ __forceinline__ int rswz(int row) { return (row & 10) | ((row & 1) << 2) | ((row >> 2) & 1); }
 __device__ __forceinline__ int tswz(int row) { return (row >> 1) & 7; }
 
 // key held in MFMA row m of key block kb (lane group q of the B operand of
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArg
     for (int c = 0; c < CPT; ++c) {
       const int slot = (wave * CPT + c) * 64 + lane;
       const int rr = slot >> 4, pc = slot & 15;
-      const int ch = pc ^ kswz(rr);
+      const int ch = pc ^ rswz(rr);
       const size_t row = ((size_t)min(si_[c], a.n_q - 1) * a.h_q + sh_[c]) * D + ch * 8;
       const __bf16* qs = qseq + row;
       const __bf16* ds = dseq + row;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_bf16_pair_kernel(DkdvArg
   for (int rb = 0; rb < 2; ++rb) {
     const int row = 16 * rb + l16;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) roff[rb][u] = row * 256 + (((4 * grp + u) ^ kswz(row)) << 4);
+    for (int u = 0; u < 4; ++u) roff[rb][u] = row * 256 + (((4 * grp + u) ^ rswz(row)) << 4);
   }
   int toff[2];
 #pragma unroll

@@ -42,7 +42,12 @@ struct Dec2Args {
   float c;                                   // softmax scale * log2(e)
 };
 
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
+// K rows are 256 B (16 chunks); a 16-byte read of 64 lanes is served 32
+// lanes at a time from 128 banks (512 B), so rows of equal parity share
+// banks. Swapping bits 0 and 2 of the row's low four bits in the swizzle
+// puts the 32 chunks a half wave reads (lane groups 0-1 or 2-3, one row per
+// l16) on distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return (row & 10) | ((row & 1) << 2) | ((row >> 2) & 1); }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (other counters untouched)
