@@ -126,7 +126,8 @@ PASS_KERNELS = {
 }
 COUNTER_REGEX = "attn_fwd|attn_decode|decode_|score|sparse|select|transpose"
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
-                 "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+                 "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+N_CU = 256
 
 
 def _read_counter_csv(path):
@@ -322,7 +323,8 @@ def counters_summary(pmc_dir, steps_profiled=2):
                       "| pass | dispatches per step | MFMA flops per step (MOPS_BF16 x 512) "
                       "| MFMA busy (BUSY_CYCLES / (GUI_ACTIVE/XCDs x 1024 SIMDs)) "
                       "| active cycles per launch (one XCD) | VALU instr per MFMA "
-                      "| LDS instr per MFMA |", "|---|---|---|---|---|---|---|"]
+                      "| LDS instr per MFMA | LDS bank-conflict cycles (share of active, per CU) |",
+                      "|---|---|---|---|---|---|---|---|"]
             for ps, e in per.items():
                 if e.get("SQ_INSTS_MFMA", 0) == 0:
                     continue
@@ -335,11 +337,15 @@ def counters_summary(pmc_dir, steps_profiled=2):
                        "active_cycles_per_launch": round(gui / e["dispatches"]),
                        "valu_per_mfma": round(e["SQ_INSTS_VALU"] / e["SQ_INSTS_MFMA"], 3),
                        "lds_per_mfma": round(e["SQ_INSTS_LDS"] / e["SQ_INSTS_MFMA"], 3),
+                       "lds_bank_conflict_frac": (round(e["SQ_LDS_BANK_CONFLICT"] / (gui * N_CU), 4)
+                                                  if "SQ_LDS_BANK_CONFLICT" in e else None),
                        "source_sha": source_sha(KERNEL_SOURCES[ps])}
                 mfma.setdefault(ps, {})[w.name] = rec
                 lines.append(f"| {ps} | {launches:g} | {flops_step:.4e} | {100 * busy:.1f} % "
                              f"| {rec['active_cycles_per_launch']:.4e} | {rec['valu_per_mfma']:.2f} "
-                             f"| {rec['lds_per_mfma']:.2f} |")
+                             f"| {rec['lds_per_mfma']:.2f} | "
+                             + ("n/a" if rec["lds_bank_conflict_frac"] is None
+                                else f"{100 * rec['lds_bank_conflict_frac']:.1f} %") + " |")
         md[w.name] = (cmds, lines)
     cal_cmds = [f"rocprofv3 --pmc {c} --kernel-include-regex \"neg\" -f csv -d "
                 f"$R/gpurun_out/pmc/{sub}_copy -o run -- python3 $R/bench.py --copy-calibration 2048"
