@@ -80,16 +80,17 @@ def source_sha(paths):
 
 
 _CSRC = "token_level_sparse_pass_amd/csrc/"
+_BUILD = "token_level_sparse_pass_amd/build.py"       # compiler flags shape the code too
 KERNEL_SOURCES = {
     "full_attention": [_CSRC + "attn_fwd_bf16.hip", _CSRC + "attn_fwd.hip",
-                       _CSRC + "attn_decode_bf16.hip", _CSRC + "hs2_device.h"],
+                       _CSRC + "attn_decode_bf16.hip", _CSRC + "hs2_device.h", _BUILD],
     # decode's score step (decode_score_kernel) lives in attn_fwd.hip
     "score": [_CSRC + "score_bf16.hip", _CSRC + "score.hip", _CSRC + "attn_fwd.hip",
-              _CSRC + "hs2_device.h"],
-    "select": [_CSRC + "select.hip"],
+              _CSRC + "hs2_device.h", _BUILD],
+    "select": [_CSRC + "select.hip", _BUILD],
     "sparse_attention": [_CSRC + "sparse_attn_bf16.hip", _CSRC + "sparse_attn.hip",
-                         _CSRC + "hs2_device.h"],
-    "v_layout": [_CSRC + "attn_fwd_bf16.hip"],
+                         _CSRC + "hs2_device.h", _BUILD],
+    "v_layout": [_CSRC + "attn_fwd_bf16.hip", _BUILD],
 }
 
 
@@ -204,8 +205,9 @@ def trace_summary(trace_dir, cid):
     lines = [f"# Kernel trace: Hybrid Block step, {w.name}", "",
              "Command (from /tmp, with R = the repository root, on one MI355X; summarised by "
              "`python bench.py --trace-summary DIR --config N`):", "", "```",
-             f"rocprofv3 --kernel-trace --stats -d $R/gpurun_out/prof/trace_c{cid} -o run -- "
-             f"python3 $R/bench.py --config {cid} --steps 3 --warmup 1 --no-cpu-baseline", "```", "",
+             f"rocprofv3 --kernel-trace --stats -f csv -d $R/gpurun_out/prof/trace_c{cid} -o run -- "
+             f"python3 $R/bench.py --config {cid} --steps 3 --warmup 1 --no-cpu-baseline "
+             f"> $R/gpurun_out/prof/trace_c{cid}.log", "```", "",
              "Kernel trace statistics (durations in microseconds; the bench runs 1 warm-up and "
              "3 timed steps, so each launch slot of a step is counted 4 times):", "",
              "| kernel | calls | total (us) | average (us) | % of GPU time |", "|---|---|---|---|---|"]

@@ -23,6 +23,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 math stays off: plain scalar/float2 code only
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results and accumulators in ordinary VGPRs: otherwise the
+         # compiler parks some kernels' accumulators in AGPRs and copies them
+         # to VGPRs and back on every loop trip around a VALU rescale (the
+         # sparse layers, decode pass 1); kernels that use no AGPRs compile
+         # to the same code either way
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", INCLUDE, "-I", CSRC]
 # per-source additions: the bf16 pass-1 kernels take their row maxima with
 # plain max instructions, which fmaxf emits only when NaNs need no handling

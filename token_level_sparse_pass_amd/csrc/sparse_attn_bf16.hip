@@ -16,7 +16,10 @@
 // kept shallow so that four work-groups fit a CU (36.6 KB of LDS with a
 // 1152-entry index row): more independent work-groups in flight beat a
 // deeper ring per work-group (at the 32K prefill 8.4 ms with two stages,
-// 9.3 ms with three, 12.6 ms with four, 23.8 ms with five).
+// 9.3 ms with three, 12.6 ms with four, 23.8 ms with five). The PV operand
+// V^T comes from LDS through gfx950's transposing reads (two 8-byte reads
+// per operand) instead of 16-byte reads and an 8 x 8 transpose in
+// registers (32K prefill 6.58 -> 6.36 ms, 1M chunk 8.83 -> 7.91 ms).
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
@@ -49,6 +52,44 @@ struct Sp2Args {
 // puts the 32 chunks a half wave reads (lane groups 0-1 or 2-3, one row per
 // l16) on distinct bank groups.
 __device__ __forceinline__ int kswz(int row) { return (row & 10) | ((row & 1) << 2) | ((row >> 2) & 1); }
+
+// The many-query kernel keeps the 32-byte chunk pairs of its V rows
+// XOR-swizzled by y = (key mod 8) ^ bit 3 of the tile key, so that its
+// transposing reads (16 keys x 32 bytes per instruction) are free of bank
+// conflicts whether the LDS serves them 64 lanes at a time from 128 banks
+// (the eight keys of each parity get distinct y) or 32 lanes at a time from
+// 64 banks (each run of eight consecutive keys gets distinct y); with
+// y = bits 1-3 of the key the counters showed conflicts on 14 % of the
+// pass's cycles.
+__device__ __forceinline__ int vswz(int key) { return ((key & 7) ^ ((key >> 3) & 1)) << 1; }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// The P^T operand of lane group grp holds keys 4 grp + 0..3 and
+// 16 + 4 grp + 0..3 of a 32-key tile. The matching V^T operand of head-dim
+// block db comes straight from LDS with two transposing reads
+// (ds_read_b64_tr_b16 gives lane 4a + b of each 16-lane group element b of
+// the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12): lane
+// a + 4c addresses head-dim elements 16 db + 4a .. + 3 of key 4 grp + c
+// (then of key 16 + 4 grp + c), so lane l16 receives head-dim row
+// 16 db + l16 of its group's eight keys. v_lane_offsets gives a lane's byte
+// offsets of its two pieces for every db, relative to the tile's V rows.
+__device__ __forceinline__ void v_lane_offsets(int grp, int l16, int (&o1)[8], int (&o2)[8]) {
+  const int a = l16 & 3, c = l16 >> 2;
+  const int k1 = 4 * grp + c, k2 = 16 + 4 * grp + c;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const int chunk = 2 * db + (a >> 1);
+    o1[db] = k1 * 256 + ((chunk ^ vswz(k1)) << 4) + ((a & 1) << 3);
+    o2[db] = k2 * 256 + ((chunk ^ vswz(k2)) << 4) + ((a & 1) << 3);
+  }
+}
+__device__ __forceinline__ bf16x8 v_operand(const char* vrows, int o1, int o2) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrows + o1));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrows + o2));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (other counters untouched)
@@ -137,7 +178,7 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
       const int pc = l16;
       __builtin_amdgcn_global_load_lds(kseq + row + ((pc ^ kswz(key)) << 3),
                                        (lds_void*)(base + slot_base * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseq + row + (pc << 3),
+      __builtin_amdgcn_global_load_lds(vseq + row + ((pc ^ vswz(key)) << 3),
                                        (lds_void*)(base + HALF + slot_base * 16), 16, 0, 0);
     }
   };
@@ -157,6 +198,8 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   f32x4 acc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int vo1[8], vo2[8];
+  v_lane_offsets(grp, l16, vo1, vo2);
 
   // prologue: tiles 0 .. NS-2 in flight
 #pragma unroll
@@ -194,15 +237,6 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
       }
       s[kb] = x;
     }
-    // V rows of the lane's 8 key slots (k<4: 4g+k, k>=4: 16+4g+k-4); read
-    // with the bf16 vector type like every other LDS read here, which keeps
-    // the compiler from adding a full wait on the gathers in flight
-    bf16x8 vraw[8];
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl) {
-      const int key = sl < 4 ? 4 * grp + sl : 16 + 4 * grp + (sl - 4);
-      vraw[sl] = *reinterpret_cast<const bf16x8*>(base + HALF + key * 256 + l16 * 16);
-    }
 
     const int kbase = t * TK;
     float tmax = -INFINITY;
@@ -237,14 +271,9 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
       }
     l_run += psum;
 
-    // O^T += V^T . P^T: head-dim rows permuted so lane l reads V[key][8*l16..+7]
+    // O^T += V^T . P^T, V^T read transposed from LDS
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      bf16x8 vu;
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl) vu[sl] = vraw[sl][db];
-      acc[db] = OP::mma(vu, pu, acc[db]);
-    }
+    for (int db = 0; db < 8; ++db) acc[db] = OP::mma(v_operand(base + HALF, vo1[db], vo2[db]), pu, acc[db]);
   }
 
   if (r >= rows_total) return;
@@ -253,14 +282,15 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int layer = r / G, hh = r - (r / G) * G;
-  __bf16* orow = a.o + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D) + grp * 32;
-  bf16x8 outv[4];
+  // lane (grp, l16) holds head-dim elements 16 db + 4 grp .. + 3 of its row
+  __bf16* orow = a.o + ((size_t)layer * a.layer_stride + (((size_t)b * a.n_q + i) * a.h_q + g * G + hh) * D) + grp * 4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int db = 0; db < 8; ++db) {
+    bf16x4 w;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) outv[e][db] = (__bf16)(acc[db][e] * inv);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) reinterpret_cast<bf16x8*>(orow)[e] = outv[e];
+    for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][e] * inv);
+    *reinterpret_cast<bf16x4*>(orow + db * 16) = w;
+  }
 }
 
 // Decode-shaped calls (few index lists, fewer work-groups than the chip
@@ -273,7 +303,9 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
 // result does not depend on timing.
 // (three partitions of three stages, or two of four, keep more tiles in
 // flight per partition but measured the same on the 64 x 128K decode: the
-// gathers, not their latency, set the time)
+// gathers, not their latency, set the time). V^T is transposed in
+// registers here: the many-query kernel's transposing LDS reads measured
+// about 2 % slower in this kernel.
 constexpr int NP = 4;
 constexpr int NSS = 2;
 constexpr size_t SPLIT_RING_BYTES = (size_t)NP * NSS * TILE_BYTES;   // 128 KB
