@@ -30,10 +30,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # to the same code either way
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", INCLUDE, "-I", CSRC]
-# per-source additions: the bf16 pass-1 kernels take their row maxima with
-# plain max instructions, which fmaxf emits only when NaNs need no handling
-# (their logits are finite or -inf)
-EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_decode_bf16.hip": ["-fno-honor-nans"]}
+# per-source additions: the bf16 pass-1 and sparse-layer kernels take their
+# row maxima with plain max instructions, which fmaxf emits only when NaNs
+# need no handling (their logits are finite or -inf)
+EXTRA = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_decode_bf16.hip": ["-fno-honor-nans"],
+         "sparse_attn_bf16.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

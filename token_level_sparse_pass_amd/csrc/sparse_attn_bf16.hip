@@ -110,6 +110,30 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 
 }  // namespace
 
+// Index-row slots in LDS: the row padded to whole tiles, then one slot for
+// the count of valid entries and three of padding (16-byte multiple).
+__host__ __device__ constexpr int idx_row_slots(int width) { return (width + TK - 1) / TK * TK + 4; }
+
+// Copies one index row (ascending, -1 padded) into LDS as K/V buffer rows,
+// every slot past the valid entries (up to whole tiles) holding the first
+// row, so the gather loop reads it unguarded; the slot after the padded row
+// receives the number of valid entries (written by the one thread that holds
+// the last valid entry, or by thread 0 when there is none).
+template <int NTHREADS>
+__device__ __forceinline__ int stage_index_row(const int32_t* irow, int W, int b, const KvRows& kv, int* sidx) {
+  const int w_pad = (W + TK - 1) / TK * TK;
+  const int j_first = W > 0 ? irow[0] : -1;
+  const int first_row = j_first >= 0 ? (int)kv.row(b, j_first) : 0;
+  if (threadIdx.x == 0 && j_first < 0) sidx[w_pad] = 0;
+  for (int t = threadIdx.x; t < w_pad; t += NTHREADS) {
+    const int j = t < W ? irow[t] : -1;
+    sidx[t] = j >= 0 ? (int)kv.row(b, j) : first_row;
+    if (j >= 0 && (t + 1 == W || irow[t + 1] < 0)) sidx[w_pad] = t + 1;
+  }
+  __syncthreads();
+  return sidx[w_pad];
+}
+
 // NWV waves; wave w gathers keys [w*32/NWV, (w+1)*32/NWV) of every tile (K
 // and V) and computes row block w.
 template <int NWV>
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS targets stay scalar
   const int grp = lane >> 4;
   const int l16 = lane & 15;
   const int G = a.h_q / a.h_kv;
@@ -143,42 +167,37 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   // never waits on the gathers in flight
   // (entries become K/V buffer rows here: contiguous or through the page table)
   int* sidx = reinterpret_cast<int*>(smem + NS * TILE_BYTES);
-  for (int t = threadIdx.x; t < a.W; t += 64 * NWV) {
-    const int j = irow[t];
-    sidx[t] = j >= 0 ? (int)a.kv.row(b, j) : -1;
-  }
-  __syncthreads();
-  int n_valid = 0;
-  for (int t = lane; t < a.W; t += 64) n_valid += (sidx[t] >= 0) ? 1 : 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
+  const int n_valid = stage_index_row<64 * NWV>(irow, a.W, b, a.kv, sidx);
   const int n_tiles = (n_valid + TK - 1) / TK;
-  const int fallback = n_valid > 0 ? sidx[0] : 0;
 
-  const size_t kvs = (size_t)a.h_kv * D;
-  const __bf16* kseq = a.k + (size_t)g * D;             // + buffer row * kvs
-  const __bf16* vseq = a.v + (size_t)g * D;
+  // the 16-byte chunk a lane moves in gather instruction j, as an address in
+  // buffer row 0 (K chunks and V chunk pairs swizzled for the reads); a
+  // gather adds the row's byte offset (32-bit row times row bytes)
+  const uint32_t row_bytes = (uint32_t)a.h_kv * D * 2;
+  const char* ksrc[IPW];
+  const char* vsrc[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int key = wave * KPW + j * 4 + grp;          // tile-local key of this lane
+    ksrc[j] = reinterpret_cast<const char*>(a.k + (size_t)g * D) + ((l16 ^ kswz(key)) << 4);
+    vsrc[j] = reinterpret_cast<const char*>(a.v + (size_t)g * D) + ((l16 ^ vswz(key)) << 4);
+  }
 
   // index entries of the lane's keys in the next tile to gather
   int nidx[IPW];
   auto read_idx = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int pos = t * TK + wave * KPW + j * 4 + grp;
-      nidx[j] = pos < n_valid ? sidx[pos] : fallback;
-    }
+    for (int j = 0; j < IPW; ++j) nidx[j] = sidx[t * TK + wave * KPW + j * 4 + grp];
   };
   auto issue = [&](int stage) {
     char* base = smem + stage * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int key = wave * KPW + j * 4 + grp;        // tile-local key of this lane
-      const size_t row = (size_t)nidx[j] * kvs;
+      const uint64_t off = (uint64_t)(uint32_t)nidx[j] * row_bytes;
       const int slot_base = (wave * KPW + j * 4) * 16;  // first 16-byte slot of the instruction
-      const int pc = l16;
-      __builtin_amdgcn_global_load_lds(kseq + row + ((pc ^ kswz(key)) << 3),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(ksrc[j] + off),
                                        (lds_void*)(base + slot_base * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseq + row + ((pc ^ vswz(key)) << 3),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(vsrc[j] + off),
                                        (lds_void*)(base + HALF + slot_base * 16), 16, 0, 0);
     }
   };
@@ -239,16 +258,15 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
     }
 
     const int kbase = t * TK;
-    float tmax = -INFINITY;
+    if (kbase + TK > n_valid) {                         // the last tile: keys past the list
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (kbase + kb * 16 + 4 * grp + e >= n_valid) s[kb][e] = -INFINITY;
-        tmax = fmaxf(tmax, s[kb][e]);
-      }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+        for (int e = 0; e < 4; ++e)
+          if (kbase + kb * 16 + 4 * grp + e >= n_valid) s[kb][e] = -INFINITY;
+    }
+    const float tmax = row_group_max(max2f(max3f(s[0][0], s[0][1], s[0][2]),
+                                           max3f(s[0][3], max3f(s[1][0], s[1][1], s[1][2]), s[1][3])));
     const float m_tile = tmax * a.c;
     const bool grow = m_tile > m_run + RESCALE_GAP;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -337,46 +355,41 @@ __global__ __launch_bounds__(64 * NWV * NP) void sparse_bf16_split_kernel(Sp2Arg
 
   // the index row (as K/V buffer rows) after the rings
   int* sidx = reinterpret_cast<int*>(smem + SPLIT_RING_BYTES);
-  for (int t = threadIdx.x; t < a.W; t += 64 * NWV * NP) {
-    const int j = irow[t];
-    sidx[t] = j >= 0 ? (int)a.kv.row(b, j) : -1;
-  }
-  __syncthreads();
-  int n_valid = 0;
-  for (int t = lane; t < a.W; t += 64) n_valid += (sidx[t] >= 0) ? 1 : 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) n_valid += __shfl_xor(n_valid, m, 64);
+  const int n_valid = stage_index_row<64 * NWV * NP>(irow, a.W, b, a.kv, sidx);
   const int n_tiles = (n_valid + TK - 1) / TK;
-  const int fallback = n_valid > 0 ? sidx[0] : 0;
   // this partition's tiles [t_lo, t_lo + n_mine); every wave runs `steps`
   // barrier steps, the largest partition's tile count
   const int t_lo = n_tiles * part / NP;
   const int n_mine = n_tiles * (part + 1) / NP - t_lo;
   const int steps = (n_tiles + NP - 1) / NP;
 
-  const size_t kvs = (size_t)a.h_kv * D;
-  const __bf16* kseq = a.k + (size_t)g * D;             // + buffer row * kvs
-  const __bf16* vseq = a.v + (size_t)g * D;
   char* ring = smem + (size_t)part * NSS * TILE_BYTES;
+  // the chunk a lane moves in gather instruction j, as an address in buffer
+  // row 0; a gather adds the row's byte offset
+  const uint32_t row_bytes = (uint32_t)a.h_kv * D * 2;
+  const char* ksrc[IPW];
+  const char* vsrc[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int key = wave * KPW + j * 4 + grp;          // tile-local key of this lane
+    ksrc[j] = reinterpret_cast<const char*>(a.k + (size_t)g * D) + ((l16 ^ kswz(key)) << 4);
+    vsrc[j] = reinterpret_cast<const char*>(a.v + (size_t)g * D) + (l16 << 4);
+  }
 
   int nidx[IPW];
   auto read_idx = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int pos = (t_lo + t) * TK + wave * KPW + j * 4 + grp;
-      nidx[j] = pos < n_valid ? sidx[pos] : fallback;
-    }
+    for (int j = 0; j < IPW; ++j) nidx[j] = sidx[(t_lo + t) * TK + wave * KPW + j * 4 + grp];
   };
   auto issue = [&](int stage) {
     char* base = ring + stage * TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      const int key = wave * KPW + j * 4 + grp;        // tile-local key of this lane
-      const size_t row = (size_t)nidx[j] * kvs;
+      const uint64_t off = (uint64_t)(uint32_t)nidx[j] * row_bytes;
       const int slot_base = (wave * KPW + j * 4) * 16;
-      __builtin_amdgcn_global_load_lds(kseq + row + ((l16 ^ kswz(key)) << 3),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(ksrc[j] + off),
                                        (lds_void*)(base + slot_base * 16), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vseq + row + (l16 << 3),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(vsrc[j] + off),
                                        (lds_void*)(base + HALF + slot_base * 16), 16, 0, 0);
     }
   };
@@ -440,16 +453,15 @@ __global__ __launch_bounds__(64 * NWV * NP) void sparse_bf16_split_kernel(Sp2Arg
     }
 
     const int kbase = (t_lo + t) * TK;
-    float tmax = -INFINITY;
+    if (kbase + TK > n_valid) {                         // the last tile: keys past the list
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (kbase + kb * 16 + 4 * grp + e >= n_valid) s[kb][e] = -INFINITY;
-        tmax = fmaxf(tmax, s[kb][e]);
-      }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
+        for (int e = 0; e < 4; ++e)
+          if (kbase + kb * 16 + 4 * grp + e >= n_valid) s[kb][e] = -INFINITY;
+    }
+    const float tmax = row_group_max(max2f(max3f(s[0][0], s[0][1], s[0][2]),
+                                           max3f(s[0][3], max3f(s[1][0], s[1][1], s[1][2]), s[1][3])));
     const float m_tile = tmax * a.c;
     const bool grow = m_tile > m_run + RESCALE_GAP;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -534,7 +546,7 @@ __global__ __launch_bounds__(64 * NWV * NP) void sparse_bf16_split_kernel(Sp2Arg
 // go to the generic kernel, which keeps no index row in LDS.
 constexpr size_t SPARSE_LDS_LIMIT = 64 * 1024;
 
-size_t sparse_bf16_lds_bytes(int width) { return (size_t)NS * TILE_BYTES + (size_t)width * sizeof(int); }
+size_t sparse_bf16_lds_bytes(int width) { return (size_t)NS * TILE_BYTES + (size_t)idx_row_slots(width) * sizeof(int); }
 
 bool sparse_uses_bf16_kernel(const SparsePlan& p) {
   return p.bf16 && p.head_dim == D && (size_t)p.batch * p.n_q * p.h_kv >= 2048 &&
@@ -547,7 +559,7 @@ constexpr size_t SPLIT_LDS_LIMIT = 160 * 1024;
 
 static size_t sparse_bf16_split_lds_bytes(int width, int nwv) {
   const size_t merge = (size_t)NP * nwv * (32 * 64 + 2 * 16) * sizeof(float);
-  const size_t ring = SPLIT_RING_BYTES + (size_t)width * sizeof(int);
+  const size_t ring = SPLIT_RING_BYTES + (size_t)idx_row_slots(width) * sizeof(int);
   return ring > merge ? ring : merge;
 }
 
