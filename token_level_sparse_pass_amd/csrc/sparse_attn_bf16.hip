@@ -23,6 +23,8 @@
 #include "hs2_device.h"
 #include "hs2_launch.h"
 
+#include <type_traits>
+
 namespace hs2 {
 
 namespace {
@@ -85,9 +87,11 @@ __device__ __forceinline__ void v_lane_offsets(int grp, int l16, int (&o1)[8], i
     o2[db] = k2 * 256 + ((chunk ^ vswz(k2)) << 4) + ((a & 1) << 3);
   }
 }
-__device__ __forceinline__ bf16x8 v_operand(const char* vrows, int o1, int o2) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrows + o1));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrows + o2));
+typedef __attribute__((address_space(3))) const char lds_cchar;
+// the two pieces at LDS addresses p1 and p2
+__device__ __forceinline__ bf16x8 v_operand(lds_cchar* p1, lds_cchar* p2) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p1);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p2);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -141,7 +145,6 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   using OP = Op<__bf16, D>;
   constexpr int KPW = TK / NWV;              // keys gathered per wave per tile
   constexpr int IPW = KPW / 4;               // 1 KB load instructions per half
-  constexpr int LPW = 2 * IPW;               // load instructions per wave per tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -217,8 +220,28 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   f32x4 acc[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int vo1[8], vo2[8];
-  v_lane_offsets(grp, l16, vo1, vo2);
+  // each lane's LDS addresses in ring stage 0: its four K-fragment chunks
+  // of key block 0 and its V^T pieces of every head-dim block (a tile's
+  // stage and key block only add constants, which fold into the reads)
+  lds_cchar* lsm = (lds_cchar*)smem;
+  lds_cchar* kp[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kp[u] = lsm + l16 * 256 + (((4 * grp + u) ^ kswz(l16)) << 4);
+  lds_cchar* vp1[8];
+  lds_cchar* vp2[8];
+  {
+    int vo1[8], vo2[8];
+    v_lane_offsets(grp, l16, vo1, vo2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      vp1[db] = lsm + HALF + vo1[db];
+      vp2[db] = lsm + HALF + vo2[db];
+      // opaque from here on: kept in registers, not recomputed per tile
+      asm volatile("" : "+v"(vp1[db]), "+v"(vp2[db]));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(kp[u]));
 
   // prologue: tiles 0 .. NS-2 in flight
 #pragma unroll
@@ -230,28 +253,30 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
   }
   if (NS - 1 < n_tiles) read_idx(NS - 1);
 
-  for (int t = 0; t < n_tiles; ++t) {
-    // own loads of tile t done (later tiles may stay in flight), then all waves'
-    const int ahead = min(NS - 2, n_tiles - 1 - t);
-    static_assert((NS - 2) * LPW <= 63, "vmcnt range");
-    wait_ahead<NS - 2, LPW>(ahead);
+  // one tile; the loop below runs tiles in pairs so that each one's ring
+  // stage is a constant (its LDS offsets become instruction immediates)
+  static_assert(NS == 2, "tiles alternate between two ring stages");
+  auto tile = [&](int t, auto stage_c) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_c)::value;
+    // own loads of tile t done, then all waves'
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    if (t + NS - 1 < n_tiles) {
-      issue((t + NS - 1) % NS);
-      if (t + NS < n_tiles) read_idx(t + NS);
+    if (t + 1 < n_tiles) {
+      issue(ST ^ 1);
+      if (t + 2 < n_tiles) read_idx(t + 2);
     }
-    if (!wave_active) continue;
-    const char* base = smem + (t % NS) * TILE_BYTES;
+    if (!wave_active) return;
 
+    // K rows kb * 16 + l16 share the swizzle of l16, so key block kb sits a
+    // constant 4 KB past block 0
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 16 + l16;
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(base + key * 256 + (((4 * grp + u) ^ kswz(key)) << 4));
+        const bf16x8 kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            kp[u] + ST * TILE_BYTES + kb * 4096);
         x = OP::mma(kf, qf.u[u], x);
       }
       s[kb] = x;
@@ -291,8 +316,15 @@ __global__ __launch_bounds__(64 * NWV) void sparse_bf16_kernel(Sp2Args a) {
 
     // O^T += V^T . P^T, V^T read transposed from LDS
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc[db] = OP::mma(v_operand(base + HALF, vo1[db], vo2[db]), pu, acc[db]);
+    for (int db = 0; db < 8; ++db)
+      acc[db] = OP::mma(v_operand(vp1[db] + ST * TILE_BYTES, vp2[db] + ST * TILE_BYTES), pu, acc[db]);
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    tile(t, std::integral_constant<int, 0>{});
+    tile(t + 1, std::integral_constant<int, 1>{});
   }
+  if (t < n_tiles) tile(t, std::integral_constant<int, 0>{});
 
   if (r >= rows_total) return;
   float l = l_run;
