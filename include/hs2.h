@@ -123,7 +123,8 @@ hs2_status hs2_full_attn_select(const hs2_problem* p, const void* q,
 
 /* n_layers sparse layers over a given index set (KV Reuse): layer l reads
  * q_layers[l] and writes o_layers[l]; every layer reads the same K, V and
- * idx. idx rows must be ascending, -1 padded, entries <= p. */
+ * idx. idx rows must be ascending, -1 padded, entries <= p. A row with no
+ * entries (all -1) gives zero outputs. */
 hs2_status hs2_sparse_attn(const hs2_problem* p, int32_t n_layers,
                            const void* q_layers, const void* k, const void* v,
                            const int32_t* idx, void* o_layers, void* stream);

@@ -103,6 +103,66 @@ def test_sparse_attn_on_oracle_indices(gpu_lib, case):
 
 
 # ---------------------------------------------------------------------------
+# the bf16 sparse kernels on hand-made index rows of every fill: empty, one
+# key, around tile edges (31-33, 63-65 of 32-key tiles), a partial last
+# tile and full rows; an empty row gives zero outputs
+# ---------------------------------------------------------------------------
+RAGGED_FILLS = (0, 1, 2, 31, 32, 33, 63, 64, 65, 97, None)     # None = the whole row
+
+
+def ragged_index_rows(case, seed):
+    """[B, n_q, W] ascending, -1-padded rows of distinct keys j <= p, row r of
+    batch b filled with RAGGED_FILLS[(b * n_q + r) % len] keys (capped)."""
+    rng = np.random.default_rng(seed)
+    W = case.top_k + case.window
+    idx = np.full((case.batch, case.n_q, W), -1, dtype=np.int32)
+    for b in range(case.batch):
+        for i in range(case.n_q):
+            p = case.n_kv - case.n_q + i
+            want = RAGGED_FILLS[(b * case.n_q + i) % len(RAGGED_FILLS)]
+            n = min(W, p + 1) if want is None else min(want, W, p + 1)
+            idx[b, i, :n] = np.sort(rng.choice(p + 1, size=n, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("case", [
+    # many (query, KV head) lists: the many-query kernel; W = 120, not a
+    # multiple of the 32-key tile, 24 rows (two waves)
+    small("rag_many", "bf16", 1, 1024, 1500, 16, 2, 128, 100, 20, L=3),
+    # few lists: the decode-shaped kernel with four key partitions
+    small("rag_decode", "bf16", 11, 1, 3000, 16, 2, 128, 500, 60, L=3),
+], ids=lambda c: c.name)
+def test_sparse_kernels_on_ragged_index_rows(gpu_lib, case):
+    say("case", case)
+    inp = make_inputs(case, device="cuda")
+    idx = ragged_index_rows(case, seed=7)
+    out = gpu_lib.sparse_attn(inp["q_sparse"], inp["k"], inp["v"],
+                              torch.from_numpy(idx).cuda(), top_k=case.top_k, window=case.window)
+    torch.cuda.synchronize()
+    got = as_np(out)
+    k, v, qs = (host(inp[n]) for n in ("k", "v", "q_sparse"))
+    fills = (idx >= 0).sum(axis=2)
+    checked = set()
+    worst = 0.0
+    for b in range(case.batch):
+        # every row of small batches; otherwise the first 64 rows (all fills)
+        # and the last 64
+        rows = list(range(case.n_q)) if case.n_q <= 128 else \
+            list(range(64)) + list(range(case.n_q - 64, case.n_q))
+        empty = [r for r in rows if fills[b, r] == 0]
+        full = [r for r in rows if fills[b, r] > 0]
+        if empty:
+            assert np.all(got[:, b, empty] == 0.0), "an empty index row must give zero outputs"
+        if full:
+            ref = O.sparse_rows(qs, k, v, b, full, idx[b, full])
+            worst = max(worst, float(np.abs(got[:, b, full] - ref).max()))
+        checked.update(int(f) for f in fills[b, rows])
+    say("fills checked:", sorted(checked), "max abs err", worst)
+    assert {0, 1, 31, 32, 33, 64, 65}.issubset(checked)
+    assert worst <= TOL[case.dtype]
+
+
+# ---------------------------------------------------------------------------
 # full layer + selection, small shapes against the dense oracle
 # ---------------------------------------------------------------------------
 FULL_CASES = [
