@@ -196,6 +196,34 @@ def run_full_case(gpu_lib, case, select="token", block_size=64, top_blocks=16, d
     return inp, o, idx, lse, scores, ref
 
 
+def test_full_attention_runaway_logits(gpu_lib):
+    """Keys planted along one query's direction, so that their logits pass
+    that row's running max (from the first key tile) by far more than fp32
+    can hold as a probability (2^(s c - m) overflows), and pass other rows'
+    maxima by less: pass 1 must still give the oracle's O and LSE."""
+    case = small("runaway", "bf16", 1, 256, 2048, 8, 2, 128, 128, 32)
+    say("case", case)
+    inp = make_inputs(case, device="cuda")
+    q, k = inp["q_full"], inp["k"].clone()
+    d = case.d
+    # query rows i0 (head 0) and i1 (head 5): keys in later tiles of their KV
+    # heads along their directions; logit 200 and 120 (softmax scale 1/sqrt(d))
+    for i0, h, j, logit in ((10, 0, 900, 200.0), (200, 5, 1500, 120.0), (30, 0, 1790, 60.0)):
+        g = h // (case.h_q // case.h_kv)
+        qv = q[0, i0, h].float()
+        k[0, j, g] = (qv / qv.norm() * logit * math.sqrt(d) / qv.norm()).to(k.dtype)
+    kw = dict(top_k=case.top_k, window=case.window)
+    o, idx, lse, _ = gpu_lib.full_attn_select(q, k, inp["v"], **kw)
+    torch.cuda.synchronize()
+    qh, kh, vh = host(q), host(k), host(inp["v"])
+    ref = O.block_forward(qh, np.zeros((0,) + qh.shape, dtype=qh.dtype), kh, vh, **kw)
+    err_o = np.abs(as_np(o) - ref["o_full"]).max()
+    err_lse = np.abs(lse.cpu().numpy() - ref["lse"]).max()
+    say("o_full err", err_o, "lse err", err_lse, "max lse", float(np.abs(ref["lse"]).max()))
+    assert err_o <= TOL["bf16"]
+    assert err_lse <= 1e-4 * max(1.0, float(np.abs(ref["lse"]).max()))
+
+
 @pytest.mark.parametrize("case", FULL_CASES, ids=lambda c: c.name)
 def test_full_attn_select(gpu_lib, case):
     say("case", case)

@@ -38,9 +38,14 @@
 //    such that the P^T operand of each lane covers 8 consecutive keys;
 //  * the running max is only moved (and O rescaled) when it grows by more
 //    than 2^8, so the rescale multiply almost never runs; exponents are
-//    formed with one FMA (logit * c - m) from the raw MFMA result; a tile's
-//    row sums are added during its PV product, beside the MFMAs, rather
-//    than in the softmax phase (1 % faster, same order of additions);
+//    formed with one FMA (logit * c - m) from the raw MFMA result;
+//  * on open tiles after the first (every row then holds a finite running
+//    max) the probabilities are formed with the max as it stands and no
+//    lane maximum is taken: only where a lane's 16 probabilities sum past
+//    2^12 is the max looked at again (from log2 of the largest probability,
+//    or, when one overflowed fp32, from the tile's logits formed again with
+//    K read from memory); the sums serve the row sums as well (2.5 % faster
+//    at 262K and 1M);
 //  * the causal mask is applied only on tiles that reach the diagonal.
 // Rows, as in the generic kernel, are (query, head-of-group) pairs: RBW
 // 16-row MFMA blocks per wave, eight waves (two per SIMD) per work-group,
@@ -65,6 +70,7 @@ constexpr int D = 128;
 constexpr int KT_BYTES = TK * D * 2;        // 16 KB
 constexpr int STAGE_BYTES = 2 * KT_BYTES;   // K tile + Vt tile
 constexpr float RESCALE_GAP = 8.0f;         // log2 units
+constexpr float SPEC_LIMIT = 4096.0f;       // a lane's tile row sum past this rechecks the max
 constexpr float LN2 = 0.69314718055994530942f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -290,6 +296,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
 
   float m_run[RBW];
   float thr[RBW];                                       // (m_run + gap) / c: a raw logit past it moves the max
+  float lsum[RBW];                                      // this lane's share of the tile's row sums
   float l_s[RBW], l_c[RBW];                             // compensated row sums
   f32x4 acc[RBW][8];
 #pragma unroll
@@ -318,14 +325,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   bf16x8 pu[RBW][2];                                    // the previous tile's P^T operands
 
   // O^T += V^T . P^T for the tile whose P is in pu (its Vt rows at vbase),
-  // and that tile's row sums from its fp32 probabilities (still in s): the
-  // adds have no part in the product, so they fill VALU slots beside its
-  // MFMAs instead of lengthening the softmax phase
+  // then the compensated add of that tile's row sums (formed with its
+  // probabilities in the softmax phase)
   auto pv = [&](auto stage_c) __attribute__((always_inline)) {
     const char* vbase = smem + decltype(stage_c)::value * STAGE_BYTES;
-    float psum[RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) psum[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vbase + voff[0] + db * 2048);
@@ -335,17 +338,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
         acc[rb][db] = OP::mma(v0, pu[rb][0], acc[rb][db]);
         acc[rb][db] = OP::mma(v1, pu[rb][1], acc[rb][db]);
       }
-      // two of the 16 probabilities of each row block per head-dim block
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        psum[rb] += s[rb][db >> 1][2 * (db & 1)];
-        psum[rb] += s[rb][db >> 1][2 * (db & 1) + 1];
-      }
     }
-    // compensated add of the tile's row sums
+    // compensated add of the tile's row sums (formed with its probabilities)
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      const float y = psum[rb] - l_c[rb];
+      const float y = lsum[rb] - l_c[rb];
       const float tt = l_s[rb] + y;
       l_c[rb] = (tt - l_s[rb]) - y;
       l_s[rb] = tt;
@@ -378,8 +375,25 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   };
   // softmax of tile t: row maxima, lazy rescale, P = 2^(s c - m), row sums,
   // P^T operands in bf16
-  auto softmax = [&](int t, auto masked_c) __attribute__((always_inline)) {
+  // this lane's 16 probabilities of row block rb summed in key order
+  auto row_part = [&](int rb) __attribute__((always_inline)) {
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ls += s[rb][kb][e];
+    return ls;
+  };
+  // softmax of tile t: row maxima, lazy rescale, P = 2^(s c - m), row sums,
+  // P^T operands in bf16. The exact form forms each lane's maximum first; the
+  // speculative form (open tiles after the first, whose rows all hold a
+  // finite running max) forms P with the running max as it stands and only
+  // looks for a new maximum on the rare tiles where a lane's row sum passes
+  // SPEC_LIMIT (then every P was at most that, or some logit ran past the
+  // range of fp32 and the tile's logits are recomputed from K in memory)
+  auto softmax = [&](int t, auto masked_c, auto spec_c) __attribute__((always_inline)) {
     constexpr bool masked = decltype(masked_c)::value;
+    constexpr bool spec = decltype(spec_c)::value;
     const int j0 = t * TK;
     // while one wave of a SIMD pair is in this phase its partner is in its
     // MFMA phase; raising this wave's issue priority lets its VALU work go
@@ -387,42 +401,101 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      if constexpr (masked) {
-        // key j0 + 8 grp + off is past this row when off > lim
-        const int lim = row_pos[rb] - j0 - 8 * grp;
+      if constexpr (spec) {
+        const float neg_m = -m_run[rb];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (32 * (kb >> 1) + 4 * (kb & 1) + e > lim) s[rb][kb][e] = -INFINITY;
+          for (int e = 0; e < 4; ++e) s[rb][kb][e] = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
+        float ls = row_part(rb);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= SPEC_LIMIT))) {
+          // the lane's largest probability; +inf: a logit passed the running
+          // max by more than fp32 holds, so the logits are formed again
+          const float pmax = max2f(max3f(max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]),
+                                         max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]),
+                                         max3f(s[rb][1][2], s[rb][1][3], s[rb][2][0])),
+                                   max3f(max3f(s[rb][2][1], s[rb][2][2], s[rb][2][3]),
+                                         max3f(s[rb][3][0], s[rb][3][1], s[rb][3][2]), s[rb][3][3]));
+          const bool lost = __builtin_amdgcn_ballot_w64(pmax == INFINITY) != 0;
+          float m_tile;
+          if (lost) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const __bf16* krow = kseq + (size_t)(j0 + tile_key(kb, l16)) * kstride + 8 * (4 * grp);
+              f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                x = OP::mma(*reinterpret_cast<const bf16x8*>(krow + 8 * u), qf[rb].u[u], x);
+              s[rb][kb] = x;
+            }
+            const float lmax = max2f(max3f(max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]),
+                                           max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]),
+                                           max3f(s[rb][1][2], s[rb][1][3], s[rb][2][0])),
+                                     max3f(max3f(s[rb][2][1], s[rb][2][2], s[rb][2][3]),
+                                           max3f(s[rb][3][0], s[rb][3][1], s[rb][3][2]), s[rb][3][3]));
+            m_tile = row_group_max(lmax) * a.c;
+          } else {
+            m_tile = m_run[rb] + __builtin_amdgcn_logf(row_group_max(pmax));
+          }
+          const bool grow = m_tile > m_run[rb] + RESCALE_GAP;
+          const float m_new = grow ? m_tile : m_run[rb];
+          const float alpha = fast_exp2(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+          thr[rb] = (m_new + RESCALE_GAP) / a.c;
+          l_s[rb] *= alpha;
+          l_c[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha;
+          if (lost) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[rb][kb][e] = fast_exp2(fmaf(s[rb][kb][e], a.c, -m_new));
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) s[rb][kb] *= alpha;
+          }
+          ls = row_part(rb);
+        }
+        lsum[rb] = ls;
+      } else {
+        if constexpr (masked) {
+          // key j0 + 8 grp + off is past this row when off > lim
+          const int lim = row_pos[rb] - j0 - 8 * grp;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (32 * (kb >> 1) + 4 * (kb & 1) + e > lim) s[rb][kb][e] = -INFINITY;
+        }
+        const float m0 = max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]);
+        const float m1 = max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]);
+        const float m2 = max3f(s[rb][1][2], s[rb][1][3], s[rb][2][0]);
+        const float m3 = max3f(s[rb][2][1], s[rb][2][2], s[rb][2][3]);
+        const float m4 = max3f(s[rb][3][0], s[rb][3][1], s[rb][3][2]);
+        // this lane's 16 logits of the row: a row grows exactly when one of
+        // its four lanes does, so the cross-lane maximum is only formed on
+        // the (rare) tiles where some lane of the wave grows
+        const float lmax = max2f(max3f(m0, m1, m2), max3f(m3, m4, s[rb][3][3]));
+        if (__builtin_amdgcn_ballot_w64(lmax > thr[rb])) {
+          const float m_tile = row_group_max(lmax) * a.c;
+          const bool grow = m_tile > m_run[rb] + RESCALE_GAP;
+          const float m_new = grow ? m_tile : m_run[rb];
+          const float alpha = fast_exp2(m_run[rb] - m_new);
+          m_run[rb] = m_new;
+          thr[rb] = (m_new + RESCALE_GAP) / a.c;
+          l_s[rb] *= alpha;
+          l_c[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha;
+        }
+        const float neg_m = -m_run[rb];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[rb][kb][e] = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
+        lsum[rb] = row_part(rb);
       }
-      const float m0 = max3f(s[rb][0][0], s[rb][0][1], s[rb][0][2]);
-      const float m1 = max3f(s[rb][0][3], s[rb][1][0], s[rb][1][1]);
-      const float m2 = max3f(s[rb][1][2], s[rb][1][3], s[rb][2][0]);
-      const float m3 = max3f(s[rb][2][1], s[rb][2][2], s[rb][2][3]);
-      const float m4 = max3f(s[rb][3][0], s[rb][3][1], s[rb][3][2]);
-      // this lane's 16 logits of the row: a row grows exactly when one of
-      // its four lanes does, so the cross-lane maximum is only formed on the
-      // (rare) tiles where some lane of the wave grows
-      const float lmax = max2f(max3f(m0, m1, m2), max3f(m3, m4, s[rb][3][3]));
-      if (__builtin_amdgcn_ballot_w64(lmax > thr[rb])) {
-        const float m_tile = row_group_max(lmax) * a.c;
-        const bool grow = m_tile > m_run[rb] + RESCALE_GAP;
-        const float m_new = grow ? m_tile : m_run[rb];
-        const float alpha = fast_exp2(m_run[rb] - m_new);
-        m_run[rb] = m_new;
-        thr[rb] = (m_new + RESCALE_GAP) / a.c;
-        l_s[rb] *= alpha;
-        l_c[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha;
-      }
-      const float neg_m = -m_run[rb];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[rb][kb][e] = fast_exp2(fmaf(s[rb][kb][e], a.c, neg_m));
-      // the row sums are added during this tile's PV product (pv)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -470,7 +543,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
       __syncthreads();                                  // barrier t + 1
       if (t + 1 < n_tiles) loads(t + 1, ST ^ 1);
     }
-    softmax(t, masked_c);
+    softmax(t, masked_c, std::integral_constant<bool, !decltype(masked_c)::value &&
+                                                     !decltype(first_c)::value>{});
   };
   using Open = std::false_type;
   using Diag = std::true_type;
