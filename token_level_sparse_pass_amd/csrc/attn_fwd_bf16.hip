@@ -376,12 +376,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
   // softmax of tile t: row maxima, lazy rescale, P = 2^(s c - m), row sums,
   // P^T operands in bf16
   // this lane's 16 probabilities of row block rb summed in key order
+  // (starting from the first term: the probabilities are never -0, so
+  // 0 + x = x and the sum is the one a zero start gives)
   auto row_part = [&](int rb) __attribute__((always_inline)) {
-    float ls = 0.f;
+    float ls = s[rb][0][0];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ls += s[rb][kb][e];
+      for (int e = 0; e < 4; ++e)
+        if (kb + e > 0) ls += s[rb][kb][e];
     return ls;
   };
   // softmax of tile t: row maxima, lazy rescale, P = 2^(s c - m), row sums,
