@@ -196,6 +196,43 @@ def run_full_case(gpu_lib, case, select="token", block_size=64, top_blocks=16, d
     return inp, o, idx, lse, scores, ref
 
 
+def test_sparse_kernel_runaway_logits(gpu_lib):
+    """Index rows whose later keys lie along one sparse-layer query's
+    direction, with logits that pass that row's running max (from the first
+    32-key tile) by far more than fp32 can hold as a probability, or by less:
+    the many-query sparse kernel must still give the oracle's outputs."""
+    case = small("sp_runaway", "bf16", 1, 1024, 1500, 16, 2, 128, 100, 20, L=3)
+    say("case", case)
+    inp = make_inputs(case, device="cuda")
+    k = inp["k"].clone()
+    qs = inp["q_sparse"]
+    idx = ragged_index_rows(case, seed=11)
+    G = case.h_q // case.h_kv
+    d = case.d
+    # (layer, query, head, position in the row, logit)
+    plants = ((0, 5, 0, 40, 200.0), (2, 20, 9, 70, 120.0), (1, 64, 3, 110, 60.0))
+    for layer, i, h, pos, logit in plants:
+        n = int((idx[0, i] >= 0).sum())
+        if n <= pos:                       # make the row long enough
+            p = case.n_kv - case.n_q + i
+            idx[0, i, :] = -1
+            idx[0, i, :pos + 10] = np.sort(np.random.default_rng(i).choice(p + 1, pos + 10,
+                                                                        replace=False))
+        j = int(idx[0, i, pos])
+        qv = qs[layer, 0, i, h].float()
+        k[0, j, h // G] = (qv / qv.norm() * logit * math.sqrt(d) / qv.norm()).to(k.dtype)
+    out = gpu_lib.sparse_attn(qs, k, inp["v"], torch.from_numpy(idx).cuda(),
+                              top_k=case.top_k, window=case.window)
+    torch.cuda.synchronize()
+    got = as_np(out)
+    rows = sorted({i for _, i, _, _, _ in plants} | set(range(0, 64)))
+    rows = [r for r in rows if (idx[0, r] >= 0).any()]
+    ref = O.sparse_rows(host(qs), host(k), host(inp["v"]), 0, rows, idx[0, rows])
+    err = float(np.abs(got[:, 0, rows] - ref).max())
+    say("max abs err", err)
+    assert err <= TOL["bf16"]
+
+
 def test_full_attention_runaway_logits(gpu_lib):
     """Keys planted along one query's direction, so that their logits pass
     that row's running max (from the first key tile) by far more than fp32
