@@ -398,10 +398,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
     constexpr bool masked = decltype(masked_c)::value;
     constexpr bool spec = decltype(spec_c)::value;
     const int j0 = t * TK;
-    // while one wave of a SIMD pair is in this phase its partner is in its
-    // MFMA phase; raising this wave's issue priority lets its VALU work go
-    // first, since the partner's MFMAs keep the matrix core busy anyway
-    __builtin_amdgcn_s_setprio(2);
+    // (a raised issue priority for this phase, s_setprio, had gained 0.5 %
+    // before the speculative form; with the shorter phase it cost about 1 %)
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       if constexpr (spec) {
@@ -507,7 +505,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void attn_fwd_bf16_kernel(Fwd2Args a) 
           pu[rb][st][4 + e] = (__bf16)s[rb][2 * st + 1][e];
         }
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // one tile step; stage_c = t % 2 (known at compile time in the unrolled
